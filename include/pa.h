@@ -1,0 +1,184 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged-attention library.
+ *
+ * The operation: attention over a KV cache split into fixed-size blocks of B
+ * tokens, reached through a per-request block table that maps logical block
+ * j to a physical block anywhere in a pool (itwiki "vLLM", section
+ * "PagedAttention": "Block table" and "Block-wise attention"; the page states
+ * the block-wise sum is mathematically ordinary attention).  One call serves
+ * a token-budgeted step that mixes one-token decode rows with causal prompt
+ * chunks (techknowgenie "vLLM V1 core refactoring", section "Dynamic Chunked
+ * Prefill").  New K/V reach the cache through a per-token slot mapping, and
+ * the step is described by seq_lens and query_start_loc (llm-wiki "vLLM 0.25
+ * Model Runner V2", sections "Redesign 3" and "Redesign 4").
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked [device] are device pointers on the current HIP device;
+ *    [host] pointers are read during the call only.  The library keeps no
+ *    pointer after returning, allocates no memory, and is re-entrant.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without synchronising.  Inputs must stay valid and
+ *    unmodified until the stream has executed the work; outputs are ready
+ *    when the stream reaches that point.
+ *  - Argument errors are detected before anything is enqueued and returned as
+ *    a pa_status_t; nothing is launched then.  A failed launch returns
+ *    PA_ERR_HIP.  There is no fallback path: an unsupported combination is an
+ *    error, never a slower substitute.
+ *  - The *contents* of metadata arrays are not checked (out-of-range block
+ *    ids, q_len > seq_len or a decreasing query_start_loc are undefined
+ *    behaviour); pa_check_metadata checks them on request.
+ *
+ * Cache layout (the pages give none; this is the library's definition):
+ *    k_cache [num_blocks][num_kv_heads][block_size][head_dim]
+ *    v_cache [num_blocks][num_kv_heads][head_dim][block_size]
+ * i.e. every (block, kv head) tile is one contiguous run; keys are rows of
+ * the K tile and columns of the V tile.  Slot s of the pool is token offset
+ * s % B of physical block s / B.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  PA_FP8_E4M3 = 3 /* OCP E4M3FN: bias 7, max 448, NaN = S.1111.111, no inf */
+} pa_dtype_t;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  PA_ERR_SHAPE = 2,       /* a size is negative/zero where it must not be, or
+                             shapes disagree (e.g. Hq % Hkv != 0)             */
+  PA_ERR_DTYPE = 3,       /* unknown dtype, or a dtype pairing the path lacks  */
+  PA_ERR_UNSUPPORTED = 4, /* block size / head dim / scale outside the path    */
+  PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required           */
+  PA_ERR_HIP = 6,         /* a HIP runtime call or launch failed               */
+  PA_ERR_METADATA = 7     /* pa_check_metadata found an invalid entry          */
+} pa_status_t;
+
+/* Description of a KV cache pool (host struct, read during the call only). */
+typedef struct {
+  int32_t num_blocks;   /* N: physical blocks in the pool                     */
+  int32_t block_size;   /* B: tokens per block, one of 16, 32, 64             */
+  int32_t num_kv_heads; /* Hkv                                                */
+  int32_t head_dim;     /* d: 64 or 128                                       */
+  int32_t kv_dtype;     /* a pa_dtype_t                                       */
+  float k_scale;        /* dequantisation multipliers: value = code * scale.  */
+  float v_scale;        /* Must be 1.0f unless kv_dtype is PA_FP8_E4M3.       */
+} pa_cache_t;
+
+/*
+ * Write new tokens' K and V into their cache slots.
+ *
+ * For each token t in [0, num_tokens) with s = slot_mapping[t] >= 0:
+ *   k_cache[s / B][h][s % B][:] = enc(key[t][h][:])   for every kv head h
+ *   v_cache[s / B][h][:][s % B] = enc(value[t][h][:])
+ * where enc widens the source to fp32 exactly and then stores it as the
+ * cache dtype: identity for fp32, round-to-nearest-even for fp16/bf16, and
+ * for fp8 e4m3(fl32(x / scale)) with a correctly rounded fp32 division,
+ * round-to-nearest-even, finite overflow and infinities saturated to +-448
+ * and NaN kept as NaN.  Slots < 0 are skipped (padding).  Slot values must
+ * be < num_blocks * B and unique among the non-negative entries.
+ *
+ *   key, value   [device] [num_tokens][num_kv_heads][head_dim], src_dtype
+ *                (PA_F32, PA_F16 or PA_BF16), contiguous.
+ *   k_cache, v_cache [device] pools in the layout above, cache->kv_dtype.
+ *   slot_mapping [device] int64 [num_tokens].
+ * num_tokens == 0 is a no-op returning PA_OK.
+ */
+pa_status_t pa_reshape_and_cache(const void* key, const void* value, int32_t src_dtype,
+                                 void* k_cache, void* v_cache, const pa_cache_t* cache,
+                                 const int64_t* slot_mapping, int32_t num_tokens,
+                                 void* stream);
+
+/*
+ * Bytes of device workspace pa_attention needs for these sizes (written to
+ * *bytes [host]).  The same arguments must be passed to pa_attention.
+ */
+pa_status_t pa_attention_workspace_size(const pa_cache_t* cache, int32_t num_q_heads,
+                                        int32_t num_seqs, int32_t num_tokens,
+                                        int32_t max_seq_len, int32_t max_query_len,
+                                        size_t* bytes);
+
+/*
+ * Paged attention of one mixed step.
+ *
+ * Sequence i owns query rows [query_start_loc[i], query_start_loc[i+1]) of q;
+ * q_len_i is their count and seq_lens[i] = L_i counts its cache tokens
+ * including this step's (already written by pa_reshape_and_cache).  Query t
+ * of sequence i sits at position L_i - q_len_i + t and sees the keys at
+ * positions <= its own (causal within a chunk; a decode row sees all L_i).
+ * Cache position p of sequence i is in physical block
+ * block_tables[i * max_blocks_per_seq + p / B], offset p % B.  q head h
+ * reads kv head h / (num_q_heads / num_kv_heads).  Then
+ *   out[t][h][:] = sum_p softmax_p(scale * q[t][h] . k_p) v_p
+ * computed with fp32 accumulation.
+ *
+ *   q        [device] [num_tokens][num_q_heads][head_dim], q_dtype, contiguous.
+ *   out      [device] same shape and dtype as q; every row of a sequence with
+ *            q_len > 0 is written (rounded to nearest even from fp32).
+ *   block_tables [device] int32 [num_seqs][max_blocks_per_seq]; entries past
+ *            a sequence's ceil(L/B) blocks are never read.
+ *   seq_lens [device] int32 [num_seqs]; query_start_loc [device] int32
+ *            [num_seqs + 1], 0 = qsl[0] <= ... <= qsl[num_seqs] = num_tokens.
+ *   max_seq_len, max_query_len: host-side upper bounds of L_i and q_len_i
+ *            (they size the launch; an actual value above them is undefined).
+ *   workspace [device] at least pa_attention_workspace_size bytes, 256-byte
+ *            aligned; its contents on entry do not matter.
+ * dtype pairings: fp32 q with an fp32 cache; fp16 q with an fp16 or fp8
+ * cache; bf16 q with a bf16 or fp8 cache.  Anything else is PA_ERR_DTYPE.
+ * Sequences with q_len = 0 are no-ops.  num_seqs == 0 is a no-op.
+ */
+pa_status_t pa_attention(const void* q, int32_t q_dtype, const void* k_cache,
+                         const void* v_cache, const pa_cache_t* cache,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, const int32_t* query_start_loc,
+                         int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                         int32_t max_seq_len, int32_t max_query_len, float scale,
+                         void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Debug check of metadata contents.  Synchronous: copies the metadata to the
+ * host (on `stream`) and returns PA_ERR_METADATA if any sequence has
+ * q_len < 0, q_len > L, L > max_seq_len, q_len > max_query_len,
+ * ceil(L/B) > max_blocks_per_seq, or a used block id outside [0, num_blocks);
+ * PA_OK otherwise.  When it fails, *bad_seq [host, may be NULL] receives the
+ * first offending sequence (-1 for a query_start_loc that does not start at
+ * 0 or end at num_tokens).
+ */
+pa_status_t pa_check_metadata(const pa_cache_t* cache, const int32_t* block_tables,
+                              int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                              const int32_t* query_start_loc, int32_t num_seqs,
+                              int32_t num_tokens, int32_t max_seq_len, int32_t max_query_len,
+                              int32_t* bad_seq, void* stream);
+
+/*
+ * Measurement hook.  When both are non-NULL, every later pa_attention call
+ * records hipEvent_t `before` on its stream immediately before launching the
+ * attention kernel and `after` immediately after it, so hipEventElapsedTime
+ * gives that one kernel's duration (the work-list and partition-merge
+ * kernels fall outside).  Pass NULL, NULL to turn it off.  This is the
+ * library's only global state; it is meant for timing harnesses and is not
+ * thread-safe.
+ */
+pa_status_t pa_set_attention_events(void* before, void* after);
+
+/* Static text for a status code. */
+const char* pa_status_string(pa_status_t status);
+
+/* Library version, e.g. "0.1.0". */
+const char* pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -28,6 +28,14 @@ def encode_tokens(src: np.ndarray, src_dtype: str, kv_dtype: str, scale: float) 
     The source is widened to float32 exactly, then encoded: identity for an
     fp32 cache, RNE for fp16/bf16, and ``e4m3(fl32(x / scale))`` for fp8.
     """
+    if src_dtype == kv_dtype and kv_dtype in ("bf16", "f16"):
+        # a value already in the cache format rounds to itself; only NaN
+        # payloads change, to the canonical quiet NaN with the sign kept
+        bits = np.asarray(src)
+        bits = bits.view(np.uint16) if bits.dtype != np.uint16 else bits
+        mag = bits & np.uint16(0x7FFF)
+        inf, qnan = (0x7F80, 0x7FC0) if kv_dtype == "bf16" else (0x7C00, 0x7E00)
+        return np.where(mag > inf, (bits & np.uint16(0x8000)) | np.uint16(qnan), bits).astype(np.uint16)
     x = codecs.to_f32(src, src_dtype)
     return codecs.encode(x, kv_dtype, scale)
 

@@ -1,0 +1,242 @@
+"""MI355X (gfx950) paged attention -- Python face of ``libpa.so``.
+
+A thin ``ctypes`` binding over the C ABI in ``include/pa.h``: it checks
+tensor shapes and dtypes, passes raw device pointers, sizes and the current
+torch stream, and turns status codes into exceptions.  Every step of the
+computation runs in the library's HIP kernels; torch only provides device
+memory and the stream.  If the library is not built this module raises on
+first use -- there is no other path.
+
+    k_cache: [num_blocks, num_kv_heads, block_size, head_dim]
+    v_cache: [num_blocks, num_kv_heads, head_dim, block_size]
+    dtypes : torch.float32 / float16 / bfloat16, or torch.float8_e4m3fn
+             (uint8 storage is accepted as fp8 codes).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "PagedAttentionError", "library", "library_path", "reshape_and_cache", "attention",
+    "attention_workspace_size", "check_metadata", "set_attention_events", "PA_F32", "PA_F16", "PA_BF16", "PA_FP8_E4M3",
+]
+
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
+PA_OK = 0
+PA_ERR_METADATA = 7
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "_lib", "libpa.so")
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load ``libpa.so`` (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise ImportError(f"{library_path} is missing: build it with "
+                          "`python -m paged_kv_cache_141_amd.build`")
+    try:
+        # torch ships its own HIP runtime with the same soname; loading torch
+        # first makes the library bind to that one runtime (one set of streams)
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(library_path)
+    P, I32, I64, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    CP = ctypes.POINTER(_Cache)
+    sig = {
+        "pa_reshape_and_cache": [P, P, I32, P, P, CP, P, I32, P],
+        "pa_attention_workspace_size": [CP, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
+        "pa_attention": [P, I32, P, P, CP, P, I32, P, P, I32, I32, I32, I32, I32, F, P, P, SZ, P],
+        "pa_check_metadata": [CP, P, I32, P, P, I32, I32, I32, I32, ctypes.POINTER(I32), P],
+        "pa_set_attention_events": [P, P],
+        "pa_status_string": [I32],
+        "pa_version": [],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name in ("pa_status_string", "pa_version") else ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return library().pa_status_string(status).decode()
+
+
+def version() -> str:
+    return library().pa_version().decode()
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
+         torch.uint8: PA_FP8_E4M3}
+    if hasattr(torch, "float8_e4m3fn"):
+        m[torch.float8_e4m3fn] = PA_FP8_E4M3
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def cache_spec(k_cache, v_cache, k_scale: float = 1.0, v_scale: float = 1.0) -> _Cache:
+    if k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("caches must be 4-D")
+    N, H, B, d = k_cache.shape
+    if tuple(v_cache.shape) != (N, H, d, B):
+        raise ValueError(f"v_cache must be [N, Hkv, d, B] = {(N, H, d, B)}, got {tuple(v_cache.shape)}")
+    if k_cache.dtype != v_cache.dtype:
+        raise TypeError("k_cache and v_cache dtypes differ")
+    return _Cache(N, B, H, d, _dtype_code(k_cache), float(k_scale), float(v_scale))
+
+
+def _check(status: int, where: str):
+    if status != PA_OK:
+        raise PagedAttentionError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, k_scale: float = 1.0,
+                      v_scale: float = 1.0, stream=None) -> None:
+    """Scatter key/value ``[T, Hkv, d]`` into their cache slots (``pa_reshape_and_cache``)."""
+    torch = _torch()
+    spec = cache_spec(k_cache, v_cache, k_scale, v_scale)
+    if key.shape != value.shape or key.dtype != value.dtype:
+        raise ValueError("key and value must match in shape and dtype")
+    T = key.shape[0]
+    if key.dim() != 3 or key.shape[1] != spec.num_kv_heads or key.shape[2] != spec.head_dim:
+        raise ValueError(f"key must be [T, {spec.num_kv_heads}, {spec.head_dim}]")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must be int64 [T]")
+    if T == 0:
+        return
+    st = library().pa_reshape_and_cache(
+        _dev(key, "key"), _dev(value, "value"), _dtype_code(key), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), ctypes.byref(spec), _dev(slot_mapping, "slot_mapping"), T,
+        _stream(stream))
+    _check(st, "pa_reshape_and_cache")
+
+
+def attention_workspace_size(k_cache, v_cache, num_q_heads: int, num_seqs: int, num_tokens: int,
+                             max_seq_len: int, max_query_len: int) -> int:
+    spec = cache_spec(k_cache, v_cache)
+    out = ctypes.c_size_t(0)
+    st = library().pa_attention_workspace_size(ctypes.byref(spec), num_q_heads, num_seqs,
+                                               num_tokens, max_seq_len, max_query_len,
+                                               ctypes.byref(out))
+    _check(st, "pa_attention_workspace_size")
+    return int(out.value)
+
+
+def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale: float, *,
+              max_seq_len: Optional[int] = None, max_query_len: Optional[int] = None,
+              out=None, workspace=None, k_scale: float = 1.0, v_scale: float = 1.0,
+              stream=None):
+    """Paged attention of one mixed step (``pa_attention``); returns ``out``.
+
+    max_seq_len / max_query_len are host-side upper bounds; if omitted they
+    are read from the device tensors, which synchronises the stream.
+    """
+    torch = _torch()
+    spec = cache_spec(k_cache, v_cache, k_scale, v_scale)
+    if q.dim() != 3 or q.shape[2] != spec.head_dim:
+        raise ValueError(f"q must be [T, Hq, {spec.head_dim}]")
+    T, Hq, _ = q.shape
+    S = seq_lens.numel()
+    for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens),
+                    ("query_start_loc", query_start_loc)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if query_start_loc.numel() != S + 1 or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("metadata shapes disagree")
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if S else 0
+    if max_query_len is None:
+        max_query_len = int((query_start_loc[1:] - query_start_loc[:-1]).max().item()) if S else 0
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    lib = library()
+    need = ctypes.c_size_t(0)
+    _check(lib.pa_attention_workspace_size(ctypes.byref(spec), Hq, S, T, max_seq_len,
+                                           max_query_len, ctypes.byref(need)),
+           "pa_attention_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(max(int(need.value), 256), dtype=torch.uint8, device=q.device)
+    st = lib.pa_attention(
+        _dev(q, "q"), _dtype_code(q), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        ctypes.byref(spec), _dev(block_tables, "block_tables"), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens"), _dev(query_start_loc, "query_start_loc"), S, T, Hq,
+        int(max_seq_len), int(max_query_len), float(scale), _dev(out, "out"),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "pa_attention")
+    return out
+
+
+def set_attention_events(before, after) -> None:
+    """Bracket the attention kernel with two hipEvent_t handles (ints), or None, None."""
+    _check(library().pa_set_attention_events(before, after), "pa_set_attention_events")
+
+
+def check_metadata(k_cache, v_cache, block_tables, seq_lens, query_start_loc, num_tokens: int,
+                   max_seq_len: int, max_query_len: int, stream=None):
+    """Synchronous debug check of metadata contents; returns (ok, bad_seq)."""
+    spec = cache_spec(k_cache, v_cache)
+    bad = ctypes.c_int32(-1)
+    st = library().pa_check_metadata(
+        ctypes.byref(spec), _dev(block_tables, "block_tables"), block_tables.shape[1],
+        _dev(seq_lens, "seq_lens"), _dev(query_start_loc, "query_start_loc"), seq_lens.numel(),
+        num_tokens, max_seq_len, max_query_len, ctypes.byref(bad), _stream(stream))
+    if st == PA_ERR_METADATA:
+        return False, int(bad.value)
+    _check(st, "pa_check_metadata")
+    return True, -1

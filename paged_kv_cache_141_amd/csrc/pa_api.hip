@@ -1,0 +1,215 @@
+// pa_api.hip -- the C ABI declared in include/pa.h: argument validation,
+// workspace sizing and kernel dispatch.  Allocates nothing; the only state is
+// the optional timing-event pair of pa_set_attention_events.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+using pa::ceil_div;
+
+// The measurement hook of pa_set_attention_events (the library's only state).
+hipEvent_t g_before = nullptr;
+hipEvent_t g_after = nullptr;
+
+bool dtype_known(int32_t d) { return d >= PA_F32 && d <= PA_FP8_E4M3; }
+
+pa_status_t check_cache(const pa_cache_t* c) {
+  if (!c) return PA_ERR_NULL;
+  if (!dtype_known(c->kv_dtype)) return PA_ERR_DTYPE;
+  if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return PA_ERR_SHAPE;
+  if (c->block_size != 16 && c->block_size != 32 && c->block_size != 64) return PA_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (c->kv_dtype == PA_FP8_E4M3) {
+    if (!(c->k_scale > 0.f) || !(c->v_scale > 0.f) || !isfinite(c->k_scale) || !isfinite(c->v_scale))
+      return PA_ERR_UNSUPPORTED;
+  } else if (c->k_scale != 1.f || c->v_scale != 1.f) {
+    return PA_ERR_UNSUPPORTED;
+  }
+  return PA_OK;
+}
+
+// The (q dtype, cache dtype) pairs the attention kernels compute: the MFMA
+// operands share one type, fp8 codes widen exactly to the query's type.
+bool pairing_ok(int32_t q, int32_t kv) {
+  return (q == PA_F32 && kv == PA_F32) || (q == PA_F16 && (kv == PA_F16 || kv == PA_FP8_E4M3)) ||
+         (q == PA_BF16 && (kv == PA_BF16 || kv == PA_FP8_E4M3));
+}
+
+pa_status_t check_attention_sizes(const pa_cache_t* c, int32_t num_q_heads, int32_t num_seqs,
+                                  int32_t num_tokens, int32_t max_seq_len, int32_t max_query_len) {
+  pa_status_t st = check_cache(c);
+  if (st != PA_OK) return st;
+  if (num_q_heads <= 0 || num_seqs < 0 || num_tokens < 0 || max_seq_len < 0 || max_query_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_q_heads % c->num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (max_query_len > max_seq_len) return PA_ERR_SHAPE;
+  const int64_t group = num_q_heads / c->num_kv_heads;
+  // work items pack (tile, partition) into 16 bits each
+  if (ceil_div(static_cast<int64_t>(max_query_len) * group, pa::kTileRows) > 0xFFFF) return PA_ERR_UNSUPPORTED;
+  if (ceil_div(max_seq_len, pa::kPartition) > 0xFFFF) return PA_ERR_UNSUPPORTED;
+  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, c->num_kv_heads,
+                                                     c->head_dim, max_seq_len);
+  if (w.max_items > 0x7FFFFFFF / 64) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_version(void) { return "0.1.0"; }
+
+const char* pa_status_string(pa_status_t s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "inconsistent or invalid sizes";
+    case PA_ERR_DTYPE: return "unknown dtype or unsupported dtype pairing";
+    case PA_ERR_UNSUPPORTED: return "block size, head dim, scale or size outside the supported path";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_METADATA: return "invalid metadata contents";
+  }
+  return "unknown status";
+}
+
+pa_status_t pa_reshape_and_cache(const void* key, const void* value, int32_t src_dtype, void* k_cache,
+                                 void* v_cache, const pa_cache_t* cache, const int64_t* slot_mapping,
+                                 int32_t num_tokens, void* stream) {
+  pa_status_t st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (src_dtype != PA_F32 && src_dtype != PA_F16 && src_dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+  pa::CacheWriteArgs a{};
+  a.key = key;
+  a.value = value;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.slots = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.block_size = cache->block_size;
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  const hipError_t e = pa::launch_reshape_and_cache(src_dtype, cache->kv_dtype, a,
+                                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status_t pa_attention_workspace_size(const pa_cache_t* cache, int32_t num_q_heads, int32_t num_seqs,
+                                        int32_t num_tokens, int32_t max_seq_len, int32_t max_query_len,
+                                        size_t* bytes) {
+  if (!bytes) return PA_ERR_NULL;
+  pa_status_t st = check_attention_sizes(cache, num_q_heads, num_seqs, num_tokens, max_seq_len, max_query_len);
+  if (st != PA_OK) return st;
+  *bytes = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                                max_seq_len)
+               .total;
+  return PA_OK;
+}
+
+pa_status_t pa_attention(const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
+                         const pa_cache_t* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                         int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
+                         int32_t max_query_len, float scale, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  pa_status_t st = check_attention_sizes(cache, num_q_heads, num_seqs, num_tokens, max_seq_len, max_query_len);
+  if (st != PA_OK) return st;
+  if (!dtype_known(q_dtype)) return PA_ERR_DTYPE;
+  if (!pairing_ok(q_dtype, cache->kv_dtype)) return PA_ERR_DTYPE;
+  if (!isfinite(scale)) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !out)
+    return PA_ERR_NULL;
+  if (max_blocks_per_seq <= 0 || static_cast<int64_t>(max_blocks_per_seq) * cache->block_size <
+                                     static_cast<int64_t>(max_seq_len))
+    return PA_ERR_SHAPE;
+  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, cache->num_kv_heads,
+                                                     cache->head_dim, max_seq_len);
+  if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return PA_ERR_WORKSPACE;
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  pa::AttnArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.qsl = query_start_loc;
+  a.out = out;
+  a.header = reinterpret_cast<int32_t*>(ws + w.header);
+  a.items = reinterpret_cast<int32_t*>(ws + w.items);
+  a.part_m = reinterpret_cast<float*>(ws + w.part_m);
+  a.part_l = reinterpret_cast<float*>(ws + w.part_l);
+  a.part_acc = reinterpret_cast<float*>(ws + w.part_acc);
+  a.max_items = w.max_items;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.group = num_q_heads / cache->num_kv_heads;
+  a.max_parts = w.max_parts;
+  a.score_scale = scale * cache->k_scale * 1.4426950408889634f;
+  a.v_scale = cache->v_scale;
+  const hipError_t e = pa::launch_attention(q_dtype, cache->kv_dtype, cache->head_dim, cache->block_size, a,
+                                            static_cast<hipStream_t>(stream), g_before, g_after);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status_t pa_set_attention_events(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr)) return PA_ERR_NULL;
+  g_before = static_cast<hipEvent_t>(before);
+  g_after = static_cast<hipEvent_t>(after);
+  return PA_OK;
+}
+
+pa_status_t pa_check_metadata(const pa_cache_t* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                              int32_t num_tokens, int32_t max_seq_len, int32_t max_query_len, int32_t* bad_seq,
+                              void* stream) {
+  pa_status_t st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_tokens < 0 || max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (bad_seq) *bad_seq = -1;
+  if (num_seqs == 0) return num_tokens == 0 ? PA_OK : PA_ERR_METADATA;
+  if (!block_tables || !seq_lens || !query_start_loc) return PA_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<int32_t> lens(num_seqs), qsl(num_seqs + 1),
+      bt(static_cast<size_t>(num_seqs) * max_blocks_per_seq);
+  if (hipMemcpyAsync(lens.data(), seq_lens, lens.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipMemcpyAsync(qsl.data(), query_start_loc, qsl.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipMemcpyAsync(bt.data(), block_tables, bt.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return PA_ERR_HIP;
+  if (qsl[0] != 0 || qsl[num_seqs] != num_tokens) return PA_ERR_METADATA;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int32_t ql = qsl[i + 1] - qsl[i];
+    const int32_t L = lens[i];
+    bool ok = ql >= 0 && ql <= L && L <= max_seq_len && ql <= max_query_len;
+    const int64_t nb = ceil_div(L, cache->block_size);
+    ok = ok && nb <= max_blocks_per_seq;
+    for (int64_t j = 0; ok && j < nb; ++j) {
+      const int32_t p = bt[static_cast<size_t>(i) * max_blocks_per_seq + j];
+      ok = p >= 0 && p < cache->num_blocks;
+    }
+    if (!ok) {
+      if (bad_seq) *bad_seq = i;
+      return PA_ERR_METADATA;
+    }
+  }
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+"""The C-ABI library: loads, exports every declared symbol, validates
+arguments before touching the GPU (CPU only; no compute calls)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_141_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:pa_status_t|const char\*)\s+(pa_\w+)\s*\(", text, re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = pa.library()
+    names = declared_symbols()
+    assert {"pa_reshape_and_cache", "pa_attention", "pa_attention_workspace_size",
+            "pa_check_metadata", "pa_status_string", "pa_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(8):
+        assert pa.status_string(s)
+    assert pa.status_string(99) == "unknown status"
+
+
+def _cache(**kw):
+    c = dict(num_blocks=16, block_size=16, num_kv_heads=2, head_dim=64, kv_dtype=pa.PA_BF16,
+             k_scale=1.0, v_scale=1.0)
+    c.update(kw)
+    return pa._Cache(c["num_blocks"], c["block_size"], c["num_kv_heads"], c["head_dim"],
+                     c["kv_dtype"], c["k_scale"], c["v_scale"])
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def _attn(cache, q_dtype=pa.PA_BF16, q=FAKE, ws=FAKE, ws_bytes=1 << 40, Hq=4, S=2, T=2,
+          max_seq=40, max_q=1, mbps=3, out=FAKE, scale=0.125):
+    lib = pa.library()
+    return lib.pa_attention(q, q_dtype, FAKE, FAKE, ctypes.byref(cache), FAKE, mbps, FAKE, FAKE,
+                            S, T, Hq, max_seq, max_q, scale, out, ws, ws_bytes, None)
+
+
+def test_attention_argument_errors():
+    assert _attn(_cache(block_size=8)) == 4                       # PA_ERR_UNSUPPORTED
+    assert _attn(_cache(head_dim=96)) == 4
+    assert _attn(_cache(kv_dtype=9)) == 3                         # PA_ERR_DTYPE
+    assert _attn(_cache(), q_dtype=pa.PA_F32) == 3                # bf16 cache with fp32 q
+    assert _attn(_cache(kv_dtype=pa.PA_FP8_E4M3, k_scale=0.5), q_dtype=pa.PA_F32) == 3
+    assert _attn(_cache(), Hq=3) == 2                             # Hq % Hkv != 0
+    assert _attn(_cache(k_scale=2.0)) == 4                        # scale on a non-fp8 cache
+    assert _attn(_cache(kv_dtype=pa.PA_FP8_E4M3, k_scale=0.0)) == 4
+    assert _attn(_cache(), q=ctypes.c_void_p(0)) == 1             # PA_ERR_NULL
+    assert _attn(_cache(), out=ctypes.c_void_p(0)) == 1
+    assert _attn(_cache(), ws=ctypes.c_void_p(0)) == 5            # PA_ERR_WORKSPACE
+    assert _attn(_cache(), ws_bytes=16) == 5
+    assert _attn(_cache(), ws=ctypes.c_void_p(0x1010)) == 5       # misaligned
+    assert _attn(_cache(), mbps=2) == 2                           # 2 blocks < max_seq_len 40
+    assert _attn(_cache(), max_q=50) == 2                         # q_len bound above L bound
+    assert _attn(_cache(), S=0, T=0) == 0                         # empty step: no-op
+    assert _attn(_cache(), scale=float("nan")) == 4
+
+
+def test_reshape_and_cache_argument_errors():
+    lib = pa.library()
+    c = _cache()
+    assert lib.pa_reshape_and_cache(FAKE, FAKE, 7, FAKE, FAKE, ctypes.byref(c), FAKE, 4, None) == 3
+    assert lib.pa_reshape_and_cache(FAKE, FAKE, pa.PA_FP8_E4M3, FAKE, FAKE, ctypes.byref(c), FAKE,
+                                    4, None) == 3       # fp8 is not a source dtype
+    assert lib.pa_reshape_and_cache(None, FAKE, pa.PA_BF16, FAKE, FAKE, ctypes.byref(c), FAKE, 4,
+                                    None) == 1
+    assert lib.pa_reshape_and_cache(FAKE, FAKE, pa.PA_BF16, FAKE, FAKE, ctypes.byref(c), FAKE, -1,
+                                    None) == 2
+    assert lib.pa_reshape_and_cache(None, None, pa.PA_BF16, None, None, ctypes.byref(c), None, 0,
+                                    None) == 0          # nothing to write
+    assert lib.pa_reshape_and_cache(FAKE, FAKE, pa.PA_BF16, FAKE, FAKE, None, FAKE, 4, None) == 1
+
+
+def test_workspace_size_grows_with_partitions():
+    lib = pa.library()
+    c = _cache(head_dim=128, num_kv_heads=8)
+    sizes = []
+    for L in (100, 600, 5000):
+        b = ctypes.c_size_t(0)
+        assert lib.pa_attention_workspace_size(ctypes.byref(c), 32, 4, 4, L, 1, ctypes.byref(b)) == 0
+        sizes.append(b.value)
+    assert sizes[0] < sizes[1] < sizes[2]
+    assert lib.pa_attention_workspace_size(ctypes.byref(c), 32, 4, 4, 100, 1, None) == 1
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    k = torch.zeros(4, 2, 16, 64, dtype=torch.bfloat16)
+    v = torch.zeros(4, 2, 64, 16, dtype=torch.bfloat16)
+    key = torch.zeros(1, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pa.reshape_and_cache(key, key, k, v, torch.zeros(1, dtype=torch.int64))
+    with pytest.raises(ValueError):
+        pa.cache_spec(k, k)      # V must be [N, H, d, B]

@@ -1,0 +1,258 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Cache writes must match the oracle byte for byte; attention must be within
+max-abs 2e-3 (fp32/fp16 KV), 1e-2 (bf16 KV) or 4e-2 (fp8 KV) of the oracle,
+with no NaN.  Invariants (placement permutation, shared vs private prefix
+blocks, run-to-run) must hold bit-exactly on the GPU.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from oracle import codecs
+from workloads import device as wd
+from workloads.generate import build, random_mixed
+
+torch = pytest.importorskip("torch")
+import paged_kv_cache_141_amd as pa  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 2e-3, "f16": 2e-3, "bf16": 1e-2, "fp8_e4m3": 4e-2}
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def oracle_out(w, seqs=None):
+    kp, vp = oracle.cache.fill_pools(w, seqs)
+    return oracle.attention.paged_attention(
+        w.q_values(), w.q_dtype, kp, vp, w.kv_dtype, w.block_tables, w.seq_lens,
+        w.query_start_loc, w.block_size, w.scale, w.k_scale, w.v_scale, seqs=seqs)
+
+
+def gpu_out(step):
+    out = step.attend()
+    torch.cuda.synchronize()
+    return codecs.decode(wd.to_host_bits(out), step.w.q_dtype)
+
+
+def rows_of(w, seqs):
+    qsl = w.query_start_loc
+    return np.concatenate([np.arange(qsl[i], qsl[i + 1]) for i in seqs]) if len(seqs) else \
+        np.zeros(0, dtype=np.int64)
+
+
+def assert_close(w, got, ref, seqs=None, label=""):
+    rows = rows_of(w, range(w.num_seqs) if seqs is None else seqs)
+    g, r = got[rows], ref[rows]
+    assert not np.isnan(g).any(), f"{label}: NaN in GPU output"
+    err = np.abs(g - r).max() if g.size else 0.0
+    say(f"{label}: max-abs err {err:.3e} (tol {TOL[w.kv_dtype]:.0e}) over {g.size} values")
+    assert err <= TOL[w.kv_dtype], f"{label}: max-abs error {err} > {TOL[w.kv_dtype]}"
+
+
+# ------------------------------------------------------------------ cache write
+
+SPECIAL_F32 = np.array([0.0, -0.0, 1.0, -1.5, 3.0e38, -3.4e38, np.inf, -np.inf, np.nan, 1e-40,
+                        -1e-45, 6e-8, 65504.0, 65520.0, 70000.0, 448.0, 464.0, 480.0, -1e6,
+                        1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -11, 2 ** -10, 3 * 2 ** -10,
+                        2 ** -7 * 1.0625, 0.0009765625, 5.9604645e-08, 2.9802322e-08],
+                       dtype=np.float32)
+
+
+def _src_values(shape, src, seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(shape) * 4).astype(np.float32)
+    flat = x.reshape(-1)
+    flat[:SPECIAL_F32.size] = SPECIAL_F32
+    flat[-SPECIAL_F32.size:] = SPECIAL_F32[::-1] * np.float32(0.37)
+    if src == "f32":
+        return x
+    if src == "f16":
+        with np.errstate(over="ignore"):
+            return x.astype(np.float16)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)        # bf16 bits
+
+
+@pytest.mark.parametrize("src,kv,B,d,scale", [
+    ("f32", "f32", 16, 64, 1.0), ("bf16", "bf16", 16, 128, 1.0), ("f16", "f16", 32, 64, 1.0),
+    ("f32", "bf16", 16, 128, 1.0), ("f32", "f16", 64, 128, 1.0), ("bf16", "f16", 16, 64, 1.0),
+    ("bf16", "fp8_e4m3", 16, 128, 2.0 ** -5), ("bf16", "fp8_e4m3", 64, 128, 0.0123),
+    ("f32", "fp8_e4m3", 32, 64, 0.37), ("f16", "fp8_e4m3", 16, 64, 1.0)])
+def test_cache_write_bit_exact(src, kv, B, d, scale):
+    say(f"cache write {src}->{kv} B={B} d={d} scale={scale}")
+    H, T, N = 3, 77, 24
+    w = build("cw", 5, [T], [T], num_q_heads=H, num_kv_heads=H, head_dim=d, block_size=B,
+              kv_dtype=kv, src_dtype=src, q_dtype="bf16" if kv != "f32" else "f32",
+              k_scale=scale if kv == "fp8_e4m3" else 1.0, v_scale=scale / 3 if kv == "fp8_e4m3" else 1.0,
+              num_blocks=N)
+    key = _src_values((T, H, d), src, 1)
+    val = _src_values((T, H, d), src, 2)
+    rng = np.random.default_rng(3)
+    slots = rng.permutation(N * B)[:T].astype(np.int64)
+    slots[::7] = -1                                     # padding tokens are skipped
+    kp, vp = w.initial_pool()
+    oracle.cache.reshape_and_cache(kp, vp, key, val, src, kv, slots, B, w.k_scale, w.v_scale)
+    kc, vc = wd.poisoned_pool(w, "cuda")
+    pa.reshape_and_cache(wd.to_device(key, src, "cuda"), wd.to_device(val, src, "cuda"), kc, vc,
+                         torch.from_numpy(slots).cuda(), w.k_scale, w.v_scale)
+    torch.cuda.synchronize()
+    gk, gv = wd.to_host_bits(kc), wd.to_host_bits(vc)
+    bad_k = np.argwhere(gk != kp)
+    bad_v = np.argwhere(gv != vp)
+    assert bad_k.size == 0, f"K differs at {bad_k[:5].tolist()}: gpu {gk[tuple(bad_k[0])]:#x} oracle {kp[tuple(bad_k[0])]:#x}"
+    assert bad_v.size == 0, f"V differs at {bad_v[:5].tolist()}"
+
+
+# ------------------------------------------------------------------ attention, small
+
+SMALL = [
+    # kv, q, B, d, Hq, Hkv, chunks
+    ("f32", "f32", 16, 64, 2, 2, []),
+    ("f32", "f32", 32, 128, 8, 2, [(0, 40), (70, 33)]),
+    ("bf16", "bf16", 16, 128, 32, 8, [(0, 24), (100, 50)]),
+    ("bf16", "bf16", 32, 64, 4, 4, [(0, 64), (33, 17)]),
+    ("bf16", "bf16", 64, 128, 16, 2, [(5, 30)]),
+    ("f16", "f16", 16, 128, 8, 8, [(0, 21)]),
+    ("f16", "f16", 64, 64, 6, 2, [(12, 31)]),                 # G = 3
+    ("fp8_e4m3", "bf16", 16, 128, 32, 8, [(0, 40)]),
+    ("fp8_e4m3", "bf16", 32, 128, 16, 1, [(9, 9)]),           # G = 16
+    ("fp8_e4m3", "f16", 64, 64, 8, 4, [(0, 3), (200, 20)]),
+]
+
+
+@pytest.mark.parametrize("kv,q,B,d,Hq,Hkv,chunks", SMALL)
+def test_attention_small(kv, q, B, d, Hq, Hkv, chunks):
+    label = f"small kv={kv} q={q} B={B} d={d} Hq={Hq} Hkv={Hkv} chunks={chunks}"
+    say(label)
+    fp8 = kv == "fp8_e4m3"
+    w = random_mixed(17, num_decode=9, chunk_specs=chunks, max_decode_len=1400, num_q_heads=Hq,
+                     num_kv_heads=Hkv, head_dim=d, block_size=B, kv_dtype=kv, q_dtype=q,
+                     k_scale=2.0 ** -5 if fp8 else 1.0, v_scale=1.5 * 2.0 ** -5 if fp8 else 1.0)
+    step = wd.stage(w)
+    assert_close(w, gpu_out(step), oracle_out(w), label=label)
+
+
+def test_tiny_decode():
+    w = workloads.make("tiny_decode")
+    say("tiny_decode", w.summary())
+    step = wd.stage(w)
+    assert_close(w, gpu_out(step), oracle_out(w), label="tiny_decode")
+
+
+def test_edge_lengths():
+    # L = 1, lengths at block/step/partition boundaries, a q_len = 0 sequence,
+    # a chunk that is the whole prompt, and a length past one partition.
+    lens = [1, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1024, 1025, 7, 300]
+    qlens = [1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 0, 300]
+    for kv, q, B in (("bf16", "bf16", 16), ("fp8_e4m3", "bf16", 64), ("f32", "f32", 32)):
+        sc = 0.05 if kv == "fp8_e4m3" else 1.0
+        w = build("edge", 23, lens, qlens, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                  block_size=B, kv_dtype=kv, q_dtype=q, k_scale=sc, v_scale=sc)
+        say("edge", kv, B)
+        step = wd.stage(w)
+        assert_close(w, gpu_out(step), oracle_out(w), label=f"edge {kv} B={B}")
+
+
+# ------------------------------------------------------------------ invariants
+
+def test_placement_permutation_bit_exact():
+    a = wd.stage(workloads.make("llama7b_decode", num_seqs=24))
+    b = wd.stage(workloads.make("llama7b_decode", num_seqs=24, placement="identity"))
+    oa, ob = wd.to_host_bits(a.attend()), wd.to_host_bits(b.attend())
+    assert np.array_equal(oa, ob)
+
+
+def test_shared_prefix_equals_private_bit_exact():
+    s = wd.stage(workloads.make("fp8_shared_prefix", num_seqs=8))
+    p = wd.stage(workloads.make("fp8_shared_prefix", num_seqs=8, placement="private"))
+    assert np.array_equal(wd.to_host_bits(s.attend()), wd.to_host_bits(p.attend()))
+
+
+def test_deterministic_run_to_run():
+    st = wd.stage(workloads.make("gqa_long_decode", num_seqs=6))
+    first = wd.to_host_bits(st.attend()).copy()
+    for _ in range(3):
+        assert np.array_equal(first, wd.to_host_bits(st.attend()))
+
+
+def test_metadata_checker():
+    w = workloads.make("tiny_decode")
+    st = wd.stage(w)
+    ok, bad = pa.check_metadata(st.k_cache, st.v_cache, st.block_tables, st.seq_lens,
+                                st.query_start_loc, w.num_tokens, w.max_seq_len, w.max_query_len)
+    assert ok and bad == -1
+    bt = st.block_tables.clone()
+    bt[2, 0] = w.num_blocks
+    ok, bad = pa.check_metadata(st.k_cache, st.v_cache, bt, st.seq_lens, st.query_start_loc,
+                                w.num_tokens, w.max_seq_len, w.max_query_len)
+    assert not ok and bad == 2
+    lens = st.seq_lens.clone()
+    lens[1] = 0                                   # q_len 1 > L 0
+    ok, bad = pa.check_metadata(st.k_cache, st.v_cache, st.block_tables, lens, st.query_start_loc,
+                                w.num_tokens, w.max_seq_len, w.max_query_len)
+    assert not ok and bad == 1
+
+
+# ------------------------------------------------------------------ full sizes, sampled
+
+def _sample(w, k, seed=0, must=()):
+    rng = np.random.default_rng(seed)
+    pick = set(must) | set(rng.choice(w.num_seqs, size=min(k, w.num_seqs), replace=False).tolist())
+    return sorted(pick)
+
+
+def test_full_llama7b_decode_sampled():
+    w = workloads.make("llama7b_decode")
+    say("full llama7b_decode: staging", w.summary())
+    step = wd.stage(w)
+    got = gpu_out(step)
+    seqs = _sample(w, 16, must=[int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens))])
+    assert_close(w, got, oracle_out(w, seqs), seqs, label="llama7b_decode sampled")
+    assert not np.isnan(got).any()
+
+
+def test_full_gqa_long_decode_sampled():
+    w = workloads.make("gqa_long_decode")
+    say("full gqa_long_decode: staging", w.summary())
+    step = wd.stage(w)
+    got = gpu_out(step)
+    seqs = _sample(w, 6, must=[int(np.argmax(w.seq_lens))])
+    assert_close(w, got, oracle_out(w, seqs), seqs, label="gqa_long_decode sampled")
+    assert not np.isnan(got).any()
+
+
+def test_full_mixed_chunked_prefill_sampled():
+    w = workloads.make("mixed_chunked_prefill")
+    say("full mixed_chunked_prefill: staging", w.summary())
+    step = wd.stage(w, write_new=False)
+    out = step.step()                         # cache write of all new tokens + attention
+    torch.cuda.synchronize()
+    got = codecs.decode(wd.to_host_bits(out), w.q_dtype)
+    # the step's cache write, byte for byte, at every new slot
+    kbits, vbits = wd.to_host_bits(step.k_cache), wd.to_host_bits(step.v_cache)
+    nk, nv, ns = w.new_token_batch()
+    B = w.block_size
+    blk, off = ns // B, ns % B
+    assert np.array_equal(kbits[blk, :, off, :], nk)
+    assert np.array_equal(vbits[blk, :, :, off], nv)
+    seqs = _sample(w, 6, must=[256, 257, 259])
+    assert_close(w, got, oracle_out(w, seqs), seqs, label="mixed sampled (decode + chunks)")
+    assert not np.isnan(got).any()
+
+
+@pytest.mark.parametrize("B", [16, 32, 64])
+def test_full_fp8_shared_prefix_sampled(B):
+    w = workloads.make("fp8_shared_prefix", block_size=B)
+    say(f"full fp8_shared_prefix B={B}: staging", w.summary())
+    step = wd.stage(w)
+    got = gpu_out(step)
+    seqs = _sample(w, 6, seed=B)
+    assert_close(w, got, oracle_out(w, seqs), seqs, label=f"fp8 shared prefix B={B} sampled")
+    assert not np.isnan(got).any()

@@ -293,3 +293,14 @@ def test_cache_write_skips_negative_slots():
     assert np.all(kp[blk, 0, 0::2, :] == w.poison())
     assert np.array_equal(kp[blk, 0, 1:8:2, :], k[1::2, 0, :])
     assert np.array_equal(vp[blk, 0, :, 1:8:2], v[1::2, 0, :].T)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_same_format_write_equals_generic_rounding(dt):
+    # the same-format shortcut must agree with widening to fp32 and rounding back
+    rng = np.random.default_rng(8)
+    bits = rng.integers(0, 1 << 16, size=200_000, dtype=np.uint32).astype(np.uint16)
+    src = bits if dt == "bf16" else bits.view(np.float16)
+    short = C.encode_tokens(src, dt, dt, 1.0)
+    generic = codecs.encode(codecs.to_f32(src, dt), dt)
+    assert np.array_equal(short, generic)

@@ -1,0 +1,158 @@
+"""Stage a workload in device memory (torch tensors) for the HIP path.
+
+The pool starts filled with the poison pattern; every cached token is then
+written through the library's own cache-write entry point, prior context
+first (setup) and this step's tokens on demand (``write_new``), as a serving
+engine's earlier steps would have done.  Nothing here computes attention or
+encodes values.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from .generate import Workload, poison_pattern
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def torch_dtype(dtype: str):
+    torch = _torch()
+    return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
+            "fp8_e4m3": torch.uint8}[dtype]
+
+
+def to_device(arr: np.ndarray, dtype: str, device):
+    """Storage representation (see ``draw_values``) -> device tensor of ``dtype``."""
+    torch = _torch()
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    elif dtype == "f16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).astype(np.float16, copy=False))
+    elif dtype == "f32":
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.uint8))
+    return t.to(device)
+
+
+def to_host_bits(t) -> np.ndarray:
+    """Device tensor -> numpy array of its raw storage bits."""
+    torch = _torch()
+    t = t.detach().contiguous().cpu()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    return t.view(torch.uint8).numpy()
+
+
+def poisoned_pool(w: Workload, device):
+    torch = _torch()
+    N, H, B, d = w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim
+    bits = poison_pattern(w.kv_dtype)
+    if w.kv_dtype == "f32":
+        k = torch.full((N, H, B, d), bits, dtype=torch.int32, device=device).view(torch.float32)
+        v = torch.full((N, H, d, B), bits, dtype=torch.int32, device=device).view(torch.float32)
+    elif w.kv_dtype in ("f16", "bf16"):
+        td = torch_dtype(w.kv_dtype)
+        k = torch.full((N, H, B, d), bits, dtype=torch.int16, device=device).view(td)
+        v = torch.full((N, H, d, B), bits, dtype=torch.int16, device=device).view(td)
+    else:
+        k = torch.full((N, H, B, d), bits, dtype=torch.uint8, device=device)
+        v = torch.full((N, H, d, B), bits, dtype=torch.uint8, device=device)
+    return k, v
+
+
+@dataclass
+class DeviceStep:
+    w: Workload
+    k_cache: object
+    v_cache: object
+    block_tables: object
+    seq_lens: object
+    query_start_loc: object
+    q: object
+    new_key: object
+    new_value: object
+    new_slots: object
+    out: object
+    workspace: object
+
+    def write_new(self, stream=None):
+        import paged_kv_cache_141_amd as pa
+        pa.reshape_and_cache(self.new_key, self.new_value, self.k_cache, self.v_cache,
+                             self.new_slots, self.w.k_scale, self.w.v_scale, stream=stream)
+
+    def attend(self, out=None, stream=None):
+        import paged_kv_cache_141_amd as pa
+        w = self.w
+        return pa.attention(self.q, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
+                            self.query_start_loc, w.scale, max_seq_len=w.max_seq_len,
+                            max_query_len=w.max_query_len, out=self.out if out is None else out,
+                            workspace=self.workspace, k_scale=w.k_scale, v_scale=w.v_scale,
+                            stream=stream)
+
+    def step(self, stream=None):
+        """One pass of the hot path: cache write of the new tokens + attention."""
+        self.write_new(stream)
+        return self.attend(stream=stream)
+
+
+def stage(w: Workload, device="cuda", batch_tokens: Optional[int] = None,
+          write_new: bool = True) -> DeviceStep:
+    """Upload ``w`` and write its prior context (and, by default, the new tokens)."""
+    torch = _torch()
+    import paged_kv_cache_141_amd as pa
+    k_cache, v_cache = poisoned_pool(w, device)
+    per_tok = w.num_kv_heads * w.head_dim
+    if batch_tokens is None:
+        batch_tokens = max(1, (64 << 20) // per_tok)
+    pend_k, pend_v, pend_s, n = [], [], [], 0
+
+    def flush():
+        nonlocal pend_k, pend_v, pend_s, n
+        if not n:
+            return
+        k = to_device(np.concatenate(pend_k), w.src_dtype, device)
+        v = to_device(np.concatenate(pend_v), w.src_dtype, device)
+        s = torch.from_numpy(np.concatenate(pend_s).astype(np.int64)).to(device)
+        pa.reshape_and_cache(k, v, k_cache, v_cache, s, w.k_scale, w.v_scale)
+        pend_k, pend_v, pend_s, n = [], [], [], 0
+
+    new_k, new_v, new_s = [], [], []
+    for kind, _i, k, v, s in w.iter_token_writes():
+        if kind == "new":
+            new_k.append(k), new_v.append(v), new_s.append(s)
+            continue
+        pend_k.append(k), pend_v.append(v), pend_s.append(s)
+        n += k.shape[0]
+        if n >= batch_tokens:
+            flush()
+    flush()
+    shape = (0, w.num_kv_heads, w.head_dim)
+    nk = np.concatenate(new_k) if new_k else np.zeros(shape, dtype=np.float32)
+    nv = np.concatenate(new_v) if new_v else np.zeros(shape, dtype=np.float32)
+    ns = np.concatenate(new_s) if new_s else np.zeros(0, dtype=np.int64)
+    step = DeviceStep(
+        w=w, k_cache=k_cache, v_cache=v_cache,
+        block_tables=torch.from_numpy(w.block_tables.astype(np.int32)).to(device),
+        seq_lens=torch.from_numpy(w.seq_lens.astype(np.int32)).to(device),
+        query_start_loc=torch.from_numpy(w.query_start_loc.astype(np.int32)).to(device),
+        q=to_device(w.q_values(), w.q_dtype, device),
+        new_key=to_device(nk, w.src_dtype, device), new_value=to_device(nv, w.src_dtype, device),
+        new_slots=torch.from_numpy(ns.astype(np.int64)).to(device),
+        out=None, workspace=None)
+    step.out = torch.empty_like(step.q)
+    nbytes = pa.attention_workspace_size(k_cache, v_cache, w.num_q_heads, w.num_seqs,
+                                         w.num_tokens, w.max_seq_len, w.max_query_len)
+    step.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if write_new:
+        step.write_new()
+    return step

@@ -32,6 +32,9 @@ decode tokens with prompt chunks under a 4,096-token budget, and a shared
 from __future__ import annotations
 
 import math
+import os
+from collections import deque
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Callable, Dict, Iterator, List, Optional, Sequence, Tuple
 
@@ -65,7 +68,8 @@ def draw_values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
     if dtype == "f16":
         return x.astype(np.float16)
     if dtype == "bf16":
-        return (x.view(np.uint32) >> 16).astype(np.uint16)
+        # the high half of each little-endian float32
+        return np.ascontiguousarray(x.view(np.uint16)[..., 1::2])
     raise ValueError(f"no source representation for {dtype}")
 
 
@@ -157,6 +161,31 @@ class Workload:
             v = np.concatenate([pv, v], axis=0)
         return k, v
 
+    def iter_kv_values(self, seqs: Sequence[int], workers: Optional[int] = None,
+                       lookahead: int = 16) -> Iterator[Tuple[np.ndarray, np.ndarray]]:
+        """``kv_values(i)`` for each i in order, drawn on a small thread pool
+        (every sequence has its own generator, so the values do not depend on
+        the pool)."""
+        if self.shared_prefix_len:
+            self._prefix_values()
+        workers = workers or min(16, os.cpu_count() or 1)
+        if workers <= 1 or len(seqs) <= 1:
+            for i in seqs:
+                yield self.kv_values(i)
+            return
+        with ThreadPoolExecutor(workers) as ex:
+            pending = deque()
+            it = iter(seqs)
+            for i in it:
+                pending.append(ex.submit(self.kv_values, i))
+                if len(pending) >= lookahead:
+                    break
+            for i in it:
+                yield pending.popleft().result()
+                pending.append(ex.submit(self.kv_values, i))
+            while pending:
+                yield pending.popleft().result()
+
     def q_values(self) -> np.ndarray:
         """Queries of the step, ``[T][Hq][d]`` in the q dtype."""
         rng = np.random.default_rng([self.seed, 4])
@@ -180,14 +209,12 @@ class Workload:
         as "prior", with seq = -1, when its blocks are shared; a prefix held in
         private copies is written with each sequence.
         """
-        seqs = range(self.num_seqs) if seqs is None else seqs
+        seqs = list(range(self.num_seqs)) if seqs is None else list(seqs)
         P = self.shared_prefix_len if self.prefix_blocks_shared else 0
         if P and len(seqs):
             pk, pv = self._prefix_values()
-            first = seqs[0] if not isinstance(seqs, range) else seqs.start
-            yield "prior", -1, pk, pv, self.slots(first)[:P]
-        for i in seqs:
-            k, v = self.kv_values(i)
+            yield "prior", -1, pk, pv, self.slots(seqs[0])[:P]
+        for i, (k, v) in zip(seqs, self.iter_kv_values(seqs)):
             s = self.slots(i)
             L = int(self.seq_lens[i])
             n_new = int(self.query_lens[i])
@@ -200,11 +227,9 @@ class Workload:
     def new_token_batch(self) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
         """This step's key/value ``[T][Hkv][d]`` and int64 slot mapping ``[T]``."""
         ks, vs, ss = [], [], []
-        for i in range(self.num_seqs):
+        seqs = [i for i in range(self.num_seqs) if int(self.query_lens[i])]
+        for i, (k, v) in zip(seqs, self.iter_kv_values(seqs)):
             n_new = int(self.query_lens[i])
-            if not n_new:
-                continue
-            k, v = self.kv_values(i)
             ks.append(k[-n_new:])
             vs.append(v[-n_new:])
             ss.append(self.slots(i)[-n_new:])
