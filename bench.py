@@ -43,6 +43,9 @@ def parse():
                          "mixed_chunked_prefill | fp8_shared_prefix")
     ap.add_argument("--block-size", type=int, default=None, help="for fp8_shared_prefix")
     ap.add_argument("--placement", default=None, help="shuffled | identity | private")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the step: copy a MIB-mebibyte device buffer --steps times "
+                         "(the known-size reference for HBM counter scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's timed sample (0 disables it)")
     return ap.parse_args()
@@ -157,6 +160,22 @@ def main():
         sys.exit(2)
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"calibrate_copy_bytes": n, "us_per_copy": round(dt * 1e6, 2),
+                          "copy_GBps_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
+        return
 
     import workloads
     from workloads import accounting

@@ -206,20 +206,36 @@ __device__ __forceinline__ Frag<CT> frag_zero() {
   return f;
 }
 
-// Load 8 consecutive cache elements of storage type SRC as compute type CT.
-// fp8 codes widen exactly to bf16/f16 (every E4M3 value is representable).
-template <int CT, int SRC>
-__device__ __forceinline__ Frag<CT> load_frag(const uint8_t* p) {
-  Frag<CT> f;
+// Eight consecutive elements of storage type SRC as loaded from memory
+// (kept raw so that prefetched data costs the fewest registers).
+template <int SRC> struct Raw { u32x4 w; };
+template <> struct Raw<DT_F32> { u32x4 w[2]; };
+template <> struct Raw<DT_FP8> { u32x2 w; };
+
+template <int SRC>
+__device__ __forceinline__ Raw<SRC> load_raw(const uint8_t* p) {
+  Raw<SRC> r;
   if constexpr (SRC == DT_F32) {
-    f.w[0] = reinterpret_cast<const u32x4*>(p)[0];
-    f.w[1] = reinterpret_cast<const u32x4*>(p)[1];
+    r.w[0] = reinterpret_cast<const u32x4*>(p)[0];
+    r.w[1] = reinterpret_cast<const u32x4*>(p)[1];
   } else if constexpr (SRC == DT_FP8) {
-    const u32x2 c = *reinterpret_cast<const u32x2*>(p);
+    r.w = *reinterpret_cast<const u32x2*>(p);
+  } else {
+    r.w = *reinterpret_cast<const u32x4*>(p);
+  }
+  return r;
+}
+
+// Raw elements -> MFMA operand of compute type CT.  fp8 codes widen exactly
+// to bf16/f16 (every E4M3 value is representable in both).
+template <int CT, int SRC>
+__device__ __forceinline__ Frag<CT> to_frag(const Raw<SRC>& r) {
+  Frag<CT> f;
+  if constexpr (SRC == DT_FP8) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(c[e], false);
-      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(c[e], true);
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(r.w[e], false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(r.w[e], true);
       if constexpr (CT == DT_BF16) {
         // exact: an E4M3 value has at most 4 significant bits, so the low half is zero
         f.w[2 * e] = __builtin_amdgcn_perm(f2u(lo[1]), f2u(lo[0]), 0x07060302u);
@@ -229,10 +245,18 @@ __device__ __forceinline__ Frag<CT> load_frag(const uint8_t* p) {
         f.w[2 * e + 1] = f32_to_f16(hi[0]) | (f32_to_f16(hi[1]) << 16);
       }
     }
+  } else if constexpr (SRC == DT_F32) {
+    f.w[0] = r.w[0];
+    f.w[1] = r.w[1];
   } else {
-    f.w = *reinterpret_cast<const u32x4*>(p);
+    f.w = r.w;
   }
   return f;
+}
+
+template <int CT, int SRC>
+__device__ __forceinline__ Frag<CT> load_frag(const uint8_t* p) {
+  return to_frag<CT, SRC>(load_raw<SRC>(p));
 }
 
 // acc += A(16 x 32) * B(32 x 16).  A lane's 8 elements sit in the same K
@@ -351,11 +375,17 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   }
 
   const int nblk = (L + BS - 1) / BS;
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(i) * a.max_blocks_per_seq;
   const int64_t tile_bytes = static_cast<int64_t>(BS) * D * EBK;
   const int64_t blk_stride = tile_bytes * a.num_kv_heads;
   const uint8_t* kc = static_cast<const uint8_t*>(a.k_cache) + h * tile_bytes;
   const uint8_t* vc = static_cast<const uint8_t*>(a.v_cache) + h * tile_bytes;
+
+  // The partition's block-table entries, one per lane (at most P/B <= 32):
+  // each step then reads its physical block ids with readlane, no memory trip.
+  const int jbase = kstart / BS;
+  const int nbt = min(nblk - jbase, kPartition / BS);
+  const int32_t* bt = a.block_tables + static_cast<int64_t>(i) * a.max_blocks_per_seq + jbase;
+  const int btv = lane < nbt ? bt[lane] : 0;
 
   // per-lane key offsets inside a 32-key step
   const int kkey0 = 8 * (r >> 2) + (r & 3);      // sub-tile 0; sub-tile 1 adds 4
@@ -367,15 +397,18 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = kstart; k0 < kend; k0 += 32) {
-    // ---- block-table gather: physical block(s) of this 32-key step
+  struct Step {
+    Raw<KV> k[2][KS];
+    Raw<KV> v[NT];
+  };
+  // Issue the loads of the 32-key step starting at key k0 (block-table
+  // gather: physical block(s) from the table register, then 16-byte reads).
+  auto issue = [&](Step& st, int k0) {
     const int j0 = k0 / BS;
-    const int64_t p0 = uniform(bt[j0]);
+    const int64_t p0 = __builtin_amdgcn_readlane(btv, j0 - jbase);
     int64_t p1 = p0;
-    if constexpr (BS == 16) p1 = uniform(bt[min(j0 + 1, nblk - 1)]);
+    if constexpr (BS == 16) p1 = __builtin_amdgcn_readlane(btv, min(j0 + 1, nblk - 1) - jbase);
     const int inblk = k0 - j0 * BS;   // 0 for BS <= 32; 0 or 32 for BS = 64
-
-    Frag<CT> kf[2][KS];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const int kk = kkey0 + 4 * tau;                  // key within the step
@@ -383,28 +416,27 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
       const int off = (BS == 16) ? (kk & 15) : inblk + kk;
       const uint8_t* kp = kc + pb * blk_stride + (static_cast<int64_t>(off) * D + 8 * lg) * EBK;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kf[tau][s] = load_frag<CT, KV>(kp + 32 * s * EBK);
+      for (int s = 0; s < KS; ++s) st.k[tau][s] = load_raw<KV>(kp + 32 * s * EBK);
     }
-    Frag<CT> vf[NT];
-    {
-      const int64_t pb = (BS == 16 && vkey >= 16) ? p1 : p0;
-      const int off = (BS == 16) ? (vkey & 15) : inblk + vkey;
-      const uint8_t* vp = vc + pb * blk_stride + (static_cast<int64_t>(r) * BS + off) * EBK;
+    const int64_t pb = (BS == 16 && vkey >= 16) ? p1 : p0;
+    const int off = (BS == 16) ? (vkey & 15) : inblk + vkey;
+    const uint8_t* vp = vc + pb * blk_stride + (static_cast<int64_t>(r) * BS + off) * EBK;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) vf[n] = load_frag<CT, KV>(vp + static_cast<int64_t>(16 * n) * BS * EBK);
-    }
+    for (int n = 0; n < NT; ++n) st.v[n] = load_raw<KV>(vp + static_cast<int64_t>(16 * n) * BS * EBK);
+  };
 
+  auto compute = [&](const Step& st, int k0) {
     // ---- S^T = K Q^T
-    f32x4 st[2];
+    f32x4 sf[2];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
-      st[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sf[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) st[tau] = mma<CT>(st[tau], kf[tau][s], qf[s]);
+      for (int s = 0; s < KS; ++s) sf[tau] = mma<CT>(sf[tau], to_frag<CT, KV>(st.k[tau][s]), qf[s]);
     }
     float sc[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { sc[e] = st[0][e] * a.score_scale; sc[4 + e] = st[1][e] * a.score_scale; }
+    for (int e = 0; e < 4; ++e) { sc[e] = sf[0][e] * a.score_scale; sc[4 + e] = sf[1][e] * a.score_scale; }
     if (k0 + 31 > min_pos) {   // some key of this step is past some row's position
 #pragma unroll
       for (int e = 0; e < 8; ++e) sc[e] = (k0 + vkey + e <= row_pos) ? sc[e] : -__builtin_inff();
@@ -429,16 +461,37 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
     for (int n = 0; n < NT; ++n) acc[n] *= alpha;
 
     // ---- O^T += V^T P^T
-    if (k0 + 32 > L) {         // keys past the end hold poison: drop them by selection
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (k0 + vkey + e >= L)
-#pragma unroll
-          for (int n = 0; n < NT; ++n) frag_zero_elem<CT>(vf[n], e);
-    }
     const Frag<CT> pf = pack_p<CT>(p);
+    const bool tail = k0 + 32 > L;   // keys past the end hold poison: drop them by selection
 #pragma unroll
-    for (int n = 0; n < NT; ++n) acc[n] = mma<CT>(acc[n], vf[n], pf);
+    for (int n = 0; n < NT; ++n) {
+      Frag<CT> vf = to_frag<CT, KV>(st.v[n]);
+      if (tail) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (k0 + vkey + e >= L) frag_zero_elem<CT>(vf, e);
+      }
+      acc[n] = mma<CT>(acc[n], vf, pf);
+    }
+  };
+
+  // Software pipeline: the loads of step s + PF are in flight while step s
+  // computes.  fp8 steps are half the bytes, so they run one step deeper.
+  constexpr int PF = (KV == DT_FP8) ? 2 : (KV == DT_F32 ? 0 : 1);
+  constexpr int NB = PF + 1;
+  Step buf[NB];
+  const int nsteps = (kend - kstart + 31) / 32;
+#pragma unroll
+  for (int s = 0; s < PF; ++s)
+    if (s < nsteps) issue(buf[s], kstart + 32 * s);
+  for (int s0 = 0; s0 < nsteps; s0 += NB) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int s = s0 + b;
+      if (s >= nsteps) break;
+      if (s + PF < nsteps) issue(buf[(b + PF) % NB], kstart + 32 * (s + PF));
+      compute(buf[b], kstart + 32 * s);
+    }
   }
 
   // ---- finish: whole-row denominator, then the output or a partial
@@ -469,7 +522,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
 // Waves draw work items from a counter; item w covers list entry w / Hkv and
 // kv head w % Hkv.  Every wave exits once the counter passes the item count.
 template <int CT, int KV, int D, int BS>
-__global__ __launch_bounds__(64) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64, 2) void attn_kernel(AttnArgs a) {
   const int lane = threadIdx.x;
   const int64_t total = static_cast<int64_t>(uniform(a.header[1])) * a.num_kv_heads;
   while (true) {
@@ -565,15 +618,26 @@ hipError_t launch_reshape_and_cache(int src, int kv, const CacheWriteArgs& a, hi
   return hipErrorInvalidValue;
 }
 
+// Waves of a 64-thread kernel that fit on the device at once (0 -> a default).
+static int64_t resident_waves(const void* kernel) {
+  int dev = 0, per_cu = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64, 0) != hipSuccess || per_cu <= 0)
+    return 2048;
+  return static_cast<int64_t>(per_cu) * prop.multiProcessorCount;
+}
+
 template <int CT, int KV, int D, int BS>
 static hipError_t launch_attn(const AttnArgs& a, hipStream_t stream, hipEvent_t before, hipEvent_t after) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a.seq_lens, a.qsl, a.num_seqs,
                      a.group, a.header, a.items, a.max_items);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // enough waves to fill every CU several times; each loops over work items
+  // one wave per resident slot; each loops over work items until the list is done
+  static const int64_t slots = resident_waves(reinterpret_cast<const void*>(&attn_kernel<CT, KV, D, BS>));
   const int64_t want = a.max_items * a.num_kv_heads;
-  const int64_t waves = want < 8192 ? (want > 0 ? want : 1) : 8192;
+  const int64_t waves = want < slots ? (want > 0 ? want : 1) : slots;
   if (before && (e = hipEventRecord(before, stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((attn_kernel<CT, KV, D, BS>), dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream, a);
   e = hipGetLastError();
