@@ -198,6 +198,10 @@ def main():
     stream = torch.cuda.current_stream()
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    # the chunk (prefill) kernel runs when a sequence has >= 65 (token, head) rows per kv head
+    chunk_rows = w.query_lens.astype(np.int64) * w.group
+    is_chunk = (chunk_rows >= 65) & (w.q_dtype != "f32")
+    chunk_pairs = [(ev.create(), ev.create()) for _ in range(args.steps)] if is_chunk.any() else None
     cw = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
 
@@ -207,6 +211,8 @@ def main():
     t0 = time.perf_counter()
     for k in range(args.steps):
         pa.set_attention_events(pairs[k][0], pairs[k][1])
+        if chunk_pairs:
+            pa.set_chunk_events(chunk_pairs[k][0], chunk_pairs[k][1])
         cw[k][0].record(stream)
         step.write_new()
         cw[k][1].record(stream)
@@ -214,14 +220,19 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     pa.set_attention_events(None, None)
+    pa.set_chunk_events(None, None)
 
     step_s = (t1 - t0) / args.steps
     attn_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
     cw_ms = [a.elapsed_time(b) for a, b in cw]
-    for a, b in pairs:
+    chunk_ms = [ev.elapsed_ms(a, b) for a, b in chunk_pairs] if chunk_pairs else None
+    for a, b in pairs + (chunk_pairs or []):
         ev.destroy(a), ev.destroy(b)
     attn_s = float(np.mean(attn_ms)) / 1e3
-    achieved = kv_bytes / attn_s / 1e9
+    # the decode kernel reads the KV of the sequences routed to it (all but chunk sequences)
+    eb = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}[w.kv_dtype]
+    decode_bytes = int((w.seq_lens.astype(np.int64) * ~is_chunk).sum()) * w.num_kv_heads * 2 * w.head_dim * eb
+    achieved = decode_bytes / attn_s / 1e9
     traffic = measured_traffic(w.name, "attn_kernel")
 
     line = {
@@ -245,12 +256,25 @@ def main():
         "query_tokens_per_s": round(w.num_tokens / step_s, 1),
         "hbm_frac_step": round(kv_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "attention_kernel_us": round(attn_s * 1e6, 2),
+        "attention_kernel_kv_bytes": decode_bytes,
         "cache_write_us": round(float(np.mean(cw_ms)) * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "cpu_baseline": None,
     }
+    if chunk_ms:
+        L = w.seq_lens.astype(np.int64)
+        c = w.query_lens.astype(np.int64)
+        pairs_chunk = int(((c * (L - c) + c * (c + 1) // 2) * is_chunk).sum())
+        flops = 4 * w.head_dim * w.num_q_heads * pairs_chunk
+        t = float(np.mean(chunk_ms)) / 1e3
+        peak = 2500.0   # dense bf16/fp16 MFMA, TFLOP/s
+        line["chunk_kernel_us"] = round(t * 1e6, 2)
+        line["roofline_chunk"] = {"bound": "mfma", "achieved": round(flops / t / 1e12, 2), "peak": peak,
+                                  "unit": "TFLOP/s", "frac": round(flops / t / 1e12 / peak, 4),
+                                  "flops": flops, "traffic": None}
+        line["config"]["chunk_tokens"] = int((c * is_chunk).sum())
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -133,6 +133,7 @@ pa_status_t pa_attention_workspace_size(const pa_cache_t* cache, int32_t num_q_h
  *            (they size the launch; an actual value above them is undefined).
  *   workspace [device] at least pa_attention_workspace_size bytes, 256-byte
  *            aligned; its contents on entry do not matter.
+ * scale must be finite and > 0 (PA_ERR_UNSUPPORTED otherwise).
  * dtype pairings: fp32 q with an fp32 cache; fp16 q with an fp16 or fp8
  * cache; bf16 q with a bf16 or fp8 cache.  Anything else is PA_ERR_DTYPE.
  * Sequences with q_len = 0 are no-ops.  num_seqs == 0 is a no-op.
@@ -163,13 +164,21 @@ pa_status_t pa_check_metadata(const pa_cache_t* cache, const int32_t* block_tabl
 /*
  * Measurement hook.  When both are non-NULL, every later pa_attention call
  * records hipEvent_t `before` on its stream immediately before launching the
- * attention kernel and `after` immediately after it, so hipEventElapsedTime
- * gives that one kernel's duration (the work-list and partition-merge
- * kernels fall outside).  Pass NULL, NULL to turn it off.  This is the
+ * decode attention kernel and `after` immediately after it, so
+ * hipEventElapsedTime gives that one kernel's duration (the work-list, chunk
+ * and partition-merge kernels fall outside).  Pass NULL, NULL to turn it off.  This is the
  * library's only global state; it is meant for timing harnesses and is not
  * thread-safe.
  */
 pa_status_t pa_set_attention_events(void* before, void* after);
+
+/*
+ * The same hook for the chunk kernel, which pa_attention launches (after the
+ * decode kernel) when some sequence may have at least 65 (query token, q head)
+ * rows per kv head, i.e. a prompt chunk (max_query_len * Hq / Hkv >= 65 with
+ * a 16-bit q); the events are recorded only on calls that launch it.
+ */
+pa_status_t pa_set_chunk_events(void* before, void* after);
 
 /* Static text for a status code. */
 const char* pa_status_string(pa_status_t status);

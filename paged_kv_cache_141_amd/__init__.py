@@ -71,6 +71,7 @@ def library() -> ctypes.CDLL:
         "pa_attention": [P, I32, P, P, CP, P, I32, P, P, I32, I32, I32, I32, I32, F, P, P, SZ, P],
         "pa_check_metadata": [CP, P, I32, P, P, I32, I32, I32, I32, ctypes.POINTER(I32), P],
         "pa_set_attention_events": [P, P],
+        "pa_set_chunk_events": [P, P],
         "pa_status_string": [I32],
         "pa_version": [],
     }
@@ -225,6 +226,11 @@ def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scal
 def set_attention_events(before, after) -> None:
     """Bracket the attention kernel with two hipEvent_t handles (ints), or None, None."""
     _check(library().pa_set_attention_events(before, after), "pa_set_attention_events")
+
+
+def set_chunk_events(before, after) -> None:
+    """Bracket the chunk (prefill) kernel with two hipEvent_t handles, or None, None."""
+    _check(library().pa_set_chunk_events(before, after), "pa_set_chunk_events")
 
 
 def check_metadata(k_cache, v_cache, block_tables, seq_lens, query_start_loc, num_tokens: int,

@@ -22,6 +22,8 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # keep the compiler from forming packed-fp32 ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: no AGPR<->VGPR copies around the softmax
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     # IEEE fp32 division (the fp8 cache write divides by the scale)
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math", "-ffp-contract=fast",
     "-Wall", "-Wno-unused-function",

@@ -13,9 +13,9 @@ namespace {
 
 using pa::ceil_div;
 
-// The measurement hook of pa_set_attention_events (the library's only state).
-hipEvent_t g_before = nullptr;
-hipEvent_t g_after = nullptr;
+// The measurement hooks of pa_set_attention_events / pa_set_chunk_events
+// (the library's only state): decode kernel pair, then chunk kernel pair.
+hipEvent_t g_events[4] = {nullptr, nullptr, nullptr, nullptr};
 
 bool dtype_known(int32_t d) { return d >= PA_F32 && d <= PA_FP8_E4M3; }
 
@@ -25,6 +25,9 @@ pa_status_t check_cache(const pa_cache_t* c) {
   if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return PA_ERR_SHAPE;
   if (c->block_size != 16 && c->block_size != 32 && c->block_size != 64) return PA_ERR_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  // one block of all kv heads must stay below 4 GiB (32-bit block strides)
+  if (static_cast<int64_t>(c->num_kv_heads) * c->block_size * c->head_dim * 4 >= (int64_t(1) << 32))
+    return PA_ERR_UNSUPPORTED;
   if (c->kv_dtype == PA_FP8_E4M3) {
     if (!(c->k_scale > 0.f) || !(c->v_scale > 0.f) || !isfinite(c->k_scale) || !isfinite(c->v_scale))
       return PA_ERR_UNSUPPORTED;
@@ -55,7 +58,7 @@ pa_status_t check_attention_sizes(const pa_cache_t* c, int32_t num_q_heads, int3
   if (ceil_div(max_seq_len, pa::kPartition) > 0xFFFF) return PA_ERR_UNSUPPORTED;
   const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, c->num_kv_heads,
                                                      c->head_dim, max_seq_len);
-  if (w.max_items > 0x7FFFFFFF / 64) return PA_ERR_UNSUPPORTED;
+  if (w.max_items > 0x7FFFFFFF / 64 || w.max_citems > 0x7FFFFFFF / 64) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
@@ -127,7 +130,7 @@ pa_status_t pa_attention(const void* q, int32_t q_dtype, const void* k_cache, co
   if (st != PA_OK) return st;
   if (!dtype_known(q_dtype)) return PA_ERR_DTYPE;
   if (!pairing_ok(q_dtype, cache->kv_dtype)) return PA_ERR_DTYPE;
-  if (!isfinite(scale)) return PA_ERR_UNSUPPORTED;
+  if (!isfinite(scale) || !(scale > 0.f)) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_tokens == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !out)
     return PA_ERR_NULL;
@@ -150,28 +153,39 @@ pa_status_t pa_attention(const void* q, int32_t q_dtype, const void* k_cache, co
   a.out = out;
   a.header = reinterpret_cast<int32_t*>(ws + w.header);
   a.items = reinterpret_cast<int32_t*>(ws + w.items);
+  a.citems = reinterpret_cast<int32_t*>(ws + w.citems);
   a.part_m = reinterpret_cast<float*>(ws + w.part_m);
   a.part_l = reinterpret_cast<float*>(ws + w.part_l);
   a.part_acc = reinterpret_cast<float*>(ws + w.part_acc);
   a.max_items = w.max_items;
+  a.max_citems = w.max_citems;
+  a.chunk_path = q_dtype != PA_F32;   // the chunk kernel stages 16-bit operands
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_seqs = num_seqs;
   a.num_tokens = num_tokens;
   a.num_q_heads = num_q_heads;
+  a.max_query_len = max_query_len;
   a.num_kv_heads = cache->num_kv_heads;
   a.group = num_q_heads / cache->num_kv_heads;
   a.max_parts = w.max_parts;
   a.score_scale = scale * cache->k_scale * 1.4426950408889634f;
   a.v_scale = cache->v_scale;
   const hipError_t e = pa::launch_attention(q_dtype, cache->kv_dtype, cache->head_dim, cache->block_size, a,
-                                            static_cast<hipStream_t>(stream), g_before, g_after);
+                                            static_cast<hipStream_t>(stream), g_events);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 pa_status_t pa_set_attention_events(void* before, void* after) {
   if ((before == nullptr) != (after == nullptr)) return PA_ERR_NULL;
-  g_before = static_cast<hipEvent_t>(before);
-  g_after = static_cast<hipEvent_t>(after);
+  g_events[0] = static_cast<hipEvent_t>(before);
+  g_events[1] = static_cast<hipEvent_t>(after);
+  return PA_OK;
+}
+
+pa_status_t pa_set_chunk_events(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr)) return PA_ERR_NULL;
+  g_events[2] = static_cast<hipEvent_t>(before);
+  g_events[3] = static_cast<hipEvent_t>(after);
   return PA_OK;
 }
 

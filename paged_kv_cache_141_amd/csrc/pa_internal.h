@@ -17,26 +17,39 @@ constexpr int kTileRows = 16;
 // log-sum-exp reduce merges.
 constexpr int kPartition = 512;
 
+// A sequence with more than kChunkMinRows - 1 (token, head) rows per kv head
+// (a prompt chunk) goes to the chunk kernel: 256-row blocks, 64-key LDS
+// tiles, context partitions of kChunkPartition keys.  Fewer rows (decode,
+// short speculative runs) stay on the 16-row decode kernel.
+constexpr int kChunkMinRows = 65;
+constexpr int kChunkWaves = 8;                 // waves per chunk workgroup (2 per SIMD)
+constexpr int kChunkThreads = 64 * kChunkWaves;
+constexpr int kChunkRows = 32 * kChunkWaves;   // two 16-row tiles per wave
+constexpr int kChunkKeys = 64;
+constexpr int kChunkPartition = 4096;
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Upper bound on the number of (sequence, row tile, partition) work items,
-// from host-side bounds only: sum_i ceil(q_i*G/16) <= ceil(T*G/16) + S.
+// from host-side bounds only: sum_i ceil(q_i*G/rows) <= ceil(T*G/rows) + S.
 inline int64_t max_work_items(int64_t num_seqs, int64_t num_tokens, int64_t group,
-                              int64_t max_seq_len) {
-  const int64_t tiles = ceil_div(num_tokens * group, kTileRows) + num_seqs;
-  const int64_t parts = ceil_div(max_seq_len > 0 ? max_seq_len : 1, kPartition);
+                              int64_t max_seq_len, int64_t rows_per_item, int64_t partition) {
+  const int64_t tiles = ceil_div(num_tokens * group, rows_per_item) + num_seqs;
+  const int64_t parts = ceil_div(max_seq_len > 0 ? max_seq_len : 1, partition);
   return tiles * parts;
 }
 
 // Workspace carve-up (byte offsets, each 256-byte aligned).
 struct WorkspaceLayout {
-  size_t header;   // int32 [64]: [0] work counter, [1] item count
-  size_t items;    // int32x2 [max_items]: (seq, tile << 16 | partition)
+  size_t header;   // int32 [64]: [0]/[1] decode work counter/count, [2]/[3] chunk's
+  size_t items;    // int32x2 [max_items]: decode items (seq, tile << 16 | partition)
+  size_t citems;   // int32x2 [max_citems]: chunk items (seq, row block << 16 | partition)
   size_t part_m;   // float [T][Hq][MP]: running max (log2 units) per partition
   size_t part_l;   // float [T][Hq][MP]: softmax denominator per partition
   size_t part_acc; // float [T][Hq][MP][d]: un-normalised output per partition
   size_t total;
   int64_t max_items;
+  int64_t max_citems;
   int32_t max_parts;
 };
 
@@ -47,12 +60,14 @@ inline WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_tokens, in
                                         int64_t max_seq_len) {
   WorkspaceLayout w{};
   const int64_t group = num_kv_heads > 0 ? num_q_heads / num_kv_heads : 1;
-  w.max_items = max_work_items(num_seqs, num_tokens, group, max_seq_len);
+  w.max_items = max_work_items(num_seqs, num_tokens, group, max_seq_len, kTileRows, kPartition);
+  w.max_citems = max_work_items(num_seqs, num_tokens, group, max_seq_len, kChunkRows, kChunkPartition);
   w.max_parts = static_cast<int32_t>(ceil_div(max_seq_len > 0 ? max_seq_len : 1, kPartition));
   const size_t rows = static_cast<size_t>(num_tokens) * num_q_heads * w.max_parts;
   size_t off = 0;
   w.header = off;   off = align256(off + 64 * sizeof(int32_t));
   w.items = off;    off = align256(off + static_cast<size_t>(w.max_items) * 2 * sizeof(int32_t));
+  w.citems = off;   off = align256(off + static_cast<size_t>(w.max_citems) * 2 * sizeof(int32_t));
   w.part_m = off;   off = align256(off + rows * sizeof(float));
   w.part_l = off;   off = align256(off + rows * sizeof(float));
   w.part_acc = off; off = align256(off + rows * head_dim * sizeof(float));
@@ -80,12 +95,16 @@ struct AttnArgs {
   void* out;
   int32_t* header;
   int32_t* items;
+  int32_t* citems;
   float* part_m;
   float* part_l;
   float* part_acc;
   int64_t max_items;
+  int64_t max_citems;
+  int32_t chunk_path;   // 1: sequences with >= kChunkMinRows rows use the chunk kernel
   int32_t max_blocks_per_seq;
   int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, group;
+  int32_t max_query_len;
   int32_t max_parts;
   float score_scale;   // scale * k_scale * log2(e)
   float v_scale;
@@ -95,9 +114,9 @@ struct AttnArgs {
 hipError_t launch_reshape_and_cache(int src_dtype, int kv_dtype, const CacheWriteArgs& a,
                                     hipStream_t stream);
 // kv_dtype, q_dtype: pa_dtype_t values; head_dim 64|128; block_size 16|32|64.
-// `before`/`after` (may be null) are recorded around the attention kernel.
+// events[0..1] (may be null) are recorded around the decode kernel and
+// events[2..3] around the chunk kernel.
 hipError_t launch_attention(int q_dtype, int kv_dtype, int head_dim, int block_size,
-                            const AttnArgs& a, hipStream_t stream, hipEvent_t before,
-                            hipEvent_t after);
+                            const AttnArgs& a, hipStream_t stream, const hipEvent_t* events);
 
 }  // namespace pa

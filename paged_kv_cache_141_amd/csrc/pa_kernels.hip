@@ -136,56 +136,76 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a
 // step plan: the work list
 // ============================================================================
 
-// One workgroup.  For each sequence with q_len > 0: tiles = ceil(q_len*G/16)
-// row tiles, parts = ceil(L/P) context partitions; its tiles*parts items are
-// appended in (tile, partition) order after an exclusive prefix sum.  Also
-// resets the work counter the attention kernel's waves draw from.
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ seq_lens,
-                                                    const int32_t* __restrict__ qsl, int num_seqs,
-                                                    int group, int32_t* __restrict__ header,
-                                                    int32_t* __restrict__ items,
-                                                    int64_t max_items) {
-  __shared__ int32_t scan[1024];
-  __shared__ int64_t carry;
+// Does sequence i (rows = q_len * G) use the chunk kernel?
+__device__ __forceinline__ bool is_chunk_seq(const AttnArgs& a, int rows) {
+  return a.chunk_path && rows >= kChunkMinRows;
+}
+
+// One workgroup.  For each sequence with q_len > 0 it counts work items --
+// decode: ceil(rows/16) row tiles x ceil(L/512) partitions; chunk:
+// ceil(rows/128) row blocks x ceil(L/4096) partitions -- takes exclusive
+// prefix sums and appends the items in (tile, partition) order to the two
+// lists.  It also resets the work counters the attention kernels draw from.
+__global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
+  __shared__ int32_t scan[2][1024];
+  __shared__ int64_t carry[2];
   const int tid = threadIdx.x;
-  if (tid == 0) carry = 0;
+  if (tid < 2) carry[tid] = 0;
   __syncthreads();
-  for (int base = 0; base < num_seqs; base += 1024) {
+  for (int base = 0; base < a.num_seqs; base += 1024) {
     const int i = base + tid;
-    int n = 0, parts = 1;
-    if (i < num_seqs) {
-      const int L = seq_lens[i];
-      const int ql = qsl[i + 1] - qsl[i];
+    int n[2] = {0, 0}, parts[2] = {1, 1};
+    if (i < a.num_seqs) {
+      const int L = a.seq_lens[i];
+      const int ql = a.qsl[i + 1] - a.qsl[i];
+      const int rows = ql * a.group;
       if (ql > 0 && L > 0) {
-        const int tiles = (ql * group + kTileRows - 1) / kTileRows;
-        parts = (L + kPartition - 1) / kPartition;
-        n = tiles * parts;
+        if (is_chunk_seq(a, rows)) {
+          parts[1] = (L + kChunkPartition - 1) / kChunkPartition;
+          n[1] = ((rows + kChunkRows - 1) / kChunkRows) * parts[1];
+        } else {
+          parts[0] = (L + kPartition - 1) / kPartition;
+          n[0] = ((rows + kTileRows - 1) / kTileRows) * parts[0];
+        }
       }
     }
-    scan[tid] = n;
+    scan[0][tid] = n[0];
+    scan[1][tid] = n[1];
     __syncthreads();
-    for (int ofs = 1; ofs < 1024; ofs <<= 1) {   // inclusive Hillis-Steele scan
-      const int v = tid >= ofs ? scan[tid - ofs] : 0;
+    for (int ofs = 1; ofs < 1024; ofs <<= 1) {   // inclusive Hillis-Steele scans
+      const int v0 = tid >= ofs ? scan[0][tid - ofs] : 0;
+      const int v1 = tid >= ofs ? scan[1][tid - ofs] : 0;
       __syncthreads();
-      scan[tid] += v;
+      scan[0][tid] += v0;
+      scan[1][tid] += v1;
       __syncthreads();
     }
-    const int64_t start = carry + scan[tid] - n;
-    for (int k = 0; k < n; ++k) {
-      const int64_t pos = start + k;
-      if (pos >= max_items) break;          // only with metadata beyond the host bounds
-      const int tile = k / parts;
-      const int part = k - tile * parts;
-      items[2 * pos] = i;
-      items[2 * pos + 1] = (tile << 16) | part;
+#pragma unroll
+    for (int list = 0; list < 2; ++list) {
+      int32_t* out = list ? a.citems : a.items;
+      const int64_t cap = list ? a.max_citems : a.max_items;
+      const int64_t start = carry[list] + scan[list][tid] - n[list];
+      for (int k = 0; k < n[list]; ++k) {
+        const int64_t pos = start + k;
+        if (pos >= cap) break;              // only with metadata beyond the host bounds
+        const int tile = k / parts[list];
+        const int part = k - tile * parts[list];
+        out[2 * pos] = i;
+        out[2 * pos + 1] = (tile << 16) | part;
+      }
     }
     __syncthreads();
-    if (tid == 1023) carry += scan[1023];
+    if (tid == 1023) {
+      carry[0] += scan[0][1023];
+      carry[1] += scan[1][1023];
+    }
     __syncthreads();
   }
   if (tid == 0) {
-    header[0] = 0;
-    header[1] = static_cast<int32_t>(carry < max_items ? carry : max_items);
+    a.header[0] = 0;
+    a.header[1] = static_cast<int32_t>(carry[0] < a.max_items ? carry[0] : a.max_items);
+    a.header[2] = 0;
+    a.header[3] = static_cast<int32_t>(carry[1] < a.max_citems ? carry[1] : a.max_citems);
   }
 }
 
@@ -280,46 +300,97 @@ __device__ __forceinline__ f32x4 mma(f32x4 acc, const Frag<CT>& a, const Frag<CT
   }
 }
 
-// Zero element e of a fragment (used to drop NaN-poisoned V slots past the end).
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two packed 16-bit values (hardware conversion, round to nearest
+// even; used for probabilities and outputs, never for cache contents).
 template <int CT>
-__device__ __forceinline__ void frag_zero_elem(Frag<CT>& f, int e) {
-  if constexpr (CT == DT_F32) {
-    f.w[e >> 2][e & 3] = 0u;
-  } else {
-    const uint32_t keep = (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-    f.w[e >> 1] &= keep;
-  }
+__device__ __forceinline__ uint32_t cvt2(float x, float y) {
+  if constexpr (CT == DT_BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x, y}, bf16x2v));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x, y}, f16x2v));
 }
 
-// fp32 probabilities -> operand elements (round to nearest even).
+// fp32 probabilities -> operand elements.
 template <int CT>
 __device__ __forceinline__ Frag<CT> pack_p(const float (&p)[8]) {
   Frag<CT> f;
   if constexpr (CT == DT_F32) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) { f.w[0][e] = f2u(p[e]); f.w[1][e] = f2u(p[e + 4]); }
-  } else if constexpr (CT == DT_BF16) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) f.w[e] = f32_to_bf16(p[2 * e]) | (f32_to_bf16(p[2 * e + 1]) << 16);
   } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) f.w[e] = f32_to_f16(p[2 * e]) | (f32_to_f16(p[2 * e + 1]) << 16);
+    for (int e = 0; e < 4; ++e) f.w[e] = cvt2<CT>(p[2 * e], p[2 * e + 1]);
   }
   return f;
 }
 
 template <int OT>
 __device__ __forceinline__ void store4(uint8_t* p, float a, float b, float c, float d) {
-  if constexpr (OT == DT_F32) {
+  if constexpr (OT == DT_F32)
     *reinterpret_cast<u32x4*>(p) = u32x4{f2u(a), f2u(b), f2u(c), f2u(d)};
-  } else if constexpr (OT == DT_BF16) {
-    *reinterpret_cast<u32x2*>(p) =
-        u32x2{f32_to_bf16(a) | (f32_to_bf16(b) << 16), f32_to_bf16(c) | (f32_to_bf16(d) << 16)};
+  else
+    *reinterpret_cast<u32x2*>(p) = u32x2{cvt2<OT>(a, b), cvt2<OT>(c, d)};
+}
+
+// Per-element keep-masks for an 8-element operand whose element e is kept
+// when e < n (n may be <= 0 or >= 8): zeroes elements by selection, no branches.
+template <int CT>
+__device__ __forceinline__ void frag_keep_first(Frag<CT>& f, int n) {
+  if constexpr (CT == DT_F32) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.w[e >> 2][e & 3] = e < n ? f.w[e >> 2][e & 3] : 0u;
   } else {
-    *reinterpret_cast<u32x2*>(p) =
-        u32x2{f32_to_f16(a) | (f32_to_f16(b) << 16), f32_to_f16(c) | (f32_to_f16(d) << 16)};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t keep = (2 * q < n ? 0x0000FFFFu : 0u) | (2 * q + 1 < n ? 0xFFFF0000u : 0u);
+      f.w[q] &= keep;
+    }
   }
 }
+
+// Rescale threshold (log2 units): the running reference max of a row moves
+// only when a new score exceeds it by more than this, so the accumulator
+// rescale is skipped for most tiles; probabilities stay below 2^8.
+constexpr float kRescaleSlack = 8.f;
+
+// Online-softmax update for one query row whose keys are spread over the four
+// lanes r, r+16, r+32, r+48 (N raw scores per lane, already -inf where
+// masked).  m is the row's reference max in raw-score units, the same in the
+// four lanes; c = scale * k_scale * log2(e) > 0 turns raw scores into log2
+// units.  The reference moves -- and lsum and the accumulator are rescaled
+// -- only when some lane of the wave holds a score more than `slack`
+// (kRescaleSlack / c) above it; only then is the cross-lane row max taken.
+// Returns the probabilities 2^(c*(s - m)) <= 2^kRescaleSlack in p.
+template <int N, int NACC>
+__device__ __forceinline__ void softmax_update(const float (&s)[N], float& m, float& lsum,
+                                               f32x4 (&acc)[NACC], float c, float slack, float (&p)[N]) {
+  float lm = s[0];
+#pragma unroll
+  for (int e = 1; e < N; ++e) lm = fmaxf(lm, s[e]);
+  if (__any(lm > m + slack)) {
+    float rm = fmaxf(lm, __shfl_xor(lm, 16));
+    rm = fmaxf(rm, __shfl_xor(rm, 32));
+    const float mnew = fmaxf(m, rm);
+    const float alpha = (mnew == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f((m - mnew) * c);
+    lsum *= alpha;
+#pragma unroll
+    for (int n = 0; n < NACC; ++n) acc[n] *= alpha;
+    m = mnew;
+  }
+  const float cm = (m == -__builtin_inff()) ? 0.f : m * c;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -cm));
+    lsum += p[e];
+  }
+}
+
+// Reference max in log2 units, as stored for the partition merge.
+__device__ __forceinline__ float max_log2(float m, float c) { return m == -__builtin_inff() ? m : m * c; }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -393,6 +464,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
 
   float m = -__builtin_inff();
   float lsum = 0.f;
+  const float slack = kRescaleSlack / a.score_scale;
   f32x4 acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -436,41 +508,24 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
     }
     float sc[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { sc[e] = sf[0][e] * a.score_scale; sc[4 + e] = sf[1][e] * a.score_scale; }
+    for (int e = 0; e < 4; ++e) { sc[e] = sf[0][e]; sc[4 + e] = sf[1][e]; }
     if (k0 + 31 > min_pos) {   // some key of this step is past some row's position
 #pragma unroll
       for (int e = 0; e < 8; ++e) sc[e] = (k0 + vkey + e <= row_pos) ? sc[e] : -__builtin_inff();
     }
-
     // ---- online softmax (row r; the four lane groups share the row)
-    float mt = sc[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sc[e]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mnew = fmaxf(m, mt);
-    const float mref = (mnew == -__builtin_inff()) ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(m - mref);
     float p[8];
-    float ps = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) { p[e] = __builtin_amdgcn_exp2f(sc[e] - mref); ps += p[e]; }
-    lsum = lsum * alpha + ps;
-    m = mnew;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+    softmax_update<8, NT>(sc, m, lsum, acc, a.score_scale, slack, p);
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T (keys past the end hold poison: their V elements
+    // are replaced by zero, by selection)
     const Frag<CT> pf = pack_p<CT>(p);
-    const bool tail = k0 + 32 > L;   // keys past the end hold poison: drop them by selection
+    const bool tail = k0 + 32 > L;
+    const int keep = L - (k0 + vkey);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       Frag<CT> vf = to_frag<CT, KV>(st.v[n]);
-      if (tail) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (k0 + vkey + e >= L) frag_zero_elem<CT>(vf, e);
-      }
+      if (tail) frag_keep_first<CT>(vf, keep);
       acc[n] = mma<CT>(acc[n], vf, pf);
     }
   };
@@ -509,7 +564,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   } else {
     const int64_t rowp = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts + part;
     if (lg == 0) {
-      a.part_m[rowp] = m;
+      a.part_m[rowp] = max_log2(m, a.score_scale);
       a.part_l[rowp] = ltot;
     }
     float* pa = a.part_acc + rowp * D + 4 * lg;
@@ -538,6 +593,389 @@ __global__ __launch_bounds__(64, 2) void attn_kernel(AttnArgs a) {
   }
 }
 
+// ============================================================================
+// chunked prefill: 128-row blocks over LDS-staged 64-key tiles
+// ============================================================================
+
+// LDS image of one 64-key tile in the 16-bit compute type: K rows [64][d]
+// and V^T rows [d][64], unpadded.  The 16-byte chunks of a row are XOR-
+// swizzled so that the 16 lanes of each MFMA operand read (16 different
+// rows, one chunk column) land in 16 different 16-byte bank groups.
+template <int D>
+struct ChunkLds {
+  static constexpr int KROW = D * 2;                   // bytes per K row
+  static constexpr int VROW = kChunkKeys * 2;          // bytes per V^T row (128)
+  static constexpr int KBYTES = kChunkKeys * KROW;
+  static constexpr int BUF = KBYTES + D * VROW;
+  // The K rows one read touches are {8*(r/4) + 4*tau + r%4} (mod 32).
+  static __device__ __forceinline__ int kswz(int key) {
+    if constexpr (D == 128) return (key & 3) | (((key >> 3) & 3) << 2);
+    else return ((key >> 1) & 1) | (((key >> 3) & 3) << 1);   // 128-byte rows pair up per 256 bytes
+  }
+  // The V^T rows one read touches are 16 consecutive dims.
+  static __device__ __forceinline__ int vswz(int dim) { return (dim >> 1) & 7; }
+  static __device__ __forceinline__ int koff(int key, int chunk) { return key * KROW + ((chunk ^ kswz(key)) << 4); }
+  static __device__ __forceinline__ int voff(int dim, int chunk) { return KBYTES + dim * VROW + ((chunk ^ vswz(dim)) << 4); }
+};
+
+// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4):
+// lane l's data lands at LDS byte offset lds_base + 16 * l, lds_base being
+// wave-uniform.  Issued as inline assembly so that the compiler does not
+// guard every later LDS read with a wait for it (it cannot tell the ring
+// buffers apart); the kernel waits for these loads itself, with s_waitcnt
+// vmcnt and a barrier, before any wave reads the buffer they fill.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base) : "memory", "m0");
+}
+
+// s_waitcnt immediate: at most n vector-memory operations outstanding
+// (expcnt and lgkmcnt left unconstrained).
+constexpr int vmcnt_imm(int n) { return 0xF70 | (n & 15) | ((n >> 4) << 14); }
+
+// 16 raw fp8 codes -> 16 elements of the 16-bit compute type (two 16-byte halves).
+template <int CT>
+__device__ __forceinline__ void widen16(const u32x4& raw, u32x4& lo, u32x4& hi) {
+  Raw<DT_FP8> a, b;
+  a.w = u32x2{raw[0], raw[1]};
+  b.w = u32x2{raw[2], raw[3]};
+  lo = to_frag<CT, DT_FP8>(a).w;
+  hi = to_frag<CT, DT_FP8>(b).w;
+}
+
+// One workgroup (8 waves, two per SIMD) per work item: sequence i, kv head h,
+// rows [256*rb, 256*rb + 256) of the sequence's (token, head-in-group) rows, keys
+// of context partition `part` (4096 keys).  Wave w owns rows 32w..32w+31 as
+// two 16-row tiles.  Each 64-key tile is gathered through the block table by
+// all 512 threads with 16-byte loads -- straight into LDS for 16-bit caches
+// (global_load_lds), through registers for fp8, which is widened to the
+// compute type on the way -- while the previous tile computes; each wave
+// then runs the same transposed-score MFMA scheme as the decode kernel,
+// every LDS operand read feeding both of its row tiles.  Keys past the end
+// are never used: their scores are replaced by -inf and their V elements by
+// zero, by selection.
+template <int CT, int KV, int D, int BS>
+__global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
+  using Lds = ChunkLds<D>;
+  // 16-bit caches: three tile buffers (two tiles in flight); fp8: two
+  // buffers plus two register sets.
+  constexpr bool DIRECT = (KV != DT_FP8);                // 16-bit cache: global -> LDS directly
+  constexpr int NBUF = DIRECT ? 3 : 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * Lds::BUF];
+  __shared__ int32_t btl[kChunkPartition / BS];          // the partition's physical block ids
+  __shared__ int slot;
+  constexpr int EBQ = Bytes<CT>::v;
+  constexpr int EBK = Bytes<KV>::v;
+  constexpr int KS = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int RT = 2;                                  // row tiles per wave
+
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid >> 6);                    // wave-uniform: keeps its branches scalar
+  const int lane = tid & 63;
+  const int r = lane & 15;
+  const int lg = lane >> 4;
+  const int64_t total = static_cast<int64_t>(uniform(a.header[3])) * a.num_kv_heads;
+  const int64_t tile_bytes = static_cast<int64_t>(BS) * D * EBK;
+  const int64_t blk_stride = tile_bytes * a.num_kv_heads;
+  const uint32_t blk_stride32 = static_cast<uint32_t>(blk_stride);   // Hkv * B * d * eb < 2^32
+
+  // Direct-to-LDS loads: wave w's load j fills tile bytes [base, base + 1 KB).
+  // Tiles start at multiples of 64 >= B, so which key (or dim) and which
+  // 16-byte chunk a lane fetches, its block relative to the tile's first
+  // block and its offset inside that block are the same for every tile.
+  constexpr int NI = Lds::BUF / 1024 / kChunkWaves;       // loads per wave per tile
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  int dma_base[NI], dma_rel[NI], dma_off[NI];
+  bool dma_is_v[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int base = (wave * NI + j) * 1024;
+    const int pos = base + lane * 16;
+    dma_base[j] = base;
+    dma_is_v[j] = base >= Lds::KBYTES;
+    if (!dma_is_v[j]) {
+      const int kk = pos / Lds::KROW;
+      const int chunk = ((pos % Lds::KROW) >> 4) ^ Lds::kswz(kk);
+      dma_rel[j] = kk / BS;
+      dma_off[j] = ((kk % BS) * D + 8 * chunk) * EBK;
+    } else {
+      const int pv = pos - Lds::KBYTES;
+      const int dim = pv / Lds::VROW;
+      const int kk = 8 * (((pv % Lds::VROW) >> 4) ^ Lds::vswz(dim));   // first of the chunk's 8 keys
+      dma_rel[j] = kk / BS;
+      dma_off[j] = (dim * BS + kk % BS) * EBK;
+    }
+  }
+
+  // LDS operand reads: lane (r, lg) reads K row kg*32 + 4*tau + rb, chunk
+  // 4s + lg, and V^T row 16n + r, chunk 4kg + lg.  The swizzle of those rows
+  // depends on r alone, so each lane needs one offset per s (K) and per kg
+  // (V); kg, tau and n then enter as immediate offsets.
+  const int rb = 8 * (r >> 2) + (r & 3);
+  int kls[KS], vls[2];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) kls[s] = Lds::koff(rb, 4 * s + lg);
+#pragma unroll
+  for (int kg = 0; kg < 2; ++kg) vls[kg] = Lds::voff(r, 4 * kg + lg);
+
+  while (true) {
+    if (tid == 0) slot = atomicAdd(a.header + 2, 1);
+    __syncthreads();
+    const int w = slot;
+    if (w >= total) break;
+    const int e = w / a.num_kv_heads;
+    const int h = w - e * a.num_kv_heads;
+    const int i = a.citems[2 * e];
+    const int tp = a.citems[2 * e + 1];
+    const int rb = tp >> 16;
+    const int part = tp & 0xFFFF;
+
+    const int L = a.seq_lens[i];
+    const int q0 = a.qsl[i];
+    const int ql = a.qsl[i + 1] - q0;
+    const int G = a.group;
+    const int rows = ql * G;
+    const int base_pos = L - ql;
+    const int wrow0 = rb * kChunkRows + wave * (16 * RT);
+    const int wlast = min(rows, wrow0 + 16 * RT) - 1;     // last row of this wave (< wrow0: none)
+    const int wave_min_pos = base_pos + wrow0 / G;
+    const int wave_max_pos = wlast >= wrow0 ? base_pos + wlast / G : -1;
+    const int wg_max_pos = base_pos + (min(rows, rb * kChunkRows + kChunkRows) - 1) / G;
+    const int kstart = part * kChunkPartition;
+    const int kend = min(min(L, kstart + kChunkPartition), wg_max_pos + 1);
+
+    if (kstart < kend) {
+      int row_pos[RT], token[RT], head[RT];
+      bool valid[RT];
+      Frag<CT> qf[RT][KS];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int R = wrow0 + 16 * rt + r;
+        valid[rt] = R < rows;
+        const int t = R / G;
+        token[rt] = q0 + t;
+        head[rt] = h * G + (R - t * G);
+        row_pos[rt] = valid[rt] ? base_pos + t : -1;
+        const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
+                            ((static_cast<int64_t>(token[rt]) * a.num_q_heads + head[rt]) * D + 8 * lg) * EBQ;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          qf[rt][s] = valid[rt] ? load_frag<CT, CT>(qp + 32 * s * EBQ) : frag_zero<CT>();
+      }
+      float m[RT], lsum[RT];
+      const float slack = kRescaleSlack / a.score_scale;
+      f32x4 acc[RT][NT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        m[rt] = -__builtin_inff();
+        lsum[rt] = 0.f;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[rt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+
+      const int nblk = (L + BS - 1) / BS;
+      const int jbase = kstart / BS;
+      {
+        const int32_t* bt = a.block_tables + static_cast<int64_t>(i) * a.max_blocks_per_seq + jbase;
+        for (int j = tid; j < min(nblk - jbase, kChunkPartition / BS); j += kChunkThreads) btl[j] = bt[j];
+      }
+      __syncthreads();
+      const uint8_t* kc = static_cast<const uint8_t*>(a.k_cache) + h * tile_bytes;
+      const uint8_t* vc = static_cast<const uint8_t*>(a.v_cache) + h * tile_bytes;
+      // physical block of tile-relative key index kk (clamped to the last block:
+      // keys past the end are loaded but never used)
+      auto phys_of = [&](int kt, int kk) -> int64_t { return btl[min((kt + kk) / BS, nblk - 1) - jbase]; };
+
+      // ---- 16-bit caches: the tile goes straight to LDS, 1 KB per wave instruction
+      auto issue_direct = [&](int b, int kt) {
+        const int jt = kt / BS - jbase;                     // tile's first block, table-relative
+        const int jlast = nblk - 1 - jbase;
+        uint32_t phys[NI];
+#pragma unroll
+        for (int j = 0; j < NI; ++j) phys[j] = static_cast<uint32_t>(btl[min(jt + dma_rel[j], jlast)]);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+          // a block id times the per-block stride (< 2^32 bytes) needs one 32x32->64 multiply-add
+          const uint8_t* src = (dma_is_v[j] ? vc : kc) +
+                               (static_cast<uint64_t>(phys[j]) * blk_stride32 + static_cast<uint32_t>(dma_off[j]));
+          lds_dma16(src, uniform(static_cast<int>(lds0 + b * Lds::BUF + dma_base[j])));
+        }
+      };
+
+      // ---- fp8 caches: 16 codes per thread-chunk through registers, widened
+      constexpr int FCH = kChunkKeys * D / 16;                // 16-code chunks of K (and of V) per tile
+      constexpr int FPT = (FCH + kChunkThreads - 1) / kChunkThreads;
+      using Regs = u32x4[DIRECT ? 1 : FPT];
+      Regs kreg0, vreg0, kreg1, vreg1;
+      auto gather_fp8 = [&](Regs& kreg, Regs& vreg, int kt) {
+#pragma unroll
+        for (int j = 0; j < FPT; ++j) {
+          const int c = tid + kChunkThreads * j;
+          if (FCH % kChunkThreads != 0 && c >= FCH) break;
+          const int kk = c / (D / 16);
+          const int cc = c % (D / 16);
+          kreg[j] = *reinterpret_cast<const u32x4*>(
+              kc + phys_of(kt, kk) * blk_stride + static_cast<int64_t>((kt + kk) % BS) * D + cc * 16);
+          const int dim = c / (kChunkKeys / 16);
+          const int kv0 = (c % (kChunkKeys / 16)) * 16;      // first of 16 keys
+          vreg[j] = *reinterpret_cast<const u32x4*>(
+              vc + phys_of(kt, kv0) * blk_stride + static_cast<int64_t>(dim) * BS + (kt + kv0) % BS);
+        }
+      };
+      auto stage_fp8 = [&](const Regs& kreg, const Regs& vreg, uint8_t* buf) {
+#pragma unroll
+        for (int j = 0; j < FPT; ++j) {
+          const int c = tid + kChunkThreads * j;
+          if (FCH % kChunkThreads != 0 && c >= FCH) break;
+          u32x4 lo, hi;
+          const int kk = c / (D / 16);
+          const int cc = c % (D / 16);                       // 16 codes = 16-bit chunks 2cc, 2cc+1
+          widen16<CT>(kreg[j], lo, hi);
+          *reinterpret_cast<u32x4*>(buf + Lds::koff(kk, 2 * cc)) = lo;
+          *reinterpret_cast<u32x4*>(buf + Lds::koff(kk, 2 * cc + 1)) = hi;
+          const int dim = c / (kChunkKeys / 16);
+          const int vc2 = (c % (kChunkKeys / 16)) * 2;
+          widen16<CT>(vreg[j], lo, hi);
+          *reinterpret_cast<u32x4*>(buf + Lds::voff(dim, vc2)) = lo;
+          *reinterpret_cast<u32x4*>(buf + Lds::voff(dim, vc2 + 1)) = hi;
+        }
+      };
+
+      // ---- one tile on this wave's rows
+      auto compute = [&](const uint8_t* buf, int kt) {
+        f32x4 sf[RT][2][2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) sf[rt][kg][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+          for (int tau = 0; tau < 2; ++tau) {
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+              Frag<CT> kf;
+              kf.w = *reinterpret_cast<const u32x4*>(buf + kls[s] + (kg * 32 + 4 * tau) * Lds::KROW);
+#pragma unroll
+              for (int rt = 0; rt < RT; ++rt) sf[rt][kg][tau] = mma<CT>(sf[rt][kg][tau], kf, qf[rt][s]);
+            }
+          }
+        Frag<CT> pf[RT][2];
+        const bool edge = kt + kChunkKeys - 1 > wave_min_pos;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          float sc[16];
+#pragma unroll
+          for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) {
+              float v = sf[rt][kg][e2 >> 2][e2 & 3];
+              if (edge && kt + kg * 32 + 8 * lg + e2 > row_pos[rt]) v = -__builtin_inff();
+              sc[kg * 8 + e2] = v;
+            }
+          float p[16];
+          softmax_update<16, NT>(sc, m[rt], lsum[rt], acc[rt], a.score_scale, slack, p);
+#pragma unroll
+          for (int kg = 0; kg < 2; ++kg) {
+            float pk[8];
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) pk[e2] = p[kg * 8 + e2];
+            pf[rt][kg] = pack_p<CT>(pk);
+          }
+        }
+        const bool tail = kt + kChunkKeys > L;   // V of keys past the end: replaced by zero
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+          for (int kg = 0; kg < 2; ++kg) {
+            Frag<CT> vf;
+            vf.w = *reinterpret_cast<const u32x4*>(buf + vls[kg] + 16 * n * Lds::VROW);
+            if (tail) frag_keep_first<CT>(vf, L - (kt + kg * 32 + 8 * lg));
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) acc[rt][n] = mma<CT>(acc[rt][n], vf, pf[rt][kg]);
+          }
+      };
+
+      const int ntiles = (kend - kstart + kChunkKeys - 1) / kChunkKeys;
+      auto tile_key = [&](int ti) { return kstart + ti * kChunkKeys; };
+      if constexpr (DIRECT) {
+        // The compiler cannot see the LDS loads; retire its own loads (q) here
+        // so that it has no reason to wait on the vector-memory counter later.
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        // tile ti lives in buffer ti % 3; tiles ti+1 and ti+2 load while ti computes
+        issue_direct(0, tile_key(0));
+        if (ntiles > 1) {
+          issue_direct(1, tile_key(1));
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));
+        } else {
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+        __syncthreads();
+        for (int ti = 0; ti < ntiles; ++ti) {
+          const int kt = tile_key(ti);
+          const bool ahead = ti + 2 < ntiles;
+          if (ahead) issue_direct((ti + 2) % 3, tile_key(ti + 2));
+          if (kt <= wave_max_pos) compute(lds + (ti % 3) * Lds::BUF, kt);
+          if (ahead) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));   // tile ti+1 has landed
+          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+          __syncthreads();
+        }
+      } else {
+        // tile ti lives in buffer ti % 2 and, before that, register set ti % 2
+        gather_fp8(kreg0, vreg0, tile_key(0));
+        stage_fp8(kreg0, vreg0, lds);
+        if (ntiles > 1) gather_fp8(kreg1, vreg1, tile_key(1));
+        __syncthreads();
+        for (int ti = 0; ti < ntiles; ti += 2) {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int tj = ti + half;
+            if (tj < ntiles) {
+              Regs& kr = half ? kreg1 : kreg0;   // holds tile tj (already staged): free
+              Regs& vr = half ? vreg1 : vreg0;
+              Regs& kn = half ? kreg0 : kreg1;   // holds tile tj + 1
+              Regs& vn = half ? vreg0 : vreg1;
+              if (tj + 2 < ntiles) gather_fp8(kr, vr, tile_key(tj + 2));
+              const int kt = tile_key(tj);
+              if (kt <= wave_max_pos) compute(lds + half * Lds::BUF, kt);
+              if (tj + 1 < ntiles) stage_fp8(kn, vn, lds + (1 - half) * Lds::BUF);
+              __syncthreads();
+            }
+          }
+        }
+      }
+
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        float ltot = lsum[rt] + __shfl_xor(lsum[rt], 16);
+        ltot += __shfl_xor(ltot, 32);
+        if (!valid[rt] || row_pos[rt] < kstart) continue;
+        if (row_pos[rt] / kChunkPartition == 0) {
+          const float inv = a.v_scale / ltot;
+          uint8_t* op = static_cast<uint8_t*>(a.out) +
+                        ((static_cast<int64_t>(token[rt]) * a.num_q_heads + head[rt]) * D + 4 * lg) * EBQ;
+#pragma unroll
+          for (int n = 0; n < NT; ++n)
+            store4<CT>(op + 16 * n * EBQ, acc[rt][n][0] * inv, acc[rt][n][1] * inv, acc[rt][n][2] * inv,
+                       acc[rt][n][3] * inv);
+        } else {
+          const int64_t rowp = (static_cast<int64_t>(token[rt]) * a.num_q_heads + head[rt]) * a.max_parts + part;
+          if (lg == 0) {
+            a.part_m[rowp] = max_log2(m[rt], a.score_scale);
+            a.part_l[rowp] = ltot;
+          }
+          float* pp = a.part_acc + rowp * D + 4 * lg;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(pp + 16 * n) = acc[rt][n] * a.v_scale;
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // One workgroup per (token, q head); rows whose keys fit one partition were
 // written by the attention kernel and are skipped here.
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p
@@ -555,7 +993,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttnArgs a) {
   const int q0 = a.qsl[i];
   const int ql = a.qsl[i + 1] - q0;
   const int row_pos = a.seq_lens[i] - ql + (token - q0);
-  const int np = row_pos / kPartition + 1;
+  const int np = row_pos / (is_chunk_seq(a, ql * a.group) ? kChunkPartition : kPartition) + 1;
   if (np <= 1) return;
   const int64_t row = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts;
   float M = -__builtin_inff();
@@ -618,32 +1056,45 @@ hipError_t launch_reshape_and_cache(int src, int kv, const CacheWriteArgs& a, hi
   return hipErrorInvalidValue;
 }
 
-// Waves of a 64-thread kernel that fit on the device at once (0 -> a default).
-static int64_t resident_waves(const void* kernel) {
+// Workgroups of `threads` threads of `kernel` that fit on the device at once.
+static int64_t resident_groups(const void* kernel, int threads) {
   int dev = 0, per_cu = 0;
   hipDeviceProp_t prop;
   if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64, 0) != hipSuccess || per_cu <= 0)
-    return 2048;
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu <= 0)
+    return 512;
   return static_cast<int64_t>(per_cu) * prop.multiProcessorCount;
 }
 
+// plan -> decode kernel -> chunk kernel (when a prompt chunk can be present)
+// -> partition merge.  ev[0..1] bracket the decode kernel, ev[2..3] the chunk
+// kernel (each may be null).
 template <int CT, int KV, int D, int BS>
-static hipError_t launch_attn(const AttnArgs& a, hipStream_t stream, hipEvent_t before, hipEvent_t after) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a.seq_lens, a.qsl, a.num_seqs,
-                     a.group, a.header, a.items, a.max_items);
+static hipError_t launch_attn(const AttnArgs& a, hipStream_t stream, const hipEvent_t* ev) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // one wave per resident slot; each loops over work items until the list is done
-  static const int64_t slots = resident_waves(reinterpret_cast<const void*>(&attn_kernel<CT, KV, D, BS>));
+  static const int64_t slots = resident_groups(reinterpret_cast<const void*>(&attn_kernel<CT, KV, D, BS>), 64);
   const int64_t want = a.max_items * a.num_kv_heads;
   const int64_t waves = want < slots ? (want > 0 ? want : 1) : slots;
-  if (before && (e = hipEventRecord(before, stream)) != hipSuccess) return e;
+  if (ev[0] && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
   hipLaunchKernelGGL((attn_kernel<CT, KV, D, BS>), dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (after && (e = hipEventRecord(after, stream)) != hipSuccess) return e;
-  if (e != hipSuccess) return e;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev[1] && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
+  if constexpr (CT != DT_F32) {
+    if (a.chunk_path && static_cast<int64_t>(a.max_query_len) * a.group >= kChunkMinRows) {
+      static const int64_t groups =
+          resident_groups(reinterpret_cast<const void*>(&chunk_kernel<CT, KV, D, BS>), kChunkThreads);
+      const int64_t cwant = a.max_citems * a.num_kv_heads;
+      const int64_t cgrid = cwant < groups ? (cwant > 0 ? cwant : 1) : groups;
+      if (ev[2] && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
+      hipLaunchKernelGGL((chunk_kernel<CT, KV, D, BS>), dim3(static_cast<unsigned>(cgrid)), dim3(kChunkThreads), 0, stream,
+                         a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if (ev[3] && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
+    }
+  }
   if (a.max_parts > 1 && a.num_tokens > 0) {
     hipLaunchKernelGGL((reduce_kernel<CT, D>), dim3(a.num_tokens, a.num_q_heads), dim3(64), 0, stream, a);
     e = hipGetLastError();
@@ -652,27 +1103,26 @@ static hipError_t launch_attn(const AttnArgs& a, hipStream_t stream, hipEvent_t 
 }
 
 template <int CT, int KV>
-static hipError_t launch_attn_shape(int d, int bs, const AttnArgs& a, hipStream_t s, hipEvent_t b,
-                                    hipEvent_t e) {
+static hipError_t launch_attn_shape(int d, int bs, const AttnArgs& a, hipStream_t s, const hipEvent_t* ev) {
   if (d == 64) {
-    if (bs == 16) return launch_attn<CT, KV, 64, 16>(a, s, b, e);
-    if (bs == 32) return launch_attn<CT, KV, 64, 32>(a, s, b, e);
-    if (bs == 64) return launch_attn<CT, KV, 64, 64>(a, s, b, e);
+    if (bs == 16) return launch_attn<CT, KV, 64, 16>(a, s, ev);
+    if (bs == 32) return launch_attn<CT, KV, 64, 32>(a, s, ev);
+    if (bs == 64) return launch_attn<CT, KV, 64, 64>(a, s, ev);
   } else if (d == 128) {
-    if (bs == 16) return launch_attn<CT, KV, 128, 16>(a, s, b, e);
-    if (bs == 32) return launch_attn<CT, KV, 128, 32>(a, s, b, e);
-    if (bs == 64) return launch_attn<CT, KV, 128, 64>(a, s, b, e);
+    if (bs == 16) return launch_attn<CT, KV, 128, 16>(a, s, ev);
+    if (bs == 32) return launch_attn<CT, KV, 128, 32>(a, s, ev);
+    if (bs == 64) return launch_attn<CT, KV, 128, 64>(a, s, ev);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attention(int q, int kv, int d, int bs, const AttnArgs& a, hipStream_t s,
-                            hipEvent_t b, hipEvent_t e) {
-  if (q == DT_F32 && kv == DT_F32) return launch_attn_shape<DT_F32, DT_F32>(d, bs, a, s, b, e);
-  if (q == DT_F16 && kv == DT_F16) return launch_attn_shape<DT_F16, DT_F16>(d, bs, a, s, b, e);
-  if (q == DT_F16 && kv == DT_FP8) return launch_attn_shape<DT_F16, DT_FP8>(d, bs, a, s, b, e);
-  if (q == DT_BF16 && kv == DT_BF16) return launch_attn_shape<DT_BF16, DT_BF16>(d, bs, a, s, b, e);
-  if (q == DT_BF16 && kv == DT_FP8) return launch_attn_shape<DT_BF16, DT_FP8>(d, bs, a, s, b, e);
+                            const hipEvent_t* ev) {
+  if (q == DT_F32 && kv == DT_F32) return launch_attn_shape<DT_F32, DT_F32>(d, bs, a, s, ev);
+  if (q == DT_F16 && kv == DT_F16) return launch_attn_shape<DT_F16, DT_F16>(d, bs, a, s, ev);
+  if (q == DT_F16 && kv == DT_FP8) return launch_attn_shape<DT_F16, DT_FP8>(d, bs, a, s, ev);
+  if (q == DT_BF16 && kv == DT_BF16) return launch_attn_shape<DT_BF16, DT_BF16>(d, bs, a, s, ev);
+  if (q == DT_BF16 && kv == DT_FP8) return launch_attn_shape<DT_BF16, DT_FP8>(d, bs, a, s, ev);
   return hipErrorInvalidValue;
 }
 

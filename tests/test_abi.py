@@ -68,6 +68,8 @@ def test_attention_argument_errors():
     assert _attn(_cache(), max_q=50) == 2                         # q_len bound above L bound
     assert _attn(_cache(), S=0, T=0) == 0                         # empty step: no-op
     assert _attn(_cache(), scale=float("nan")) == 4
+    assert _attn(_cache(), scale=0.0) == 4
+    assert _attn(_cache(), scale=-0.125) == 4
 
 
 def test_reshape_and_cache_argument_errors():
