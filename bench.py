@@ -273,7 +273,7 @@ def main():
         line["chunk_kernel_us"] = round(t * 1e6, 2)
         line["roofline_chunk"] = {"bound": "mfma", "achieved": round(flops / t / 1e12, 2), "peak": peak,
                                   "unit": "TFLOP/s", "frac": round(flops / t / 1e12 / peak, 4),
-                                  "flops": flops, "traffic": None}
+                                  "flops": flops, "traffic": measured_traffic(w.name, "chunk_kernel")}
         line["config"]["chunk_tokens"] = int((c * is_chunk).sum())
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
