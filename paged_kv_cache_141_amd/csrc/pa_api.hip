@@ -55,7 +55,7 @@ pa_status_t check_attention_sizes(const pa_cache_t* c, int32_t num_q_heads, int3
   const int64_t group = num_q_heads / c->num_kv_heads;
   // work items pack (tile, partition) into 16 bits each
   if (ceil_div(static_cast<int64_t>(max_query_len) * group, pa::kTileRows) > 0xFFFF) return PA_ERR_UNSUPPORTED;
-  if (ceil_div(max_seq_len, pa::kPartition) > 0xFFFF) return PA_ERR_UNSUPPORTED;
+  if (ceil_div(max_seq_len, pa::decode_partition(max_seq_len)) > 0xFFFF) return PA_ERR_UNSUPPORTED;
   const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, c->num_kv_heads,
                                                      c->head_dim, max_seq_len);
   if (w.max_items > 0x7FFFFFFF / 64 || w.max_citems > 0x7FFFFFFF / 64) return PA_ERR_UNSUPPORTED;
@@ -168,6 +168,7 @@ pa_status_t pa_attention(const void* q, int32_t q_dtype, const void* k_cache, co
   a.num_kv_heads = cache->num_kv_heads;
   a.group = num_q_heads / cache->num_kv_heads;
   a.max_parts = w.max_parts;
+  a.partition = w.partition;
   a.score_scale = scale * cache->k_scale * 1.4426950408889634f;
   a.v_scale = cache->v_scale;
   const hipError_t e = pa::launch_attention(q_dtype, cache->kv_dtype, cache->head_dim, cache->block_size, a,

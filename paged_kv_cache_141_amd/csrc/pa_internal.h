@@ -12,10 +12,21 @@ namespace pa {
 // q head) pairs of one sequence and kv head.
 constexpr int kTileRows = 16;
 
-// Keys of one context partition handled by one work item.  A row whose keys
-// span more than one partition gets partial (max, sum, acc) results that a
-// log-sum-exp reduce merges.
-constexpr int kPartition = 512;
+// Keys of one context partition handled by one decode work item.  A row
+// whose keys span more than one partition gets partial (max, sum, acc)
+// results that a log-sum-exp reduce merges.  Steps whose longest context
+// reaches kLongContext use the longer partition: fewer items and partials
+// per row, while still leaving thousands of items to spread over the chip.
+// A partition holds at most 64 blocks (one block id per lane of a wave).
+constexpr int kPartitionShort = 512;
+constexpr int kPartitionLong = 1024;
+#ifndef PA_LONG_CONTEXT
+#define PA_LONG_CONTEXT 8192
+#endif
+constexpr int64_t kLongContext = PA_LONG_CONTEXT;
+inline int decode_partition(int64_t max_seq_len) {
+  return max_seq_len >= kLongContext ? kPartitionLong : kPartitionShort;
+}
 
 // A sequence with more than kChunkMinRows - 1 (token, head) rows per kv head
 // (a prompt chunk) goes to the chunk kernel: 256-row blocks, 64-key LDS
@@ -51,6 +62,7 @@ struct WorkspaceLayout {
   int64_t max_items;
   int64_t max_citems;
   int32_t max_parts;
+  int32_t partition;   // decode partition length in keys
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -60,9 +72,10 @@ inline WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_tokens, in
                                         int64_t max_seq_len) {
   WorkspaceLayout w{};
   const int64_t group = num_kv_heads > 0 ? num_q_heads / num_kv_heads : 1;
-  w.max_items = max_work_items(num_seqs, num_tokens, group, max_seq_len, kTileRows, kPartition);
+  w.partition = decode_partition(max_seq_len);
+  w.max_items = max_work_items(num_seqs, num_tokens, group, max_seq_len, kTileRows, w.partition);
   w.max_citems = max_work_items(num_seqs, num_tokens, group, max_seq_len, kChunkRows, kChunkPartition);
-  w.max_parts = static_cast<int32_t>(ceil_div(max_seq_len > 0 ? max_seq_len : 1, kPartition));
+  w.max_parts = static_cast<int32_t>(ceil_div(max_seq_len > 0 ? max_seq_len : 1, w.partition));
   const size_t rows = static_cast<size_t>(num_tokens) * num_q_heads * w.max_parts;
   size_t off = 0;
   w.header = off;   off = align256(off + 64 * sizeof(int32_t));
@@ -106,6 +119,7 @@ struct AttnArgs {
   int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, group;
   int32_t max_query_len;
   int32_t max_parts;
+  int32_t partition;   // decode partition length in keys (decode_partition)
   float score_scale;   // scale * k_scale * log2(e)
   float v_scale;
 };

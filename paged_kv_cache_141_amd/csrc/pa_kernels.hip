@@ -27,6 +27,15 @@ typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
 
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
 
+// Decode-kernel tuning: steps of 16-bit K/V kept in flight ahead of the one
+// being computed, and the occupancy the register budget is cut for.
+#ifndef PA_DECODE_PREFETCH
+#define PA_DECODE_PREFETCH 2
+#endif
+#ifndef PA_DECODE_WAVES_PER_SIMD
+#define PA_DECODE_WAVES_PER_SIMD 1
+#endif
+
 template <int DT> struct Bytes;
 template <> struct Bytes<DT_F32> { static constexpr int v = 4; };
 template <> struct Bytes<DT_F16> { static constexpr int v = 2; };
@@ -142,7 +151,7 @@ __device__ __forceinline__ bool is_chunk_seq(const AttnArgs& a, int rows) {
 }
 
 // One workgroup.  For each sequence with q_len > 0 it counts work items --
-// decode: ceil(rows/16) row tiles x ceil(L/512) partitions; chunk:
+// decode: ceil(rows/16) row tiles x ceil(L/P) partitions (P = 512 or 1024); chunk:
 // ceil(rows/128) row blocks x ceil(L/4096) partitions -- takes exclusive
 // prefix sums and appends the items in (tile, partition) order to the two
 // lists.  It also resets the work counters the attention kernels draw from.
@@ -164,7 +173,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
           parts[1] = (L + kChunkPartition - 1) / kChunkPartition;
           n[1] = ((rows + kChunkRows - 1) / kChunkRows) * parts[1];
         } else {
-          parts[0] = (L + kPartition - 1) / kPartition;
+          parts[0] = (L + a.partition - 1) / a.partition;
           n[0] = ((rows + kTileRows - 1) / kTileRows) * parts[0];
         }
       }
@@ -432,8 +441,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   const int last_R = min(rows, row0 + kTileRows) - 1;
   const int max_pos = base_pos + last_R / G;
   const int min_pos = base_pos + row0 / G;
-  const int kstart = part * kPartition;
-  const int kend = min(min(L, kstart + kPartition), max_pos + 1);
+  const int kstart = part * a.partition;
+  const int kend = min(min(L, kstart + a.partition), max_pos + 1);
   if (kstart >= kend) return;
 
   // Q^T operand: row r's dims [32s + 8lg, +8)
@@ -451,10 +460,10 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   const uint8_t* kc = static_cast<const uint8_t*>(a.k_cache) + h * tile_bytes;
   const uint8_t* vc = static_cast<const uint8_t*>(a.v_cache) + h * tile_bytes;
 
-  // The partition's block-table entries, one per lane (at most P/B <= 32):
+  // The partition's block-table entries, one per lane (at most P/B <= 64):
   // each step then reads its physical block ids with readlane, no memory trip.
   const int jbase = kstart / BS;
-  const int nbt = min(nblk - jbase, kPartition / BS);
+  const int nbt = min(nblk - jbase, a.partition / BS);
   const int32_t* bt = a.block_tables + static_cast<int64_t>(i) * a.max_blocks_per_seq + jbase;
   const int btv = lane < nbt ? bt[lane] : 0;
 
@@ -532,7 +541,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
 
   // Software pipeline: the loads of step s + PF are in flight while step s
   // computes.  fp8 steps are half the bytes, so they run one step deeper.
-  constexpr int PF = (KV == DT_FP8) ? 2 : (KV == DT_F32 ? 0 : 1);
+  constexpr int PF = (KV == DT_FP8) ? 2 : (KV == DT_F32 ? 0 : PA_DECODE_PREFETCH);
   constexpr int NB = PF + 1;
   Step buf[NB];
   const int nsteps = (kend - kstart + 31) / 32;
@@ -553,7 +562,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   float ltot = lsum + __shfl_xor(lsum, 16);
   ltot += __shfl_xor(ltot, 32);
   if (!valid || row_pos < kstart) return;
-  const int nparts_row = row_pos / kPartition + 1;
+  const int nparts_row = row_pos / a.partition + 1;
   if (nparts_row == 1) {
     const float inv = a.v_scale / ltot;
     uint8_t* op = static_cast<uint8_t*>(a.out) +
@@ -577,7 +586,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
 // Waves draw work items from a counter; item w covers list entry w / Hkv and
 // kv head w % Hkv.  Every wave exits once the counter passes the item count.
 template <int CT, int KV, int D, int BS>
-__global__ __launch_bounds__(64, 2) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64, PA_DECODE_WAVES_PER_SIMD) void attn_kernel(AttnArgs a) {
   const int lane = threadIdx.x;
   const int64_t total = static_cast<int64_t>(uniform(a.header[1])) * a.num_kv_heads;
   while (true) {
@@ -624,8 +633,18 @@ struct ChunkLds {
 // guard every later LDS read with a wait for it (it cannot tell the ring
 // buffers apart); the kernel waits for these loads itself, with s_waitcnt
 // vmcnt and a barrier, before any wave reads the buffer they fill.
+// M0 carries the LDS address; it is saved and restored around the load so
+// that the compiler's own use of M0 is never disturbed.
 __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base) : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_base)
+      : "memory");
 }
 
 // s_waitcnt immediate: at most n vector-memory operations outstanding
@@ -993,7 +1012,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttnArgs a) {
   const int q0 = a.qsl[i];
   const int ql = a.qsl[i + 1] - q0;
   const int row_pos = a.seq_lens[i] - ql + (token - q0);
-  const int np = row_pos / (is_chunk_seq(a, ql * a.group) ? kChunkPartition : kPartition) + 1;
+  const int np = row_pos / (is_chunk_seq(a, ql * a.group) ? kChunkPartition : a.partition) + 1;
   if (np <= 1) return;
   const int64_t row = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts;
   float M = -__builtin_inff();
