@@ -77,9 +77,14 @@ class HipEvents:
         self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def kernel_source_hash():
+KERNEL_SOURCES = {"attn_kernel": "pa_decode.hip", "chunk_kernel": "pa_chunk.hip"}
+
+
+def kernel_source_hash(kernel):
+    """Hash of the sources one kernel is compiled from (its own file plus the
+    shared device headers): counter runs stay valid until these change."""
     h = hashlib.sha256()
-    for f in ("pa_kernels.hip", "pa_codec.h", "pa_internal.h"):
+    for f in (KERNEL_SOURCES[kernel], "pa_device.h", "pa_codec.h", "pa_internal.h"):
         h.update(open(os.path.join(ROOT, "paged_kv_cache_141_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -91,7 +96,7 @@ def measured_traffic(workload_name, kernel):
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    if d.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None
     return d.get("hbm_bytes_per_launch")
 

@@ -1,0 +1,246 @@
+// pa_device.h -- device-side building blocks of the attention kernels:
+// vector types, element sizes, MFMA operand fragments, and the online-softmax
+// step.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "pa_codec.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_FP8 = 3 };
+
+template <int DT> struct Bytes;
+template <> struct Bytes<DT_F32> { static constexpr int v = 4; };
+template <> struct Bytes<DT_F16> { static constexpr int v = 2; };
+template <> struct Bytes<DT_BF16> { static constexpr int v = 2; };
+template <> struct Bytes<DT_FP8> { static constexpr int v = 1; };
+
+// Does sequence i (rows = q_len * G) use the chunk kernel?
+__device__ __forceinline__ bool is_chunk_seq(const AttnArgs& a, int rows) {
+  return a.chunk_path && rows >= kChunkMinRows;
+}
+
+// Eight operand elements of one lane for a K=32 MFMA step (or eight K=4
+// steps for fp32): 16 bytes for 16-bit types, 32 bytes for fp32.
+template <int CT> struct Frag { u32x4 w; };
+template <> struct Frag<DT_F32> { u32x4 w[2]; };
+
+template <int CT>
+__device__ __forceinline__ Frag<CT> frag_zero() {
+  Frag<CT> f;
+  if constexpr (CT == DT_F32) { f.w[0] = u32x4{0, 0, 0, 0}; f.w[1] = f.w[0]; }
+  else f.w = u32x4{0, 0, 0, 0};
+  return f;
+}
+
+// Eight consecutive elements of storage type SRC as loaded from memory
+// (kept raw so that prefetched data costs the fewest registers).
+template <int SRC> struct Raw { u32x4 w; };
+template <> struct Raw<DT_F32> { u32x4 w[2]; };
+template <> struct Raw<DT_FP8> { u32x2 w; };
+
+template <int SRC>
+__device__ __forceinline__ Raw<SRC> load_raw(const uint8_t* p) {
+  Raw<SRC> r;
+  if constexpr (SRC == DT_F32) {
+    r.w[0] = reinterpret_cast<const u32x4*>(p)[0];
+    r.w[1] = reinterpret_cast<const u32x4*>(p)[1];
+  } else if constexpr (SRC == DT_FP8) {
+    r.w = *reinterpret_cast<const u32x2*>(p);
+  } else {
+    r.w = *reinterpret_cast<const u32x4*>(p);
+  }
+  return r;
+}
+
+// Raw elements -> MFMA operand of compute type CT.  fp8 codes widen exactly
+// to bf16/f16 (every E4M3 value is representable in both).
+template <int CT, int SRC>
+__device__ __forceinline__ Frag<CT> to_frag(const Raw<SRC>& r) {
+  Frag<CT> f;
+  if constexpr (SRC == DT_FP8) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(r.w[e], false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(r.w[e], true);
+      if constexpr (CT == DT_BF16) {
+        // exact: an E4M3 value has at most 4 significant bits, so the low half is zero
+        f.w[2 * e] = __builtin_amdgcn_perm(f2u(lo[1]), f2u(lo[0]), 0x07060302u);
+        f.w[2 * e + 1] = __builtin_amdgcn_perm(f2u(hi[1]), f2u(hi[0]), 0x07060302u);
+      } else {
+        f.w[2 * e] = f32_to_f16(lo[0]) | (f32_to_f16(lo[1]) << 16);
+        f.w[2 * e + 1] = f32_to_f16(hi[0]) | (f32_to_f16(hi[1]) << 16);
+      }
+    }
+  } else if constexpr (SRC == DT_F32) {
+    f.w[0] = r.w[0];
+    f.w[1] = r.w[1];
+  } else {
+    f.w = r.w;
+  }
+  return f;
+}
+
+template <int CT, int SRC>
+__device__ __forceinline__ Frag<CT> load_frag(const uint8_t* p) {
+  return to_frag<CT, SRC>(load_raw<SRC>(p));
+}
+
+// acc += A(16 x 32) * B(32 x 16).  A lane's 8 elements sit in the same K
+// slots of A and B, so the pairing of A and B elements only needs both
+// operands to use one assignment of data to (lane group, element).
+template <int CT>
+__device__ __forceinline__ f32x4 mma(f32x4 acc, const Frag<CT>& a, const Frag<CT>& b) {
+  if constexpr (CT == DT_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.w),
+                                                   __builtin_bit_cast(bf16x8, b.w), acc, 0, 0, 0);
+  } else if constexpr (CT == DT_F16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a.w),
+                                                  __builtin_bit_cast(f16x8, b.w), acc, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(u2f(a.w[h][e]), u2f(b.w[h][e]), acc, 0, 0, 0);
+    return acc;
+  }
+}
+
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two packed 16-bit values (hardware conversion, round to nearest
+// even; used for probabilities and outputs, never for cache contents).
+template <int CT>
+__device__ __forceinline__ uint32_t cvt2(float x, float y) {
+  if constexpr (CT == DT_BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x, y}, bf16x2v));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x, y}, f16x2v));
+}
+
+// fp32 probabilities -> operand elements.
+template <int CT>
+__device__ __forceinline__ Frag<CT> pack_p(const float (&p)[8]) {
+  Frag<CT> f;
+  if constexpr (CT == DT_F32) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.w[0][e] = f2u(p[e]); f.w[1][e] = f2u(p[e + 4]); }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f.w[e] = cvt2<CT>(p[2 * e], p[2 * e + 1]);
+  }
+  return f;
+}
+
+template <int OT>
+__device__ __forceinline__ void store4(uint8_t* p, float a, float b, float c, float d) {
+  if constexpr (OT == DT_F32)
+    *reinterpret_cast<u32x4*>(p) = u32x4{f2u(a), f2u(b), f2u(c), f2u(d)};
+  else
+    *reinterpret_cast<u32x2*>(p) = u32x2{cvt2<OT>(a, b), cvt2<OT>(c, d)};
+}
+
+// Per-element keep-masks for an 8-element operand whose element e is kept
+// when e < n (n may be <= 0 or >= 8): zeroes elements by selection, no branches.
+template <int CT>
+__device__ __forceinline__ void frag_keep_first(Frag<CT>& f, int n) {
+  if constexpr (CT == DT_F32) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.w[e >> 2][e & 3] = e < n ? f.w[e >> 2][e & 3] : 0u;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t keep = (2 * q < n ? 0x0000FFFFu : 0u) | (2 * q + 1 < n ? 0xFFFF0000u : 0u);
+      f.w[q] &= keep;
+    }
+  }
+}
+
+// Rescale threshold (log2 units): the running reference max of a row moves
+// only when a new score exceeds it by more than this, so the accumulator
+// rescale is skipped for most tiles; probabilities stay below 2^8.
+constexpr float kRescaleSlack = 8.f;
+
+// Online-softmax update for one query row whose keys are spread over the four
+// lanes r, r+16, r+32, r+48 (N raw scores per lane, already -inf where
+// masked).  m is the row's reference max in raw-score units, the same in the
+// four lanes; c = scale * k_scale * log2(e) > 0 turns raw scores into log2
+// units.  The reference moves -- and lsum and the accumulator are rescaled
+// -- only when some lane of the wave holds a score more than `slack`
+// (kRescaleSlack / c) above it; only then is the cross-lane row max taken.
+// Returns the probabilities 2^(c*(s - m)) <= 2^kRescaleSlack in p.
+template <int N, int NACC>
+__device__ __forceinline__ void softmax_update(const float (&s)[N], float& m, float& lsum,
+                                               f32x4 (&acc)[NACC], float c, float slack, float (&p)[N]) {
+  float lm = s[0];
+#pragma unroll
+  for (int e = 1; e < N; ++e) lm = fmaxf(lm, s[e]);
+  if (__any(lm > m + slack)) {
+    float rm = fmaxf(lm, __shfl_xor(lm, 16));
+    rm = fmaxf(rm, __shfl_xor(rm, 32));
+    const float mnew = fmaxf(m, rm);
+    const float alpha = (mnew == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f((m - mnew) * c);
+    lsum *= alpha;
+#pragma unroll
+    for (int n = 0; n < NACC; ++n) acc[n] *= alpha;
+    m = mnew;
+  }
+  const float cm = (m == -__builtin_inff()) ? 0.f : m * c;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c, -cm));
+    lsum += p[e];
+  }
+}
+
+// Reference max in log2 units, as stored for the partition merge.
+__device__ __forceinline__ float max_log2(float m, float c) { return m == -__builtin_inff() ? m : m * c; }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Host-side dispatch of a runtime (q dtype, kv dtype, head dim, block size)
+// to f(ct, kv, d, bs), each an std::integral_constant, for the combinations
+// the kernels are built for; others give hipErrorInvalidValue.
+template <int V> using IC = std::integral_constant<int, V>;
+
+template <int CT, int KV, class F>
+hipError_t dispatch_shape(int d, int bs, F&& f) {
+  if (d == 64) {
+    if (bs == 16) return f(IC<CT>{}, IC<KV>{}, IC<64>{}, IC<16>{});
+    if (bs == 32) return f(IC<CT>{}, IC<KV>{}, IC<64>{}, IC<32>{});
+    if (bs == 64) return f(IC<CT>{}, IC<KV>{}, IC<64>{}, IC<64>{});
+  } else if (d == 128) {
+    if (bs == 16) return f(IC<CT>{}, IC<KV>{}, IC<128>{}, IC<16>{});
+    if (bs == 32) return f(IC<CT>{}, IC<KV>{}, IC<128>{}, IC<32>{});
+    if (bs == 64) return f(IC<CT>{}, IC<KV>{}, IC<128>{}, IC<64>{});
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class F>
+hipError_t dispatch_attention(int q, int kv, int d, int bs, F&& f) {
+  if (q == DT_F32 && kv == DT_F32) return dispatch_shape<DT_F32, DT_F32>(d, bs, f);
+  if (q == DT_F16 && kv == DT_F16) return dispatch_shape<DT_F16, DT_F16>(d, bs, f);
+  if (q == DT_F16 && kv == DT_FP8) return dispatch_shape<DT_F16, DT_FP8>(d, bs, f);
+  if (q == DT_BF16 && kv == DT_BF16) return dispatch_shape<DT_BF16, DT_BF16>(d, bs, f);
+  if (q == DT_BF16 && kv == DT_FP8) return dispatch_shape<DT_BF16, DT_FP8>(d, bs, f);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

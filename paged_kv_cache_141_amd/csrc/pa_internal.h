@@ -124,13 +124,30 @@ struct AttnArgs {
   float v_scale;
 };
 
-// Launchers (defined in pa_kernels.hip).  Return hipSuccess or the launch error.
+// Workgroups of `threads` threads of `kernel` that fit on the device at once.
+inline int64_t resident_groups(const void* kernel, int threads) {
+  int dev = 0, per_cu = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu <= 0)
+    return 512;
+  return static_cast<int64_t>(per_cu) * prop.multiProcessorCount;
+}
+
+// Launchers.  Each returns hipSuccess or the launch error.
+
 hipError_t launch_reshape_and_cache(int src_dtype, int kv_dtype, const CacheWriteArgs& a,
-                                    hipStream_t stream);
+                                    hipStream_t stream);   // (pa_cache_write.hip)
 // kv_dtype, q_dtype: pa_dtype_t values; head_dim 64|128; block_size 16|32|64.
 // events[0..1] (may be null) are recorded around the decode kernel and
-// events[2..3] around the chunk kernel.
+// events[2..3] around the chunk kernel.  (pa_attention.hip)
 hipError_t launch_attention(int q_dtype, int kv_dtype, int head_dim, int block_size,
                             const AttnArgs& a, hipStream_t stream, const hipEvent_t* events);
+// The decode kernel alone (pa_decode.hip) and the chunk kernel alone
+// (pa_chunk.hip; 16-bit q only); both draw items from the plan's lists.
+hipError_t launch_decode(int q_dtype, int kv_dtype, int head_dim, int block_size, const AttnArgs& a,
+                         hipStream_t stream);
+hipError_t launch_chunk(int q_dtype, int kv_dtype, int head_dim, int block_size, const AttnArgs& a,
+                        hipStream_t stream);
 
 }  // namespace pa
