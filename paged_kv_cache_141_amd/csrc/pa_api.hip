@@ -170,6 +170,7 @@ pa_status_t pa_attention(const void* q, int32_t q_dtype, const void* k_cache, co
   a.max_parts = w.max_parts;
   a.partition = w.partition;
   a.score_scale = scale * cache->k_scale * 1.4426950408889634f;
+  a.rescale_slack = pa::kRescaleSlack / a.score_scale;
   a.v_scale = cache->v_scale;
   const hipError_t e = pa::launch_attention(q_dtype, cache->kv_dtype, cache->head_dim, cache->block_size, a,
                                             static_cast<hipStream_t>(stream), g_events);

@@ -5,71 +5,90 @@
 
 namespace pa {
 
-// One workgroup.  For each sequence with q_len > 0 it counts work items --
-// decode: ceil(rows/16) row tiles x ceil(L/P) partitions (P = 512 or 1024); chunk:
-// ceil(rows/256) row blocks x ceil(L/4096) partitions -- takes exclusive
-// prefix sums and appends the items in (tile, partition) order to the two
-// lists.  It also resets the work counters the attention kernels draw from.
+// Keys a work item visits (its partition clipped to the sequence and to the
+// causal reach of its last row), in units of the kernel's key step; 0 for an
+// item with nothing to do.  Must agree with the kernels' own bounds.
+__device__ __forceinline__ int item_size(int L, int ql, int G, int row0, int nrows, int part, int P,
+                                         int step) {
+  const int rows = ql * G;
+  const int last = min(rows, row0 + nrows) - 1;
+  const int max_pos = L - ql + last / G;
+  const int kstart = part * P;
+  const int kend = min(min(L, kstart + P), max_pos + 1);
+  return kend > kstart ? (kend - kstart + step - 1) / step : 0;
+}
+
+// One workgroup builds both work lists -- decode: (sequence, 16-row tile,
+// partition of a.partition keys); chunk: (sequence, 256-row block, partition
+// of 4096 keys) -- longest item first: items are bucketed by the number of
+// key steps they visit (32 keys for decode, 64 for chunks) and the buckets
+// are laid out in descending order, so the persistent kernels, which take
+// items in list order, start the long ones first and end on short ones.
+// Order within a bucket is arbitrary; no result depends on it.  It also
+// resets the work counters the attention kernels draw from.
 __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
-  __shared__ int32_t scan[2][1024];
-  __shared__ int64_t carry[2];
+  constexpr int NB0 = kPartitionLong / 32 + 1;           // decode buckets: 0 .. 32 steps
+  constexpr int NB1 = kChunkPartition / kChunkKeys + 1;   // chunk buckets: 0 .. 64 tiles
+  __shared__ int hist0[NB0], hist1[NB1];
+  __shared__ int total[2];
   const int tid = threadIdx.x;
-  if (tid < 2) carry[tid] = 0;
+  const int G = a.group;
+  for (int b = tid; b < NB0; b += 1024) hist0[b] = 0;
+  for (int b = tid; b < NB1; b += 1024) hist1[b] = 0;
   __syncthreads();
-  for (int base = 0; base < a.num_seqs; base += 1024) {
-    const int i = base + tid;
-    int n[2] = {0, 0}, parts[2] = {1, 1};
-    if (i < a.num_seqs) {
-      const int L = a.seq_lens[i];
-      const int ql = a.qsl[i + 1] - a.qsl[i];
-      const int rows = ql * a.group;
-      if (ql > 0 && L > 0) {
-        if (is_chunk_seq(a, rows)) {
-          parts[1] = (L + kChunkPartition - 1) / kChunkPartition;
-          n[1] = ((rows + kChunkRows - 1) / kChunkRows) * parts[1];
-        } else {
-          parts[0] = (L + a.partition - 1) / a.partition;
-          n[0] = ((rows + kTileRows - 1) / kTileRows) * parts[0];
-        }
-      }
+
+  // visit(list, i, tile, part, bucket) for every item of sequence i
+  auto items_of = [&](int i, auto&& visit) {
+    const int L = a.seq_lens[i];
+    const int ql = a.qsl[i + 1] - a.qsl[i];
+    const int rows = ql * G;
+    if (ql <= 0 || L <= 0) return;
+    if (is_chunk_seq(a, rows)) {
+      const int np = (L + kChunkPartition - 1) / kChunkPartition;
+      const int nt = (rows + kChunkRows - 1) / kChunkRows;
+      for (int t = 0; t < nt; ++t)
+        for (int p = 0; p < np; ++p)
+          visit(1, t, p, item_size(L, ql, G, t * kChunkRows, kChunkRows, p, kChunkPartition, kChunkKeys));
+    } else {
+      const int np = (L + a.partition - 1) / a.partition;
+      const int nt = (rows + kTileRows - 1) / kTileRows;
+      for (int t = 0; t < nt; ++t)
+        for (int p = 0; p < np; ++p)
+          visit(0, t, p, item_size(L, ql, G, t * kTileRows, kTileRows, p, a.partition, 32));
     }
-    scan[0][tid] = n[0];
-    scan[1][tid] = n[1];
-    __syncthreads();
-    for (int ofs = 1; ofs < 1024; ofs <<= 1) {   // inclusive Hillis-Steele scans
-      const int v0 = tid >= ofs ? scan[0][tid - ofs] : 0;
-      const int v1 = tid >= ofs ? scan[1][tid - ofs] : 0;
-      __syncthreads();
-      scan[0][tid] += v0;
-      scan[1][tid] += v1;
-      __syncthreads();
+  };
+
+  // pass 1: bucket sizes
+  for (int i = tid; i < a.num_seqs; i += 1024)
+    items_of(i, [&](int list, int, int, int bucket) { atomicAdd(list ? &hist1[bucket] : &hist0[bucket], 1); });
+  __syncthreads();
+  // bucket starts, longest bucket first
+  if (tid < 2) {
+    int* hist = tid ? hist1 : hist0;
+    const int nb = tid ? NB1 : NB0;
+    int run = 0;
+    for (int b = nb - 1; b >= 0; --b) {
+      const int c = hist[b];
+      hist[b] = run;
+      run += c;
     }
-#pragma unroll
-    for (int list = 0; list < 2; ++list) {
-      int32_t* out = list ? a.citems : a.items;
-      const int64_t cap = list ? a.max_citems : a.max_items;
-      const int64_t start = carry[list] + scan[list][tid] - n[list];
-      for (int k = 0; k < n[list]; ++k) {
-        const int64_t pos = start + k;
-        if (pos >= cap) break;              // only with metadata beyond the host bounds
-        const int tile = k / parts[list];
-        const int part = k - tile * parts[list];
-        out[2 * pos] = i;
-        out[2 * pos + 1] = (tile << 16) | part;
-      }
-    }
-    __syncthreads();
-    if (tid == 1023) {
-      carry[0] += scan[0][1023];
-      carry[1] += scan[1][1023];
-    }
-    __syncthreads();
+    total[tid] = run;
   }
+  __syncthreads();
+  // pass 2: place every item in its bucket
+  for (int i = tid; i < a.num_seqs; i += 1024)
+    items_of(i, [&](int list, int t, int p, int bucket) {
+      const int pos = atomicAdd(list ? &hist1[bucket] : &hist0[bucket], 1);
+      if (pos >= (list ? a.max_citems : a.max_items)) return;   // only with metadata beyond the host bounds
+      int32_t* out = list ? a.citems : a.items;
+      out[2 * pos] = i;
+      out[2 * pos + 1] = (t << 16) | p;
+    });
   if (tid == 0) {
     a.header[0] = 0;
-    a.header[1] = static_cast<int32_t>(carry[0] < a.max_items ? carry[0] : a.max_items);
+    a.header[1] = static_cast<int32_t>(total[0] < a.max_items ? total[0] : a.max_items);
     a.header[2] = 0;
-    a.header[3] = static_cast<int32_t>(carry[1] < a.max_citems ? carry[1] : a.max_citems);
+    a.header[3] = static_cast<int32_t>(total[1] < a.max_citems ? total[1] : a.max_citems);
   }
 }
 

@@ -67,27 +67,71 @@ __device__ __forceinline__ void widen16(const u32x4& raw, u32x4& lo, u32x4& hi) 
   hi = to_frag<CT, DT_FP8>(b).w;
 }
 
+// Softmax step of one 16-row tile over one 64-key tile, without the row sum
+// (the row sums come from the PV product with an all-ones operand): updates
+// the reference max m (lazily, as in softmax_update) and rescales the
+// accumulators, returns p = 2^(c*s - c*m) in the MFMA operand type.
+template <int CT, int NACC>
+__device__ __forceinline__ void chunk_softmax(const float (&s)[16], float& m, f32x4 (&acc)[NACC], f32x4& lacc,
+                                              float c, float slack, Frag<CT> (&pf)[2]) {
+  float lm = s[0];
+#pragma unroll
+  for (int e = 1; e < 16; ++e) lm = fmaxf(lm, s[e]);
+  if (__any(lm > m + slack)) {
+    float rm = fmaxf(lm, __shfl_xor(lm, 16));
+    rm = fmaxf(rm, __shfl_xor(rm, 32));
+    const float mnew = fmaxf(m, rm);
+    const float alpha = (mnew == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f((m - mnew) * c);
+    lacc *= alpha;
+#pragma unroll
+    for (int n = 0; n < NACC; ++n) acc[n] *= alpha;
+    m = mnew;
+  }
+  const float cm = (m == -__builtin_inff()) ? 0.f : m * c;
+#pragma unroll
+  for (int kg = 0; kg < 2; ++kg) {
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * kg + e], c, -cm));
+    pf[kg] = pack_p<CT>(p);
+  }
+}
+
+// SIMD of the calling wave (hardware id register, bits 5:4).
+__device__ __forceinline__ int simd_id() {
+  return (__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4)) & 3;
+}
+
 // One workgroup (8 waves, two per SIMD) per work item: sequence i, kv head h,
-// rows [256*rb, 256*rb + 256) of the sequence's (token, head-in-group) rows, keys
-// of context partition `part` (4096 keys).  Wave w owns rows 32w..32w+31 as
-// two 16-row tiles.  Each 64-key tile is gathered through the block table by
-// all 512 threads with 16-byte loads -- straight into LDS for 16-bit caches
-// (global_load_lds), through registers for fp8, which is widened to the
-// compute type on the way -- while the previous tile computes; each wave
-// then runs the same transposed-score MFMA scheme as the decode kernel,
-// every LDS operand read feeding both of its row tiles.  Keys past the end
-// are never used: their scores are replaced by -inf and their V elements by
-// zero, by selection.
+// rows [256*rb, 256*rb + 256) of the sequence's (token, head-in-group) rows,
+// keys of context partition `part` (4096 keys).  Wave w owns rows
+// 32w..32w+31 as two 16-row tiles.  Each 64-key tile is gathered through the
+// block table by all 512 threads with 16-byte loads -- straight into LDS for
+// 16-bit caches (global_load_lds), through registers for fp8, which is
+// widened to the compute type on the way -- two tiles ahead of the one being
+// computed.  Each wave runs the transposed-score MFMA scheme of the decode
+// kernel, every LDS operand read feeding both of its row tiles.
+//
+// The two waves that share a SIMD take different roles so that one's
+// softmax (VALU) overlaps the other's products (MFMA): in the round of tile
+// t, a "lead" wave does QK^T(t), softmax(t), PV(t); a "trail" wave does
+// PV(t-1), QK^T(t), softmax(t), finishing PV of the last tile after the
+// loop.  The LDS ring therefore keeps tile t-1 alive for one more round.
+//
+// Keys past a row's position get score -inf by selection, on the tiles that
+// hold such keys only; V columns of keys past the end of the sequence (they
+// hold whatever the pool has there) are overwritten with zero in LDS.
 template <int CT, int KV, int D, int BS>
 __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
   using Lds = ChunkLds<D>;
-  // 16-bit caches: three tile buffers (two tiles in flight); fp8: two
-  // buffers plus two register sets.
   constexpr bool DIRECT = (KV != DT_FP8);                // 16-bit cache: global -> LDS directly
-  constexpr int NBUF = DIRECT ? 3 : 2;
+  // 16-bit caches: tiles t-1 .. t+2 (two loading); fp8: t-1 .. t+1 (t+1 staged
+  // from registers after round t computes).
+  constexpr int NBUF = DIRECT ? 4 : 3;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * Lds::BUF];
   __shared__ int32_t btl[kChunkPartition / BS];          // the partition's physical block ids
   __shared__ int slot;
+  __shared__ int simd_of[kChunkWaves];
   constexpr int EBQ = Bytes<CT>::v;
   constexpr int EBK = Bytes<KV>::v;
   constexpr int KS = D / 32;
@@ -104,13 +148,28 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
   const int64_t blk_stride = tile_bytes * a.num_kv_heads;
   const uint32_t blk_stride32 = static_cast<uint32_t>(blk_stride);   // Hkv * B * d * eb < 2^32
 
+  // Role: the second wave (in wave order) on a SIMD trails.  Any assignment
+  // gives the same results; this one pairs a lead with a trail per SIMD.
+  if (lane == 0) simd_of[wave] = simd_id();
+  __syncthreads();
+  bool trail;
+  {
+    const int mine = simd_of[wave];
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < kChunkWaves; ++w) before += (w < wave && simd_of[w] == mine) ? 1 : 0;
+    trail = uniform(before & 1) != 0;
+  }
+
   // Direct-to-LDS loads: wave w's load j fills tile bytes [base, base + 1 KB).
   // Tiles start at multiples of 64 >= B, so which key (or dim) and which
   // 16-byte chunk a lane fetches, its block relative to the tile's first
   // block and its offset inside that block are the same for every tile.
   constexpr int NI = Lds::BUF / 1024 / kChunkWaves;       // loads per wave per tile
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
-  int dma_base[NI], dma_rel[NI], dma_off[NI];
+  // Per load: (block relative to the tile's first) << 20 | byte offset in
+  // the block, one register each.
+  int dma_base[NI], dma_pk[NI];
   bool dma_is_v[NI];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
@@ -121,14 +180,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
     if (!dma_is_v[j]) {
       const int kk = pos / Lds::KROW;
       const int chunk = ((pos % Lds::KROW) >> 4) ^ Lds::kswz(kk);
-      dma_rel[j] = kk / BS;
-      dma_off[j] = ((kk % BS) * D + 8 * chunk) * EBK;
+      dma_pk[j] = (kk / BS) << 20 | ((kk % BS) * D + 8 * chunk) * EBK;
     } else {
       const int pv = pos - Lds::KBYTES;
       const int dim = pv / Lds::VROW;
       const int kk = 8 * (((pv % Lds::VROW) >> 4) ^ Lds::vswz(dim));   // first of the chunk's 8 keys
-      dma_rel[j] = kk / BS;
-      dma_off[j] = (dim * BS + kk % BS) * EBK;
+      dma_pk[j] = (kk / BS) << 20 | (dim * BS + kk % BS) * EBK;
     }
   }
 
@@ -143,6 +200,13 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
 #pragma unroll
   for (int kg = 0; kg < 2; ++kg) vls[kg] = Lds::voff(r, 4 * kg + lg);
 
+  // all-ones A operand: the PV product with it yields the row sums of P
+  Frag<CT> ones;
+  {
+    const uint32_t one2 = CT == DT_BF16 ? 0x3F803F80u : 0x3C003C00u;
+    ones.w = u32x4{one2, one2, one2, one2};
+  }
+
   while (true) {
     if (tid == 0) slot = atomicAdd(a.header + 2, 1);
     __syncthreads();
@@ -152,7 +216,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
     const int h = w - e * a.num_kv_heads;
     const int i = a.citems[2 * e];
     const int tp = a.citems[2 * e + 1];
-    const int rb = tp >> 16;
+    const int rblk = tp >> 16;
     const int part = tp & 0xFFFF;
 
     const int L = a.seq_lens[i];
@@ -161,39 +225,37 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
     const int G = a.group;
     const int rows = ql * G;
     const int base_pos = L - ql;
-    const int wrow0 = rb * kChunkRows + wave * (16 * RT);
+    const int wrow0 = rblk * kChunkRows + wave * (16 * RT);
     const int wlast = min(rows, wrow0 + 16 * RT) - 1;     // last row of this wave (< wrow0: none)
     const int wave_min_pos = base_pos + wrow0 / G;
     const int wave_max_pos = wlast >= wrow0 ? base_pos + wlast / G : -1;
-    const int wg_max_pos = base_pos + (min(rows, rb * kChunkRows + kChunkRows) - 1) / G;
+    const int wg_max_pos = base_pos + (min(rows, rblk * kChunkRows + kChunkRows) - 1) / G;
     const int kstart = part * kChunkPartition;
     const int kend = min(min(L, kstart + kChunkPartition), wg_max_pos + 1);
 
     if (kstart < kend) {
-      int row_pos[RT], token[RT], head[RT];
-      bool valid[RT];
+      int row_pos[RT];
       Frag<CT> qf[RT][KS];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int R = wrow0 + 16 * rt + r;
-        valid[rt] = R < rows;
+        const bool valid = R < rows;
         const int t = R / G;
-        token[rt] = q0 + t;
-        head[rt] = h * G + (R - t * G);
-        row_pos[rt] = valid[rt] ? base_pos + t : -1;
+        row_pos[rt] = valid ? base_pos + t : -1;
         const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
-                            ((static_cast<int64_t>(token[rt]) * a.num_q_heads + head[rt]) * D + 8 * lg) * EBQ;
+                            ((static_cast<int64_t>(q0 + t) * a.num_q_heads + h * G + (R - t * G)) * D + 8 * lg) * EBQ;
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-          qf[rt][s] = valid[rt] ? load_frag<CT, CT>(qp + 32 * s * EBQ) : frag_zero<CT>();
+          qf[rt][s] = valid ? load_frag<CT, CT>(qp + 32 * s * EBQ) : frag_zero<CT>();
       }
-      float m[RT], lsum[RT];
-      const float slack = kRescaleSlack / a.score_scale;
+      float m[RT];
+      f32x4 lacc[RT];
+      const float slack = a.rescale_slack;
       f32x4 acc[RT][NT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         m[rt] = -__builtin_inff();
-        lsum[rt] = 0.f;
+        lacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[rt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -215,14 +277,20 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
       auto issue_direct = [&](int b, int kt) {
         const int jt = kt / BS - jbase;                     // tile's first block, table-relative
         const int jlast = nblk - 1 - jbase;
-        uint32_t phys[NI];
+        uint32_t phys[NI], off[NI];
 #pragma unroll
-        for (int j = 0; j < NI; ++j) phys[j] = static_cast<uint32_t>(btl[min(jt + dma_rel[j], jlast)]);
+        for (int j = 0; j < NI; ++j) {
+          // unpacked here, every tile: values derived from the packed word
+          // would otherwise be kept in registers for the whole loop
+          int pk = dma_pk[j];
+          asm volatile("" : "+v"(pk));
+          off[j] = static_cast<uint32_t>(pk & 0xFFFFF);
+          phys[j] = static_cast<uint32_t>(btl[min(jt + (pk >> 20), jlast)]);
+        }
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
           // a block id times the per-block stride (< 2^32 bytes) needs one 32x32->64 multiply-add
-          const uint8_t* src = (dma_is_v[j] ? vc : kc) +
-                               (static_cast<uint64_t>(phys[j]) * blk_stride32 + static_cast<uint32_t>(dma_off[j]));
+          const uint8_t* src = (dma_is_v[j] ? vc : kc) + (static_cast<uint64_t>(phys[j]) * blk_stride32 + off[j]);
           lds_dma16(src, uniform(static_cast<int>(lds0 + b * Lds::BUF + dma_base[j])));
         }
       };
@@ -265,9 +333,20 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
           *reinterpret_cast<u32x4*>(buf + Lds::voff(dim, vc2 + 1)) = hi;
         }
       };
+      // V^T columns of keys kt + [live, 64) are past the end: overwrite them
+      // with zero (all threads; the caller fences with a barrier).
+      auto zero_tail = [&](uint8_t* buf, int live) {
+        for (int x = tid; x < D * kChunkKeys; x += kChunkThreads) {
+          const int dim = x / kChunkKeys;
+          const int key = x % kChunkKeys;
+          if (key >= live)
+            *reinterpret_cast<uint16_t*>(buf + Lds::voff(dim, key >> 3) + 2 * (key & 7)) = 0;
+        }
+      };
 
-      // ---- one tile on this wave's rows
-      auto compute = [&](const uint8_t* buf, int kt) {
+      // ---- the two halves of a tile's work on this wave's rows
+      Frag<CT> pf[RT][2];                                    // P of the last softmax, MFMA operand
+      auto qk_softmax = [&](const uint8_t* buf, int kt) {
         f32x4 sf[RT][2][2];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -287,49 +366,66 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
               for (int rt = 0; rt < RT; ++rt) sf[rt][kg][tau] = mma<CT>(sf[rt][kg][tau], kf, qf[rt][s]);
             }
           }
-        Frag<CT> pf[RT][2];
-        const bool edge = kt + kChunkKeys - 1 > wave_min_pos;
+        float sc[RT][16];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          float sc[16];
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int kg = 0; kg < 2; ++kg)
+          for (int x = 0; x < 16; ++x) sc[rt][x] = sf[rt][x >> 3][(x >> 2) & 1][x & 3];
+        if (kt + kChunkKeys - 1 > wave_min_pos) {
+          // the lane's keys are kt + 8lg + {0..7} and kt + 8lg + 32 + {0..7}
 #pragma unroll
-            for (int e2 = 0; e2 < 8; ++e2) {
-              float v = sf[rt][kg][e2 >> 2][e2 & 3];
-              if (edge && kt + kg * 32 + 8 * lg + e2 > row_pos[rt]) v = -__builtin_inff();
-              sc[kg * 8 + e2] = v;
-            }
-          float p[16];
-          softmax_update<16, NT>(sc, m[rt], lsum[rt], acc[rt], a.score_scale, slack, p);
+          for (int rt = 0; rt < RT; ++rt) {
+            const int vis = row_pos[rt] - kt - 8 * lg;      // visible: offset <= vis
 #pragma unroll
-          for (int kg = 0; kg < 2; ++kg) {
-            float pk[8];
-#pragma unroll
-            for (int e2 = 0; e2 < 8; ++e2) pk[e2] = p[kg * 8 + e2];
-            pf[rt][kg] = pack_p<CT>(pk);
+            for (int x = 0; x < 16; ++x)
+              sc[rt][x] = ((x >> 3) * 32 + (x & 7) > vis) ? -__builtin_inff() : sc[rt][x];
           }
         }
-        const bool tail = kt + kChunkKeys > L;   // V of keys past the end: replaced by zero
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
+        for (int rt = 0; rt < RT; ++rt)
+          chunk_softmax<CT, NT>(sc[rt], m[rt], acc[rt], lacc[rt], a.score_scale, slack, pf[rt]);
+      };
+      auto pv = [&](const uint8_t* buf) {
 #pragma unroll
-          for (int kg = 0; kg < 2; ++kg) {
+        for (int kg = 0; kg < 2; ++kg) {
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
             Frag<CT> vf;
             vf.w = *reinterpret_cast<const u32x4*>(buf + vls[kg] + 16 * n * Lds::VROW);
-            if (tail) frag_keep_first<CT>(vf, L - (kt + kg * 32 + 8 * lg));
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) acc[rt][n] = mma<CT>(acc[rt][n], vf, pf[rt][kg]);
           }
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) lacc[rt] = mma<CT>(lacc[rt], ones, pf[rt][kg]);
+        }
       };
 
       const int ntiles = (kend - kstart + kChunkKeys - 1) / kChunkKeys;
       auto tile_key = [&](int ti) { return kstart + ti * kChunkKeys; };
+      auto bufp = [&](int ti) { return lds + (ti % NBUF) * Lds::BUF; };
+      // one round: tile ti is in LDS (and, for a trailing wave, tile ti-1)
+      bool pending = false;                                  // trailing wave: PV(ti-1) still to do
+      auto do_round = [&](int ti) {
+        const int kt = tile_key(ti);
+        if (kt + kChunkKeys > L) {                           // the sequence's last keys: V tail to zero
+          zero_tail(bufp(ti), L - kt);
+          __syncthreads();
+        }
+        const bool active = kt <= wave_max_pos;
+        if (trail) {
+          if (pending) pv(bufp(ti - 1));
+          if (active) qk_softmax(bufp(ti), kt);
+          pending = active;
+        } else if (active) {
+          qk_softmax(bufp(ti), kt);
+          pv(bufp(ti));
+        }
+      };
+
       if constexpr (DIRECT) {
         // The compiler cannot see the LDS loads; retire its own loads (q) here
         // so that it has no reason to wait on the vector-memory counter later.
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        // tile ti lives in buffer ti % 3; tiles ti+1 and ti+2 load while ti computes
         issue_direct(0, tile_key(0));
         if (ntiles > 1) {
           issue_direct(1, tile_key(1));
@@ -339,18 +435,18 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
         }
         __syncthreads();
         for (int ti = 0; ti < ntiles; ++ti) {
-          const int kt = tile_key(ti);
+          // buffer (ti+2) % 4 last held tile ti-2, finished in round ti-1
           const bool ahead = ti + 2 < ntiles;
-          if (ahead) issue_direct((ti + 2) % 3, tile_key(ti + 2));
-          if (kt <= wave_max_pos) compute(lds + (ti % 3) * Lds::BUF, kt);
+          if (ahead) issue_direct((ti + 2) % NBUF, tile_key(ti + 2));
+          do_round(ti);
           if (ahead) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));   // tile ti+1 has landed
           else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
           __syncthreads();
         }
       } else {
-        // tile ti lives in buffer ti % 2 and, before that, register set ti % 2
+        // register set ti % 2 holds tile ti between its gather and its staging
         gather_fp8(kreg0, vreg0, tile_key(0));
-        stage_fp8(kreg0, vreg0, lds);
+        stage_fp8(kreg0, vreg0, bufp(0));
         if (ntiles > 1) gather_fp8(kreg1, vreg1, tile_key(1));
         __syncthreads();
         for (int ti = 0; ti < ntiles; ti += 2) {
@@ -358,35 +454,39 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
           for (int half = 0; half < 2; ++half) {
             const int tj = ti + half;
             if (tj < ntiles) {
-              Regs& kr = half ? kreg1 : kreg0;   // holds tile tj (already staged): free
+              Regs& kr = half ? kreg1 : kreg0;   // held tile tj (already staged): free
               Regs& vr = half ? vreg1 : vreg0;
               Regs& kn = half ? kreg0 : kreg1;   // holds tile tj + 1
               Regs& vn = half ? vreg0 : vreg1;
               if (tj + 2 < ntiles) gather_fp8(kr, vr, tile_key(tj + 2));
-              const int kt = tile_key(tj);
-              if (kt <= wave_max_pos) compute(lds + half * Lds::BUF, kt);
-              if (tj + 1 < ntiles) stage_fp8(kn, vn, lds + (1 - half) * Lds::BUF);
+              do_round(tj);
+              // buffer (tj+1) % 3 last held tile tj-2, finished in round tj-1
+              if (tj + 1 < ntiles) stage_fp8(kn, vn, bufp(tj + 1));
               __syncthreads();
             }
           }
         }
       }
+      if (pending) pv(bufp(ntiles - 1));
 
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        float ltot = lsum[rt] + __shfl_xor(lsum[rt], 16);
-        ltot += __shfl_xor(ltot, 32);
-        if (!valid[rt] || row_pos[rt] < kstart) continue;
+        const int R = wrow0 + 16 * rt + r;
+        if (R >= rows || row_pos[rt] < kstart) continue;
+        const int t = R / G;
+        const int token = q0 + t;
+        const int head = h * G + (R - t * G);
+        const float ltot = lacc[rt][0];
         if (row_pos[rt] / kChunkPartition == 0) {
           const float inv = a.v_scale / ltot;
           uint8_t* op = static_cast<uint8_t*>(a.out) +
-                        ((static_cast<int64_t>(token[rt]) * a.num_q_heads + head[rt]) * D + 4 * lg) * EBQ;
+                        ((static_cast<int64_t>(token) * a.num_q_heads + head) * D + 4 * lg) * EBQ;
 #pragma unroll
           for (int n = 0; n < NT; ++n)
             store4<CT>(op + 16 * n * EBQ, acc[rt][n][0] * inv, acc[rt][n][1] * inv, acc[rt][n][2] * inv,
                        acc[rt][n][3] * inv);
         } else {
-          const int64_t rowp = (static_cast<int64_t>(token[rt]) * a.num_q_heads + head[rt]) * a.max_parts + part;
+          const int64_t rowp = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts + part;
           if (lg == 0) {
             a.part_m[rowp] = max_log2(m[rt], a.score_scale);
             a.part_l[rowp] = ltot;

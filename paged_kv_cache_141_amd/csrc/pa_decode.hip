@@ -89,7 +89,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
 
   float m = -__builtin_inff();
   float lsum = 0.f;
-  const float slack = kRescaleSlack / a.score_scale;
+  const float slack = a.rescale_slack;
   f32x4 acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};

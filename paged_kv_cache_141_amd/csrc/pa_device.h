@@ -172,10 +172,6 @@ __device__ __forceinline__ void frag_keep_first(Frag<CT>& f, int n) {
   }
 }
 
-// Rescale threshold (log2 units): the running reference max of a row moves
-// only when a new score exceeds it by more than this, so the accumulator
-// rescale is skipped for most tiles; probabilities stay below 2^8.
-constexpr float kRescaleSlack = 8.f;
 
 // Online-softmax update for one query row whose keys are spread over the four
 // lanes r, r+16, r+32, r+48 (N raw scores per lane, already -inf where
@@ -183,7 +179,8 @@ constexpr float kRescaleSlack = 8.f;
 // four lanes; c = scale * k_scale * log2(e) > 0 turns raw scores into log2
 // units.  The reference moves -- and lsum and the accumulator are rescaled
 // -- only when some lane of the wave holds a score more than `slack`
-// (kRescaleSlack / c) above it; only then is the cross-lane row max taken.
+// (kRescaleSlack / c, AttnArgs::rescale_slack) above it; only then is the
+// cross-lane row max taken.
 // Returns the probabilities 2^(c*(s - m)) <= 2^kRescaleSlack in p.
 template <int N, int NACC>
 __device__ __forceinline__ void softmax_update(const float (&s)[N], float& m, float& lsum,

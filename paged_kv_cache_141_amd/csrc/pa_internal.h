@@ -39,6 +39,11 @@ constexpr int kChunkRows = 32 * kChunkWaves;   // two 16-row tiles per wave
 constexpr int kChunkKeys = 64;
 constexpr int kChunkPartition = 4096;
 
+// Rescale threshold (log2 units): the running reference max of a row moves
+// only when a new score exceeds it by more than this, so the accumulator
+// rescale is skipped for most tiles; probabilities stay below 2^8.
+constexpr float kRescaleSlack = 8.f;
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Upper bound on the number of (sequence, row tile, partition) work items,
@@ -121,6 +126,7 @@ struct AttnArgs {
   int32_t max_parts;
   int32_t partition;   // decode partition length in keys (decode_partition)
   float score_scale;   // scale * k_scale * log2(e)
+  float rescale_slack; // kRescaleSlack / score_scale (raw-score units)
   float v_scale;
 };
 
