@@ -26,64 +26,115 @@ __device__ __forceinline__ int item_size(int L, int ql, int G, int row0, int nro
 // items in list order, start the long ones first and end on short ones.
 // Order within a bucket is arbitrary; no result depends on it.  It also
 // resets the work counters the attention kernels draw from.
+//
+// Sequences are taken 1024 at a time; a scan of their item counts flattens
+// the batch's items so that all threads share them evenly.
 __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
   constexpr int NB0 = kPartitionLong / 32 + 1;           // decode buckets: 0 .. 32 steps
   constexpr int NB1 = kChunkPartition / kChunkKeys + 1;   // chunk buckets: 0 .. 64 tiles
-  __shared__ int hist0[NB0], hist1[NB1];
+  __shared__ int hist[2][80];
+  __shared__ int scan[1024];                             // inclusive item-count scan of the batch
+  __shared__ int sL[1024], sQ[1024], sNP[1024];          // per sequence: L, q_len, partitions (<0: chunk list)
   __shared__ int total[2];
   const int tid = threadIdx.x;
   const int G = a.group;
-  for (int b = tid; b < NB0; b += 1024) hist0[b] = 0;
-  for (int b = tid; b < NB1; b += 1024) hist1[b] = 0;
-  __syncthreads();
+  for (int x = tid; x < 2 * 80; x += 1024) hist[x / 80][x % 80] = 0;
 
-  // visit(list, i, tile, part, bucket) for every item of sequence i
-  auto items_of = [&](int i, auto&& visit) {
-    const int L = a.seq_lens[i];
-    const int ql = a.qsl[i + 1] - a.qsl[i];
-    const int rows = ql * G;
-    if (ql <= 0 || L <= 0) return;
-    if (is_chunk_seq(a, rows)) {
-      const int np = (L + kChunkPartition - 1) / kChunkPartition;
-      const int nt = (rows + kChunkRows - 1) / kChunkRows;
-      for (int t = 0; t < nt; ++t)
-        for (int p = 0; p < np; ++p)
-          visit(1, t, p, item_size(L, ql, G, t * kChunkRows, kChunkRows, p, kChunkPartition, kChunkKeys));
-    } else {
-      const int np = (L + a.partition - 1) / a.partition;
-      const int nt = (rows + kTileRows - 1) / kTileRows;
-      for (int t = 0; t < nt; ++t)
-        for (int p = 0; p < np; ++p)
-          visit(0, t, p, item_size(L, ql, G, t * kTileRows, kTileRows, p, a.partition, 32));
+  // batch of sequences [base, base + 1024): fill the per-sequence table and the scan
+  auto load_batch = [&](int base) {
+    const int i = base + tid;
+    int n = 0, L = 0, ql = 0, np = 0;
+    if (i < a.num_seqs) {
+      L = a.seq_lens[i];
+      ql = a.qsl[i + 1] - a.qsl[i];
+      const int rows = ql * G;
+      if (ql > 0 && L > 0) {
+        if (is_chunk_seq(a, rows)) {
+          np = (L + kChunkPartition - 1) / kChunkPartition;
+          n = ((rows + kChunkRows - 1) / kChunkRows) * np;
+          np = -np;
+        } else {
+          np = (L + a.partition - 1) / a.partition;
+          n = ((rows + kTileRows - 1) / kTileRows) * np;
+        }
+      }
     }
+    __syncthreads();                                     // the previous batch is done with the table
+    sL[tid] = L;
+    sQ[tid] = ql;
+    sNP[tid] = np;
+    scan[tid] = n;
+    __syncthreads();
+    for (int ofs = 1; ofs < 1024; ofs <<= 1) {           // inclusive Hillis-Steele scan
+      const int v = tid >= ofs ? scan[tid - ofs] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+  };
+  // item k of the batch: its sequence (batch-relative), list, tile, partition and bucket
+  auto item = [&](int k, int& j, int& list, int& t, int& p, int& bucket) {
+    int lo = 0, hi = 1023;                               // first j with scan[j] > k
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (scan[mid] > k) hi = mid; else lo = mid + 1;
+    }
+    j = lo;
+    const int idx = k - (j ? scan[j - 1] : 0);
+    const int L = sL[j], ql = sQ[j], np = sNP[j];
+    list = np < 0 ? 1 : 0;
+    const int npp = np < 0 ? -np : np;
+    t = idx / npp;
+    p = idx - t * npp;
+    bucket = list ? item_size(L, ql, G, t * kChunkRows, kChunkRows, p, kChunkPartition, kChunkKeys)
+                  : item_size(L, ql, G, t * kTileRows, kTileRows, p, a.partition, 32);
   };
 
   // pass 1: bucket sizes
-  for (int i = tid; i < a.num_seqs; i += 1024)
-    items_of(i, [&](int list, int, int, int bucket) { atomicAdd(list ? &hist1[bucket] : &hist0[bucket], 1); });
-  __syncthreads();
-  // bucket starts, longest bucket first
-  if (tid < 2) {
-    int* hist = tid ? hist1 : hist0;
-    const int nb = tid ? NB1 : NB0;
-    int run = 0;
-    for (int b = nb - 1; b >= 0; --b) {
-      const int c = hist[b];
-      hist[b] = run;
-      run += c;
+  for (int base = 0; base < a.num_seqs; base += 1024) {
+    load_batch(base);
+    for (int k = tid; k < scan[1023]; k += 1024) {
+      int j, list, t, p, bucket;
+      item(k, j, list, t, p, bucket);
+      atomicAdd(&hist[list][bucket], 1);
     }
-    total[tid] = run;
   }
   __syncthreads();
-  // pass 2: place every item in its bucket
-  for (int i = tid; i < a.num_seqs; i += 1024)
-    items_of(i, [&](int list, int t, int p, int bucket) {
-      const int pos = atomicAdd(list ? &hist1[bucket] : &hist0[bucket], 1);
-      if (pos >= (list ? a.max_citems : a.max_items)) return;   // only with metadata beyond the host bounds
+  // bucket starts, longest bucket first: one wave per list scans the reversed
+  // histogram (at most 80 buckets: lanes take buckets b and b + 64)
+  if (tid < 128) {
+    const int list = tid >> 6, lane = tid & 63;
+    const int nb = list ? NB1 : NB0;
+    int carry = 0;
+    for (int half = 0; half < 2; ++half) {
+      const int r = lane + 64 * half;                    // rank from the longest bucket
+      const int b = nb - 1 - r;
+      const int c = b >= 0 ? hist[list][b] : 0;
+      int incl = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
+      }
+      if (b >= 0) hist[list][b] = carry + incl - c;
+      carry += __shfl(incl, 63);
+    }
+    if (lane == 0) total[list] = carry;
+  }
+  __syncthreads();
+  // pass 2: place every item in its bucket (a single batch is still loaded)
+  for (int base = 0; base < a.num_seqs; base += 1024) {
+    if (a.num_seqs > 1024) load_batch(base);
+    for (int k = tid; k < scan[1023]; k += 1024) {
+      int j, list, t, p, bucket;
+      item(k, j, list, t, p, bucket);
+      const int pos = atomicAdd(&hist[list][bucket], 1);
+      if (pos >= (list ? a.max_citems : a.max_items)) continue;   // only with metadata beyond the host bounds
       int32_t* out = list ? a.citems : a.items;
-      out[2 * pos] = i;
+      out[2 * pos] = base + j;
       out[2 * pos + 1] = (t << 16) | p;
-    });
+    }
+  }
   if (tid == 0) {
     a.header[0] = 0;
     a.header[1] = static_cast<int32_t>(total[0] < a.max_items ? total[0] : a.max_items);
@@ -92,13 +143,16 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
   }
 }
 
-// One workgroup per (token, q head); rows whose keys fit one partition were
-// written by the attention kernel and are skipped here.
+// Merge of split-context partials.  One workgroup (4 waves) per token and
+// group of kReduceHeads q heads; tokens whose keys fit one partition were
+// written by the attention kernels and leave at once.  Each head takes D/4
+// lanes, 4 dims per lane (16-byte loads):
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p
 template <int OT, int D>
-__global__ __launch_bounds__(64) void reduce_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
+  constexpr int LPH = D / 4;                             // lanes per head
+  constexpr int HPB = 4 * (64 / LPH);                    // heads per workgroup
   const int token = blockIdx.x;
-  const int head = blockIdx.y;
   // sequence of this token: last i with qsl[i] <= token
   int lo = 0, hi = a.num_seqs - 1;
   while (lo < hi) {
@@ -111,31 +165,30 @@ __global__ __launch_bounds__(64) void reduce_kernel(AttnArgs a) {
   const int row_pos = a.seq_lens[i] - ql + (token - q0);
   const int np = row_pos / (is_chunk_seq(a, ql * a.group) ? kChunkPartition : a.partition) + 1;
   if (np <= 1) return;
+  const int head = blockIdx.y * HPB + static_cast<int>(threadIdx.x) / LPH;
+  if (head >= a.num_q_heads) return;
+  const int d0 = (threadIdx.x % LPH) * 4;
   const int64_t row = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts;
   float M = -__builtin_inff();
   for (int p = 0; p < np; ++p) M = fmaxf(M, a.part_m[row + p]);
   float den = 0.f;
-  constexpr int PER = D / 64;
-  float num[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) num[k] = 0.f;
+  f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int p = 0; p < np; ++p) {
     const float wgt = __builtin_amdgcn_exp2f(a.part_m[row + p] - M);
     den += wgt * a.part_l[row + p];
-    const float* ap = a.part_acc + (row + p) * D;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) num[k] += wgt * ap[threadIdx.x + 64 * k];
+    num += wgt * *reinterpret_cast<const f32x4*>(a.part_acc + (row + p) * D + d0);
   }
-  constexpr int EBO = Bytes<OT>::v;
-  uint8_t* op = static_cast<uint8_t*>(a.out) + ((static_cast<int64_t>(token) * a.num_q_heads + head) * D) * EBO;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const float v = num[k] / den;
-    const int dd = threadIdx.x + 64 * k;
-    if constexpr (OT == DT_F32) reinterpret_cast<float*>(op)[dd] = v;
-    else if constexpr (OT == DT_BF16) reinterpret_cast<uint16_t*>(op)[dd] = static_cast<uint16_t>(f32_to_bf16(v));
-    else reinterpret_cast<uint16_t*>(op)[dd] = static_cast<uint16_t>(f32_to_f16(v));
-  }
+  const float inv = 1.f / den;
+  uint8_t* op = static_cast<uint8_t*>(a.out) +
+                ((static_cast<int64_t>(token) * a.num_q_heads + head) * D + d0) * Bytes<OT>::v;
+  store4<OT>(op, num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
+}
+
+template <int OT, int D>
+static void launch_reduce(const AttnArgs& a, hipStream_t stream) {
+  constexpr int HPB = 4 * (64 / (D / 4));
+  const dim3 grid(a.num_tokens, (a.num_q_heads + HPB - 1) / HPB);
+  hipLaunchKernelGGL((reduce_kernel<OT, D>), grid, dim3(256), 0, stream, a);
 }
 
 // plan -> decode kernel -> chunk kernel (when a prompt chunk can be present)
@@ -157,16 +210,15 @@ hipError_t launch_attention(int q, int kv, int d, int bs, const AttnArgs& a, hip
     if (ev[3] && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
   }
   if (a.max_parts > 1 && a.num_tokens > 0) {
-    const dim3 grid(a.num_tokens, a.num_q_heads);
     if (q == DT_F32) {
-      if (d == 64) hipLaunchKernelGGL((reduce_kernel<DT_F32, 64>), grid, dim3(64), 0, stream, a);
-      else hipLaunchKernelGGL((reduce_kernel<DT_F32, 128>), grid, dim3(64), 0, stream, a);
+      if (d == 64) launch_reduce<DT_F32, 64>(a, stream);
+      else launch_reduce<DT_F32, 128>(a, stream);
     } else if (q == DT_F16) {
-      if (d == 64) hipLaunchKernelGGL((reduce_kernel<DT_F16, 64>), grid, dim3(64), 0, stream, a);
-      else hipLaunchKernelGGL((reduce_kernel<DT_F16, 128>), grid, dim3(64), 0, stream, a);
+      if (d == 64) launch_reduce<DT_F16, 64>(a, stream);
+      else launch_reduce<DT_F16, 128>(a, stream);
     } else {
-      if (d == 64) hipLaunchKernelGGL((reduce_kernel<DT_BF16, 64>), grid, dim3(64), 0, stream, a);
-      else hipLaunchKernelGGL((reduce_kernel<DT_BF16, 128>), grid, dim3(64), 0, stream, a);
+      if (d == 64) launch_reduce<DT_BF16, 64>(a, stream);
+      else launch_reduce<DT_BF16, 128>(a, stream);
     }
     e = hipGetLastError();
   }
