@@ -167,9 +167,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
   // block and its offset inside that block are the same for every tile.
   constexpr int NI = Lds::BUF / 1024 / kChunkWaves;       // loads per wave per tile
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
-  // Per load: (block relative to the tile's first) << 20 | byte offset in
-  // the block, one register each.
-  int dma_base[NI], dma_pk[NI];
+  // Per load: the block relative to the tile's first block, and the byte
+  // offset inside the block.
+  int dma_base[NI], dma_rel[NI], dma_off[NI];
   bool dma_is_v[NI];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
@@ -180,12 +180,14 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
     if (!dma_is_v[j]) {
       const int kk = pos / Lds::KROW;
       const int chunk = ((pos % Lds::KROW) >> 4) ^ Lds::kswz(kk);
-      dma_pk[j] = (kk / BS) << 20 | ((kk % BS) * D + 8 * chunk) * EBK;
+      dma_rel[j] = kk / BS;
+      dma_off[j] = ((kk % BS) * D + 8 * chunk) * EBK;
     } else {
       const int pv = pos - Lds::KBYTES;
       const int dim = pv / Lds::VROW;
       const int kk = 8 * (((pv % Lds::VROW) >> 4) ^ Lds::vswz(dim));   // first of the chunk's 8 keys
-      dma_pk[j] = (kk / BS) << 20 | (dim * BS + kk % BS) * EBK;
+      dma_rel[j] = kk / BS;
+      dma_off[j] = (dim * BS + kk % BS) * EBK;
     }
   }
 
@@ -263,8 +265,12 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
       const int nblk = (L + BS - 1) / BS;
       const int jbase = kstart / BS;
       {
+        // the partition's block ids; past the sequence's last block the
+        // table repeats that block (keys past the end are loaded but never
+        // used), so tile loads need no clamp
         const int32_t* bt = a.block_tables + static_cast<int64_t>(i) * a.max_blocks_per_seq + jbase;
-        for (int j = tid; j < min(nblk - jbase, kChunkPartition / BS); j += kChunkThreads) btl[j] = bt[j];
+        const int nb = min(nblk - jbase, kChunkPartition / BS);
+        for (int j = tid; j < kChunkPartition / BS; j += kChunkThreads) btl[j] = bt[min(j, nb - 1)];
       }
       __syncthreads();
       const uint8_t* kc = static_cast<const uint8_t*>(a.k_cache) + h * tile_bytes;
@@ -276,21 +282,13 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
       // ---- 16-bit caches: the tile goes straight to LDS, 1 KB per wave instruction
       auto issue_direct = [&](int b, int kt) {
         const int jt = kt / BS - jbase;                     // tile's first block, table-relative
-        const int jlast = nblk - 1 - jbase;
-        uint32_t phys[NI], off[NI];
+        uint32_t phys[NI];
 #pragma unroll
-        for (int j = 0; j < NI; ++j) {
-          // unpacked here, every tile: values derived from the packed word
-          // would otherwise be kept in registers for the whole loop
-          int pk = dma_pk[j];
-          asm volatile("" : "+v"(pk));
-          off[j] = static_cast<uint32_t>(pk & 0xFFFFF);
-          phys[j] = static_cast<uint32_t>(btl[min(jt + (pk >> 20), jlast)]);
-        }
+        for (int j = 0; j < NI; ++j) phys[j] = static_cast<uint32_t>(btl[jt + dma_rel[j]]);
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
           // a block id times the per-block stride (< 2^32 bytes) needs one 32x32->64 multiply-add
-          const uint8_t* src = (dma_is_v[j] ? vc : kc) + (static_cast<uint64_t>(phys[j]) * blk_stride32 + off[j]);
+          const uint8_t* src = ((dma_is_v[j] ? vc : kc) + dma_off[j]) + static_cast<uint64_t>(phys[j]) * blk_stride32;
           lds_dma16(src, uniform(static_cast<int>(lds0 + b * Lds::BUF + dma_base[j])));
         }
       };
@@ -411,15 +409,13 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
           zero_tail(bufp(ti), L - kt);
           __syncthreads();
         }
+        // one code path for both roles (so that the accumulators keep their
+        // registers): [PV of the previous tile] QK^T + softmax [PV of this tile]
         const bool active = kt <= wave_max_pos;
-        if (trail) {
-          if (pending) pv(bufp(ti - 1));
-          if (active) qk_softmax(bufp(ti), kt);
-          pending = active;
-        } else if (active) {
-          qk_softmax(bufp(ti), kt);
-          pv(bufp(ti));
-        }
+        if (pending) pv(bufp(ti - 1));
+        if (active) qk_softmax(bufp(ti), kt);
+        if (active && !trail) pv(bufp(ti));
+        pending = active && trail;
       };
 
       if constexpr (DIRECT) {
