@@ -97,41 +97,34 @@ __device__ __forceinline__ void chunk_softmax(const float (&s)[16], float& m, f3
   }
 }
 
-// SIMD of the calling wave (hardware id register, bits 5:4).
-__device__ __forceinline__ int simd_id() {
-  return (__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4)) & 3;
-}
-
 // One workgroup (8 waves, two per SIMD) per work item: sequence i, kv head h,
 // rows [256*rb, 256*rb + 256) of the sequence's (token, head-in-group) rows,
 // keys of context partition `part` (4096 keys).  Wave w owns rows
 // 32w..32w+31 as two 16-row tiles.  Each 64-key tile is gathered through the
 // block table by all 512 threads with 16-byte loads -- straight into LDS for
 // 16-bit caches (global_load_lds), through registers for fp8, which is
-// widened to the compute type on the way -- two tiles ahead of the one being
-// computed.  Each wave runs the transposed-score MFMA scheme of the decode
-// kernel, every LDS operand read feeding both of its row tiles.
-//
-// The two waves that share a SIMD take different roles so that one's
-// softmax (VALU) overlaps the other's products (MFMA): in the round of tile
-// t, a "lead" wave does QK^T(t), softmax(t), PV(t); a "trail" wave does
-// PV(t-1), QK^T(t), softmax(t), finishing PV of the last tile after the
-// loop.  The LDS ring therefore keeps tile t-1 alive for one more round.
+// widened to the compute type on the way -- kChunkAhead tiles ahead of the
+// one being computed.  Each wave runs the transposed-score MFMA scheme of
+// the decode kernel, every LDS operand read feeding both of its row tiles.
 //
 // Keys past a row's position get score -inf by selection, on the tiles that
 // hold such keys only; V columns of keys past the end of the sequence (they
 // hold whatever the pool has there) are overwritten with zero in LDS.
+#ifndef PA_CHUNK_AHEAD
+#define PA_CHUNK_AHEAD 2
+#endif
+constexpr int kChunkAhead = PA_CHUNK_AHEAD;              // tiles in flight (16-bit caches)
+
 template <int CT, int KV, int D, int BS>
 __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
   using Lds = ChunkLds<D>;
   constexpr bool DIRECT = (KV != DT_FP8);                // 16-bit cache: global -> LDS directly
-  // 16-bit caches: tiles t-1 .. t+2 (two loading); fp8: t-1 .. t+1 (t+1 staged
-  // from registers after round t computes).
-  constexpr int NBUF = DIRECT ? 4 : 3;
+  // 16-bit caches: tile t and the kChunkAhead tiles loading behind it; fp8:
+  // tiles t and t+1 (staged from registers after round t computes).
+  constexpr int NBUF = DIRECT ? kChunkAhead + 1 : 2;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * Lds::BUF];
   __shared__ int32_t btl[kChunkPartition / BS];          // the partition's physical block ids
   __shared__ int slot;
-  __shared__ int simd_of[kChunkWaves];
   constexpr int EBQ = Bytes<CT>::v;
   constexpr int EBK = Bytes<KV>::v;
   constexpr int KS = D / 32;
@@ -147,19 +140,6 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
   const int64_t tile_bytes = static_cast<int64_t>(BS) * D * EBK;
   const int64_t blk_stride = tile_bytes * a.num_kv_heads;
   const uint32_t blk_stride32 = static_cast<uint32_t>(blk_stride);   // Hkv * B * d * eb < 2^32
-
-  // Role: the second wave (in wave order) on a SIMD trails.  Any assignment
-  // gives the same results; this one pairs a lead with a trail per SIMD.
-  if (lane == 0) simd_of[wave] = simd_id();
-  __syncthreads();
-  bool trail;
-  {
-    const int mine = simd_of[wave];
-    int before = 0;
-#pragma unroll
-    for (int w = 0; w < kChunkWaves; ++w) before += (w < wave && simd_of[w] == mine) ? 1 : 0;
-    trail = uniform(before & 1) != 0;
-  }
 
   // Direct-to-LDS loads: wave w's load j fills tile bytes [base, base + 1 KB).
   // Tiles start at multiples of 64 >= B, so which key (or dim) and which
@@ -401,42 +381,42 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
       const int ntiles = (kend - kstart + kChunkKeys - 1) / kChunkKeys;
       auto tile_key = [&](int ti) { return kstart + ti * kChunkKeys; };
       auto bufp = [&](int ti) { return lds + (ti % NBUF) * Lds::BUF; };
-      // one round: tile ti is in LDS (and, for a trailing wave, tile ti-1)
-      bool pending = false;                                  // trailing wave: PV(ti-1) still to do
+      // wait until at most the loads of the n most recently issued tiles are outstanding
+      auto wait_later = [&](int n) {
+        static_assert(kChunkAhead >= 1 && kChunkAhead <= 3, "tiles in flight: 1 to 3");
+        if (kChunkAhead >= 3 && n >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI));
+        else if (kChunkAhead >= 2 && n >= 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      };
+      // one round: tile ti is in LDS
       auto do_round = [&](int ti) {
         const int kt = tile_key(ti);
         if (kt + kChunkKeys > L) {                           // the sequence's last keys: V tail to zero
           zero_tail(bufp(ti), L - kt);
           __syncthreads();
         }
-        // one code path for both roles (so that the accumulators keep their
-        // registers): [PV of the previous tile] QK^T + softmax [PV of this tile]
-        const bool active = kt <= wave_max_pos;
-        if (pending) pv(bufp(ti - 1));
-        if (active) qk_softmax(bufp(ti), kt);
-        if (active && !trail) pv(bufp(ti));
-        pending = active && trail;
+        if (kt <= wave_max_pos) {
+          qk_softmax(bufp(ti), kt);
+          pv(bufp(ti));
+        }
       };
 
       if constexpr (DIRECT) {
         // The compiler cannot see the LDS loads; retire its own loads (q) here
         // so that it has no reason to wait on the vector-memory counter later.
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        issue_direct(0, tile_key(0));
-        if (ntiles > 1) {
-          issue_direct(1, tile_key(1));
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));
-        } else {
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        }
+        // tiles 0 .. kChunkAhead-1 in flight, then wait for tile 0
+#pragma unroll
+        for (int x = 0; x < kChunkAhead; ++x)
+          if (x < ntiles) issue_direct(x, tile_key(x));
+        wait_later(min(ntiles, kChunkAhead) - 1);
         __syncthreads();
         for (int ti = 0; ti < ntiles; ++ti) {
-          // buffer (ti+2) % 4 last held tile ti-2, finished in round ti-1
-          const bool ahead = ti + 2 < ntiles;
-          if (ahead) issue_direct((ti + 2) % NBUF, tile_key(ti + 2));
+          // buffer (ti + ahead) % NBUF last held tile ti-1, finished in round ti-1
+          if (ti + kChunkAhead < ntiles) issue_direct((ti + kChunkAhead) % NBUF, tile_key(ti + kChunkAhead));
           do_round(ti);
-          if (ahead) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));   // tile ti+1 has landed
-          else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+          // tile ti+1 has landed once at most the loads of the tiles after it are outstanding
+          wait_later(min(ntiles - 2 - ti, kChunkAhead - 1));
           __syncthreads();
         }
       } else {
@@ -456,14 +436,13 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
               Regs& vn = half ? vreg0 : vreg1;
               if (tj + 2 < ntiles) gather_fp8(kr, vr, tile_key(tj + 2));
               do_round(tj);
-              // buffer (tj+1) % 3 last held tile tj-2, finished in round tj-1
+              // buffer (tj+1) % 2 last held tile tj-1, finished in round tj-1
               if (tj + 1 < ntiles) stage_fp8(kn, vn, bufp(tj + 1));
               __syncthreads();
             }
           }
         }
       }
-      if (pending) pv(bufp(ntiles - 1));
 
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {

@@ -37,7 +37,10 @@ constexpr int kChunkWaves = 8;                 // waves per chunk workgroup (2 p
 constexpr int kChunkThreads = 64 * kChunkWaves;
 constexpr int kChunkRows = 32 * kChunkWaves;   // two 16-row tiles per wave
 constexpr int kChunkKeys = 64;
-constexpr int kChunkPartition = 4096;
+#ifndef PA_CHUNK_PARTITION
+#define PA_CHUNK_PARTITION 4096
+#endif
+constexpr int kChunkPartition = PA_CHUNK_PARTITION;
 
 // Rescale threshold (log2 units): the running reference max of a row moves
 // only when a new score exceeds it by more than this, so the accumulator
