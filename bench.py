@@ -48,6 +48,11 @@ def parse():
                          "(the known-size reference for HBM counter scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's timed sample (0 disables it)")
+    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "swap"],
+                    help="step: the attention step (default).  copy_blocks: copy-on-write of "
+                         "--pairs blocks within one pool.  swap: --pairs blocks out to page-locked "
+                         "host memory and back in.  Both use the pool geometry of --config.")
+    ap.add_argument("--pairs", type=int, default=2048, help="block pairs per copy for --op")
     return ap.parse_args()
 
 
@@ -157,12 +162,87 @@ def cpu_baseline(w, budget_s):
     }
 
 
+def bench_block_copies(args):
+    """Whole-block copies in the pool geometry of --config: copy-on-write of
+    --pairs blocks within a device pool (HBM: each pair reads and writes one K
+    and one V block), or a swap of --pairs blocks out to a page-locked host pool
+    and back (each direction moves one K and one V block per pair across the
+    host link).  Timed with events on the current stream."""
+    import numpy as np
+    import torch
+
+    import workloads
+    import paged_kv_cache_141_amd as pa
+
+    w = workloads.make(args.config)
+    eb = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}[w.kv_dtype]
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8_e4m3": torch.uint8}[w.kv_dtype]
+    H, B, d, n = w.num_kv_heads, w.block_size, w.head_dim, args.pairs
+    block_bytes = H * B * d * eb
+    nblocks = 2 * n + 1
+    gen = torch.Generator(device="cuda").manual_seed(141)
+    kd = torch.randint(0, 127, (nblocks, H, B, d), dtype=torch.int8, device="cuda", generator=gen)
+    vd = torch.randint(0, 127, (nblocks, H, d, B), dtype=torch.int8, device="cuda", generator=gen)
+    kd = kd.view(torch.uint8).view(dt) if eb == 1 else kd.view(torch.uint8).repeat_interleave(eb, -1).view(dt)
+    vd = vd.view(torch.uint8).view(dt) if eb == 1 else vd.view(torch.uint8).repeat_interleave(eb, -1).view(dt)
+    rng = np.random.default_rng(141)
+    perm = rng.permutation(nblocks)
+    stream = torch.cuda.current_stream()
+    if args.op == "copy_blocks":
+        mapping = torch.from_numpy(np.stack([perm[:n], perm[n:2 * n]], 1).astype(np.int64)).cuda()
+        run = [lambda: pa.copy_blocks(kd, vd, kd, vd, mapping)]
+        moved = 2 * 2 * block_bytes * n          # K and V, read and written
+        names, bound, peak = ["copy_blocks"], "hbm", HBM_PEAK_GBS
+    else:
+        kh = torch.empty((n, H, B, d), dtype=dt, pin_memory=True)
+        vh = torch.empty((n, H, d, B), dtype=dt, pin_memory=True)
+        out = torch.from_numpy(np.stack([perm[:n], np.arange(n)], 1).astype(np.int64)).cuda()
+        back = torch.from_numpy(np.stack([np.arange(n), perm[n:2 * n]], 1).astype(np.int64)).cuda()
+        run = [lambda: pa.copy_blocks(kd, vd, kh, vh, out), lambda: pa.copy_blocks(kh, vh, kd, vd, back)]
+        moved = 2 * block_bytes * n              # K and V cross the link once per direction
+        names, bound, peak = ["swap_out", "swap_in"], "host link", None
+        # the link's own rate for contiguous page-locked copies, for scale
+        big = torch.empty(n * 2 * block_bytes, dtype=torch.uint8, pin_memory=True)
+        dev = torch.empty(n * 2 * block_bytes, dtype=torch.uint8, device="cuda")
+    res = {}
+    for name, fn in zip(names, run):
+        for _ in range(args.warmup):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        res[name] = ms
+    line = {"op": args.op, "workload": w.name, "pairs": n, "block_bytes_k_plus_v": 2 * block_bytes,
+            "steps": args.steps, "warmup": args.warmup}
+    for name in names:
+        gbs = moved / (res[name] * 1e-3) / 1e9
+        line[name] = {"us": round(res[name] * 1e3, 2), "GBps": round(gbs, 1), "bound": bound,
+                      "peak": peak, "frac": round(gbs / peak, 4) if peak else None}
+    if args.op == "swap":
+        for name, src, dst in (("memcpy_d2h", dev, big), ("memcpy_h2d", big, dev)):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                dst.copy_(src, non_blocking=True)
+            torch.cuda.synchronize()
+            dt_s = (time.perf_counter() - t0) / args.steps
+            line[name + "_contiguous_GBps"] = round(big.numel() / dt_s / 1e9, 1)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(each sequence is independent; see the sharding notes).", file=sys.stderr)
         sys.exit(2)
+    if args.op != "step":
+        return bench_block_copies(args)
     import numpy as np
     import torch
 

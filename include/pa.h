@@ -147,6 +147,38 @@ pa_status_t pa_attention(const void* q, int32_t q_dtype, const void* k_cache,
                          void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Copy whole blocks: copy-on-write within a pool, or swapping between a
+ * device pool and a host pool.
+ *
+ * For each pair k in [0, num_pairs) with s = block_mapping[2k] and
+ * t = block_mapping[2k+1]: block t of the destination K pool (all kv heads)
+ * becomes a copy of block s of the source K pool, and likewise for V.  A
+ * block shared by several sequences is copied before one of them writes a
+ * token into it (pass the same pool as source and destination), and the
+ * blocks of a preempted request move out to host memory and back (itwiki
+ * "vLLM", sections on block sharing with copy-on-write, and on scheduling
+ * and preemption).  The copy is byte-exact.
+ *
+ *   src_k, src_v  source pool, [device] or page-locked [host], in the layout
+ *                 above for src_cache.
+ *   dst_k, dst_v  destination pool, [device] or page-locked [host], dst_cache.
+ *   src_cache, dst_cache [host]: must agree on block_size, num_kv_heads,
+ *                 head_dim and kv_dtype (PA_ERR_SHAPE otherwise); num_blocks
+ *                 may differ; the scales are not used.
+ *   block_mapping [device] int64 [num_pairs][2].
+ * Host pools must be page-locked allocations the device can address
+ * (hipHostMalloc, torch pin_memory); a pointer the runtime does not know,
+ * or device memory of another device, is PA_ERR_UNSUPPORTED, detected
+ * before anything is enqueued.  Pairs with an id outside its pool are
+ * skipped.  Destination blocks must be distinct and, within one pool, no
+ * destination may also be a source (the result would depend on order).
+ * num_pairs == 0 is a no-op.
+ */
+pa_status_t pa_copy_blocks(const void* src_k, const void* src_v, const pa_cache_t* src_cache, void* dst_k,
+                           void* dst_v, const pa_cache_t* dst_cache, const int64_t* block_mapping,
+                           int32_t num_pairs, void* stream);
+
+/*
  * Debug check of metadata contents.  Synchronous: copies the metadata to the
  * host (on `stream`) and returns PA_ERR_METADATA if any sequence has
  * q_len < 0, q_len > L, L > max_seq_len, q_len > max_query_len,

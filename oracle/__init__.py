@@ -15,11 +15,13 @@ function cites the passage of the pages it follows:
   (block tables and slot mapping survive the kernel rewrite) and
   "Redesign 4" (query_start_loc, seq_lens, slot mapping as step inputs);
 * the vLLM V1 article (techknowgenie), "Dynamic Chunked Prefill" (decode and
-  prompt chunks share one step) and "FP8 KV cache quantization".
+  prompt chunks share one step) and "FP8 KV cache quantization";
+* the itwiki "vLLM" article's sections on block sharing with copy-on-write
+  and on scheduling and preemption (whole-block copies, ``blocks``).
 
 Pins: every function is checked in ``tests/test_oracle_*.py`` against
 something other than itself (library casts, brute force, closed forms,
 invariants the pages state).  No function here is "parity unpinned".
 """
 
-from . import codecs, cache, attention  # noqa: F401
+from . import codecs, cache, attention, blocks  # noqa: F401

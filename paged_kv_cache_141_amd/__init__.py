@@ -21,7 +21,8 @@ from typing import Optional
 
 __all__ = [
     "PagedAttentionError", "library", "library_path", "reshape_and_cache", "attention",
-    "attention_workspace_size", "check_metadata", "set_attention_events", "PA_F32", "PA_F16", "PA_BF16", "PA_FP8_E4M3",
+    "attention_workspace_size", "check_metadata", "copy_blocks", "set_attention_events", "PA_F32", "PA_F16",
+    "PA_BF16", "PA_FP8_E4M3",
 ]
 
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
@@ -70,6 +71,7 @@ def library() -> ctypes.CDLL:
         "pa_attention_workspace_size": [CP, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
         "pa_attention": [P, I32, P, P, CP, P, I32, P, P, I32, I32, I32, I32, I32, F, P, P, SZ, P],
         "pa_check_metadata": [CP, P, I32, P, P, I32, I32, I32, I32, ctypes.POINTER(I32), P],
+        "pa_copy_blocks": [P, P, CP, P, P, CP, P, I32, P],
         "pa_set_attention_events": [P, P],
         "pa_set_chunk_events": [P, P],
         "pa_status_string": [I32],
@@ -221,6 +223,35 @@ def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scal
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "pa_attention")
     return out
+
+
+def _pool(t, name):
+    """Pointer of a pool tensor that the device can address: device memory or
+    page-locked host memory (pin_memory)."""
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be a device tensor or page-locked host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def copy_blocks(src_k, src_v, dst_k, dst_v, block_mapping, stream=None) -> None:
+    """Copy whole blocks (``pa_copy_blocks``): for each row (s, t) of the int64
+    ``[n, 2]`` device tensor ``block_mapping``, block t of (dst_k, dst_v)
+    becomes block s of (src_k, src_v).  The same pool on both sides is a
+    copy-on-write; a pinned host pool on one side is a swap."""
+    torch = _torch()
+    src = cache_spec(src_k, src_v)
+    dst = cache_spec(dst_k, dst_v)
+    if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be int64 [n, 2]")
+    n = block_mapping.shape[0]
+    if n == 0:
+        return
+    st = library().pa_copy_blocks(_pool(src_k, "src_k"), _pool(src_v, "src_v"), ctypes.byref(src),
+                                  _pool(dst_k, "dst_k"), _pool(dst_v, "dst_v"), ctypes.byref(dst),
+                                  _dev(block_mapping, "block_mapping"), n, _stream(stream))
+    _check(st, "pa_copy_blocks")
 
 
 def set_attention_events(before, after) -> None:

@@ -62,6 +62,28 @@ pa_status_t check_attention_sizes(const pa_cache_t* c, int32_t num_q_heads, int3
   return PA_OK;
 }
 
+// The address a kernel uses for pool pointer p: device memory of the current
+// device as is, page-locked host memory through its device mapping.  False
+// for anything else (pageable host memory, another device's memory).
+bool kernel_address(const void* p, const void** out) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();   // clear the sticky error of the failed query
+    return false;
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (attr.type == hipMemoryTypeDevice && attr.device == dev) {
+    *out = p;
+    return true;
+  }
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer) {
+    *out = attr.devicePointer;
+    return true;
+  }
+  return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -105,6 +127,40 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value, int32_t src
   a.v_scale = cache->v_scale;
   const hipError_t e = pa::launch_reshape_and_cache(src_dtype, cache->kv_dtype, a,
                                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status_t pa_copy_blocks(const void* src_k, const void* src_v, const pa_cache_t* src_cache, void* dst_k,
+                           void* dst_v, const pa_cache_t* dst_cache, const int64_t* block_mapping,
+                           int32_t num_pairs, void* stream) {
+  pa_status_t st = check_cache(src_cache);
+  if (st != PA_OK) return st;
+  if ((st = check_cache(dst_cache)) != PA_OK) return st;
+  if (src_cache->block_size != dst_cache->block_size || src_cache->num_kv_heads != dst_cache->num_kv_heads ||
+      src_cache->head_dim != dst_cache->head_dim || src_cache->kv_dtype != dst_cache->kv_dtype)
+    return PA_ERR_SHAPE;
+  if (num_pairs < 0) return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !block_mapping) return PA_ERR_NULL;
+  pa::BlockCopyArgs a{};
+  const void* p = nullptr;
+  if (!kernel_address(src_k, &p)) return PA_ERR_UNSUPPORTED;
+  a.src_k = p;
+  if (!kernel_address(src_v, &p)) return PA_ERR_UNSUPPORTED;
+  a.src_v = p;
+  if (!kernel_address(dst_k, &p)) return PA_ERR_UNSUPPORTED;
+  a.dst_k = const_cast<void*>(p);
+  if (!kernel_address(dst_v, &p)) return PA_ERR_UNSUPPORTED;
+  a.dst_v = const_cast<void*>(p);
+  if (!kernel_address(block_mapping, &p)) return PA_ERR_UNSUPPORTED;
+  a.mapping = static_cast<const int64_t*>(p);
+  static const int kEb[] = {4, 2, 2, 1};
+  a.block_bytes = static_cast<int64_t>(src_cache->num_kv_heads) * src_cache->block_size * src_cache->head_dim *
+                  kEb[src_cache->kv_dtype];
+  a.src_blocks = src_cache->num_blocks;
+  a.dst_blocks = dst_cache->num_blocks;
+  a.num_pairs = num_pairs;
+  const hipError_t e = pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -143,10 +143,22 @@ inline int64_t resident_groups(const void* kernel, int threads) {
   return static_cast<int64_t>(per_cu) * prop.multiProcessorCount;
 }
 
+struct BlockCopyArgs {
+  const void* src_k;
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
+  const int64_t* mapping;   // [num_pairs][2]: (src block, dst block)
+  int64_t block_bytes;      // Hkv * B * d * eb: one block of K (or of V)
+  int64_t src_blocks, dst_blocks;
+  int32_t num_pairs;
+};
+
 // Launchers.  Each returns hipSuccess or the launch error.
 
 hipError_t launch_reshape_and_cache(int src_dtype, int kv_dtype, const CacheWriteArgs& a,
                                     hipStream_t stream);   // (pa_cache_write.hip)
+hipError_t launch_copy_blocks(const BlockCopyArgs& a, hipStream_t stream);   // (pa_blocks.hip)
 // kv_dtype, q_dtype: pa_dtype_t values; head_dim 64|128; block_size 16|32|64.
 // events[0..1] (may be null) are recorded around the decode kernel and
 // events[2..3] around the chunk kernel.  (pa_attention.hip)

@@ -108,3 +108,19 @@ def test_binding_rejects_host_tensors():
         pa.reshape_and_cache(key, key, k, v, torch.zeros(1, dtype=torch.int64))
     with pytest.raises(ValueError):
         pa.cache_spec(k, k)      # V must be [N, H, d, B]
+
+
+def test_copy_blocks_argument_errors():
+    lib = pa.library()
+    c = _cache()
+    m = FAKE
+    assert lib.pa_copy_blocks(FAKE, FAKE, ctypes.byref(c), FAKE, FAKE, ctypes.byref(c), m, 0, None) == 0
+    assert lib.pa_copy_blocks(FAKE, FAKE, ctypes.byref(c), FAKE, FAKE, ctypes.byref(c), m, -1, None) == 2
+    assert lib.pa_copy_blocks(FAKE, FAKE, None, FAKE, FAKE, ctypes.byref(c), m, 1, None) == 1
+    assert lib.pa_copy_blocks(None, FAKE, ctypes.byref(c), FAKE, FAKE, ctypes.byref(c), m, 1, None) == 1
+    assert lib.pa_copy_blocks(FAKE, FAKE, ctypes.byref(c), FAKE, FAKE, ctypes.byref(c), None, 1, None) == 1
+    other = _cache(num_blocks=99)                                # pool sizes may differ ...
+    assert lib.pa_copy_blocks(FAKE, FAKE, ctypes.byref(c), FAKE, FAKE, ctypes.byref(other), m, 0, None) == 0
+    for bad in (_cache(block_size=32), _cache(num_kv_heads=4), _cache(head_dim=128),
+                _cache(kv_dtype=pa.PA_F16)):                     # ... the block geometry may not
+        assert lib.pa_copy_blocks(FAKE, FAKE, ctypes.byref(c), FAKE, FAKE, ctypes.byref(bad), m, 1, None) == 2
