@@ -48,10 +48,12 @@ def parse():
                          "(the known-size reference for HBM counter scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's timed sample (0 disables it)")
-    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "swap"],
+    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "swap", "prepare"],
                     help="step: the attention step (default).  copy_blocks: copy-on-write of "
                          "--pairs blocks within one pool.  swap: --pairs blocks out to page-locked "
-                         "host memory and back in.  Both use the pool geometry of --config.")
+                         "host memory and back in.  Both use the pool geometry of --config.  prepare: "
+                         "the step inputs of --config built on the GPU from 1,024 persistent request "
+                         "slots (staged block-table writes + pa_prepare_step).")
     ap.add_argument("--pairs", type=int, default=2048, help="block pairs per copy for --op")
     return ap.parse_args()
 
@@ -235,12 +237,97 @@ def bench_block_copies(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_prepare(args):
+    """Step inputs of --config from persistent state: the sequences sit in
+    scattered slots of a 1,024-slot table; this step's new blocks (those past
+    the blocks of the cached tokens) arrive as staged runs in page-locked host
+    memory.  Times the two GPU calls with events, and, for scale, the same
+    preparation done with vectorised NumPy on the host plus the upload of the
+    whole table that the staged writes avoid."""
+    import numpy as np
+    import torch
+
+    import workloads
+    import paged_kv_cache_141_amd as pa
+
+    w = workloads.make(args.config)
+    R, S, B = 1024, w.num_seqs, w.block_size
+    W = max(512, w.block_tables.shape[1])
+    rng = np.random.default_rng(141)
+    slot_of = rng.permutation(R)[:S].astype(np.int32)
+    done = np.zeros(R, np.int32)
+    done[slot_of] = w.seq_lens - w.query_lens
+    table = np.zeros((R, W), np.int32)
+    table[slot_of, :w.block_tables.shape[1]] = w.block_tables
+    first_new = -(-(w.seq_lens - w.query_lens) // B)          # blocks already holding cached tokens
+    last = -(-w.seq_lens // B)
+    runs = [(int(slot_of[i]), int(first_new[i]), w.block_tables[i, first_new[i]:last[i]]) for i in range(S)
+            if last[i] > first_new[i]]
+    rows = torch.tensor([r[0] for r in runs], dtype=torch.int32).pin_memory()
+    starts = torch.tensor([r[1] for r in runs], dtype=torch.int32).pin_memory()
+    offs = torch.from_numpy(np.concatenate([[0], np.cumsum([len(r[2]) for r in runs])]).astype(np.int32)).pin_memory()
+    vals = torch.from_numpy(np.concatenate([r[2] for r in runs]).astype(np.int32)).pin_memory()
+    g_table = torch.from_numpy(table).cuda()
+    g_idx = torch.from_numpy(slot_of).cuda()
+    g_done = torch.from_numpy(done).cuda()
+    g_sched = torch.from_numpy(w.query_lens.astype(np.int32)).cuda()
+    stream = torch.cuda.current_stream()
+
+    def gpu():
+        pa.apply_block_table_writes(g_table, rows, starts, offs, vals)
+        return pa.prepare_step(g_table, g_idx, g_done, g_sched, w.num_tokens, B)
+
+    for _ in range(args.warmup):
+        gpu()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        gpu()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    gpu_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+
+    def host():
+        sched = w.query_lens.astype(np.int64)
+        qsl = np.concatenate([[0], np.cumsum(sched)])
+        base = done[slot_of].astype(np.int64)
+        lens = base + sched
+        tok_req = np.repeat(np.arange(S), sched)
+        pos = base[tok_req] + (np.arange(w.num_tokens) - qsl[tok_req])
+        slots = table[slot_of[tok_req], pos // B].astype(np.int64) * B + pos % B
+        return qsl, lens, pos, slots, table[slot_of]
+
+    for _ in range(3):
+        host()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        host()
+    host_us = (time.perf_counter() - t0) / args.steps * 1e6
+    full = torch.from_numpy(table).pin_memory()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g_table.copy_(full, non_blocking=True)
+    torch.cuda.synchronize()
+    upload_us = (time.perf_counter() - t0) / args.steps * 1e6
+    print(json.dumps({"op": "prepare", "workload": w.name, "persistent_slots": R, "table_width": W,
+                      "requests": S, "tokens": w.num_tokens, "staged_runs": len(runs), "staged_values": int(vals.numel()),
+                      "gpu_us": round(gpu_us, 2), "gpu_wall_us_per_step": round(wall * 1e6, 2), "bound": "latency",
+                      "host_numpy_us": round(host_us, 2), "full_table_upload_us": round(upload_us, 2),
+                      "full_table_bytes": int(table.nbytes)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(each sequence is independent; see the sharding notes).", file=sys.stderr)
         sys.exit(2)
+    if args.op == "prepare":
+        return bench_prepare(args)
     if args.op != "step":
         return bench_block_copies(args)
     import numpy as np

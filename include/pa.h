@@ -179,6 +179,68 @@ pa_status_t pa_copy_blocks(const void* src_k, const void* src_v, const pa_cache_
                            int32_t num_pairs, void* stream);
 
 /*
+ * Staged block-table writes.  The block table lives in device memory, one
+ * row per persistent request slot; the host records only what changed, as
+ * runs (row, start, values), packs them into one small buffer and has one
+ * kernel apply them (llm-wiki "vLLM 0.25 Model Runner V2", "Redesign 3").
+ *
+ * For each write k in [0, num_writes):
+ *   block_table[write_rows[k]][write_starts[k] + j] = write_values[write_offsets[k] + j]
+ *   for j in [0, write_offsets[k+1] - write_offsets[k]).
+ *
+ *   block_table  [device] int32 [max_reqs][max_blocks], updated in place.
+ *   write_rows, write_starts [device or page-locked host] int32 [num_writes].
+ *   write_offsets [device or page-locked host] int32 [num_writes + 1],
+ *                non-decreasing, write_offsets[0] = 0, last = num_values.
+ *   write_values [device or page-locked host] int32 [num_values].
+ * Staging buffers in page-locked host memory are read by the kernel over
+ * the host link (no separate copy); other host memory is
+ * PA_ERR_UNSUPPORTED.  Writes whose row or columns fall outside the table
+ * are skipped.  Two writes to one entry leave either value.  A call with no
+ * writes is a no-op.
+ */
+pa_status_t pa_apply_block_table_writes(int32_t* block_table, int32_t max_reqs, int32_t max_blocks,
+                                        const int32_t* write_rows, const int32_t* write_starts,
+                                        const int32_t* write_offsets, const int32_t* write_values,
+                                        int32_t num_writes, int32_t num_values, void* stream);
+
+/*
+ * Inputs of one step from persistent request state, built on the GPU
+ * (llm-wiki "vLLM 0.25 Model Runner V2", "Redesign 1": a request keeps its
+ * slot while active and idx_mapping names the slot each batch position
+ * reads; "Redesign 4": query_start_loc is the running sum of the per-request
+ * token counts, and positions, seq_lens and the slot mapping are built on
+ * the GPU).  For batch position b in [0, num_reqs) with s = idx_mapping[b]:
+ *   query_start_loc[0] = 0, query_start_loc[b+1] = query_start_loc[b] + num_scheduled[b]
+ *   seq_lens[b]  = num_computed[s] + num_scheduled[b]
+ *   step_block_tables[b][:] = block_table[s][:]
+ * and for query token t = query_start_loc[b] + i, i < num_scheduled[b]:
+ *   positions[t]    = num_computed[s] + i
+ *   slot_mapping[t] = block_table[s][positions[t] / block_size] * block_size
+ *                     + positions[t] % block_size
+ * num_computed counts the request's tokens already in the cache; the
+ * outputs feed pa_reshape_and_cache and pa_attention directly.
+ *
+ *   block_table [device] int32 [max_reqs][max_blocks] (by persistent slot).
+ *   idx_mapping [device] int32 [num_reqs]; num_computed [device] int32
+ *               [max_reqs]; num_scheduled [device] int32 [num_reqs].
+ *   query_start_loc [device] int32 [num_reqs + 1]; seq_lens [device] int32
+ *               [num_reqs]; positions, slot_mapping [device] int64
+ *               [num_tokens]; step_block_tables [device] int32
+ *               [num_reqs][max_blocks].
+ * num_tokens must equal the sum of num_scheduled (the scheduler knows it);
+ * tokens past that sum, tokens whose block is past the table's width and
+ * tokens of a batch position whose slot is outside [0, max_reqs) get
+ * position -1 and slot -1 (a skipped cache write).  num_reqs == 0 is a no-op.
+ */
+pa_status_t pa_prepare_step(const int32_t* block_table, int32_t max_reqs, int32_t max_blocks,
+                            const int32_t* idx_mapping, const int32_t* num_computed,
+                            const int32_t* num_scheduled, int32_t num_reqs, int32_t num_tokens,
+                            int32_t block_size, int32_t* query_start_loc, int32_t* seq_lens,
+                            int64_t* positions, int64_t* slot_mapping, int32_t* step_block_tables,
+                            void* stream);
+
+/*
  * Debug check of metadata contents.  Synchronous: copies the metadata to the
  * host (on `stream`) and returns PA_ERR_METADATA if any sequence has
  * q_len < 0, q_len > L, L > max_seq_len, q_len > max_query_len,

@@ -17,11 +17,14 @@ function cites the passage of the pages it follows:
 * the vLLM V1 article (techknowgenie), "Dynamic Chunked Prefill" (decode and
   prompt chunks share one step) and "FP8 KV cache quantization";
 * the itwiki "vLLM" article's sections on block sharing with copy-on-write
-  and on scheduling and preemption (whole-block copies, ``blocks``).
+  and on scheduling and preemption (whole-block copies, ``blocks``);
+* the llm-wiki article's "Redesign 1", "Redesign 3" and "Redesign 4" (step
+  inputs from persistent request slots and staged block-table writes,
+  ``metadata``).
 
 Pins: every function is checked in ``tests/test_oracle_*.py`` against
 something other than itself (library casts, brute force, closed forms,
 invariants the pages state).  No function here is "parity unpinned".
 """
 
-from . import codecs, cache, attention, blocks  # noqa: F401
+from . import codecs, cache, attention, blocks, metadata  # noqa: F401

@@ -21,7 +21,8 @@ from typing import Optional
 
 __all__ = [
     "PagedAttentionError", "library", "library_path", "reshape_and_cache", "attention",
-    "attention_workspace_size", "check_metadata", "copy_blocks", "set_attention_events", "PA_F32", "PA_F16",
+    "attention_workspace_size", "check_metadata", "copy_blocks", "apply_block_table_writes", "prepare_step",
+    "set_attention_events", "PA_F32", "PA_F16",
     "PA_BF16", "PA_FP8_E4M3",
 ]
 
@@ -72,6 +73,8 @@ def library() -> ctypes.CDLL:
         "pa_attention": [P, I32, P, P, CP, P, I32, P, P, I32, I32, I32, I32, I32, F, P, P, SZ, P],
         "pa_check_metadata": [CP, P, I32, P, P, I32, I32, I32, I32, ctypes.POINTER(I32), P],
         "pa_copy_blocks": [P, P, CP, P, P, CP, P, I32, P],
+        "pa_apply_block_table_writes": [P, I32, I32, P, P, P, P, I32, I32, P],
+        "pa_prepare_step": [P, I32, I32, P, P, P, I32, I32, I32, P, P, P, P, P, P],
         "pa_set_attention_events": [P, P],
         "pa_set_chunk_events": [P, P],
         "pa_status_string": [I32],
@@ -252,6 +255,57 @@ def copy_blocks(src_k, src_v, dst_k, dst_v, block_mapping, stream=None) -> None:
                                   _pool(dst_k, "dst_k"), _pool(dst_v, "dst_v"), ctypes.byref(dst),
                                   _dev(block_mapping, "block_mapping"), n, _stream(stream))
     _check(st, "pa_copy_blocks")
+
+
+def _i32(t, name, n=None, host_ok=False):
+    torch = _torch()
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    if n is not None and t.numel() != n:
+        raise ValueError(f"{name} must have {n} elements")
+    return _pool(t, name) if host_ok else _dev(t, name)
+
+
+def apply_block_table_writes(block_table, rows, starts, offsets, values, stream=None) -> None:
+    """Apply staged (row, start, values) runs to the device block table in
+    place (``pa_apply_block_table_writes``).  The staging tensors may live in
+    page-locked host memory; the kernel reads them there."""
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [max_reqs, max_blocks]")
+    n = rows.numel()
+    if n == 0 or values.numel() == 0:
+        return
+    st = library().pa_apply_block_table_writes(
+        _i32(block_table, "block_table"), block_table.shape[0], block_table.shape[1],
+        _i32(rows, "rows", n, True), _i32(starts, "starts", n, True), _i32(offsets, "offsets", n + 1, True),
+        _i32(values, "values", None, True), n, values.numel(), _stream(stream))
+    _check(st, "pa_apply_block_table_writes")
+
+
+def prepare_step(block_table, idx_mapping, num_computed, num_scheduled, num_tokens: int, block_size: int,
+                 stream=None):
+    """Build the step's query_start_loc, seq_lens, positions, slot_mapping and
+    block-table rows from persistent slot state (``pa_prepare_step``).
+    Returns them as new device tensors."""
+    torch = _torch()
+    R = idx_mapping.numel()
+    dev = block_table.device
+    qsl = torch.empty(R + 1, dtype=torch.int32, device=dev)
+    lens = torch.empty(R, dtype=torch.int32, device=dev)
+    pos = torch.empty(num_tokens, dtype=torch.int64, device=dev)
+    slots = torch.empty(num_tokens, dtype=torch.int64, device=dev)
+    tables = torch.empty(R, block_table.shape[1], dtype=torch.int32, device=dev)
+    if R == 0:
+        qsl.zero_()
+        return qsl, lens, pos, slots, tables
+    st = library().pa_prepare_step(
+        _i32(block_table, "block_table"), block_table.shape[0], block_table.shape[1],
+        _i32(idx_mapping, "idx_mapping"), _i32(num_computed, "num_computed", block_table.shape[0]),
+        _i32(num_scheduled, "num_scheduled", R), R, num_tokens, block_size, _dev(qsl, "qsl"), _dev(lens, "lens"),
+        _dev(pos, "positions") if num_tokens else None, _dev(slots, "slot_mapping") if num_tokens else None,
+        _dev(tables, "tables"), _stream(stream))
+    _check(st, "pa_prepare_step")
+    return qsl, lens, pos, slots, tables
 
 
 def set_attention_events(before, after) -> None:

@@ -164,6 +164,63 @@ pa_status_t pa_copy_blocks(const void* src_k, const void* src_v, const pa_cache_
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+pa_status_t pa_apply_block_table_writes(int32_t* block_table, int32_t max_reqs, int32_t max_blocks,
+                                        const int32_t* write_rows, const int32_t* write_starts,
+                                        const int32_t* write_offsets, const int32_t* write_values,
+                                        int32_t num_writes, int32_t num_values, void* stream) {
+  if (max_reqs <= 0 || max_blocks <= 0 || num_writes < 0 || num_values < 0) return PA_ERR_SHAPE;
+  if (num_writes == 0 || num_values == 0) return PA_OK;
+  if (!block_table || !write_rows || !write_starts || !write_offsets || !write_values) return PA_ERR_NULL;
+  pa::TableWriteArgs a{};
+  const void* p = nullptr;
+  if (!kernel_address(block_table, &p)) return PA_ERR_UNSUPPORTED;
+  a.table = static_cast<int32_t*>(const_cast<void*>(p));
+  if (!kernel_address(write_rows, &p)) return PA_ERR_UNSUPPORTED;
+  a.rows = static_cast<const int32_t*>(p);
+  if (!kernel_address(write_starts, &p)) return PA_ERR_UNSUPPORTED;
+  a.starts = static_cast<const int32_t*>(p);
+  if (!kernel_address(write_offsets, &p)) return PA_ERR_UNSUPPORTED;
+  a.offsets = static_cast<const int32_t*>(p);
+  if (!kernel_address(write_values, &p)) return PA_ERR_UNSUPPORTED;
+  a.values = static_cast<const int32_t*>(p);
+  a.max_reqs = max_reqs;
+  a.max_blocks = max_blocks;
+  a.num_writes = num_writes;
+  a.num_values = num_values;
+  const hipError_t e = pa::launch_table_writes(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status_t pa_prepare_step(const int32_t* block_table, int32_t max_reqs, int32_t max_blocks,
+                            const int32_t* idx_mapping, const int32_t* num_computed,
+                            const int32_t* num_scheduled, int32_t num_reqs, int32_t num_tokens,
+                            int32_t block_size, int32_t* query_start_loc, int32_t* seq_lens,
+                            int64_t* positions, int64_t* slot_mapping, int32_t* step_block_tables,
+                            void* stream) {
+  if (max_reqs <= 0 || max_blocks <= 0 || num_reqs < 0 || num_tokens < 0 || block_size <= 0) return PA_ERR_SHAPE;
+  if (num_reqs == 0) return PA_OK;
+  if (!block_table || !idx_mapping || !num_computed || !num_scheduled || !query_start_loc || !seq_lens ||
+      !step_block_tables || (num_tokens > 0 && (!positions || !slot_mapping)))
+    return PA_ERR_NULL;
+  pa::StepArgs a{};
+  a.table = block_table;
+  a.idx_mapping = idx_mapping;
+  a.num_computed = num_computed;
+  a.num_scheduled = num_scheduled;
+  a.qsl = query_start_loc;
+  a.seq_lens = seq_lens;
+  a.positions = positions;
+  a.slot_mapping = slot_mapping;
+  a.step_tables = step_block_tables;
+  a.max_reqs = max_reqs;
+  a.max_blocks = max_blocks;
+  a.num_reqs = num_reqs;
+  a.num_tokens = num_tokens;
+  a.block_size = block_size;
+  const hipError_t e = pa::launch_prepare_step(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 pa_status_t pa_attention_workspace_size(const pa_cache_t* cache, int32_t num_q_heads, int32_t num_seqs,
                                         int32_t num_tokens, int32_t max_seq_len, int32_t max_query_len,
                                         size_t* bytes) {

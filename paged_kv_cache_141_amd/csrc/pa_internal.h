@@ -154,11 +154,36 @@ struct BlockCopyArgs {
   int32_t num_pairs;
 };
 
+struct TableWriteArgs {
+  int32_t* table;           // [max_reqs][max_blocks]
+  const int32_t* rows;      // [num_writes]
+  const int32_t* starts;    // [num_writes]
+  const int32_t* offsets;   // [num_writes + 1]: write k's values are values[offsets[k] .. offsets[k+1])
+  const int32_t* values;    // [num_values]
+  int32_t max_reqs, max_blocks, num_writes;
+  int64_t num_values;
+};
+
+struct StepArgs {
+  const int32_t* table;          // [max_reqs][max_blocks], by persistent slot
+  const int32_t* idx_mapping;    // [num_reqs]: persistent slot of batch position b
+  const int32_t* num_computed;   // [max_reqs]: tokens already in the cache, by slot
+  const int32_t* num_scheduled;  // [num_reqs]: query tokens this step, by batch position
+  int32_t* qsl;                  // [num_reqs + 1]
+  int32_t* seq_lens;             // [num_reqs]
+  int64_t* positions;            // [num_tokens]
+  int64_t* slot_mapping;         // [num_tokens]
+  int32_t* step_tables;          // [num_reqs][max_blocks]
+  int32_t max_reqs, max_blocks, num_reqs, num_tokens, block_size;
+};
+
 // Launchers.  Each returns hipSuccess or the launch error.
 
 hipError_t launch_reshape_and_cache(int src_dtype, int kv_dtype, const CacheWriteArgs& a,
                                     hipStream_t stream);   // (pa_cache_write.hip)
 hipError_t launch_copy_blocks(const BlockCopyArgs& a, hipStream_t stream);   // (pa_blocks.hip)
+hipError_t launch_table_writes(const TableWriteArgs& a, hipStream_t stream);  // (pa_metadata.hip)
+hipError_t launch_prepare_step(const StepArgs& a, hipStream_t stream);        // (pa_metadata.hip)
 // kv_dtype, q_dtype: pa_dtype_t values; head_dim 64|128; block_size 16|32|64.
 // events[0..1] (may be null) are recorded around the decode kernel and
 // events[2..3] around the chunk kernel.  (pa_attention.hip)
