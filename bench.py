@@ -55,6 +55,9 @@ def parse():
                          "the step inputs of --config built on the GPU from 1,024 persistent request "
                          "slots (staged block-table writes + pa_prepare_step).")
     ap.add_argument("--pairs", type=int, default=2048, help="block pairs per copy for --op")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="attend through pa_attention_shared_prefix over the workload's common prefix "
+                         "(fp8_shared_prefix): the prefix is attended once for all rows")
     return ap.parse_args()
 
 
@@ -363,6 +366,13 @@ def main():
     print(f"[bench] staging {w.name}: {json.dumps(w.summary())}", file=sys.stderr, flush=True)
     t_stage = time.perf_counter()
     step = wd.stage(w, write_new=False)
+    prefix = 0
+    if args.shared_prefix:
+        if not (w.shared_prefix_len and w.prefix_blocks_shared):
+            print("--shared-prefix needs a workload whose sequences share prefix blocks", file=sys.stderr)
+            sys.exit(2)
+        prefix = w.shared_prefix_len
+        step.use_shared_prefix(prefix)
     torch.cuda.synchronize()
     print(f"[bench] staged in {time.perf_counter() - t_stage:.1f}s", file=sys.stderr, flush=True)
 
@@ -374,6 +384,7 @@ def main():
     chunk_rows = w.query_lens.astype(np.int64) * w.group
     is_chunk = (chunk_rows >= 65) & (w.q_dtype != "f32")
     chunk_pairs = [(ev.create(), ev.create()) for _ in range(args.steps)] if is_chunk.any() else None
+    prefix_pairs = [(ev.create(), ev.create()) for _ in range(args.steps)] if prefix else None
     cw = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
 
@@ -385,6 +396,8 @@ def main():
         pa.set_attention_events(pairs[k][0], pairs[k][1])
         if chunk_pairs:
             pa.set_chunk_events(chunk_pairs[k][0], chunk_pairs[k][1])
+        if prefix_pairs:
+            pa.set_prefix_events(prefix_pairs[k][0], prefix_pairs[k][1])
         cw[k][0].record(stream)
         step.write_new()
         cw[k][1].record(stream)
@@ -393,17 +406,20 @@ def main():
     t1 = time.perf_counter()
     pa.set_attention_events(None, None)
     pa.set_chunk_events(None, None)
+    pa.set_prefix_events(None, None)
 
     step_s = (t1 - t0) / args.steps
     attn_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
     cw_ms = [a.elapsed_time(b) for a, b in cw]
     chunk_ms = [ev.elapsed_ms(a, b) for a, b in chunk_pairs] if chunk_pairs else None
-    for a, b in pairs + (chunk_pairs or []):
+    prefix_ms = [ev.elapsed_ms(a, b) for a, b in prefix_pairs] if prefix_pairs else None
+    for a, b in pairs + (chunk_pairs or []) + (prefix_pairs or []):
         ev.destroy(a), ev.destroy(b)
     attn_s = float(np.mean(attn_ms)) / 1e3
     # the decode kernel reads the KV of the sequences routed to it (all but chunk sequences)
     eb = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}[w.kv_dtype]
-    decode_bytes = int((w.seq_lens.astype(np.int64) * ~is_chunk).sum()) * w.num_kv_heads * 2 * w.head_dim * eb
+    # (with a shared prefix: the keys past it)
+    decode_bytes = int(((w.seq_lens.astype(np.int64) - prefix) * ~is_chunk).sum()) * w.num_kv_heads * 2 * w.head_dim * eb
     achieved = decode_bytes / attn_s / 1e9
     traffic = measured_traffic(w.name, "attn_kernel")
 
@@ -435,6 +451,16 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": None,
     }
+    if prefix_ms:
+        # the prefix pass: every query row against every prefix key
+        pflops = 4 * w.head_dim * w.num_q_heads * w.num_tokens * prefix
+        tp = float(np.mean(prefix_ms)) / 1e3
+        line["config"]["shared_prefix_tokens"] = prefix
+        line["prefix_pass_us"] = round(tp * 1e6, 2)
+        line["roofline_prefix"] = {"bound": "mfma", "achieved": round(pflops / tp / 1e12, 2), "peak": 2500.0,
+                                   "unit": "TFLOP/s", "frac": round(pflops / tp / 1e12 / 2500.0, 4),
+                                   "flops": pflops, "prefix_kv_bytes": prefix * w.num_kv_heads * 2 * w.head_dim * eb,
+                                   "traffic": None}
     if chunk_ms:
         L = w.seq_lens.astype(np.int64)
         c = w.query_lens.astype(np.int64)

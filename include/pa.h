@@ -147,6 +147,45 @@ pa_status_t pa_attention(const void* q, int32_t q_dtype, const void* k_cache,
                          void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Paged attention of a step whose sequences all share a prefix (cascade).
+ *
+ * Same arguments and result as pa_attention, plus prefix_len: every
+ * sequence's first prefix_len cache positions are the same physical blocks
+ * (block_tables[i][0 .. prefix_len/B) equal for all i; the kernels read
+ * sequence 0's row for them), and every query row sits at or past
+ * position prefix_len (seq_lens[i] - q_len_i >= prefix_len).  A prompt
+ * shared by many requests, such as a system prompt, keeps its blocks once
+ * with a reference count per block (itwiki "vLLM", section on block sharing
+ * with copy-on-write; techknowgenie "vLLM V1 core refactoring", section on
+ * restoring system prompts and multi-turn history without recomputation:
+ * blocks whose token hash matches are re-linked by reference count, e.g. an
+ * 8,000-token system prompt).  The shared keys are then read once for all
+ * rows of the step:
+ * one pass attends every query row to the prefix as a dense MFMA
+ * contraction, the usual kernels attend each row to its own keys past the
+ * prefix, and the log-sum-exp merge joins the two.  Mathematically the
+ * result equals pa_attention's.
+ *
+ * prefix_len must be a multiple of the block size, at most max_seq_len
+ * (PA_ERR_SHAPE otherwise); prefix_len == 0 is pa_attention.  A 16-bit
+ * query is required (PA_ERR_UNSUPPORTED for fp32).  Sequences that break
+ * the sharing or position conditions get undefined rows, never an
+ * out-of-bounds access.  The workspace comes from
+ * pa_attention_shared_prefix_workspace_size with the same arguments.
+ */
+pa_status_t pa_attention_shared_prefix_workspace_size(const pa_cache_t* cache, int32_t num_q_heads,
+                                                      int32_t num_seqs, int32_t num_tokens, int32_t max_seq_len,
+                                                      int32_t max_query_len, int32_t prefix_len, size_t* bytes);
+
+pa_status_t pa_attention_shared_prefix(const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
+                                       const pa_cache_t* cache, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                       const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                                       int32_t num_q_heads, int32_t max_seq_len, int32_t max_query_len,
+                                       int32_t prefix_len, float scale, void* out, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
  * Copy whole blocks: copy-on-write within a pool, or swapping between a
  * device pool and a host pool.
  *
@@ -273,6 +312,12 @@ pa_status_t pa_set_attention_events(void* before, void* after);
  * a 16-bit q); the events are recorded only on calls that launch it.
  */
 pa_status_t pa_set_chunk_events(void* before, void* after);
+
+/*
+ * The same hook for the shared-prefix pass of pa_attention_shared_prefix
+ * (recorded only on calls with prefix_len > 0).
+ */
+pa_status_t pa_set_prefix_events(void* before, void* after);
 
 /* Static text for a status code. */
 const char* pa_status_string(pa_status_t status);

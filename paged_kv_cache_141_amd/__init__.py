@@ -71,12 +71,15 @@ def library() -> ctypes.CDLL:
         "pa_reshape_and_cache": [P, P, I32, P, P, CP, P, I32, P],
         "pa_attention_workspace_size": [CP, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
         "pa_attention": [P, I32, P, P, CP, P, I32, P, P, I32, I32, I32, I32, I32, F, P, P, SZ, P],
+        "pa_attention_shared_prefix_workspace_size": [CP, I32, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
+        "pa_attention_shared_prefix": [P, I32, P, P, CP, P, I32, P, P, I32, I32, I32, I32, I32, I32, F, P, P, SZ, P],
         "pa_check_metadata": [CP, P, I32, P, P, I32, I32, I32, I32, ctypes.POINTER(I32), P],
         "pa_copy_blocks": [P, P, CP, P, P, CP, P, I32, P],
         "pa_apply_block_table_writes": [P, I32, I32, P, P, P, P, I32, I32, P],
         "pa_prepare_step": [P, I32, I32, P, P, P, I32, I32, I32, P, P, P, P, P, P],
         "pa_set_attention_events": [P, P],
         "pa_set_chunk_events": [P, P],
+        "pa_set_prefix_events": [P, P],
         "pa_status_string": [I32],
         "pa_version": [],
     }
@@ -185,11 +188,14 @@ def attention_workspace_size(k_cache, v_cache, num_q_heads: int, num_seqs: int, 
 def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale: float, *,
               max_seq_len: Optional[int] = None, max_query_len: Optional[int] = None,
               out=None, workspace=None, k_scale: float = 1.0, v_scale: float = 1.0,
-              stream=None):
+              prefix_len: int = 0, stream=None):
     """Paged attention of one mixed step (``pa_attention``); returns ``out``.
 
     max_seq_len / max_query_len are host-side upper bounds; if omitted they
-    are read from the device tensors, which synchronises the stream.
+    are read from the device tensors, which synchronises the stream.  With
+    ``prefix_len`` > 0 every sequence shares its first prefix_len positions
+    (the same blocks) and every query sits past them
+    (``pa_attention_shared_prefix``: the prefix is attended once for all rows).
     """
     torch = _torch()
     spec = cache_spec(k_cache, v_cache, k_scale, v_scale)
@@ -213,18 +219,28 @@ def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scal
         raise ValueError("out must match q")
     lib = library()
     need = ctypes.c_size_t(0)
-    _check(lib.pa_attention_workspace_size(ctypes.byref(spec), Hq, S, T, max_seq_len,
-                                           max_query_len, ctypes.byref(need)),
-           "pa_attention_workspace_size")
+    if prefix_len:
+        _check(lib.pa_attention_shared_prefix_workspace_size(ctypes.byref(spec), Hq, S, T, max_seq_len,
+                                                             max_query_len, int(prefix_len), ctypes.byref(need)),
+               "pa_attention_shared_prefix_workspace_size")
+    else:
+        _check(lib.pa_attention_workspace_size(ctypes.byref(spec), Hq, S, T, max_seq_len,
+                                               max_query_len, ctypes.byref(need)),
+               "pa_attention_workspace_size")
     if workspace is None:
         workspace = torch.empty(max(int(need.value), 256), dtype=torch.uint8, device=q.device)
-    st = lib.pa_attention(
-        _dev(q, "q"), _dtype_code(q), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-        ctypes.byref(spec), _dev(block_tables, "block_tables"), block_tables.shape[1],
-        _dev(seq_lens, "seq_lens"), _dev(query_start_loc, "query_start_loc"), S, T, Hq,
-        int(max_seq_len), int(max_query_len), float(scale), _dev(out, "out"),
-        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
-    _check(st, "pa_attention")
+    args = [_dev(q, "q"), _dtype_code(q), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+            ctypes.byref(spec), _dev(block_tables, "block_tables"), block_tables.shape[1],
+            _dev(seq_lens, "seq_lens"), _dev(query_start_loc, "query_start_loc"), S, T, Hq,
+            int(max_seq_len), int(max_query_len)]
+    tail = [float(scale), _dev(out, "out"), _dev(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream)]
+    if prefix_len:
+        st = lib.pa_attention_shared_prefix(*args, int(prefix_len), *tail)
+        _check(st, "pa_attention_shared_prefix")
+    else:
+        st = lib.pa_attention(*args, *tail)
+        _check(st, "pa_attention")
     return out
 
 
@@ -316,6 +332,11 @@ def set_attention_events(before, after) -> None:
 def set_chunk_events(before, after) -> None:
     """Bracket the chunk (prefill) kernel with two hipEvent_t handles, or None, None."""
     _check(library().pa_set_chunk_events(before, after), "pa_set_chunk_events")
+
+
+def set_prefix_events(before, after) -> None:
+    """Bracket the shared-prefix pass with two hipEvent_t handles, or None, None."""
+    _check(library().pa_set_prefix_events(before, after), "pa_set_prefix_events")
 
 
 def check_metadata(k_cache, v_cache, block_tables, seq_lens, query_start_loc, num_tokens: int,

@@ -13,9 +13,10 @@ namespace {
 
 using pa::ceil_div;
 
-// The measurement hooks of pa_set_attention_events / pa_set_chunk_events
-// (the library's only state): decode kernel pair, then chunk kernel pair.
-hipEvent_t g_events[4] = {nullptr, nullptr, nullptr, nullptr};
+// The measurement hooks of pa_set_attention_events / pa_set_chunk_events /
+// pa_set_prefix_events (the library's only state): decode kernel pair, chunk
+// kernel pair, shared-prefix pass pair.
+hipEvent_t g_events[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
 
 bool dtype_known(int32_t d) { return d >= PA_F32 && d <= PA_FP8_E4M3; }
 
@@ -82,6 +83,78 @@ bool kernel_address(const void* p, const void** out) {
     return true;
   }
   return false;
+}
+
+// A shared prefix: whole blocks, no longer than the longest context, and a
+// 16-bit query (the prefix pass runs on the chunk kernel).
+pa_status_t check_prefix(const pa_cache_t* c, int32_t q_dtype, int32_t max_seq_len, int32_t prefix_len) {
+  if (prefix_len == 0) return PA_OK;
+  if (prefix_len < 0 || prefix_len % c->block_size != 0 || prefix_len > max_seq_len) return PA_ERR_SHAPE;
+  if (q_dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+static pa_status_t attention_impl(const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
+                                  const pa_cache_t* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                                  int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
+                                  int32_t max_query_len, int32_t prefix_len, float scale, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  pa_status_t st = check_attention_sizes(cache, num_q_heads, num_seqs, num_tokens, max_seq_len, max_query_len);
+  if (st != PA_OK) return st;
+  if ((st = check_prefix(cache, q_dtype, max_seq_len, prefix_len)) != PA_OK) return st;
+  if (!dtype_known(q_dtype)) return PA_ERR_DTYPE;
+  if (!pairing_ok(q_dtype, cache->kv_dtype)) return PA_ERR_DTYPE;
+  if (!isfinite(scale) || !(scale > 0.f)) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !out)
+    return PA_ERR_NULL;
+  if (max_blocks_per_seq <= 0 || static_cast<int64_t>(max_blocks_per_seq) * cache->block_size <
+                                     static_cast<int64_t>(max_seq_len))
+    return PA_ERR_SHAPE;
+  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, cache->num_kv_heads,
+                                                     cache->head_dim, max_seq_len, prefix_len);
+  if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return PA_ERR_WORKSPACE;
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  pa::AttnArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.qsl = query_start_loc;
+  a.out = out;
+  a.header = reinterpret_cast<int32_t*>(ws + w.header);
+  a.items = reinterpret_cast<int32_t*>(ws + w.items);
+  a.citems = reinterpret_cast<int32_t*>(ws + w.citems);
+  a.part_m = reinterpret_cast<float*>(ws + w.part_m);
+  a.part_l = reinterpret_cast<float*>(ws + w.part_l);
+  a.part_acc = reinterpret_cast<float*>(ws + w.part_acc);
+  a.max_items = w.max_items;
+  a.max_citems = w.max_citems;
+  a.chunk_path = q_dtype != PA_F32;   // the chunk kernel stages 16-bit operands
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.max_query_len = max_query_len;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.group = num_q_heads / cache->num_kv_heads;
+  a.max_parts = w.max_parts;
+  a.partition = w.partition;
+  a.prefix_len = prefix_len;
+  a.prefix_part = w.prefix_part;
+  a.prefix_parts = w.prefix_parts;
+  a.prefix_rblocks = static_cast<int32_t>(ceil_div(static_cast<int64_t>(num_tokens) * a.group, pa::kChunkRows));
+  a.prefix_items = static_cast<int64_t>(a.prefix_rblocks) * w.prefix_parts * cache->num_kv_heads;
+  a.score_scale = scale * cache->k_scale * 1.4426950408889634f;
+  a.rescale_slack = pa::kRescaleSlack / a.score_scale;
+  a.v_scale = cache->v_scale;
+  const hipError_t e = pa::launch_attention(q_dtype, cache->kv_dtype, cache->head_dim, cache->block_size, a,
+                                            static_cast<hipStream_t>(stream), g_events);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 }  // namespace
@@ -233,61 +306,40 @@ pa_status_t pa_attention_workspace_size(const pa_cache_t* cache, int32_t num_q_h
   return PA_OK;
 }
 
+pa_status_t pa_attention_shared_prefix_workspace_size(const pa_cache_t* cache, int32_t num_q_heads,
+                                                      int32_t num_seqs, int32_t num_tokens, int32_t max_seq_len,
+                                                      int32_t max_query_len, int32_t prefix_len, size_t* bytes) {
+  if (!bytes) return PA_ERR_NULL;
+  pa_status_t st = check_attention_sizes(cache, num_q_heads, num_seqs, num_tokens, max_seq_len, max_query_len);
+  if (st != PA_OK) return st;
+  if (prefix_len < 0 || (cache && prefix_len % cache->block_size != 0) || prefix_len > max_seq_len) return PA_ERR_SHAPE;
+  *bytes = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, cache->num_kv_heads, cache->head_dim,
+                                max_seq_len, prefix_len)
+               .total;
+  return PA_OK;
+}
+
 pa_status_t pa_attention(const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
                          const pa_cache_t* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
                          const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
                          int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
                          int32_t max_query_len, float scale, void* out, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  pa_status_t st = check_attention_sizes(cache, num_q_heads, num_seqs, num_tokens, max_seq_len, max_query_len);
-  if (st != PA_OK) return st;
-  if (!dtype_known(q_dtype)) return PA_ERR_DTYPE;
-  if (!pairing_ok(q_dtype, cache->kv_dtype)) return PA_ERR_DTYPE;
-  if (!isfinite(scale) || !(scale > 0.f)) return PA_ERR_UNSUPPORTED;
-  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
-  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !out)
-    return PA_ERR_NULL;
-  if (max_blocks_per_seq <= 0 || static_cast<int64_t>(max_blocks_per_seq) * cache->block_size <
-                                     static_cast<int64_t>(max_seq_len))
-    return PA_ERR_SHAPE;
-  const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, cache->num_kv_heads,
-                                                     cache->head_dim, max_seq_len);
-  if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
-  if (reinterpret_cast<uintptr_t>(workspace) & 255) return PA_ERR_WORKSPACE;
+  return attention_impl(q, q_dtype, k_cache, v_cache, cache, block_tables, max_blocks_per_seq, seq_lens,
+                        query_start_loc, num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, 0, scale,
+                        out, workspace, workspace_bytes, stream);
+}
 
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  pa::AttnArgs a{};
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.seq_lens = seq_lens;
-  a.qsl = query_start_loc;
-  a.out = out;
-  a.header = reinterpret_cast<int32_t*>(ws + w.header);
-  a.items = reinterpret_cast<int32_t*>(ws + w.items);
-  a.citems = reinterpret_cast<int32_t*>(ws + w.citems);
-  a.part_m = reinterpret_cast<float*>(ws + w.part_m);
-  a.part_l = reinterpret_cast<float*>(ws + w.part_l);
-  a.part_acc = reinterpret_cast<float*>(ws + w.part_acc);
-  a.max_items = w.max_items;
-  a.max_citems = w.max_citems;
-  a.chunk_path = q_dtype != PA_F32;   // the chunk kernel stages 16-bit operands
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_seqs = num_seqs;
-  a.num_tokens = num_tokens;
-  a.num_q_heads = num_q_heads;
-  a.max_query_len = max_query_len;
-  a.num_kv_heads = cache->num_kv_heads;
-  a.group = num_q_heads / cache->num_kv_heads;
-  a.max_parts = w.max_parts;
-  a.partition = w.partition;
-  a.score_scale = scale * cache->k_scale * 1.4426950408889634f;
-  a.rescale_slack = pa::kRescaleSlack / a.score_scale;
-  a.v_scale = cache->v_scale;
-  const hipError_t e = pa::launch_attention(q_dtype, cache->kv_dtype, cache->head_dim, cache->block_size, a,
-                                            static_cast<hipStream_t>(stream), g_events);
-  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+pa_status_t pa_attention_shared_prefix(const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
+                                       const pa_cache_t* cache, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                       const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                                       int32_t num_q_heads, int32_t max_seq_len, int32_t max_query_len,
+                                       int32_t prefix_len, float scale, void* out, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  return attention_impl(q, q_dtype, k_cache, v_cache, cache, block_tables, max_blocks_per_seq, seq_lens,
+                        query_start_loc, num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, prefix_len,
+                        scale, out, workspace, workspace_bytes, stream);
 }
 
 pa_status_t pa_set_attention_events(void* before, void* after) {
@@ -301,6 +353,13 @@ pa_status_t pa_set_chunk_events(void* before, void* after) {
   if ((before == nullptr) != (after == nullptr)) return PA_ERR_NULL;
   g_events[2] = static_cast<hipEvent_t>(before);
   g_events[3] = static_cast<hipEvent_t>(after);
+  return PA_OK;
+}
+
+pa_status_t pa_set_prefix_events(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr)) return PA_ERR_NULL;
+  g_events[4] = static_cast<hipEvent_t>(before);
+  g_events[5] = static_cast<hipEvent_t>(after);
   return PA_OK;
 }
 

@@ -9,11 +9,11 @@ namespace pa {
 // causal reach of its last row), in units of the kernel's key step; 0 for an
 // item with nothing to do.  Must agree with the kernels' own bounds.
 __device__ __forceinline__ int item_size(int L, int ql, int G, int row0, int nrows, int part, int P,
-                                         int step) {
+                                         int step, int kbase) {
   const int rows = ql * G;
   const int last = min(rows, row0 + nrows) - 1;
   const int max_pos = L - ql + last / G;
-  const int kstart = part * P;
+  const int kstart = kbase + part * P;
   const int kend = min(min(L, kstart + P), max_pos + 1);
   return kend > kstart ? (kend - kstart + step - 1) / step : 0;
 }
@@ -48,13 +48,14 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
       L = a.seq_lens[i];
       ql = a.qsl[i + 1] - a.qsl[i];
       const int rows = ql * G;
-      if (ql > 0 && L > 0) {
+      const int own = L - a.prefix_len;                   // keys past the shared prefix
+      if (ql > 0 && own > 0) {
         if (is_chunk_seq(a, rows)) {
-          np = (L + kChunkPartition - 1) / kChunkPartition;
+          np = (own + kChunkPartition - 1) / kChunkPartition;
           n = ((rows + kChunkRows - 1) / kChunkRows) * np;
           np = -np;
         } else {
-          np = (L + a.partition - 1) / a.partition;
+          np = (own + a.partition - 1) / a.partition;
           n = ((rows + kTileRows - 1) / kTileRows) * np;
         }
       }
@@ -86,8 +87,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
     const int npp = np < 0 ? -np : np;
     t = idx / npp;
     p = idx - t * npp;
-    bucket = list ? item_size(L, ql, G, t * kChunkRows, kChunkRows, p, kChunkPartition, kChunkKeys)
-                  : item_size(L, ql, G, t * kTileRows, kTileRows, p, a.partition, 32);
+    bucket = list ? item_size(L, ql, G, t * kChunkRows, kChunkRows, p, kChunkPartition, kChunkKeys, a.prefix_len)
+                  : item_size(L, ql, G, t * kTileRows, kTileRows, p, a.partition, 32, a.prefix_len);
   };
 
   // pass 1: bucket sizes
@@ -139,6 +140,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
     a.header[0] = 0;
     a.header[1] = static_cast<int32_t>(total[0] < a.max_items ? total[0] : a.max_items);
     a.header[2] = 0;
+    a.header[4] = 0;
     a.header[3] = static_cast<int32_t>(total[1] < a.max_citems ? total[1] : a.max_citems);
   }
 }
@@ -163,8 +165,10 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
   const int q0 = a.qsl[i];
   const int ql = a.qsl[i + 1] - q0;
   const int row_pos = a.seq_lens[i] - ql + (token - q0);
-  const int np = row_pos / (is_chunk_seq(a, ql * a.group) ? kChunkPartition : a.partition) + 1;
-  if (np <= 1) return;
+  const int own = row_pos - a.prefix_len;               // the row's keys past the shared prefix, minus one
+  const int np = (a.prefix_len > 0 ? a.prefix_parts : 0) +
+                 (own >= 0 ? own / (is_chunk_seq(a, ql * a.group) ? kChunkPartition : a.partition) + 1 : 0);
+  if (np <= 1 && a.prefix_len == 0) return;
   const int head = blockIdx.y * HPB + static_cast<int>(threadIdx.x) / LPH;
   if (head >= a.num_q_heads) return;
   const int d0 = (threadIdx.x % LPH) * 4;
@@ -191,8 +195,9 @@ static void launch_reduce(const AttnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((reduce_kernel<OT, D>), grid, dim3(256), 0, stream, a);
 }
 
-// plan -> decode kernel -> chunk kernel (when a prompt chunk can be present)
-// -> partition merge.  ev[0..1] bracket the decode kernel, ev[2..3] the chunk
+// plan -> [shared-prefix pass] -> decode kernel -> chunk kernel (when a
+// prompt chunk can be present) -> partition merge.  ev[0..1] bracket the decode kernel, ev[4..5] the
+// shared-prefix pass, ev[2..3] the chunk
 // kernel (each may be null).
 hipError_t launch_attention(int q, int kv, int d, int bs, const AttnArgs& a, hipStream_t stream,
                             const hipEvent_t* ev) {
@@ -201,6 +206,13 @@ hipError_t launch_attention(int q, int kv, int d, int bs, const AttnArgs& a, hip
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.prefix_len > 0) {                     // the shared prefix, all rows at once
+    AttnArgs p = a;
+    p.prefix_pass = 1;
+    if (ev[4] && (e = hipEventRecord(ev[4], stream)) != hipSuccess) return e;
+    if ((e = launch_chunk(q, kv, d, bs, p, stream)) != hipSuccess) return e;
+    if (ev[5] && (e = hipEventRecord(ev[5], stream)) != hipSuccess) return e;
+  }
   if (ev[0] && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
   if ((e = launch_decode(q, kv, d, bs, a, stream)) != hipSuccess) return e;
   if (ev[1] && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
@@ -209,7 +221,7 @@ hipError_t launch_attention(int q, int kv, int d, int bs, const AttnArgs& a, hip
     if ((e = launch_chunk(q, kv, d, bs, a, stream)) != hipSuccess) return e;
     if (ev[3] && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
   }
-  if (a.max_parts > 1 && a.num_tokens > 0) {
+  if ((a.max_parts > 1 || a.prefix_len > 0) && a.num_tokens > 0) {
     if (q == DT_F32) {
       if (d == 64) launch_reduce<DT_F32, 64>(a, stream);
       else launch_reduce<DT_F32, 128>(a, stream);

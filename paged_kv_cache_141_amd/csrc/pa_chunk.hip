@@ -136,7 +136,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
   const int lane = tid & 63;
   const int r = lane & 15;
   const int lg = lane >> 4;
-  const int64_t total = static_cast<int64_t>(uniform(a.header[3])) * a.num_kv_heads;
+  // the prefix pass has (row block, prefix partition, kv head) items known on
+  // the host; otherwise the plan's chunk list times the kv heads
+  const bool prefix = a.prefix_pass != 0;
+  const int64_t total = prefix ? a.prefix_items : static_cast<int64_t>(uniform(a.header[3])) * a.num_kv_heads;
   const int64_t tile_bytes = static_cast<int64_t>(BS) * D * EBK;
   const int64_t blk_stride = tile_bytes * a.num_kv_heads;
   const uint32_t blk_stride32 = static_cast<uint32_t>(blk_stride);   // Hkv * B * d * eb < 2^32
@@ -190,30 +193,53 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
   }
 
   while (true) {
-    if (tid == 0) slot = atomicAdd(a.header + 2, 1);
+    if (tid == 0) slot = atomicAdd(a.header + (prefix ? 4 : 2), 1);
     __syncthreads();
     const int w = slot;
     if (w >= total) break;
-    const int e = w / a.num_kv_heads;
-    const int h = w - e * a.num_kv_heads;
-    const int i = a.citems[2 * e];
-    const int tp = a.citems[2 * e + 1];
-    const int rblk = tp >> 16;
-    const int part = tp & 0xFFFF;
-
-    const int L = a.seq_lens[i];
-    const int q0 = a.qsl[i];
-    const int ql = a.qsl[i + 1] - q0;
     const int G = a.group;
-    const int rows = ql * G;
-    const int base_pos = L - ql;
+    int i, h, rblk, part, L, q0, rows, base_pos, tstep, cpart, kstart, pslot;
+    if (prefix) {
+      // all rows of the step (every token x its kv head's group) against keys
+      // [part * P, ...) of the shared prefix, which every row sees whole: as if
+      // each row sat at position prefix_len - 1.  Row blocks vary fastest, so
+      // items that read the same keys run side by side.
+      rblk = w % a.prefix_rblocks;
+      const int ph = w / a.prefix_rblocks;
+      h = ph % a.num_kv_heads;
+      part = ph / a.num_kv_heads;
+      i = 0;                                 // the prefix blocks, read from sequence 0's table row
+      L = a.prefix_len;
+      q0 = 0;
+      rows = a.num_tokens * G;
+      base_pos = a.prefix_len - 1;
+      tstep = 0;
+      cpart = a.prefix_part;
+      kstart = part * cpart;
+      pslot = part;
+    } else {
+      const int e = w / a.num_kv_heads;
+      h = w - e * a.num_kv_heads;
+      i = a.citems[2 * e];
+      const int tp = a.citems[2 * e + 1];
+      rblk = tp >> 16;
+      part = tp & 0xFFFF;
+      L = a.seq_lens[i];
+      q0 = a.qsl[i];
+      const int ql = a.qsl[i + 1] - q0;
+      rows = ql * G;
+      base_pos = L - ql;
+      tstep = 1;
+      cpart = kChunkPartition;
+      kstart = a.prefix_len + part * cpart;   // keys past a shared prefix only
+      pslot = a.prefix_parts + part;
+    }
     const int wrow0 = rblk * kChunkRows + wave * (16 * RT);
     const int wlast = min(rows, wrow0 + 16 * RT) - 1;     // last row of this wave (< wrow0: none)
-    const int wave_min_pos = base_pos + wrow0 / G;
-    const int wave_max_pos = wlast >= wrow0 ? base_pos + wlast / G : -1;
-    const int wg_max_pos = base_pos + (min(rows, rblk * kChunkRows + kChunkRows) - 1) / G;
-    const int kstart = part * kChunkPartition;
-    const int kend = min(min(L, kstart + kChunkPartition), wg_max_pos + 1);
+    const int wave_min_pos = base_pos + tstep * (wrow0 / G);
+    const int wave_max_pos = wlast >= wrow0 ? base_pos + tstep * (wlast / G) : -1;
+    const int wg_max_pos = base_pos + tstep * ((min(rows, rblk * kChunkRows + kChunkRows) - 1) / G);
+    const int kend = min(min(L, kstart + cpart), wg_max_pos + 1);
 
     if (kstart < kend) {
       int row_pos[RT];
@@ -223,7 +249,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
         const int R = wrow0 + 16 * rt + r;
         const bool valid = R < rows;
         const int t = R / G;
-        row_pos[rt] = valid ? base_pos + t : -1;
+        row_pos[rt] = valid ? base_pos + tstep * t : -1;
         const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
                             ((static_cast<int64_t>(q0 + t) * a.num_q_heads + h * G + (R - t * G)) * D + 8 * lg) * EBQ;
 #pragma unroll
@@ -249,8 +275,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
         // table repeats that block (keys past the end are loaded but never
         // used), so tile loads need no clamp
         const int32_t* bt = a.block_tables + static_cast<int64_t>(i) * a.max_blocks_per_seq + jbase;
-        const int nb = min(nblk - jbase, kChunkPartition / BS);
-        for (int j = tid; j < kChunkPartition / BS; j += kChunkThreads) btl[j] = bt[min(j, nb - 1)];
+        const int nb = min(nblk - jbase, cpart / BS);
+        for (int j = tid; j < cpart / BS; j += kChunkThreads) btl[j] = bt[min(j, nb - 1)];
       }
       __syncthreads();
       const uint8_t* kc = static_cast<const uint8_t*>(a.k_cache) + h * tile_bytes;
@@ -452,7 +478,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
         const int token = q0 + t;
         const int head = h * G + (R - t * G);
         const float ltot = lacc[rt][0];
-        if (row_pos[rt] / kChunkPartition == 0) {
+        if (a.prefix_len == 0 && row_pos[rt] / kChunkPartition == 0) {
           const float inv = a.v_scale / ltot;
           uint8_t* op = static_cast<uint8_t*>(a.out) +
                         ((static_cast<int64_t>(token) * a.num_q_heads + head) * D + 4 * lg) * EBQ;
@@ -461,7 +487,7 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
             store4<CT>(op + 16 * n * EBQ, acc[rt][n][0] * inv, acc[rt][n][1] * inv, acc[rt][n][2] * inv,
                        acc[rt][n][3] * inv);
         } else {
-          const int64_t rowp = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts + part;
+          const int64_t rowp = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts + pslot;
           if (lg == 0) {
             a.part_m[rowp] = max_log2(m[rt], a.score_scale);
             a.part_l[rowp] = ltot;
@@ -486,7 +512,7 @@ hipError_t launch_chunk(int q, int kv, int d, int bs, const AttnArgs& a, hipStre
     } else {
       static const int64_t groups =
           resident_groups(reinterpret_cast<const void*>(&chunk_kernel<CT, KV, D, BS>), kChunkThreads);
-      const int64_t want = a.max_citems * a.num_kv_heads;
+      const int64_t want = a.prefix_pass ? a.prefix_items : a.max_citems * a.num_kv_heads;
       const int64_t grid = want < groups ? (want > 0 ? want : 1) : groups;
       hipLaunchKernelGGL((chunk_kernel<CT, KV, D, BS>), dim3(static_cast<unsigned>(grid)), dim3(kChunkThreads), 0,
                          stream, a);

@@ -57,7 +57,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   const int last_R = min(rows, row0 + kTileRows) - 1;
   const int max_pos = base_pos + last_R / G;
   const int min_pos = base_pos + row0 / G;
-  const int kstart = part * a.partition;
+  const int kstart = a.prefix_len + part * a.partition;   // keys past a shared prefix only
   const int kend = min(min(L, kstart + a.partition), max_pos + 1);
   if (kstart >= kend) return;
 
@@ -178,8 +178,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   float ltot = lsum + __shfl_xor(lsum, 16);
   ltot += __shfl_xor(ltot, 32);
   if (!valid || row_pos < kstart) return;
-  const int nparts_row = row_pos / a.partition + 1;
-  if (nparts_row == 1) {
+  const int nparts_row = (row_pos - a.prefix_len) / a.partition + 1;
+  if (nparts_row == 1 && a.prefix_len == 0) {
     const float inv = a.v_scale / ltot;
     uint8_t* op = static_cast<uint8_t*>(a.out) +
                   ((static_cast<int64_t>(token) * a.num_q_heads + head) * D + 4 * lg) * EBQ;
@@ -187,7 +187,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
     for (int n = 0; n < NT; ++n)
       store4<CT>(op + 16 * n * EBQ, acc[n][0] * inv, acc[n][1] * inv, acc[n][2] * inv, acc[n][3] * inv);
   } else {
-    const int64_t rowp = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts + part;
+    const int64_t rowp = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts + a.prefix_parts + part;
     if (lg == 0) {
       a.part_m[rowp] = max_log2(m, a.score_scale);
       a.part_l[rowp] = ltot;

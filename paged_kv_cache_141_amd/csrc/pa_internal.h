@@ -60,7 +60,7 @@ inline int64_t max_work_items(int64_t num_seqs, int64_t num_tokens, int64_t grou
 
 // Workspace carve-up (byte offsets, each 256-byte aligned).
 struct WorkspaceLayout {
-  size_t header;   // int32 [64]: [0]/[1] decode work counter/count, [2]/[3] chunk's
+  size_t header;   // int32 [64]: [0]/[1] decode work counter/count, [2]/[3] chunk's, [4] prefix pass's
   size_t items;    // int32x2 [max_items]: decode items (seq, tile << 16 | partition)
   size_t citems;   // int32x2 [max_citems]: chunk items (seq, row block << 16 | partition)
   size_t part_m;   // float [T][Hq][MP]: running max (log2 units) per partition
@@ -70,20 +70,49 @@ struct WorkspaceLayout {
   int64_t max_items;
   int64_t max_citems;
   int32_t max_parts;
-  int32_t partition;   // decode partition length in keys
+  int32_t partition;     // decode partition length in keys
+  int32_t prefix_parts;  // partials of the shared-prefix pass (first in each row's list)
+  int32_t prefix_part;   // keys per shared-prefix partition
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Shared-prefix (cascade) pass: keys per prefix partition.  The pass has
+// (row blocks x partitions x kv heads) items of one workgroup each; they are
+// sized to fill one round of kPrefixItems workgroups (one per CU of the
+// GPU) without spilling a few into a second round: as many partitions as
+// fit that round, each at least 256 keys, rounded up to whole 64-key tiles
+// and at most 4096 keys.
+#ifndef PA_PREFIX_ITEMS
+#define PA_PREFIX_ITEMS 256
+#endif
+constexpr int64_t kPrefixItems = PA_PREFIX_ITEMS;
+inline int32_t prefix_partition(int64_t prefix_len, int64_t num_tokens, int64_t group, int64_t num_kv_heads) {
+  const int64_t units = ceil_div(num_tokens * group, kChunkRows) * num_kv_heads;
+  int64_t parts = kPrefixItems / units > 1 ? kPrefixItems / units : 1;
+  const int64_t most = ceil_div(prefix_len, 256);
+  parts = parts < most ? parts : most;
+  int64_t p = ceil_div(ceil_div(prefix_len, parts), kChunkKeys) * kChunkKeys;
+  return static_cast<int32_t>(p < 256 ? 256 : (p > kChunkPartition ? kChunkPartition : p));
+}
+
 inline WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_tokens, int64_t num_q_heads,
-                                        int64_t num_kv_heads, int64_t head_dim,
-                                        int64_t max_seq_len) {
+                                        int64_t num_kv_heads, int64_t head_dim, int64_t max_seq_len,
+                                        int64_t prefix_len = 0) {
   WorkspaceLayout w{};
   const int64_t group = num_kv_heads > 0 ? num_q_heads / num_kv_heads : 1;
-  w.partition = decode_partition(max_seq_len);
-  w.max_items = max_work_items(num_seqs, num_tokens, group, max_seq_len, kTileRows, w.partition);
-  w.max_citems = max_work_items(num_seqs, num_tokens, group, max_seq_len, kChunkRows, kChunkPartition);
-  w.max_parts = static_cast<int32_t>(ceil_div(max_seq_len > 0 ? max_seq_len : 1, w.partition));
+  // keys past the shared prefix: what the decode and chunk kernels cover
+  const int64_t own = max_seq_len - prefix_len > 0 ? max_seq_len - prefix_len : 1;
+  w.partition = decode_partition(own);
+  w.max_items = max_work_items(num_seqs, num_tokens, group, own, kTileRows, w.partition);
+  w.max_citems = max_work_items(num_seqs, num_tokens, group, own, kChunkRows, kChunkPartition);
+  w.prefix_parts = 0;
+  w.prefix_part = 0;
+  if (prefix_len > 0) {
+    w.prefix_part = prefix_partition(prefix_len, num_tokens, group, num_kv_heads);
+    w.prefix_parts = static_cast<int32_t>(ceil_div(prefix_len, w.prefix_part));
+  }
+  w.max_parts = w.prefix_parts + static_cast<int32_t>(ceil_div(own, w.partition));
   const size_t rows = static_cast<size_t>(num_tokens) * num_q_heads * w.max_parts;
   size_t off = 0;
   w.header = off;   off = align256(off + 64 * sizeof(int32_t));
@@ -128,6 +157,15 @@ struct AttnArgs {
   int32_t max_query_len;
   int32_t max_parts;
   int32_t partition;   // decode partition length in keys (decode_partition)
+  // Shared prefix (cascade): every sequence's first prefix_len keys are the
+  // same blocks (sequence 0's table row is read for them) and every query row
+  // sits at or past prefix_len.  The prefix pass attends all rows to those
+  // keys (partials 0 .. prefix_parts-1); the decode and chunk kernels then
+  // cover keys from prefix_len on (partials from prefix_parts on).
+  int32_t prefix_len;
+  int32_t prefix_part, prefix_parts, prefix_rblocks;
+  int32_t prefix_pass;       // 1: this chunk-kernel launch is the prefix pass
+  int64_t prefix_items;
   float score_scale;   // scale * k_scale * log2(e)
   float rescale_slack; // kRescaleSlack / score_scale (raw-score units)
   float v_scale;
@@ -185,8 +223,9 @@ hipError_t launch_copy_blocks(const BlockCopyArgs& a, hipStream_t stream);   // 
 hipError_t launch_table_writes(const TableWriteArgs& a, hipStream_t stream);  // (pa_metadata.hip)
 hipError_t launch_prepare_step(const StepArgs& a, hipStream_t stream);        // (pa_metadata.hip)
 // kv_dtype, q_dtype: pa_dtype_t values; head_dim 64|128; block_size 16|32|64.
-// events[0..1] (may be null) are recorded around the decode kernel and
-// events[2..3] around the chunk kernel.  (pa_attention.hip)
+// events[0..1] (may be null) are recorded around the decode kernel,
+// events[2..3] around the chunk kernel and events[4..5] around the
+// shared-prefix pass.  (pa_attention.hip)
 hipError_t launch_attention(int q_dtype, int kv_dtype, int head_dim, int block_size,
                             const AttnArgs& a, hipStream_t stream, const hipEvent_t* events);
 // The decode kernel alone (pa_decode.hip) and the chunk kernel alone

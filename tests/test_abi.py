@@ -124,3 +124,24 @@ def test_copy_blocks_argument_errors():
     for bad in (_cache(block_size=32), _cache(num_kv_heads=4), _cache(head_dim=128),
                 _cache(kv_dtype=pa.PA_F16)):                     # ... the block geometry may not
         assert lib.pa_copy_blocks(FAKE, FAKE, ctypes.byref(c), FAKE, FAKE, ctypes.byref(bad), m, 1, None) == 2
+
+
+def test_shared_prefix_argument_errors():
+    lib = pa.library()
+    c = _cache()
+
+    def call(prefix, q_dtype=pa.PA_BF16, cache=c):
+        return lib.pa_attention_shared_prefix(FAKE, q_dtype, FAKE, FAKE, ctypes.byref(cache), FAKE, 3, FAKE, FAKE,
+                                              2, 2, 4, 40, 1, prefix, 0.125, FAKE, FAKE, 1 << 40, None)
+    assert call(8) == 2                           # not whole blocks (B = 16)
+    assert call(48) == 2                          # longer than max_seq_len 40
+    assert call(-16) == 2
+    assert call(16, q_dtype=pa.PA_F32, cache=_cache(kv_dtype=pa.PA_F32)) == 4
+    b = ctypes.c_size_t(0)
+    assert lib.pa_attention_shared_prefix_workspace_size(ctypes.byref(c), 4, 2, 2, 40, 1, 8, ctypes.byref(b)) == 2
+    sizes = []
+    for prefix in (0, 16, 32):
+        assert lib.pa_attention_shared_prefix_workspace_size(ctypes.byref(c), 4, 2, 2, 40, 1, prefix,
+                                                             ctypes.byref(b)) == 0
+        sizes.append(b.value)
+    assert sizes[0] > 0 and sizes[1] > 0

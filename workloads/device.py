@@ -84,6 +84,25 @@ class DeviceStep:
     new_slots: object
     out: object
     workspace: object
+    prefix_len: int = 0          # > 0: attend through the shared-prefix entry point
+
+    def use_shared_prefix(self, prefix_len: int):
+        """Attend with pa_attention_shared_prefix over the workload's common
+        prefix (prefix_len tokens, whole blocks); sizes a workspace for it."""
+        torch = _torch()
+        import ctypes
+        import paged_kv_cache_141_amd as pa
+        w = self.w
+        spec = pa.cache_spec(self.k_cache, self.v_cache, w.k_scale, w.v_scale)
+        need = ctypes.c_size_t(0)
+        st = pa.library().pa_attention_shared_prefix_workspace_size(
+            ctypes.byref(spec), w.num_q_heads, w.num_seqs, w.num_tokens, w.max_seq_len, w.max_query_len,
+            int(prefix_len), ctypes.byref(need))
+        if st != 0:
+            raise pa.PagedAttentionError(st, "pa_attention_shared_prefix_workspace_size")
+        self.workspace = torch.empty(max(int(need.value), 256), dtype=torch.uint8, device=self.q.device)
+        self.prefix_len = int(prefix_len)
+        return self
 
     def write_new(self, stream=None):
         import paged_kv_cache_141_amd as pa
@@ -97,7 +116,7 @@ class DeviceStep:
                             self.query_start_loc, w.scale, max_seq_len=w.max_seq_len,
                             max_query_len=w.max_query_len, out=self.out if out is None else out,
                             workspace=self.workspace, k_scale=w.k_scale, v_scale=w.v_scale,
-                            stream=stream)
+                            prefix_len=self.prefix_len, stream=stream)
 
     def step(self, stream=None):
         """One pass of the hot path: cache write of the new tokens + attention."""
