@@ -48,12 +48,15 @@ def parse():
                          "(the known-size reference for HBM counter scaling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle's timed sample (0 disables it)")
-    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "swap", "prepare"],
+    ap.add_argument("--op", default="step", choices=["step", "copy_blocks", "swap", "prepare", "multistep"],
                     help="step: the attention step (default).  copy_blocks: copy-on-write of "
                          "--pairs blocks within one pool.  swap: --pairs blocks out to page-locked "
                          "host memory and back in.  Both use the pool geometry of --config.  prepare: "
                          "the step inputs of --config built on the GPU from 1,024 persistent request "
-                         "slots (staged block-table writes + pa_prepare_step).")
+                         "slots (staged block-table writes + pa_prepare_step).  multistep: --graph-steps "
+                         "decode steps of --config (prepare, cache write, attention, commit per step) run "
+                         "eagerly and replayed from one captured HIP graph.")
+    ap.add_argument("--graph-steps", type=int, default=8, help="decode steps per graph for --op multistep")
     ap.add_argument("--pairs", type=int, default=2048, help="block pairs per copy for --op")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="attend through pa_attention_shared_prefix over the workload's common prefix "
@@ -323,6 +326,60 @@ def bench_prepare(args):
                       "full_table_bytes": int(table.nbytes)}), flush=True)
 
 
+def bench_multistep(args):
+    """Per-step time of --graph-steps decode steps of --config's batch: each
+    step prepares its inputs from the per-slot state on the GPU, writes one
+    new token per sequence, attends and commits.  Eager launches vs one
+    replay of the captured graph (the state is restored before each run)."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from workloads import device as wd
+    from paged_kv_cache_141_amd.multistep import DecodeLoop
+
+    w = workloads.make(args.config)
+    N, R, B = args.graph_steps, w.num_seqs, w.block_size
+    step = wd.stage(w, write_new=False)                     # context before the new token of each sequence
+    W = w.block_tables.shape[1] + -(-N // B) + 1
+    table = torch.full((R, W), int(w.spare_block), dtype=torch.int32, device="cuda")
+    table[:, :w.block_tables.shape[1]] = torch.from_numpy(w.block_tables).cuda()
+    done0 = torch.from_numpy((w.seq_lens - 1).astype(np.int32)).cuda()
+    done = done0.clone()
+    idx = torch.arange(R, dtype=torch.int32, device="cuda")
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.q_dtype]
+    sdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.src_dtype]
+    gen = torch.Generator(device="cuda").manual_seed(141)
+    q = torch.randn(N, R, w.num_q_heads, w.head_dim, device="cuda", generator=gen).to(tdt)
+    key = torch.randn(N, R, w.num_kv_heads, w.head_dim, device="cuda", generator=gen).to(sdt)
+    value = torch.randn(N, R, w.num_kv_heads, w.head_dim, device="cuda", generator=gen).to(sdt)
+    loop = DecodeLoop(step.k_cache, step.v_cache, table, done, idx, q, key, value, B, w.scale,
+                      int(w.max_seq_len) + N, w.k_scale, w.v_scale)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        ms = []
+        for k in range(args.warmup + args.steps):
+            done.copy_(done0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            if k >= args.warmup:
+                ms.append(a.elapsed_time(b))
+        return float(np.mean(ms)) * 1e3 / N
+
+    eager_us = timed(loop.run)
+    done.copy_(done0)
+    g = loop.capture()
+    graph_us = timed(g.replay)
+    print(json.dumps({"op": "multistep", "workload": w.name, "graph_steps": N, "seqs": R,
+                      "eager_us_per_step": round(eager_us, 2), "graph_us_per_step": round(graph_us, 2),
+                      "speedup": round(eager_us / graph_us, 3), "steps": args.steps, "warmup": args.warmup}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -331,6 +388,8 @@ def main():
         sys.exit(2)
     if args.op == "prepare":
         return bench_prepare(args)
+    if args.op == "multistep":
+        return bench_multistep(args)
     if args.op != "step":
         return bench_block_copies(args)
     import numpy as np

@@ -280,6 +280,24 @@ pa_status_t pa_prepare_step(const int32_t* block_table, int32_t max_reqs, int32_
                             void* stream);
 
 /*
+ * End of a step: its tokens are cached.  For b in [0, num_reqs):
+ *   num_computed[idx_mapping[b]] += num_scheduled[b]
+ * (positions outside [0, max_reqs) are skipped).  With pa_prepare_step this
+ * keeps the step loop on the GPU: prepare, write the cache, attend, commit,
+ * so several decode steps can run back to back -- captured once in a HIP
+ * graph and replayed -- without the host preparing each step (techknowgenie
+ * "vLLM V1 core refactoring", section on the PagedAttention V3 kernel
+ * architecture: a GPU graph runner executes N decode steps on its own; the
+ * blocks those steps fill must already be in the table).
+ *
+ *   num_computed [device] int32 [max_reqs], updated in place;
+ *   idx_mapping, num_scheduled [device] int32 [num_reqs].
+ * Batch positions must name distinct slots.  num_reqs == 0 is a no-op.
+ */
+pa_status_t pa_commit_step(int32_t* num_computed, int32_t max_reqs, const int32_t* idx_mapping,
+                           const int32_t* num_scheduled, int32_t num_reqs, void* stream);
+
+/*
  * Debug check of metadata contents.  Synchronous: copies the metadata to the
  * host (on `stream`) and returns PA_ERR_METADATA if any sequence has
  * q_len < 0, q_len > L, L > max_seq_len, q_len > max_query_len,

@@ -21,7 +21,7 @@ from typing import Optional
 
 __all__ = [
     "PagedAttentionError", "library", "library_path", "reshape_and_cache", "attention",
-    "attention_workspace_size", "check_metadata", "copy_blocks", "apply_block_table_writes", "prepare_step",
+    "attention_workspace_size", "check_metadata", "copy_blocks", "apply_block_table_writes", "prepare_step", "commit_step",
     "set_attention_events", "PA_F32", "PA_F16",
     "PA_BF16", "PA_FP8_E4M3",
 ]
@@ -77,6 +77,7 @@ def library() -> ctypes.CDLL:
         "pa_copy_blocks": [P, P, CP, P, P, CP, P, I32, P],
         "pa_apply_block_table_writes": [P, I32, I32, P, P, P, P, I32, I32, P],
         "pa_prepare_step": [P, I32, I32, P, P, P, I32, I32, I32, P, P, P, P, P, P],
+        "pa_commit_step": [P, I32, P, P, I32, P],
         "pa_set_attention_events": [P, P],
         "pa_set_chunk_events": [P, P],
         "pa_set_prefix_events": [P, P],
@@ -299,18 +300,22 @@ def apply_block_table_writes(block_table, rows, starts, offsets, values, stream=
 
 
 def prepare_step(block_table, idx_mapping, num_computed, num_scheduled, num_tokens: int, block_size: int,
-                 stream=None):
+                 out=None, stream=None):
     """Build the step's query_start_loc, seq_lens, positions, slot_mapping and
     block-table rows from persistent slot state (``pa_prepare_step``).
-    Returns them as new device tensors."""
+    Returns them as device tensors: new ones, or the five of ``out``."""
     torch = _torch()
     R = idx_mapping.numel()
     dev = block_table.device
-    qsl = torch.empty(R + 1, dtype=torch.int32, device=dev)
-    lens = torch.empty(R, dtype=torch.int32, device=dev)
-    pos = torch.empty(num_tokens, dtype=torch.int64, device=dev)
-    slots = torch.empty(num_tokens, dtype=torch.int64, device=dev)
-    tables = torch.empty(R, block_table.shape[1], dtype=torch.int32, device=dev)
+    if out is None:
+        out = (torch.empty(R + 1, dtype=torch.int32, device=dev), torch.empty(R, dtype=torch.int32, device=dev),
+               torch.empty(num_tokens, dtype=torch.int64, device=dev),
+               torch.empty(num_tokens, dtype=torch.int64, device=dev),
+               torch.empty(R, block_table.shape[1], dtype=torch.int32, device=dev))
+    qsl, lens, pos, slots, tables = out
+    if (qsl.numel() != R + 1 or lens.numel() != R or pos.numel() != num_tokens or slots.numel() != num_tokens
+            or tables.shape != (R, block_table.shape[1])):
+        raise ValueError("prepare_step: output shapes disagree")
     if R == 0:
         qsl.zero_()
         return qsl, lens, pos, slots, tables
@@ -322,6 +327,17 @@ def prepare_step(block_table, idx_mapping, num_computed, num_scheduled, num_toke
         _dev(tables, "tables"), _stream(stream))
     _check(st, "pa_prepare_step")
     return qsl, lens, pos, slots, tables
+
+
+def commit_step(num_computed, idx_mapping, num_scheduled, stream=None) -> None:
+    """num_computed[idx_mapping[b]] += num_scheduled[b] on the device (``pa_commit_step``)."""
+    R = idx_mapping.numel()
+    if R == 0:
+        return
+    st = library().pa_commit_step(_i32(num_computed, "num_computed"), num_computed.numel(),
+                                  _i32(idx_mapping, "idx_mapping"), _i32(num_scheduled, "num_scheduled", R), R,
+                                  _stream(stream))
+    _check(st, "pa_commit_step")
 
 
 def set_attention_events(before, after) -> None:

@@ -294,6 +294,21 @@ pa_status_t pa_prepare_step(const int32_t* block_table, int32_t max_reqs, int32_
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+pa_status_t pa_commit_step(int32_t* num_computed, int32_t max_reqs, const int32_t* idx_mapping,
+                           const int32_t* num_scheduled, int32_t num_reqs, void* stream) {
+  if (max_reqs <= 0 || num_reqs < 0) return PA_ERR_SHAPE;
+  if (num_reqs == 0) return PA_OK;
+  if (!num_computed || !idx_mapping || !num_scheduled) return PA_ERR_NULL;
+  pa::CommitArgs a{};
+  a.num_computed = num_computed;
+  a.idx_mapping = idx_mapping;
+  a.num_scheduled = num_scheduled;
+  a.max_reqs = max_reqs;
+  a.num_reqs = num_reqs;
+  const hipError_t e = pa::launch_commit_step(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 pa_status_t pa_attention_workspace_size(const pa_cache_t* cache, int32_t num_q_heads, int32_t num_seqs,
                                         int32_t num_tokens, int32_t max_seq_len, int32_t max_query_len,
                                         size_t* bytes) {

@@ -215,6 +215,13 @@ struct StepArgs {
   int32_t max_reqs, max_blocks, num_reqs, num_tokens, block_size;
 };
 
+struct CommitArgs {
+  int32_t* num_computed;         // [max_reqs], by persistent slot
+  const int32_t* idx_mapping;    // [num_reqs]
+  const int32_t* num_scheduled;  // [num_reqs]
+  int32_t max_reqs, num_reqs;
+};
+
 // Launchers.  Each returns hipSuccess or the launch error.
 
 hipError_t launch_reshape_and_cache(int src_dtype, int kv_dtype, const CacheWriteArgs& a,
@@ -222,6 +229,7 @@ hipError_t launch_reshape_and_cache(int src_dtype, int kv_dtype, const CacheWrit
 hipError_t launch_copy_blocks(const BlockCopyArgs& a, hipStream_t stream);   // (pa_blocks.hip)
 hipError_t launch_table_writes(const TableWriteArgs& a, hipStream_t stream);  // (pa_metadata.hip)
 hipError_t launch_prepare_step(const StepArgs& a, hipStream_t stream);        // (pa_metadata.hip)
+hipError_t launch_commit_step(const CommitArgs& a, hipStream_t stream);       // (pa_metadata.hip)
 // kv_dtype, q_dtype: pa_dtype_t values; head_dim 64|128; block_size 16|32|64.
 // events[0..1] (may be null) are recorded around the decode kernel,
 // events[2..3] around the chunk kernel and events[4..5] around the

@@ -112,6 +112,22 @@ __global__ __launch_bounds__(1024) void step_inputs_kernel(StepArgs a) {
   }
 }
 
+// num_computed[idx_mapping[b]] += num_scheduled[b]: the step's tokens are now
+// cached (one thread per batch position; slots outside the table skipped).
+__global__ __launch_bounds__(256) void commit_step_kernel(CommitArgs a) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= a.num_reqs) return;
+  const int slot = a.idx_mapping[b];
+  if (slot >= 0 && slot < a.max_reqs) a.num_computed[slot] += a.num_scheduled[b];
+}
+
+hipError_t launch_commit_step(const CommitArgs& a, hipStream_t stream) {
+  if (a.num_reqs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(commit_step_kernel, dim3(static_cast<unsigned>((a.num_reqs + 255) / 256)), dim3(256), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
 hipError_t launch_table_writes(const TableWriteArgs& a, hipStream_t stream) {
   if (a.num_values <= 0 || a.num_writes <= 0) return hipSuccess;
   hipLaunchKernelGGL(table_writes_kernel, dim3(static_cast<unsigned>(a.num_writes)), dim3(256), 0, stream, a);
