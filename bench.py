@@ -42,6 +42,9 @@ def parse():
                     help="tiny_decode | llama7b_decode | gqa_long_decode | "
                          "mixed_chunked_prefill | fp8_shared_prefix")
     ap.add_argument("--block-size", type=int, default=None, help="for fp8_shared_prefix")
+    ap.add_argument("--head-dim", type=int, default=None,
+                    help="for gqa_long_decode / mixed_chunked_prefill: 256 keeps the KV bytes per token "
+                         "with half the heads (16q/4kv)")
     ap.add_argument("--placement", default=None, help="shuffled | identity | private")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the step: copy a MIB-mebibyte device buffer --steps times "
@@ -421,6 +424,8 @@ def main():
         kw["block_size"] = args.block_size
     if args.placement:
         kw["placement"] = args.placement
+    if args.head_dim:
+        kw["head_dim"] = args.head_dim
     w = workloads.make(args.config, **kw)
     print(f"[bench] staging {w.name}: {json.dumps(w.summary())}", file=sys.stderr, flush=True)
     t_stage = time.perf_counter()

@@ -25,7 +25,7 @@ pa_status_t check_cache(const pa_cache_t* c) {
   if (!dtype_known(c->kv_dtype)) return PA_ERR_DTYPE;
   if (c->num_blocks <= 0 || c->num_kv_heads <= 0) return PA_ERR_SHAPE;
   if (c->block_size != 16 && c->block_size != 32 && c->block_size != 64) return PA_ERR_UNSUPPORTED;
-  if (c->head_dim != 64 && c->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) return PA_ERR_UNSUPPORTED;
   // one block of all kv heads must stay below 4 GiB (32-bit block strides)
   if (static_cast<int64_t>(c->num_kv_heads) * c->block_size * c->head_dim * 4 >= (int64_t(1) << 32))
     return PA_ERR_UNSUPPORTED;
@@ -106,6 +106,7 @@ static pa_status_t attention_impl(const void* q, int32_t q_dtype, const void* k_
   if (!dtype_known(q_dtype)) return PA_ERR_DTYPE;
   if (!pairing_ok(q_dtype, cache->kv_dtype)) return PA_ERR_DTYPE;
   if (!isfinite(scale) || !(scale > 0.f)) return PA_ERR_UNSUPPORTED;
+  if (cache->head_dim == 256 && q_dtype == PA_F32) return PA_ERR_UNSUPPORTED;   // 16-bit queries only
   if (num_seqs == 0 || num_tokens == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !out)
     return PA_ERR_NULL;
@@ -147,7 +148,8 @@ static pa_status_t attention_impl(const void* q, int32_t q_dtype, const void* k_
   a.prefix_len = prefix_len;
   a.prefix_part = w.prefix_part;
   a.prefix_parts = w.prefix_parts;
-  a.prefix_rblocks = static_cast<int32_t>(ceil_div(static_cast<int64_t>(num_tokens) * a.group, pa::kChunkRows));
+  a.chunk_rows = pa::chunk_rows_for(cache->head_dim);
+  a.prefix_rblocks = static_cast<int32_t>(ceil_div(static_cast<int64_t>(num_tokens) * a.group, a.chunk_rows));
   a.prefix_items = static_cast<int64_t>(a.prefix_rblocks) * w.prefix_parts * cache->num_kv_heads;
   a.score_scale = scale * cache->k_scale * 1.4426950408889634f;
   a.rescale_slack = pa::kRescaleSlack / a.score_scale;

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
       if (ql > 0 && own > 0) {
         if (is_chunk_seq(a, rows)) {
           np = (own + kChunkPartition - 1) / kChunkPartition;
-          n = ((rows + kChunkRows - 1) / kChunkRows) * np;
+          n = ((rows + a.chunk_rows - 1) / a.chunk_rows) * np;
           np = -np;
         } else {
           np = (own + a.partition - 1) / a.partition;
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
     const int npp = np < 0 ? -np : np;
     t = idx / npp;
     p = idx - t * npp;
-    bucket = list ? item_size(L, ql, G, t * kChunkRows, kChunkRows, p, kChunkPartition, kChunkKeys, a.prefix_len)
+    bucket = list ? item_size(L, ql, G, t * a.chunk_rows, a.chunk_rows, p, kChunkPartition, kChunkKeys, a.prefix_len)
                   : item_size(L, ql, G, t * kTileRows, kTileRows, p, a.partition, 32, a.prefix_len);
   };
 
@@ -227,10 +227,12 @@ hipError_t launch_attention(int q, int kv, int d, int bs, const AttnArgs& a, hip
       else launch_reduce<DT_F32, 128>(a, stream);
     } else if (q == DT_F16) {
       if (d == 64) launch_reduce<DT_F16, 64>(a, stream);
-      else launch_reduce<DT_F16, 128>(a, stream);
+      else if (d == 128) launch_reduce<DT_F16, 128>(a, stream);
+      else launch_reduce<DT_F16, 256>(a, stream);
     } else {
       if (d == 64) launch_reduce<DT_BF16, 64>(a, stream);
-      else launch_reduce<DT_BF16, 128>(a, stream);
+      else if (d == 128) launch_reduce<DT_BF16, 128>(a, stream);
+      else launch_reduce<DT_BF16, 256>(a, stream);
     }
     e = hipGetLastError();
   }

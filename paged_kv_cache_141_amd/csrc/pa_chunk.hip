@@ -24,7 +24,7 @@ struct ChunkLds {
   static constexpr int BUF = KBYTES + D * VROW;
   // The K rows one read touches are {8*(r/4) + 4*tau + r%4} (mod 32).
   static __device__ __forceinline__ int kswz(int key) {
-    if constexpr (D == 128) return (key & 3) | (((key >> 3) & 3) << 2);
+    if constexpr (D >= 128) return (key & 3) | (((key >> 3) & 3) << 2);   // 16 distinct 16-byte groups
     else return ((key >> 1) & 1) | (((key >> 3) & 3) << 1);   // 128-byte rows pair up per 256 bytes
   }
   // The V^T rows one read touches are 16 consecutive dims.
@@ -121,7 +121,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
   constexpr bool DIRECT = (KV != DT_FP8);                // 16-bit cache: global -> LDS directly
   // 16-bit caches: tile t and the kChunkAhead tiles loading behind it; fp8:
   // tiles t and t+1 (staged from registers after round t computes).
-  constexpr int NBUF = DIRECT ? kChunkAhead + 1 : 2;
+  constexpr int AHEAD = D == 256 ? 1 : kChunkAhead;      // a 64 KB tile at d = 256: two buffers fit LDS
+  constexpr int NBUF = DIRECT ? AHEAD + 1 : 2;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * Lds::BUF];
   __shared__ int32_t btl[kChunkPartition / BS];          // the partition's physical block ids
   __shared__ int slot;
@@ -129,7 +130,8 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
   constexpr int EBK = Bytes<KV>::v;
   constexpr int KS = D / 32;
   constexpr int NT = D / 16;
-  constexpr int RT = 2;                                  // row tiles per wave
+  constexpr int RT = D == 256 ? 1 : 2;                   // row tiles per wave
+  constexpr int ROWS = kChunkWaves * 16 * RT;            // rows of one item (chunk_rows_for(D))
 
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);                    // wave-uniform: keeps its branches scalar
@@ -234,11 +236,11 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
       kstart = a.prefix_len + part * cpart;   // keys past a shared prefix only
       pslot = a.prefix_parts + part;
     }
-    const int wrow0 = rblk * kChunkRows + wave * (16 * RT);
+    const int wrow0 = rblk * ROWS + wave * (16 * RT);
     const int wlast = min(rows, wrow0 + 16 * RT) - 1;     // last row of this wave (< wrow0: none)
     const int wave_min_pos = base_pos + tstep * (wrow0 / G);
     const int wave_max_pos = wlast >= wrow0 ? base_pos + tstep * (wlast / G) : -1;
-    const int wg_max_pos = base_pos + tstep * ((min(rows, rblk * kChunkRows + kChunkRows) - 1) / G);
+    const int wg_max_pos = base_pos + tstep * ((min(rows, rblk * ROWS + ROWS) - 1) / G);
     const int kend = min(min(L, kstart + cpart), wg_max_pos + 1);
 
     if (kstart < kend) {
@@ -409,9 +411,9 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
       auto bufp = [&](int ti) { return lds + (ti % NBUF) * Lds::BUF; };
       // wait until at most the loads of the n most recently issued tiles are outstanding
       auto wait_later = [&](int n) {
-        static_assert(kChunkAhead >= 1 && kChunkAhead <= 3, "tiles in flight: 1 to 3");
-        if (kChunkAhead >= 3 && n >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI));
-        else if (kChunkAhead >= 2 && n >= 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));
+        static_assert(AHEAD >= 1 && AHEAD <= 3, "tiles in flight: 1 to 3");
+        if (AHEAD >= 3 && n >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI));
+        else if (AHEAD >= 2 && n >= 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));
         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       };
       // one round: tile ti is in LDS
@@ -431,18 +433,18 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
         // The compiler cannot see the LDS loads; retire its own loads (q) here
         // so that it has no reason to wait on the vector-memory counter later.
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        // tiles 0 .. kChunkAhead-1 in flight, then wait for tile 0
+        // tiles 0 .. AHEAD-1 in flight, then wait for tile 0
 #pragma unroll
-        for (int x = 0; x < kChunkAhead; ++x)
+        for (int x = 0; x < AHEAD; ++x)
           if (x < ntiles) issue_direct(x, tile_key(x));
-        wait_later(min(ntiles, kChunkAhead) - 1);
+        wait_later(min(ntiles, AHEAD) - 1);
         __syncthreads();
         for (int ti = 0; ti < ntiles; ++ti) {
           // buffer (ti + ahead) % NBUF last held tile ti-1, finished in round ti-1
-          if (ti + kChunkAhead < ntiles) issue_direct((ti + kChunkAhead) % NBUF, tile_key(ti + kChunkAhead));
+          if (ti + AHEAD < ntiles) issue_direct((ti + AHEAD) % NBUF, tile_key(ti + AHEAD));
           do_round(ti);
           // tile ti+1 has landed once at most the loads of the tiles after it are outstanding
-          wait_later(min(ntiles - 2 - ti, kChunkAhead - 1));
+          wait_later(min(ntiles - 2 - ti, AHEAD - 1));
           __syncthreads();
         }
       } else {

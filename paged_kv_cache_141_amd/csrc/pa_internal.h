@@ -36,6 +36,9 @@ constexpr int kChunkMinRows = 65;
 constexpr int kChunkWaves = 8;                 // waves per chunk workgroup (2 per SIMD)
 constexpr int kChunkThreads = 64 * kChunkWaves;
 constexpr int kChunkRows = 32 * kChunkWaves;   // two 16-row tiles per wave
+// Rows of one chunk work item: 256 (two 16-row tiles per wave), or 128 for
+// head dim 256, whose accumulators leave room for one tile per wave.
+constexpr int chunk_rows_for(int64_t head_dim) { return head_dim == 256 ? kChunkRows / 2 : kChunkRows; }
 constexpr int kChunkKeys = 64;
 #ifndef PA_CHUNK_PARTITION
 #define PA_CHUNK_PARTITION 4096
@@ -87,8 +90,9 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 #define PA_PREFIX_ITEMS 256
 #endif
 constexpr int64_t kPrefixItems = PA_PREFIX_ITEMS;
-inline int32_t prefix_partition(int64_t prefix_len, int64_t num_tokens, int64_t group, int64_t num_kv_heads) {
-  const int64_t units = ceil_div(num_tokens * group, kChunkRows) * num_kv_heads;
+inline int32_t prefix_partition(int64_t prefix_len, int64_t num_tokens, int64_t group, int64_t num_kv_heads,
+                                int64_t chunk_rows) {
+  const int64_t units = ceil_div(num_tokens * group, chunk_rows) * num_kv_heads;
   int64_t parts = kPrefixItems / units > 1 ? kPrefixItems / units : 1;
   const int64_t most = ceil_div(prefix_len, 256);
   parts = parts < most ? parts : most;
@@ -105,11 +109,11 @@ inline WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_tokens, in
   const int64_t own = max_seq_len - prefix_len > 0 ? max_seq_len - prefix_len : 1;
   w.partition = decode_partition(own);
   w.max_items = max_work_items(num_seqs, num_tokens, group, own, kTileRows, w.partition);
-  w.max_citems = max_work_items(num_seqs, num_tokens, group, own, kChunkRows, kChunkPartition);
+  w.max_citems = max_work_items(num_seqs, num_tokens, group, own, chunk_rows_for(head_dim), kChunkPartition);
   w.prefix_parts = 0;
   w.prefix_part = 0;
   if (prefix_len > 0) {
-    w.prefix_part = prefix_partition(prefix_len, num_tokens, group, num_kv_heads);
+    w.prefix_part = prefix_partition(prefix_len, num_tokens, group, num_kv_heads, chunk_rows_for(head_dim));
     w.prefix_parts = static_cast<int32_t>(ceil_div(prefix_len, w.prefix_part));
   }
   w.max_parts = w.prefix_parts + static_cast<int32_t>(ceil_div(own, w.partition));
@@ -165,6 +169,7 @@ struct AttnArgs {
   int32_t prefix_len;
   int32_t prefix_part, prefix_parts, prefix_rblocks;
   int32_t prefix_pass;       // 1: this chunk-kernel launch is the prefix pass
+  int32_t chunk_rows;        // rows of one chunk item: chunk_rows_for(head dim)
   int64_t prefix_items;
   float score_scale;   // scale * k_scale * log2(e)
   float rescale_slack; // kRescaleSlack / score_scale (raw-score units)

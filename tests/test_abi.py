@@ -53,6 +53,7 @@ def _attn(cache, q_dtype=pa.PA_BF16, q=FAKE, ws=FAKE, ws_bytes=1 << 40, Hq=4, S=
 def test_attention_argument_errors():
     assert _attn(_cache(block_size=8)) == 4                       # PA_ERR_UNSUPPORTED
     assert _attn(_cache(head_dim=96)) == 4
+    assert _attn(_cache(head_dim=256, kv_dtype=pa.PA_F32), q_dtype=pa.PA_F32) == 4   # d = 256: 16-bit q only
     assert _attn(_cache(kv_dtype=9)) == 3                         # PA_ERR_DTYPE
     assert _attn(_cache(), q_dtype=pa.PA_F32) == 3                # bf16 cache with fp32 q
     assert _attn(_cache(kv_dtype=pa.PA_FP8_E4M3, k_scale=0.5), q_dtype=pa.PA_F32) == 3

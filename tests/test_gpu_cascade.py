@@ -70,6 +70,14 @@ def test_prompt_chunks_after_the_prefix():
     run(w, label="chunks after a 256-token prefix")
 
 
+def test_head_dim_256_with_chunks():
+    P = 192
+    lens = [P + 10, P + 150, P + 60, P + 333]
+    w = build("pfx_d256", 9, lens, [1, 100, 1, 33], num_q_heads=16, num_kv_heads=4, head_dim=256, block_size=64,
+              kv_dtype="bf16", shared_prefix_len=P)
+    run(w, label="d=256 with chunks")
+
+
 def test_head_dim_64_and_group_one():
     P = 128
     lens = [P + 5, P + 77, P + 1, P + 200]

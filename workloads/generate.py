@@ -353,17 +353,20 @@ def _llama7b_decode(num_seqs=256, placement="shuffled", **kw) -> Workload:
                  description="LLaMA-7B-shaped decode: 32/32 heads, d=128, L~U[128,2048]", **kw)
 
 
-def _gqa_long_decode(num_seqs=64, **kw) -> Workload:
+def _gqa_long_decode(num_seqs=64, head_dim=128, **kw) -> Workload:
+    """head_dim=256 keeps the KV bytes per token with 16q/4kv heads."""
     seed = 141003
     rng = np.random.default_rng([seed, 0])
     lens = np.floor(np.exp(rng.uniform(math.log(1024), math.log(32768), size=64))).astype(np.int64)
     lens = lens[:num_seqs]
-    return build("gqa_long_decode", seed, lens, [1] * len(lens), num_q_heads=32, num_kv_heads=8,
-                 head_dim=128, block_size=16, kv_dtype=kw.pop("kv_dtype", "bf16"),
-                 description="GQA decode, 32q/8kv, L log-uniform in [1k, 32k]", **kw)
+    hq, hkv = (32, 8) if head_dim == 128 else (32 * 128 // head_dim, 8 * 128 // head_dim)
+    return build("gqa_long_decode" + ("" if head_dim == 128 else f"_d{head_dim}"), seed, lens, [1] * len(lens),
+                 num_q_heads=hq, num_kv_heads=hkv, head_dim=head_dim, block_size=16,
+                 kv_dtype=kw.pop("kv_dtype", "bf16"),
+                 description=f"GQA decode, {hq}q/{hkv}kv, d {head_dim}, L log-uniform in [1k, 32k]", **kw)
 
 
-def _mixed_chunked_prefill(num_seqs=256, chunk_scale=1, **kw) -> Workload:
+def _mixed_chunked_prefill(num_seqs=256, chunk_scale=1, head_dim=128, **kw) -> Workload:
     """256 decode tokens, then prompt chunks (offset, length) in batch order.
 
     chunk_scale divides the chunk lengths and offsets (for reduced copies).
@@ -375,8 +378,10 @@ def _mixed_chunked_prefill(num_seqs=256, chunk_scale=1, **kw) -> Workload:
     chunks = [(o // chunk_scale, c // chunk_scale) for o, c in chunks]
     lens = list(dec) + [o + c for o, c in chunks]
     qlens = [1] * len(dec) + [c for _, c in chunks]
-    return build("mixed_chunked_prefill", seed, lens, qlens, num_q_heads=32, num_kv_heads=8,
-                 head_dim=128, block_size=16, kv_dtype=kw.pop("kv_dtype", "bf16"),
+    hq, hkv = (32, 8) if head_dim == 128 else (32 * 128 // head_dim, 8 * 128 // head_dim)
+    return build("mixed_chunked_prefill" + ("" if head_dim == 128 else f"_d{head_dim}"), seed, lens, qlens,
+                 num_q_heads=hq, num_kv_heads=hkv, head_dim=head_dim, block_size=16,
+                 kv_dtype=kw.pop("kv_dtype", "bf16"),
                  description="256 decode tokens + chunks 3x1024 (offsets 0/4096/8192) + 512, "
                              "4096-token budget, 32q/8kv, d=128", **kw)
 
