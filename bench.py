@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--config", default="llama7b_decode",
                     help="tiny_decode | llama7b_decode | gqa_long_decode | "
                          "mixed_chunked_prefill | fp8_shared_prefix")
-    ap.add_argument("--block-size", type=int, default=None, help="for fp8_shared_prefix")
+    ap.add_argument("--block-size", type=int, default=None, help="tokens per cache block (16, 32, 64)")
+    ap.add_argument("--kv-dtype", default=None, help="cache dtype override: bf16 | f16 | fp8_e4m3 (scale 2^-5)")
     ap.add_argument("--head-dim", type=int, default=None,
                     help="for gqa_long_decode / mixed_chunked_prefill: 256 keeps the KV bytes per token "
                          "with half the heads (16q/4kv)")
@@ -426,7 +427,17 @@ def main():
         kw["placement"] = args.placement
     if args.head_dim:
         kw["head_dim"] = args.head_dim
+    if args.kv_dtype:
+        kw["kv_dtype"] = args.kv_dtype
+        if args.kv_dtype == "fp8_e4m3":
+            kw.update(k_scale=workloads.generate.FP8_SCALE, v_scale=workloads.generate.FP8_SCALE)
     w = workloads.make(args.config, **kw)
+    # overrides the configuration's name does not already carry go into it
+    # (the measured-traffic records are keyed by workload name)
+    if args.kv_dtype and args.config != "fp8_shared_prefix":
+        w.name += f"_{args.kv_dtype}"
+    if args.block_size and args.config != "fp8_shared_prefix":
+        w.name += f"_B{args.block_size}"
     print(f"[bench] staging {w.name}: {json.dumps(w.summary())}", file=sys.stderr, flush=True)
     t_stage = time.perf_counter()
     step = wd.stage(w, write_new=False)

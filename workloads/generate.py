@@ -342,18 +342,18 @@ def _tiny_decode(num_seqs=None, **kw) -> Workload:
                  num_blocks=16, description="4 decode seqs, lengths {1,7,16,33}, fp32", **kw)
 
 
-def _llama7b_decode(num_seqs=256, placement="shuffled", **kw) -> Workload:
+def _llama7b_decode(num_seqs=256, placement="shuffled", block_size=16, **kw) -> Workload:
     seed = 141002
     rng = np.random.default_rng([seed, 0])
     lens = rng.integers(128, 2048, size=256, endpoint=True)[:num_seqs]
     name = "llama7b_decode" + ("_identity" if placement == "identity" else "")
     return build(name, seed, lens, [1] * len(lens), num_q_heads=32, num_kv_heads=32,
-                 head_dim=128, block_size=16, kv_dtype=kw.pop("kv_dtype", "bf16"),
+                 head_dim=128, block_size=block_size, kv_dtype=kw.pop("kv_dtype", "bf16"),
                  placement=placement,
                  description="LLaMA-7B-shaped decode: 32/32 heads, d=128, L~U[128,2048]", **kw)
 
 
-def _gqa_long_decode(num_seqs=64, head_dim=128, **kw) -> Workload:
+def _gqa_long_decode(num_seqs=64, head_dim=128, block_size=16, **kw) -> Workload:
     """head_dim=256 keeps the KV bytes per token with 16q/4kv heads."""
     seed = 141003
     rng = np.random.default_rng([seed, 0])
@@ -361,12 +361,12 @@ def _gqa_long_decode(num_seqs=64, head_dim=128, **kw) -> Workload:
     lens = lens[:num_seqs]
     hq, hkv = (32, 8) if head_dim == 128 else (32 * 128 // head_dim, 8 * 128 // head_dim)
     return build("gqa_long_decode" + ("" if head_dim == 128 else f"_d{head_dim}"), seed, lens, [1] * len(lens),
-                 num_q_heads=hq, num_kv_heads=hkv, head_dim=head_dim, block_size=16,
+                 num_q_heads=hq, num_kv_heads=hkv, head_dim=head_dim, block_size=block_size,
                  kv_dtype=kw.pop("kv_dtype", "bf16"),
                  description=f"GQA decode, {hq}q/{hkv}kv, d {head_dim}, L log-uniform in [1k, 32k]", **kw)
 
 
-def _mixed_chunked_prefill(num_seqs=256, chunk_scale=1, head_dim=128, **kw) -> Workload:
+def _mixed_chunked_prefill(num_seqs=256, chunk_scale=1, head_dim=128, block_size=16, **kw) -> Workload:
     """256 decode tokens, then prompt chunks (offset, length) in batch order.
 
     chunk_scale divides the chunk lengths and offsets (for reduced copies).
@@ -380,7 +380,7 @@ def _mixed_chunked_prefill(num_seqs=256, chunk_scale=1, head_dim=128, **kw) -> W
     qlens = [1] * len(dec) + [c for _, c in chunks]
     hq, hkv = (32, 8) if head_dim == 128 else (32 * 128 // head_dim, 8 * 128 // head_dim)
     return build("mixed_chunked_prefill" + ("" if head_dim == 128 else f"_d{head_dim}"), seed, lens, qlens,
-                 num_q_heads=hq, num_kv_heads=hkv, head_dim=head_dim, block_size=16,
+                 num_q_heads=hq, num_kv_heads=hkv, head_dim=head_dim, block_size=block_size,
                  kv_dtype=kw.pop("kv_dtype", "bf16"),
                  description="256 decode tokens + chunks 3x1024 (offsets 0/4096/8192) + 512, "
                              "4096-token budget, 32q/8kv, d=128", **kw)
