@@ -56,9 +56,9 @@ pa_status_t check_attention_sizes(const pa_cache_t* c, int32_t num_q_heads, int3
   const int64_t group = num_q_heads / c->num_kv_heads;
   // work items pack (tile, partition) into 16 bits each
   if (ceil_div(static_cast<int64_t>(max_query_len) * group, pa::kTileRows) > 0xFFFF) return PA_ERR_UNSUPPORTED;
-  if (ceil_div(max_seq_len, pa::decode_partition(max_seq_len)) > 0xFFFF) return PA_ERR_UNSUPPORTED;
   const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, c->num_kv_heads,
                                                      c->head_dim, max_seq_len);
+  if (ceil_div(max_seq_len, w.partition) > 0xFFFF) return PA_ERR_UNSUPPORTED;
   if (w.max_items > 0x7FFFFFFF / 64 || w.max_citems > 0x7FFFFFFF / 64) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }

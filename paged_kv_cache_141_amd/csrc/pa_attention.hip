@@ -30,7 +30,7 @@ __device__ __forceinline__ int item_size(int L, int ql, int G, int row0, int nro
 // Sequences are taken 1024 at a time; a scan of their item counts flattens
 // the batch's items so that all threads share them evenly.
 __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
-  constexpr int NB0 = kPartitionLong / 32 + 1;           // decode buckets: 0 .. 32 steps
+  constexpr int NB0 = kPartitionMax / 32 + 1;            // decode buckets: 0 .. 64 steps
   constexpr int NB1 = kChunkPartition / kChunkKeys + 1;   // chunk buckets: 0 .. 64 tiles
   __shared__ int hist[2][80];
   __shared__ int scan[1024];                             // inclusive item-count scan of the batch

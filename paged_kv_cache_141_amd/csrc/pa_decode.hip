@@ -15,9 +15,31 @@ namespace pa {
 #ifndef PA_DECODE_PREFETCH
 #define PA_DECODE_PREFETCH 2
 #endif
+#ifndef PA_DECODE_PREFETCH_FP8
+#define PA_DECODE_PREFETCH_FP8 2
+#endif
+#ifndef PA_DECODE_FP8_WIDE
+#define PA_DECODE_FP8_WIDE 1
+#endif
 #ifndef PA_DECODE_WAVES_PER_SIMD
 #define PA_DECODE_WAVES_PER_SIMD 1
 #endif
+
+// The physical block ids of one partition (at most 128 blocks), two per
+// lane: entry j sits in lane j % 64 of register j / 64, so a step reads its
+// block with a readlane instead of a memory trip.
+struct PartTable {
+  int lo, hi;
+  __device__ __forceinline__ void load(const int32_t* bt, int nbt, int lane) {
+    lo = lane < nbt ? bt[lane] : 0;
+    hi = lane + 64 < nbt ? bt[lane + 64] : 0;
+  }
+  __device__ __forceinline__ int64_t operator[](int j) const {   // j wave-uniform
+    const int a = __builtin_amdgcn_readlane(lo, j & 63);
+    const int b = __builtin_amdgcn_readlane(hi, j & 63);
+    return j < 64 ? a : b;
+  }
+};
 
 // One work item: sequence i, kv head h, rows [16*tile, 16*tile+16) of the
 // sequence's q_len*G (token, head-in-group) rows, keys of partition `part`.
@@ -61,13 +83,20 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   const int kend = min(min(L, kstart + a.partition), max_pos + 1);
   if (kstart >= kend) return;
 
-  // Q^T operand: row r's dims [32s + 8lg, +8)
+  // Which dims K-step s gives lane group lg: [32s + 8lg, +8) -- or, for fp8
+  // K, [64(s/2) + 16lg + 8(s%2), +8), so that one 16-byte load per lane fills
+  // the lane's slots of two K-steps.  A dot product does not depend on the
+  // order of its terms; Q and K only have to agree on it.
+  constexpr bool WIDE = KV == DT_FP8 && PA_DECODE_FP8_WIDE;
+  auto kdim = [&](int s) { return WIDE ? 64 * (s >> 1) + 16 * lg + 8 * (s & 1) : 32 * s + 8 * lg; };
+
+  // Q^T operand: row r's dims of each K-step
   Frag<CT> qf[KS];
   {
     const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
-                        ((static_cast<int64_t>(token) * a.num_q_heads + head) * D + 8 * lg) * EBQ;
+                        (static_cast<int64_t>(token) * a.num_q_heads + head) * D * EBQ;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = valid ? load_frag<CT, CT>(qp + 32 * s * EBQ) : frag_zero<CT>();
+    for (int s = 0; s < KS; ++s) qf[s] = valid ? load_frag<CT, CT>(qp + kdim(s) * EBQ) : frag_zero<CT>();
   }
 
   const int nblk = (L + BS - 1) / BS;
@@ -76,12 +105,11 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   const uint8_t* kc = static_cast<const uint8_t*>(a.k_cache) + h * tile_bytes;
   const uint8_t* vc = static_cast<const uint8_t*>(a.v_cache) + h * tile_bytes;
 
-  // The partition's block-table entries, one per lane (at most P/B <= 64):
-  // each step then reads its physical block ids with readlane, no memory trip.
+  // The partition's block-table entries, held in registers.
   const int jbase = kstart / BS;
   const int nbt = min(nblk - jbase, a.partition / BS);
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(i) * a.max_blocks_per_seq + jbase;
-  const int btv = lane < nbt ? bt[lane] : 0;
+  PartTable btv;
+  btv.load(a.block_tables + static_cast<int64_t>(i) * a.max_blocks_per_seq + jbase, nbt, lane);
 
   // per-lane key offsets inside a 32-key step
   const int kkey0 = 8 * (r >> 2) + (r & 3);      // sub-tile 0; sub-tile 1 adds 4
@@ -102,18 +130,27 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   // gather: physical block(s) from the table register, then 16-byte reads).
   auto issue = [&](Step& st, int k0) {
     const int j0 = k0 / BS;
-    const int64_t p0 = __builtin_amdgcn_readlane(btv, j0 - jbase);
+    const int64_t p0 = btv[j0 - jbase];
     int64_t p1 = p0;
-    if constexpr (BS == 16) p1 = __builtin_amdgcn_readlane(btv, min(j0 + 1, nblk - 1) - jbase);
+    if constexpr (BS == 16) p1 = btv[min(j0 + 1, nblk - 1) - jbase];
     const int inblk = k0 - j0 * BS;   // 0 for BS <= 32; 0 or 32 for BS = 64
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
       const int kk = kkey0 + 4 * tau;                  // key within the step
       const int64_t pb = (BS == 16 && kk >= 16) ? p1 : p0;
       const int off = (BS == 16) ? (kk & 15) : inblk + kk;
-      const uint8_t* kp = kc + pb * blk_stride + (static_cast<int64_t>(off) * D + 8 * lg) * EBK;
+      const uint8_t* kp = kc + pb * blk_stride + static_cast<int64_t>(off) * D * EBK;
+      if constexpr (WIDE) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) st.k[tau][s] = load_raw<KV>(kp + 32 * s * EBK);
+        for (int s = 0; s < KS; s += 2) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(kp + kdim(s));
+          st.k[tau][s].w = u32x2{x[0], x[1]};
+          st.k[tau][s + 1].w = u32x2{x[2], x[3]};
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) st.k[tau][s] = load_raw<KV>(kp + kdim(s) * EBK);
+      }
     }
     const int64_t pb = (BS == 16 && vkey >= 16) ? p1 : p0;
     const int off = (BS == 16) ? (vkey & 15) : inblk + vkey;
@@ -157,7 +194,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
 
   // Software pipeline: the loads of step s + PF are in flight while step s
   // computes.  fp8 steps are half the bytes, so they run one step deeper.
-  constexpr int PF = (KV == DT_FP8) ? 2 : (KV == DT_F32 ? 0 : PA_DECODE_PREFETCH);
+  constexpr int PF = (KV == DT_FP8) ? PA_DECODE_PREFETCH_FP8 : (KV == DT_F32 ? 0 : PA_DECODE_PREFETCH);
   constexpr int NB = PF + 1;
   Step buf[NB];
   const int nsteps = (kend - kstart + 31) / 32;
@@ -249,8 +286,8 @@ __device__ __forceinline__ void attn_item256(const AttnArgs& a, int i, int tile,
   const uint8_t* vc = static_cast<const uint8_t*>(a.v_cache) + h * tile_bytes;
   const int jbase = kstart / BS;
   const int nbt = min(nblk - jbase, a.partition / BS);
-  const int32_t* bt = a.block_tables + static_cast<int64_t>(i) * a.max_blocks_per_seq + jbase;
-  const int btv = lane < nbt ? bt[lane] : 0;
+  PartTable btv;
+  btv.load(a.block_tables + static_cast<int64_t>(i) * a.max_blocks_per_seq + jbase, nbt, lane);
   const int vkey = 4 * lg;                          // first of the lane's 4 keys for V / P
 
   float m = -__builtin_inff();
@@ -267,7 +304,7 @@ __device__ __forceinline__ void attn_item256(const AttnArgs& a, int i, int tile,
   // a 16-key step lies inside one block (B is 16, 32 or 64)
   auto issue = [&](Step& st, int k0) {
     const int j0 = k0 / BS;
-    const int64_t pb = __builtin_amdgcn_readlane(btv, j0 - jbase);
+    const int64_t pb = btv[j0 - jbase];
     const int inblk = k0 - j0 * BS;
     const uint8_t* kp = kc + pb * blk_stride + (static_cast<int64_t>(inblk + r) * D + 8 * lg) * EBK;
 #pragma unroll

@@ -14,17 +14,37 @@ constexpr int kTileRows = 16;
 
 // Keys of one context partition handled by one decode work item.  A row
 // whose keys span more than one partition gets partial (max, sum, acc)
-// results that a log-sum-exp reduce merges.  Steps whose longest context
-// reaches kLongContext use the longer partition: fewer items and partials
-// per row, while still leaving thousands of items to spread over the chip.
-// A partition holds at most 64 blocks (one block id per lane of a wave).
-constexpr int kPartitionShort = 512;
-constexpr int kPartitionLong = 1024;
+// results that a log-sum-exp reduce merges.  Longer partitions mean fewer
+// items (each pays a start-up latency before its first loads land) and
+// fewer partials; shorter ones spread few long contexts over more waves.
+// So: with at least kManyPairs (sequence, kv head) pairs -- two per decode
+// wave the chip holds (256 CUs x 4 SIMDs, one wave each) -- whole contexts
+// already keep every wave busy and partitions are as long as they go
+// (kPartitionMax); with fewer pairs, steps whose longest context reaches
+// kLongContext use kPartitionLong, shorter ones kPartitionShort.
+// A partition holds at most 128 blocks (two block ids per lane of a wave)
+// and at most kPartitionMax keys (64 steps of 32 keys).
+#ifndef PA_PARTITION_SHORT
+#define PA_PARTITION_SHORT 512
+#endif
+#ifndef PA_PARTITION_LONG
+#define PA_PARTITION_LONG 1024
+#endif
+#ifndef PA_MANY_PAIRS
+#define PA_MANY_PAIRS 2048
+#endif
+constexpr int kPartitionShort = PA_PARTITION_SHORT;
+constexpr int kPartitionLong = PA_PARTITION_LONG;
+constexpr int kPartitionMax = 2048;
+static_assert(kPartitionShort % 32 == 0 && kPartitionLong % 32 == 0, "partitions hold whole 32-key steps");
+static_assert(kPartitionShort <= kPartitionMax && kPartitionLong <= kPartitionMax, "at most 2048 keys");
 #ifndef PA_LONG_CONTEXT
 #define PA_LONG_CONTEXT 8192
 #endif
 constexpr int64_t kLongContext = PA_LONG_CONTEXT;
-inline int decode_partition(int64_t max_seq_len) {
+constexpr int64_t kManyPairs = PA_MANY_PAIRS;
+inline int decode_partition(int64_t max_seq_len, int64_t num_seqs, int64_t num_kv_heads) {
+  if (num_seqs * num_kv_heads >= kManyPairs) return kPartitionMax;
   return max_seq_len >= kLongContext ? kPartitionLong : kPartitionShort;
 }
 
@@ -107,7 +127,7 @@ inline WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_tokens, in
   const int64_t group = num_kv_heads > 0 ? num_q_heads / num_kv_heads : 1;
   // keys past the shared prefix: what the decode and chunk kernels cover
   const int64_t own = max_seq_len - prefix_len > 0 ? max_seq_len - prefix_len : 1;
-  w.partition = decode_partition(own);
+  w.partition = decode_partition(own, num_seqs, num_kv_heads);
   w.max_items = max_work_items(num_seqs, num_tokens, group, own, kTileRows, w.partition);
   w.max_citems = max_work_items(num_seqs, num_tokens, group, own, chunk_rows_for(head_dim), kChunkPartition);
   w.prefix_parts = 0;

@@ -179,6 +179,24 @@ def test_edge_lengths_long_context():
         assert_close(w, gpu_out(step), oracle_out(w), label=f"edge_long {kv} B={B}")
 
 
+def test_edge_lengths_many_pairs():
+    # 256 sequences x 8 kv heads: enough (sequence, kv head) pairs for
+    # 2048-key decode partitions (128 blocks of 16 keys: block ids in two
+    # registers per lane): lengths at those boundaries, and a prompt chunk
+    # that crosses one.
+    rng = np.random.default_rng([31, 0])
+    edges = [1, 63, 64, 65, 1023, 1024, 1025, 2047, 2048, 2049, 4095, 4096, 4097, 6000]
+    lens = edges + [int(x) for x in rng.integers(1, 400, size=255 - len(edges))] + [2300]
+    qlens = [1] * 255 + [100]
+    for kv, q, B in (("bf16", "bf16", 16), ("fp8_e4m3", "bf16", 32), ("f32", "f32", 64)):
+        sc = 0.05 if kv == "fp8_e4m3" else 1.0
+        w = build("edge_pairs", 31, lens, qlens, num_q_heads=16, num_kv_heads=8, head_dim=64,
+                  block_size=B, kv_dtype=kv, q_dtype=q, k_scale=sc, v_scale=sc)
+        say("edge_pairs", kv, B)
+        step = wd.stage(w)
+        assert_close(w, gpu_out(step), oracle_out(w), label=f"edge_pairs {kv} B={B}")
+
+
 # ------------------------------------------------------------------ invariants
 
 def test_placement_permutation_bit_exact():
