@@ -94,14 +94,17 @@ class HipEvents:
         self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-KERNEL_SOURCES = {"attn_kernel": "pa_decode.hip", "chunk_kernel": "pa_chunk.hip"}
+# the files each kernel is compiled from, beside the shared device headers
+KERNEL_SOURCES = {"attn_kernel": ("pa_decode.hip", "pa_decode_item.h"),
+                  "chunk_kernel": ("pa_chunk.hip", "pa_chunk_item.h"),
+                  "step_kernel": ("pa_step.hip", "pa_decode_item.h", "pa_chunk_item.h")}
 
 
 def kernel_source_hash(kernel):
     """Hash of the sources one kernel is compiled from (its own file plus the
     shared device headers): counter runs stay valid until these change."""
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "pa_device.h", "pa_codec.h", "pa_internal.h"):
+    for f in (*KERNEL_SOURCES[kernel], "pa_device.h", "pa_codec.h", "pa_internal.h"):
         h.update(open(os.path.join(ROOT, "paged_kv_cache_141_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -496,7 +499,12 @@ def main():
     # (with a shared prefix: the keys past it)
     decode_bytes = int(((w.seq_lens.astype(np.int64) - prefix) * ~is_chunk).sum()) * w.num_kv_heads * 2 * w.head_dim * eb
     achieved = decode_bytes / attn_s / 1e9
-    traffic = measured_traffic(w.name, "attn_kernel")
+    # A step with prompt chunks (16-bit q, head dim <= 128) runs its decode and
+    # chunk items in one fused launch: both event pairs then bracket that one
+    # kernel, and each roofline is what its own work achieved over it.
+    fused = bool(chunk_pairs) and w.head_dim <= 128
+    main_kernel = "step_kernel" if fused else "attn_kernel"
+    traffic = measured_traffic(w.name, main_kernel)
 
     line = {
         "metric": METRIC,
@@ -521,8 +529,8 @@ def main():
         "attention_kernel_us": round(attn_s * 1e6, 2),
         "attention_kernel_kv_bytes": decode_bytes,
         "cache_write_us": round(float(np.mean(cw_ms)) * 1e3, 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": main_kernel, "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "cpu_baseline": None,
     }
@@ -544,9 +552,12 @@ def main():
         t = float(np.mean(chunk_ms)) / 1e3
         peak = 2500.0   # dense bf16/fp16 MFMA, TFLOP/s
         line["chunk_kernel_us"] = round(t * 1e6, 2)
-        line["roofline_chunk"] = {"bound": "mfma", "achieved": round(flops / t / 1e12, 2), "peak": peak,
+        line["roofline_chunk"] = {"bound": "mfma", "kernel": "step_kernel" if fused else "chunk_kernel",
+                                  "achieved": round(flops / t / 1e12, 2), "peak": peak,
                                   "unit": "TFLOP/s", "frac": round(flops / t / 1e12 / peak, 4),
-                                  "flops": flops, "traffic": measured_traffic(w.name, "chunk_kernel")}
+                                  "flops": flops,
+                                  "traffic": None if fused else measured_traffic(w.name, "chunk_kernel")}
+        line["fused_step_kernel"] = fused
         line["config"]["chunk_tokens"] = int((c * is_chunk).sum())
     if args.cpu_seconds > 0:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)

@@ -101,6 +101,31 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
     }
   }
   __syncthreads();
+  // fused step: split the step kernel's workgroups between the two lists by
+  // their estimated times (the histograms hold the items' step / tile counts)
+  if (a.fused) {
+    if (tid == 0) {
+      float dsteps = 0.f, ctiles = 0.f;
+      for (int b = 1; b < NB0; ++b) dsteps += static_cast<float>(b) * hist[0][b];
+      for (int b = 1; b < NB1; ++b) ctiles += static_cast<float>(b) * hist[1][b];
+      const float td = dsteps * a.num_kv_heads * a.step_dec_us;     // whole chip, full bandwidth
+      const float tc = ctiles * a.num_kv_heads * a.step_chunk_us;   // whole chip
+      const int n = a.step_groups;
+      int nd = n;
+      if (dsteps == 0.f) {
+        nd = 0;
+      } else if (ctiles > 0.f) {
+        float best = __builtin_inff();
+        for (int k = 1; k < n; ++k) {
+          const float share = fminf(1.f, static_cast<float>(k) / (kFusedDecodeSaturation * n));
+          const float t = fmaxf(td / share, tc * n / static_cast<float>(n - k));
+          if (t < best) { best = t; nd = k; }
+        }
+      }
+      a.header[6] = nd;
+    }
+    __syncthreads();                                     // hist is rewritten below
+  }
   // bucket starts, longest bucket first: one wave per list scans the reversed
   // histogram (at most 80 buckets: lanes take buckets b and b + 64)
   if (tid < 128) {
@@ -204,7 +229,17 @@ hipError_t launch_attention(int q, int kv, int d, int bs, const AttnArgs& a, hip
   // the pairing and shape must exist before anything is enqueued
   hipError_t e = dispatch_attention(q, kv, d, bs, [](auto, auto, auto, auto) { return hipSuccess; });
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a);
+  // a step that can hold prompt chunks: one fused launch where the shape has one
+  const bool chunks = q != DT_F32 && a.chunk_path && static_cast<int64_t>(a.max_query_len) * a.group >= kChunkMinRows;
+  AttnArgs f = a;
+  const bool fused = PA_FUSED_STEP && chunks && (f.step_groups = static_cast<int32_t>(step_groups(q, kv, d, bs))) > 0;
+  if (fused) {
+    const double eb = kv == DT_F32 ? 4 : (kv == DT_FP8 ? 1 : 2);
+    f.fused = 1;
+    f.step_dec_us = static_cast<float>(32.0 * d * 2 * eb / kFusedDecodeBytesPerUs);
+    f.step_chunk_us = static_cast<float>(64.0 * a.chunk_rows * d * 4 / kFusedChunkFlopsPerUs);
+  }
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, fused ? f : a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.prefix_len > 0) {                     // the shared prefix, all rows at once
     AttnArgs p = a;
@@ -213,13 +248,21 @@ hipError_t launch_attention(int q, int kv, int d, int bs, const AttnArgs& a, hip
     if ((e = launch_chunk(q, kv, d, bs, p, stream)) != hipSuccess) return e;
     if (ev[5] && (e = hipEventRecord(ev[5], stream)) != hipSuccess) return e;
   }
-  if (ev[0] && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
-  if ((e = launch_decode(q, kv, d, bs, a, stream)) != hipSuccess) return e;
-  if (ev[1] && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
-  if (q != DT_F32 && a.chunk_path && static_cast<int64_t>(a.max_query_len) * a.group >= kChunkMinRows) {
+  if (fused) {                                // decode + chunk items in one launch
+    if (ev[0] && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
     if (ev[2] && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
-    if ((e = launch_chunk(q, kv, d, bs, a, stream)) != hipSuccess) return e;
+    if ((e = launch_step(q, kv, d, bs, f, stream)) != hipSuccess) return e;
+    if (ev[1] && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
     if (ev[3] && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
+  } else {
+    if (ev[0] && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
+    if ((e = launch_decode(q, kv, d, bs, a, stream)) != hipSuccess) return e;
+    if (ev[1] && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
+    if (chunks) {
+      if (ev[2] && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
+      if ((e = launch_chunk(q, kv, d, bs, a, stream)) != hipSuccess) return e;
+      if (ev[3] && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
+    }
   }
   if ((a.max_parts > 1 || a.prefix_len > 0) && a.num_tokens > 0) {
     if (q == DT_F32) {

@@ -1,507 +1,17 @@
 // pa_chunk.hip -- the chunked-prefill attention kernel: 8-wave workgroups
-// over 256-row blocks of one prompt chunk, 64-key tiles of the paged cache
-// staged in LDS, MFMA for both products, causal mask by selection.
+// over 256-row blocks of prompt chunks (the loop itself is chunk_items).
 //
 // Method: a step mixes one-token decode rows with causal prompt chunks
 // (techknowgenie "vLLM V1 core refactoring", section "Dynamic Chunked
 // Prefill"); the chunk's queries see the cached prefix and the chunk's own
 // earlier tokens, through the block table (itwiki "vLLM", "PagedAttention").
-#include <type_traits>
-
-#include "pa_device.h"
+#include "pa_chunk_item.h"
 
 namespace pa {
 
-// LDS image of one 64-key tile in the 16-bit compute type: K rows [64][d]
-// and V^T rows [d][64], unpadded.  The 16-byte chunks of a row are XOR-
-// swizzled so that the 16 lanes of each MFMA operand read (16 different
-// rows, one chunk column) land in 16 different 16-byte bank groups.
-template <int D>
-struct ChunkLds {
-  static constexpr int KROW = D * 2;                   // bytes per K row
-  static constexpr int VROW = kChunkKeys * 2;          // bytes per V^T row (128)
-  static constexpr int KBYTES = kChunkKeys * KROW;
-  static constexpr int BUF = KBYTES + D * VROW;
-  // The K rows one read touches are {8*(r/4) + 4*tau + r%4} (mod 32).
-  static __device__ __forceinline__ int kswz(int key) {
-    if constexpr (D >= 128) return (key & 3) | (((key >> 3) & 3) << 2);   // 16 distinct 16-byte groups
-    else return ((key >> 1) & 1) | (((key >> 3) & 3) << 1);   // 128-byte rows pair up per 256 bytes
-  }
-  // The V^T rows one read touches are 16 consecutive dims.
-  static __device__ __forceinline__ int vswz(int dim) { return (dim >> 1) & 7; }
-  static __device__ __forceinline__ int koff(int key, int chunk) { return key * KROW + ((chunk ^ kswz(key)) << 4); }
-  static __device__ __forceinline__ int voff(int dim, int chunk) { return KBYTES + dim * VROW + ((chunk ^ vswz(dim)) << 4); }
-};
-
-// 16 bytes from global memory straight into LDS (global_load_lds_dwordx4):
-// lane l's data lands at LDS byte offset lds_base + 16 * l, lds_base being
-// wave-uniform.  Issued as inline assembly so that the compiler does not
-// guard every later LDS read with a wait for it (it cannot tell the ring
-// buffers apart); the kernel waits for these loads itself, with s_waitcnt
-// vmcnt and a barrier, before any wave reads the buffer they fill.
-// M0 carries the LDS address; it is saved and restored around the load so
-// that the compiler's own use of M0 is never disturbed.
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(g), "s"(lds_base)
-      : "memory");
-}
-
-// s_waitcnt immediate: at most n vector-memory operations outstanding
-// (expcnt and lgkmcnt left unconstrained).
-constexpr int vmcnt_imm(int n) { return 0xF70 | (n & 15) | ((n >> 4) << 14); }
-
-// 16 raw fp8 codes -> 16 elements of the 16-bit compute type (two 16-byte halves).
-template <int CT>
-__device__ __forceinline__ void widen16(const u32x4& raw, u32x4& lo, u32x4& hi) {
-  Raw<DT_FP8> a, b;
-  a.w = u32x2{raw[0], raw[1]};
-  b.w = u32x2{raw[2], raw[3]};
-  lo = to_frag<CT, DT_FP8>(a).w;
-  hi = to_frag<CT, DT_FP8>(b).w;
-}
-
-// Softmax step of one 16-row tile over one 64-key tile, without the row sum
-// (the row sums come from the PV product with an all-ones operand): updates
-// the reference max m (lazily, as in softmax_update) and rescales the
-// accumulators, returns p = 2^(c*s - c*m) in the MFMA operand type.
-template <int CT, int NACC>
-__device__ __forceinline__ void chunk_softmax(const float (&s)[16], float& m, f32x4 (&acc)[NACC], f32x4& lacc,
-                                              float c, float slack, Frag<CT> (&pf)[2]) {
-  float lm = s[0];
-#pragma unroll
-  for (int e = 1; e < 16; ++e) lm = fmaxf(lm, s[e]);
-  if (__any(lm > m + slack)) {
-    float rm = fmaxf(lm, __shfl_xor(lm, 16));
-    rm = fmaxf(rm, __shfl_xor(rm, 32));
-    const float mnew = fmaxf(m, rm);
-    const float alpha = (mnew == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f((m - mnew) * c);
-    lacc *= alpha;
-#pragma unroll
-    for (int n = 0; n < NACC; ++n) acc[n] *= alpha;
-    m = mnew;
-  }
-  const float cm = (m == -__builtin_inff()) ? 0.f : m * c;
-#pragma unroll
-  for (int kg = 0; kg < 2; ++kg) {
-    float p[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * kg + e], c, -cm));
-    pf[kg] = pack_p<CT>(p);
-  }
-}
-
-// One workgroup (8 waves, two per SIMD) per work item: sequence i, kv head h,
-// rows [256*rb, 256*rb + 256) of the sequence's (token, head-in-group) rows,
-// keys of context partition `part` (4096 keys).  Wave w owns rows
-// 32w..32w+31 as two 16-row tiles.  Each 64-key tile is gathered through the
-// block table by all 512 threads with 16-byte loads -- straight into LDS for
-// 16-bit caches (global_load_lds), through registers for fp8, which is
-// widened to the compute type on the way -- kChunkAhead tiles ahead of the
-// one being computed.  Each wave runs the transposed-score MFMA scheme of
-// the decode kernel, every LDS operand read feeding both of its row tiles.
-//
-// Keys past a row's position get score -inf by selection, on the tiles that
-// hold such keys only; V columns of keys past the end of the sequence (they
-// hold whatever the pool has there) are overwritten with zero in LDS.
-#ifndef PA_CHUNK_AHEAD
-#define PA_CHUNK_AHEAD 2
-#endif
-constexpr int kChunkAhead = PA_CHUNK_AHEAD;              // tiles in flight (16-bit caches)
-
 template <int CT, int KV, int D, int BS>
 __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
-  using Lds = ChunkLds<D>;
-  constexpr bool DIRECT = (KV != DT_FP8);                // 16-bit cache: global -> LDS directly
-  // 16-bit caches: tile t and the kChunkAhead tiles loading behind it; fp8:
-  // tiles t and t+1 (staged from registers after round t computes).
-  constexpr int AHEAD = D == 256 ? 1 : kChunkAhead;      // a 64 KB tile at d = 256: two buffers fit LDS
-  constexpr int NBUF = DIRECT ? AHEAD + 1 : 2;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * Lds::BUF];
-  __shared__ int32_t btl[kChunkPartition / BS];          // the partition's physical block ids
-  __shared__ int slot;
-  constexpr int EBQ = Bytes<CT>::v;
-  constexpr int EBK = Bytes<KV>::v;
-  constexpr int KS = D / 32;
-  constexpr int NT = D / 16;
-  constexpr int RT = D == 256 ? 1 : 2;                   // row tiles per wave
-  constexpr int ROWS = kChunkWaves * 16 * RT;            // rows of one item (chunk_rows_for(D))
-
-  const int tid = threadIdx.x;
-  const int wave = uniform(tid >> 6);                    // wave-uniform: keeps its branches scalar
-  const int lane = tid & 63;
-  const int r = lane & 15;
-  const int lg = lane >> 4;
-  // the prefix pass has (row block, prefix partition, kv head) items known on
-  // the host; otherwise the plan's chunk list times the kv heads
-  const bool prefix = a.prefix_pass != 0;
-  const int64_t total = prefix ? a.prefix_items : static_cast<int64_t>(uniform(a.header[3])) * a.num_kv_heads;
-  const int64_t tile_bytes = static_cast<int64_t>(BS) * D * EBK;
-  const int64_t blk_stride = tile_bytes * a.num_kv_heads;
-  const uint32_t blk_stride32 = static_cast<uint32_t>(blk_stride);   // Hkv * B * d * eb < 2^32
-
-  // Direct-to-LDS loads: wave w's load j fills tile bytes [base, base + 1 KB).
-  // Tiles start at multiples of 64 >= B, so which key (or dim) and which
-  // 16-byte chunk a lane fetches, its block relative to the tile's first
-  // block and its offset inside that block are the same for every tile.
-  constexpr int NI = Lds::BUF / 1024 / kChunkWaves;       // loads per wave per tile
-  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
-  // Per load: the block relative to the tile's first block, and the byte
-  // offset inside the block.
-  int dma_base[NI], dma_rel[NI], dma_off[NI];
-  bool dma_is_v[NI];
-#pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int base = (wave * NI + j) * 1024;
-    const int pos = base + lane * 16;
-    dma_base[j] = base;
-    dma_is_v[j] = base >= Lds::KBYTES;
-    if (!dma_is_v[j]) {
-      const int kk = pos / Lds::KROW;
-      const int chunk = ((pos % Lds::KROW) >> 4) ^ Lds::kswz(kk);
-      dma_rel[j] = kk / BS;
-      dma_off[j] = ((kk % BS) * D + 8 * chunk) * EBK;
-    } else {
-      const int pv = pos - Lds::KBYTES;
-      const int dim = pv / Lds::VROW;
-      const int kk = 8 * (((pv % Lds::VROW) >> 4) ^ Lds::vswz(dim));   // first of the chunk's 8 keys
-      dma_rel[j] = kk / BS;
-      dma_off[j] = (dim * BS + kk % BS) * EBK;
-    }
-  }
-
-  // LDS operand reads: lane (r, lg) reads K row kg*32 + 4*tau + rb, chunk
-  // 4s + lg, and V^T row 16n + r, chunk 4kg + lg.  The swizzle of those rows
-  // depends on r alone, so each lane needs one offset per s (K) and per kg
-  // (V); kg, tau and n then enter as immediate offsets.
-  const int rb = 8 * (r >> 2) + (r & 3);
-  int kls[KS], vls[2];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) kls[s] = Lds::koff(rb, 4 * s + lg);
-#pragma unroll
-  for (int kg = 0; kg < 2; ++kg) vls[kg] = Lds::voff(r, 4 * kg + lg);
-
-  // all-ones A operand: the PV product with it yields the row sums of P
-  Frag<CT> ones;
-  {
-    const uint32_t one2 = CT == DT_BF16 ? 0x3F803F80u : 0x3C003C00u;
-    ones.w = u32x4{one2, one2, one2, one2};
-  }
-
-  while (true) {
-    if (tid == 0) slot = atomicAdd(a.header + (prefix ? 4 : 2), 1);
-    __syncthreads();
-    const int w = slot;
-    if (w >= total) break;
-    const int G = a.group;
-    int i, h, rblk, part, L, q0, rows, base_pos, tstep, cpart, kstart, pslot;
-    if (prefix) {
-      // all rows of the step (every token x its kv head's group) against keys
-      // [part * P, ...) of the shared prefix, which every row sees whole: as if
-      // each row sat at position prefix_len - 1.  Row blocks vary fastest, so
-      // items that read the same keys run side by side.
-      rblk = w % a.prefix_rblocks;
-      const int ph = w / a.prefix_rblocks;
-      h = ph % a.num_kv_heads;
-      part = ph / a.num_kv_heads;
-      i = 0;                                 // the prefix blocks, read from sequence 0's table row
-      L = a.prefix_len;
-      q0 = 0;
-      rows = a.num_tokens * G;
-      base_pos = a.prefix_len - 1;
-      tstep = 0;
-      cpart = a.prefix_part;
-      kstart = part * cpart;
-      pslot = part;
-    } else {
-      const int e = w / a.num_kv_heads;
-      h = w - e * a.num_kv_heads;
-      i = a.citems[2 * e];
-      const int tp = a.citems[2 * e + 1];
-      rblk = tp >> 16;
-      part = tp & 0xFFFF;
-      L = a.seq_lens[i];
-      q0 = a.qsl[i];
-      const int ql = a.qsl[i + 1] - q0;
-      rows = ql * G;
-      base_pos = L - ql;
-      tstep = 1;
-      cpart = kChunkPartition;
-      kstart = a.prefix_len + part * cpart;   // keys past a shared prefix only
-      pslot = a.prefix_parts + part;
-    }
-    const int wrow0 = rblk * ROWS + wave * (16 * RT);
-    const int wlast = min(rows, wrow0 + 16 * RT) - 1;     // last row of this wave (< wrow0: none)
-    const int wave_min_pos = base_pos + tstep * (wrow0 / G);
-    const int wave_max_pos = wlast >= wrow0 ? base_pos + tstep * (wlast / G) : -1;
-    const int wg_max_pos = base_pos + tstep * ((min(rows, rblk * ROWS + ROWS) - 1) / G);
-    const int kend = min(min(L, kstart + cpart), wg_max_pos + 1);
-
-    if (kstart < kend) {
-      int row_pos[RT];
-      Frag<CT> qf[RT][KS];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int R = wrow0 + 16 * rt + r;
-        const bool valid = R < rows;
-        const int t = R / G;
-        row_pos[rt] = valid ? base_pos + tstep * t : -1;
-        const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
-                            ((static_cast<int64_t>(q0 + t) * a.num_q_heads + h * G + (R - t * G)) * D + 8 * lg) * EBQ;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-          qf[rt][s] = valid ? load_frag<CT, CT>(qp + 32 * s * EBQ) : frag_zero<CT>();
-      }
-      float m[RT];
-      f32x4 lacc[RT];
-      const float slack = a.rescale_slack;
-      f32x4 acc[RT][NT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        m[rt] = -__builtin_inff();
-        lacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int n = 0; n < NT; ++n) acc[rt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-
-      const int nblk = (L + BS - 1) / BS;
-      const int jbase = kstart / BS;
-      {
-        // the partition's block ids; past the sequence's last block the
-        // table repeats that block (keys past the end are loaded but never
-        // used), so tile loads need no clamp
-        const int32_t* bt = a.block_tables + static_cast<int64_t>(i) * a.max_blocks_per_seq + jbase;
-        const int nb = min(nblk - jbase, cpart / BS);
-        for (int j = tid; j < cpart / BS; j += kChunkThreads) btl[j] = bt[min(j, nb - 1)];
-      }
-      __syncthreads();
-      const uint8_t* kc = static_cast<const uint8_t*>(a.k_cache) + h * tile_bytes;
-      const uint8_t* vc = static_cast<const uint8_t*>(a.v_cache) + h * tile_bytes;
-      // physical block of tile-relative key index kk (clamped to the last block:
-      // keys past the end are loaded but never used)
-      auto phys_of = [&](int kt, int kk) -> int64_t { return btl[min((kt + kk) / BS, nblk - 1) - jbase]; };
-
-      // ---- 16-bit caches: the tile goes straight to LDS, 1 KB per wave instruction
-      auto issue_direct = [&](int b, int kt) {
-        const int jt = kt / BS - jbase;                     // tile's first block, table-relative
-        uint32_t phys[NI];
-#pragma unroll
-        for (int j = 0; j < NI; ++j) phys[j] = static_cast<uint32_t>(btl[jt + dma_rel[j]]);
-#pragma unroll
-        for (int j = 0; j < NI; ++j) {
-          // a block id times the per-block stride (< 2^32 bytes) needs one 32x32->64 multiply-add
-          const uint8_t* src = ((dma_is_v[j] ? vc : kc) + dma_off[j]) + static_cast<uint64_t>(phys[j]) * blk_stride32;
-          lds_dma16(src, uniform(static_cast<int>(lds0 + b * Lds::BUF + dma_base[j])));
-        }
-      };
-
-      // ---- fp8 caches: 16 codes per thread-chunk through registers, widened
-      constexpr int FCH = kChunkKeys * D / 16;                // 16-code chunks of K (and of V) per tile
-      constexpr int FPT = (FCH + kChunkThreads - 1) / kChunkThreads;
-      using Regs = u32x4[DIRECT ? 1 : FPT];
-      Regs kreg0, vreg0, kreg1, vreg1;
-      auto gather_fp8 = [&](Regs& kreg, Regs& vreg, int kt) {
-#pragma unroll
-        for (int j = 0; j < FPT; ++j) {
-          const int c = tid + kChunkThreads * j;
-          if (FCH % kChunkThreads != 0 && c >= FCH) break;
-          const int kk = c / (D / 16);
-          const int cc = c % (D / 16);
-          kreg[j] = *reinterpret_cast<const u32x4*>(
-              kc + phys_of(kt, kk) * blk_stride + static_cast<int64_t>((kt + kk) % BS) * D + cc * 16);
-          const int dim = c / (kChunkKeys / 16);
-          const int kv0 = (c % (kChunkKeys / 16)) * 16;      // first of 16 keys
-          vreg[j] = *reinterpret_cast<const u32x4*>(
-              vc + phys_of(kt, kv0) * blk_stride + static_cast<int64_t>(dim) * BS + (kt + kv0) % BS);
-        }
-      };
-      auto stage_fp8 = [&](const Regs& kreg, const Regs& vreg, uint8_t* buf) {
-#pragma unroll
-        for (int j = 0; j < FPT; ++j) {
-          const int c = tid + kChunkThreads * j;
-          if (FCH % kChunkThreads != 0 && c >= FCH) break;
-          u32x4 lo, hi;
-          const int kk = c / (D / 16);
-          const int cc = c % (D / 16);                       // 16 codes = 16-bit chunks 2cc, 2cc+1
-          widen16<CT>(kreg[j], lo, hi);
-          *reinterpret_cast<u32x4*>(buf + Lds::koff(kk, 2 * cc)) = lo;
-          *reinterpret_cast<u32x4*>(buf + Lds::koff(kk, 2 * cc + 1)) = hi;
-          const int dim = c / (kChunkKeys / 16);
-          const int vc2 = (c % (kChunkKeys / 16)) * 2;
-          widen16<CT>(vreg[j], lo, hi);
-          *reinterpret_cast<u32x4*>(buf + Lds::voff(dim, vc2)) = lo;
-          *reinterpret_cast<u32x4*>(buf + Lds::voff(dim, vc2 + 1)) = hi;
-        }
-      };
-      // V^T columns of keys kt + [live, 64) are past the end: overwrite them
-      // with zero (all threads; the caller fences with a barrier).
-      auto zero_tail = [&](uint8_t* buf, int live) {
-        for (int x = tid; x < D * kChunkKeys; x += kChunkThreads) {
-          const int dim = x / kChunkKeys;
-          const int key = x % kChunkKeys;
-          if (key >= live)
-            *reinterpret_cast<uint16_t*>(buf + Lds::voff(dim, key >> 3) + 2 * (key & 7)) = 0;
-        }
-      };
-
-      // ---- the two halves of a tile's work on this wave's rows
-      Frag<CT> pf[RT][2];                                    // P of the last softmax, MFMA operand
-      auto qk_softmax = [&](const uint8_t* buf, int kt) {
-        f32x4 sf[RT][2][2];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int kg = 0; kg < 2; ++kg)
-#pragma unroll
-            for (int tau = 0; tau < 2; ++tau) sf[rt][kg][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kg = 0; kg < 2; ++kg)
-#pragma unroll
-          for (int tau = 0; tau < 2; ++tau) {
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-              Frag<CT> kf;
-              kf.w = *reinterpret_cast<const u32x4*>(buf + kls[s] + (kg * 32 + 4 * tau) * Lds::KROW);
-#pragma unroll
-              for (int rt = 0; rt < RT; ++rt) sf[rt][kg][tau] = mma<CT>(sf[rt][kg][tau], kf, qf[rt][s]);
-            }
-          }
-        float sc[RT][16];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int x = 0; x < 16; ++x) sc[rt][x] = sf[rt][x >> 3][(x >> 2) & 1][x & 3];
-        if (kt + kChunkKeys - 1 > wave_min_pos) {
-          // the lane's keys are kt + 8lg + {0..7} and kt + 8lg + 32 + {0..7}
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            const int vis = row_pos[rt] - kt - 8 * lg;      // visible: offset <= vis
-#pragma unroll
-            for (int x = 0; x < 16; ++x)
-              sc[rt][x] = ((x >> 3) * 32 + (x & 7) > vis) ? -__builtin_inff() : sc[rt][x];
-          }
-        }
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          chunk_softmax<CT, NT>(sc[rt], m[rt], acc[rt], lacc[rt], a.score_scale, slack, pf[rt]);
-      };
-      auto pv = [&](const uint8_t* buf) {
-#pragma unroll
-        for (int kg = 0; kg < 2; ++kg) {
-#pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            Frag<CT> vf;
-            vf.w = *reinterpret_cast<const u32x4*>(buf + vls[kg] + 16 * n * Lds::VROW);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) acc[rt][n] = mma<CT>(acc[rt][n], vf, pf[rt][kg]);
-          }
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) lacc[rt] = mma<CT>(lacc[rt], ones, pf[rt][kg]);
-        }
-      };
-
-      const int ntiles = (kend - kstart + kChunkKeys - 1) / kChunkKeys;
-      auto tile_key = [&](int ti) { return kstart + ti * kChunkKeys; };
-      auto bufp = [&](int ti) { return lds + (ti % NBUF) * Lds::BUF; };
-      // wait until at most the loads of the n most recently issued tiles are outstanding
-      auto wait_later = [&](int n) {
-        static_assert(AHEAD >= 1 && AHEAD <= 3, "tiles in flight: 1 to 3");
-        if (AHEAD >= 3 && n >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI));
-        else if (AHEAD >= 2 && n >= 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(NI));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      };
-      // one round: tile ti is in LDS
-      auto do_round = [&](int ti) {
-        const int kt = tile_key(ti);
-        if (kt + kChunkKeys > L) {                           // the sequence's last keys: V tail to zero
-          zero_tail(bufp(ti), L - kt);
-          __syncthreads();
-        }
-        if (kt <= wave_max_pos) {
-          qk_softmax(bufp(ti), kt);
-          pv(bufp(ti));
-        }
-      };
-
-      if constexpr (DIRECT) {
-        // The compiler cannot see the LDS loads; retire its own loads (q) here
-        // so that it has no reason to wait on the vector-memory counter later.
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        // tiles 0 .. AHEAD-1 in flight, then wait for tile 0
-#pragma unroll
-        for (int x = 0; x < AHEAD; ++x)
-          if (x < ntiles) issue_direct(x, tile_key(x));
-        wait_later(min(ntiles, AHEAD) - 1);
-        __syncthreads();
-        for (int ti = 0; ti < ntiles; ++ti) {
-          // buffer (ti + ahead) % NBUF last held tile ti-1, finished in round ti-1
-          if (ti + AHEAD < ntiles) issue_direct((ti + AHEAD) % NBUF, tile_key(ti + AHEAD));
-          do_round(ti);
-          // tile ti+1 has landed once at most the loads of the tiles after it are outstanding
-          wait_later(min(ntiles - 2 - ti, AHEAD - 1));
-          __syncthreads();
-        }
-      } else {
-        // register set ti % 2 holds tile ti between its gather and its staging
-        gather_fp8(kreg0, vreg0, tile_key(0));
-        stage_fp8(kreg0, vreg0, bufp(0));
-        if (ntiles > 1) gather_fp8(kreg1, vreg1, tile_key(1));
-        __syncthreads();
-        for (int ti = 0; ti < ntiles; ti += 2) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int tj = ti + half;
-            if (tj < ntiles) {
-              Regs& kr = half ? kreg1 : kreg0;   // held tile tj (already staged): free
-              Regs& vr = half ? vreg1 : vreg0;
-              Regs& kn = half ? kreg0 : kreg1;   // holds tile tj + 1
-              Regs& vn = half ? vreg0 : vreg1;
-              if (tj + 2 < ntiles) gather_fp8(kr, vr, tile_key(tj + 2));
-              do_round(tj);
-              // buffer (tj+1) % 2 last held tile tj-1, finished in round tj-1
-              if (tj + 1 < ntiles) stage_fp8(kn, vn, bufp(tj + 1));
-              __syncthreads();
-            }
-          }
-        }
-      }
-
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int R = wrow0 + 16 * rt + r;
-        if (R >= rows || row_pos[rt] < kstart) continue;
-        const int t = R / G;
-        const int token = q0 + t;
-        const int head = h * G + (R - t * G);
-        const float ltot = lacc[rt][0];
-        if (a.prefix_len == 0 && row_pos[rt] / kChunkPartition == 0) {
-          const float inv = a.v_scale / ltot;
-          uint8_t* op = static_cast<uint8_t*>(a.out) +
-                        ((static_cast<int64_t>(token) * a.num_q_heads + head) * D + 4 * lg) * EBQ;
-#pragma unroll
-          for (int n = 0; n < NT; ++n)
-            store4<CT>(op + 16 * n * EBQ, acc[rt][n][0] * inv, acc[rt][n][1] * inv, acc[rt][n][2] * inv,
-                       acc[rt][n][3] * inv);
-        } else {
-          const int64_t rowp = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts + pslot;
-          if (lg == 0) {
-            a.part_m[rowp] = max_log2(m[rt], a.score_scale);
-            a.part_l[rowp] = ltot;
-          }
-          float* pp = a.part_acc + rowp * D + 4 * lg;
-#pragma unroll
-          for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(pp + 16 * n) = acc[rt][n] * a.v_scale;
-        }
-      }
-    }
-    __syncthreads();
-  }
+  chunk_items<CT, KV, D, BS>(a);
 }
 
 // One workgroup per resident slot, looping over chunk items.

@@ -72,6 +72,22 @@ constexpr float kRescaleSlack = 8.f;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Fused step: a step with prompt chunks (head dim <= 128, 16-bit queries)
+// runs its decode and chunk work in one launch of one 8-wave workgroup per
+// CU, split between the two by the plan kernel so that the HBM-bound decode
+// items and the MFMA-bound chunk items run side by side.  The split is sized
+// with throughputs measured on MI355X (256 CUs): decode streams about
+// 5.5 TB/s once it holds 60 % of the CUs, proportionally less on fewer (128
+// CUs: 85 % of the full rate); the chunk loop retires about 0.8 PFLOP/s of
+// algorithmic work on the whole chip, in proportion to its CUs.  Chunk
+// workgroups that run out of chunk items go on to decode items.
+#ifndef PA_FUSED_STEP
+#define PA_FUSED_STEP 1
+#endif
+constexpr double kFusedDecodeBytesPerUs = 5.5e6;
+constexpr double kFusedChunkFlopsPerUs = 0.8e9;
+constexpr float kFusedDecodeSaturation = 0.6f;
+
 // Upper bound on the number of (sequence, row tile, partition) work items,
 // from host-side bounds only: sum_i ceil(q_i*G/rows) <= ceil(T*G/rows) + S.
 inline int64_t max_work_items(int64_t num_seqs, int64_t num_tokens, int64_t group,
@@ -194,6 +210,13 @@ struct AttnArgs {
   float score_scale;   // scale * k_scale * log2(e)
   float rescale_slack; // kRescaleSlack / score_scale (raw-score units)
   float v_scale;
+  // Fused step (decode and chunk work in one launch): the plan kernel splits
+  // the step kernel's step_groups workgroups (one per CU) into decode and
+  // chunk roles, header[6] = workgroups that start on decode items.
+  int32_t fused;
+  int32_t step_groups;
+  float step_dec_us;     // whole-chip time of one 32-key decode step of one kv head, us
+  float step_chunk_us;   // whole-chip time of one 64-key chunk tile of one kv head, us
 };
 
 // Workgroups of `threads` threads of `kernel` that fit on the device at once.
@@ -267,5 +290,10 @@ hipError_t launch_decode(int q_dtype, int kv_dtype, int head_dim, int block_size
                          hipStream_t stream);
 hipError_t launch_chunk(int q_dtype, int kv_dtype, int head_dim, int block_size, const AttnArgs& a,
                         hipStream_t stream);
+// The fused step kernel (pa_step.hip): its grid (one workgroup per CU, 0 if
+// the shape has no fused form: f32 q or head dim 256) and its launch.
+int64_t step_groups(int q_dtype, int kv_dtype, int head_dim, int block_size);
+hipError_t launch_step(int q_dtype, int kv_dtype, int head_dim, int block_size, const AttnArgs& a,
+                       hipStream_t stream);
 
 }  // namespace pa
