@@ -115,12 +115,13 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
       if (dsteps == 0.f) {
         nd = 0;
       } else if (ctiles > 0.f) {
-        float best = __builtin_inff();
-        for (int k = 1; k < n; ++k) {
-          const float share = fminf(1.f, static_cast<float>(k) / (kFusedDecodeSaturation * n));
-          const float t = fmaxf(td / share, tc * n / static_cast<float>(n - k));
-          if (t < best) { best = t; nd = k; }
-        }
+        // k decode workgroups: decode takes td * s n / k (k <= s n, s the
+        // saturation share; td beyond), chunks tc * n / (n - k).  The first
+        // falls and the second rises with k: they meet at k = s td n / (tc + s td),
+        // and past s n only the chunk time grows.
+        const float sat = kFusedDecodeSaturation * n;
+        const float k = fminf(sat, kFusedDecodeSaturation * td * n / (tc + kFusedDecodeSaturation * td));
+        nd = min(max(static_cast<int>(k + 0.5f), 1), n - 1);
       }
       a.header[6] = nd;
     }
