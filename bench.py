@@ -498,7 +498,13 @@ def main():
     eb = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}[w.kv_dtype]
     # (with a shared prefix: the keys past it)
     decode_bytes = int(((w.seq_lens.astype(np.int64) - prefix) * ~is_chunk).sum()) * w.num_kv_heads * 2 * w.head_dim * eb
-    achieved = decode_bytes / attn_s / 1e9
+    # Blocks that several sequences' tables share are fetched from HBM once
+    # and then served from cache: the HBM roofline prices the unique bytes
+    # (the shared prefix once), and the logical bytes are reported beside it.
+    unique_bytes = decode_bytes
+    if w.shared_prefix_len and w.prefix_blocks_shared and not prefix:
+        unique_bytes -= (int((~is_chunk).sum()) - 1) * w.shared_prefix_len * w.num_kv_heads * 2 * w.head_dim * eb
+    achieved = unique_bytes / attn_s / 1e9
     # A step with prompt chunks (16-bit q, head dim <= 128) runs its decode and
     # chunk items in one fused launch: both event pairs then bracket that one
     # kernel, and each roofline is what its own work achieved over it.
@@ -528,6 +534,8 @@ def main():
         "hbm_frac_step": round(kv_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "attention_kernel_us": round(attn_s * 1e6, 2),
         "attention_kernel_kv_bytes": decode_bytes,
+        "attention_kernel_unique_kv_bytes": unique_bytes,
+        "attention_kernel_logical_GBps": round(decode_bytes / attn_s / 1e9, 2),
         "cache_write_us": round(float(np.mean(cw_ms)) * 1e3, 2),
         "roofline": {"bound": "hbm", "kernel": main_kernel, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
