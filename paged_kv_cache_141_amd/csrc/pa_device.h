@@ -66,6 +66,22 @@ __device__ __forceinline__ Raw<SRC> load_raw(const uint8_t* p) {
   return r;
 }
 
+// Two fp8 codes (the low or high 16 bits of w) -> two elements of the 16-bit
+// compute type, packed.  gfx950's scaled conversion does it in one
+// instruction; with scale 1 it is exact (every E4M3 value, subnormals
+// included, is a normal bf16 and f16 value).
+template <int CT>
+__device__ __forceinline__ uint32_t widen2(uint32_t w, bool high) {
+  static_assert(CT == DT_BF16 || CT == DT_F16, "fp8 codes widen to a 16-bit compute type");
+  if constexpr (CT == DT_BF16) {
+    return high ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))
+                : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  } else {
+    return high ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))
+                : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+  }
+}
+
 // Raw elements -> MFMA operand of compute type CT.  fp8 codes widen exactly
 // to bf16/f16 (every E4M3 value is representable in both).
 template <int CT, int SRC>
@@ -74,16 +90,8 @@ __device__ __forceinline__ Frag<CT> to_frag(const Raw<SRC>& r) {
   if constexpr (SRC == DT_FP8) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(r.w[e], false);
-      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(r.w[e], true);
-      if constexpr (CT == DT_BF16) {
-        // exact: an E4M3 value has at most 4 significant bits, so the low half is zero
-        f.w[2 * e] = __builtin_amdgcn_perm(f2u(lo[1]), f2u(lo[0]), 0x07060302u);
-        f.w[2 * e + 1] = __builtin_amdgcn_perm(f2u(hi[1]), f2u(hi[0]), 0x07060302u);
-      } else {
-        f.w[2 * e] = f32_to_f16(lo[0]) | (f32_to_f16(lo[1]) << 16);
-        f.w[2 * e + 1] = f32_to_f16(hi[0]) | (f32_to_f16(hi[1]) << 16);
-      }
+      f.w[2 * e] = widen2<CT>(r.w[e], false);
+      f.w[2 * e + 1] = widen2<CT>(r.w[e], true);
     }
   } else if constexpr (SRC == DT_F32) {
     f.w[0] = r.w[0];
@@ -168,15 +176,8 @@ template <int CT, int SRC>
 __device__ __forceinline__ Frag4<CT> to_frag4(const Raw4<SRC>& r) {
   Frag4<CT> f;
   if constexpr (SRC == DT_FP8) {
-    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(r.w, false);
-    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(r.w, true);
-    if constexpr (CT == DT_BF16) {
-      f.w[0] = __builtin_amdgcn_perm(f2u(lo[1]), f2u(lo[0]), 0x07060302u);
-      f.w[1] = __builtin_amdgcn_perm(f2u(hi[1]), f2u(hi[0]), 0x07060302u);
-    } else {
-      f.w[0] = f32_to_f16(lo[0]) | (f32_to_f16(lo[1]) << 16);
-      f.w[1] = f32_to_f16(hi[0]) | (f32_to_f16(hi[1]) << 16);
-    }
+    f.w[0] = widen2<CT>(r.w, false);
+    f.w[1] = widen2<CT>(r.w, true);
   } else {
     f.w = r.w;
   }
