@@ -118,8 +118,10 @@ __device__ __forceinline__ void chunk_softmax(const float (&s)[16], float& m, f3
 #endif
 constexpr int kChunkAhead = PA_CHUNK_AHEAD;              // tiles in flight (16-bit caches)
 
+// The workgroup's first item is `first` (dealt out in advance, -1 for
+// none); after that it draws item base + k from the counter.
 template <int CT, int KV, int D, int BS>
-__device__ __forceinline__ void chunk_items(const AttnArgs& a) {
+__device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int base) {
   using Lds = ChunkLds<D>;
   constexpr bool DIRECT = (KV != DT_FP8);                // 16-bit cache: global -> LDS directly
   // 16-bit caches: tile t and the kChunkAhead tiles loading behind it; fp8:
@@ -198,9 +200,13 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a) {
   }
 
   while (true) {
-    if (tid == 0) slot = atomicAdd(a.header + (prefix ? 4 : 2), 1);
-    __syncthreads();
-    const int w = uniform(slot);
+    int w = first;
+    if (w < 0) {
+      if (tid == 0) slot = atomicAdd(a.header + (prefix ? 4 : 2), 1);
+      __syncthreads();
+      w = base + uniform(slot);
+    }
+    first = -1;
     if (w >= total) break;
     const int G = a.group;
     int i, h, rblk, part, L, q0, rows, base_pos, tstep, cpart, kstart, pslot;

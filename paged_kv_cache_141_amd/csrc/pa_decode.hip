@@ -10,10 +10,11 @@
 
 namespace pa {
 
-// Waves draw work items from a counter until the list is done.
+// Wave g starts on item g, then draws items from a counter until the list
+// is done.
 template <int CT, int KV, int D, int BS>
 __global__ __launch_bounds__(64, PA_DECODE_WAVES_PER_SIMD) void attn_kernel(AttnArgs a) {
-  decode_items<CT, KV, D, BS, PA_DECODE_PREFETCH>(a, threadIdx.x);
+  decode_items<CT, KV, D, BS, PA_DECODE_PREFETCH>(a, threadIdx.x, blockIdx.x, gridDim.x);
 }
 
 // One wave per resident slot (the persistent grid); each loops over work

@@ -380,16 +380,22 @@ __device__ __forceinline__ void attn_item256(const AttnArgs& a, int i, int tile,
   }
 }
 
-// A wave draws work items from the decode counter; item w covers list entry
-// w / Hkv and kv head w % Hkv.  The wave returns once the counter passes the
+// A wave runs decode work items; item w covers list entry w / Hkv and kv
+// head w % Hkv.  Items 0 .. base-1 are dealt out one per wave in advance
+// (`first`, -1 for none): the first round costs no atomic, so a short step is
+// not held up by a queue of atomics on one counter.  After that the wave
+// draws item base + k from the counter, and returns once it passes the
 // item count.
 template <int CT, int KV, int D, int BS, int PF16>
-__device__ __forceinline__ void decode_items(const AttnArgs& a, int lane) {
+__device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int first, int base) {
   const int64_t total = static_cast<int64_t>(uniform(a.header[1])) * a.num_kv_heads;
+  int w = first;
   while (true) {
-    int w = 0;
-    if (lane == 0) w = atomicAdd(a.header, 1);
-    w = uniform(__shfl(w, 0));
+    if (w < 0) {
+      int k = 0;
+      if (lane == 0) k = atomicAdd(a.header, 1);
+      w = base + uniform(__shfl(k, 0));
+    }
     if (w >= total) break;
     const int e = w / a.num_kv_heads;
     const int h = w - e * a.num_kv_heads;
@@ -397,6 +403,7 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a, int lane) {
     const int tp = uniform(a.items[2 * e + 1]);
     if constexpr (D == 256) attn_item256<CT, KV, BS>(a, i, tp >> 16, tp & 0xFFFF, h, lane);
     else attn_item<CT, KV, D, BS, PF16>(a, i, tp >> 16, tp & 0xFFFF, h, lane);
+    w = -1;
   }
 }
 

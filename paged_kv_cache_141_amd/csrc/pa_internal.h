@@ -21,7 +21,9 @@ constexpr int kTileRows = 16;
 // wave the chip holds (256 CUs x 4 SIMDs, one wave each) -- whole contexts
 // already keep every wave busy and partitions are as long as they go
 // (kPartitionMax); with fewer pairs, steps whose longest context reaches
-// kLongContext use kPartitionLong, shorter ones kPartitionShort.
+// kLongContext use kPartitionLong, shorter ones kPartitionShort.  (Shorter
+// partitions for few, short contexts, to give every wave an item, measured
+// slower: each item pays its start-up latency.)
 // A partition holds at most 128 blocks (two block ids per lane of a wave)
 // and at most kPartitionMax keys (64 steps of 32 keys).
 #ifndef PA_PARTITION_SHORT

@@ -23,8 +23,16 @@ constexpr int kStepDecodePrefetch = 1;
 template <int CT, int KV, int D, int BS>
 __global__ __launch_bounds__(kChunkThreads, 1) void step_kernel(AttnArgs a) {
   const int ndec = uniform(a.header[6]);
-  if (static_cast<int>(blockIdx.x) >= ndec) chunk_items<CT, KV, D, BS>(a);
-  decode_items<CT, KV, D, BS, kStepDecodePrefetch>(a, threadIdx.x & 63);
+  const int g = blockIdx.x;
+  const int wave = uniform(static_cast<int>(threadIdx.x) >> 6);
+  const int nchunk = static_cast<int>(gridDim.x) - ndec;
+  if (g >= ndec) {
+    chunk_items<CT, KV, D, BS>(a, g - ndec, nchunk);
+    decode_items<CT, KV, D, BS, kStepDecodePrefetch>(a, threadIdx.x & 63, -1, ndec * kChunkWaves);
+  } else {
+    decode_items<CT, KV, D, BS, kStepDecodePrefetch>(a, threadIdx.x & 63, g * kChunkWaves + wave,
+                                                     ndec * kChunkWaves);
+  }
 }
 
 int64_t step_groups(int q, int kv, int d, int bs) {

@@ -151,7 +151,7 @@ def test_tiny_decode():
 
 def test_edge_lengths():
     # L = 1, lengths at block/step/partition boundaries, a q_len = 0 sequence,
-    # a chunk that is the whole prompt, and a length past one partition.
+    # a chunk that is the whole prompt, and a length past one 512-key partition.
     lens = [1, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1024, 1025, 7, 300]
     qlens = [1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 0, 300]
     for kv, q, B in (("bf16", "bf16", 16), ("fp8_e4m3", "bf16", 64), ("f32", "f32", 32)):
@@ -164,15 +164,15 @@ def test_edge_lengths():
 
 
 def test_edge_lengths_long_context():
-    # A step whose longest context passes 8192 keys splits decode rows into
-    # 1024-key partitions: lengths at those boundaries, a decode row one
-    # partition long, and a prompt chunk that crosses the chunk kernel's
-    # 4096-key partition boundary.
+    # A step whose longest context passes 8192 keys, with 14 x 16 (sequence,
+    # kv head) pairs, splits decode rows into 1024-key partitions: lengths at
+    # those boundaries, a decode row one partition long, and a prompt chunk
+    # that crosses the chunk kernel's 4096-key partition boundary.
     lens = [1, 1023, 1024, 1025, 2047, 2048, 2049, 4097, 8191, 8192, 8193, 12000, 4200, 9000]
     qlens = [1] * 12 + [200, 1]
     for kv, q, B in (("bf16", "bf16", 16), ("fp8_e4m3", "bf16", 32), ("f32", "f32", 64)):
         sc = 0.05 if kv == "fp8_e4m3" else 1.0
-        w = build("edge_long", 29, lens, qlens, num_q_heads=8, num_kv_heads=2, head_dim=128,
+        w = build("edge_long", 29, lens, qlens, num_q_heads=32, num_kv_heads=16, head_dim=64,
                   block_size=B, kv_dtype=kv, q_dtype=q, k_scale=sc, v_scale=sc)
         say("edge_long", kv, B)
         step = wd.stage(w)
