@@ -11,7 +11,7 @@ namespace pa {
 
 template <int CT, int KV, int D, int BS>
 __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(AttnArgs a) {
-  chunk_items<CT, KV, D, BS>(a, blockIdx.x, gridDim.x);
+  chunk_items<CT, KV, D, BS>(a, blockIdx.x, gridDim.x, a.prefix_pass != 0);
 }
 
 // One workgroup per resident slot, looping over chunk items.

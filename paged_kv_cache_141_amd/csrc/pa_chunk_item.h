@@ -119,9 +119,10 @@ __device__ __forceinline__ void chunk_softmax(const float (&s)[16], float& m, f3
 constexpr int kChunkAhead = PA_CHUNK_AHEAD;              // tiles in flight (16-bit caches)
 
 // The workgroup's first item is `first` (dealt out in advance, -1 for
-// none); after that it draws item base + k from the counter.
+// none); after that it draws item base + k from the counter.  `prefix`: the
+// items are those of the shared-prefix pass instead of the chunk list.
 template <int CT, int KV, int D, int BS>
-__device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int base) {
+__device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int base, bool prefix) {
   using Lds = ChunkLds<D>;
   constexpr bool DIRECT = (KV != DT_FP8);                // 16-bit cache: global -> LDS directly
   // 16-bit caches: tile t and the kChunkAhead tiles loading behind it; fp8:
@@ -145,7 +146,6 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
   const int lg = lane >> 4;
   // the prefix pass has (row block, prefix partition, kv head) items known on
   // the host; otherwise the plan's chunk list times the kv heads
-  const bool prefix = a.prefix_pass != 0;
   const int64_t total = prefix ? a.prefix_items : static_cast<int64_t>(uniform(a.header[3])) * a.num_kv_heads;
   const int64_t tile_bytes = static_cast<int64_t>(BS) * D * EBK;
   const int64_t blk_stride = tile_bytes * a.num_kv_heads;
