@@ -420,6 +420,14 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) lacc[rt] = mma<CT>(lacc[rt], ones, pf[rt][kg]);
         }
+        // pipeline: V fragment j + 4 loads while fragment j multiplies
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int j = 0; j < 2 * NT; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, RT, 0);
+          if (j + 4 < 2 * NT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * RT, 0);
       };
 
       const int ntiles = (kend - kstart + kChunkKeys - 1) / kChunkKeys;

@@ -197,6 +197,19 @@ def test_edge_lengths_many_pairs():
         assert_close(w, gpu_out(step), oracle_out(w), label=f"edge_pairs {kv} B={B}")
 
 
+@pytest.mark.parametrize("chunks", [False, True])
+def test_many_sequences(chunks):
+    # 2,500 sequences: the plan takes sequences 1,024 at a time, and the merge
+    # finds a token's sequence by binary search over all of them; with prompt
+    # chunks among them the step runs the fused launch
+    specs = [(40, 100), (0, 70), (900, 80)] if chunks else []
+    w = random_mixed(59, num_decode=2500 - len(specs), chunk_specs=specs, max_decode_len=1100, num_q_heads=4,
+                     num_kv_heads=2, head_dim=64, block_size=16, kv_dtype="bf16")
+    say("many_sequences", w.num_seqs, "chunks" if chunks else "decode only")
+    step = wd.stage(w)
+    assert_close(w, gpu_out(step), oracle_out(w), label=f"many_sequences chunks={chunks}")
+
+
 # ------------------------------------------------------------------ invariants
 
 def test_placement_permutation_bit_exact():
