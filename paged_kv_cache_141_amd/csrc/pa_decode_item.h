@@ -55,7 +55,7 @@ struct PartTable {
 // eight consecutive keys 8*lg .. 8*lg+7, exactly the K slots the PV product
 // O^T = V^T * P^T needs from P^T, and V^T's rows (dims) are contiguous over
 // keys in the [d][B] tile, so both MFMA operands load straight from memory.
-template <int CT, int KV, int D, int BS, int PF16>
+template <int CT, int KV, int D, int BS, int PF16, bool STREAM>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, int part, int h,
                                           int lane) {
   constexpr int EBQ = Bytes<CT>::v;
@@ -146,20 +146,20 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
       if constexpr (WIDE) {
 #pragma unroll
         for (int s = 0; s < KS; s += 2) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(kp + kdim(s));
+          const u32x4 x = load_once<STREAM>(reinterpret_cast<const u32x4*>(kp + kdim(s)));
           st.k[tau][s].w = u32x2{x[0], x[1]};
           st.k[tau][s + 1].w = u32x2{x[2], x[3]};
         }
       } else {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) st.k[tau][s] = load_raw<KV>(kp + kdim(s) * EBK);
+        for (int s = 0; s < KS; ++s) st.k[tau][s] = load_kv<KV, STREAM>(kp + kdim(s) * EBK);
       }
     }
     const int64_t pb = (BS == 16 && vkey >= 16) ? p1 : p0;
     const int off = (BS == 16) ? (vkey & 15) : inblk + vkey;
     const uint8_t* vp = vc + pb * blk_stride + (static_cast<int64_t>(r) * BS + off) * EBK;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) st.v[n] = load_raw<KV>(vp + static_cast<int64_t>(16 * n) * BS * EBK);
+    for (int n = 0; n < NT; ++n) st.v[n] = load_kv<KV, STREAM>(vp + static_cast<int64_t>(16 * n) * BS * EBK);
   };
 
   auto compute = [&](const Step& st, int k0) {
@@ -386,7 +386,7 @@ __device__ __forceinline__ void attn_item256(const AttnArgs& a, int i, int tile,
 // not held up by a queue of atomics on one counter.  After that the wave
 // draws item base + k from the counter, and returns once it passes the
 // item count.
-template <int CT, int KV, int D, int BS, int PF16>
+template <int CT, int KV, int D, int BS, int PF16, bool STREAM>
 __device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int first, int base) {
   const int64_t total = static_cast<int64_t>(uniform(a.header[1])) * a.num_kv_heads;
   int w = first;
@@ -402,7 +402,7 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int fi
     const int i = uniform(a.items[2 * e]);
     const int tp = uniform(a.items[2 * e + 1]);
     if constexpr (D == 256) attn_item256<CT, KV, BS>(a, i, tp >> 16, tp & 0xFFFF, h, lane);
-    else attn_item<CT, KV, D, BS, PF16>(a, i, tp >> 16, tp & 0xFFFF, h, lane);
+    else attn_item<CT, KV, D, BS, PF16, STREAM>(a, i, tp >> 16, tp & 0xFFFF, h, lane);
     w = -1;
   }
 }

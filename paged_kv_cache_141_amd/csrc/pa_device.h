@@ -52,6 +52,29 @@ template <int SRC> struct Raw { u32x4 w; };
 template <> struct Raw<DT_F32> { u32x4 w[2]; };
 template <> struct Raw<DT_FP8> { u32x2 w; };
 
+// Cache data a decode item reads once: STREAM gives the loads the
+// non-temporal hint (global_load ... nt), which keeps them from displacing
+// what is worth keeping in the caches.
+template <bool STREAM, typename T>
+__device__ __forceinline__ T load_once(const T* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <int SRC, bool STREAM>
+__device__ __forceinline__ Raw<SRC> load_kv(const uint8_t* p) {
+  Raw<SRC> r;
+  if constexpr (SRC == DT_F32) {
+    r.w[0] = load_once<STREAM>(reinterpret_cast<const u32x4*>(p));
+    r.w[1] = load_once<STREAM>(reinterpret_cast<const u32x4*>(p) + 1);
+  } else if constexpr (SRC == DT_FP8) {
+    r.w = load_once<STREAM>(reinterpret_cast<const u32x2*>(p));
+  } else {
+    r.w = load_once<STREAM>(reinterpret_cast<const u32x4*>(p));
+  }
+  return r;
+}
+
 template <int SRC>
 __device__ __forceinline__ Raw<SRC> load_raw(const uint8_t* p) {
   Raw<SRC> r;
