@@ -36,6 +36,9 @@ struct ChunkLds {
   static __device__ __forceinline__ int voff(int dim, int chunk) { return KBYTES + dim * VROW + ((chunk ^ vswz(dim)) << 4); }
 };
 
+#ifndef PA_CHUNK_DMA_HINT
+#define PA_CHUNK_DMA_HINT ""
+#endif
 // 16 bytes from global memory straight into LDS (global_load_lds_dwordx4):
 // lane l's data lands at LDS byte offset lds_base + 16 * l, lds_base being
 // wave-uniform.  Issued as inline assembly so that the compiler does not
@@ -49,7 +52,7 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %1, off" PA_CHUNK_DMA_HINT "\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(g), "s"(lds_base)

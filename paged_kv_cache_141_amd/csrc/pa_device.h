@@ -187,11 +187,11 @@ template <int CT> struct Frag4 { u32x2 w; };
 template <int SRC> struct Raw4 { u32x2 w; };
 template <> struct Raw4<DT_FP8> { uint32_t w; };
 
-template <int SRC>
+template <int SRC, bool STREAM = false>
 __device__ __forceinline__ Raw4<SRC> load_raw4(const uint8_t* p) {
   Raw4<SRC> r;
-  if constexpr (SRC == DT_FP8) r.w = *reinterpret_cast<const uint32_t*>(p);
-  else r.w = *reinterpret_cast<const u32x2*>(p);
+  if constexpr (SRC == DT_FP8) r.w = load_once<STREAM>(reinterpret_cast<const uint32_t*>(p));
+  else r.w = load_once<STREAM>(reinterpret_cast<const u32x2*>(p));
   return r;
 }
 
