@@ -11,14 +11,10 @@
 namespace pa {
 
 // Wave g starts on item g, then draws items from a counter until the list
-// is done.  K/V are read with the non-temporal hint: LLaMA-7B decode 790 ->
-// 737 us, GQA decode 440 -> 430 us, head dim 256 461 -> 454 us.  For fp8 only
-// V takes it (private-prefix decode 373 -> 365 us); fp8 K rows, two 64-byte
-// halves read by two loads, measured 3 % slower with it.  (The fused step
-// kernel's decode items measured slower with it too.)
+// is done.  V is read with the non-temporal hint (STREAM; K without it).
 template <int CT, int KV, int D, int BS>
 __global__ __launch_bounds__(64, PA_DECODE_WAVES_PER_SIMD) void attn_kernel(AttnArgs a) {
-  constexpr bool STREAM = KV == DT_BF16 || KV == DT_F16 || KV == DT_FP8;   // fp8: V only
+  constexpr bool STREAM = true;
   decode_items<CT, KV, D, BS, PA_DECODE_PREFETCH, STREAM>(a, threadIdx.x, blockIdx.x, gridDim.x);
 }
 

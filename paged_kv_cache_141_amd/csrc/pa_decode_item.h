@@ -24,15 +24,6 @@ namespace pa {
 #ifndef PA_DECODE_FP8_WIDE
 #define PA_DECODE_FP8_WIDE 1
 #endif
-#ifndef PA_FP8_STREAM_K
-#define PA_FP8_STREAM_K 0
-#endif
-#ifndef PA_FP8_STREAM_V
-#define PA_FP8_STREAM_V 1
-#endif
-#ifndef PA_STREAM_D256
-#define PA_STREAM_D256 1
-#endif
 #ifndef PA_DECODE_WAVES_PER_SIMD
 #define PA_DECODE_WAVES_PER_SIMD 1
 #endif
@@ -155,21 +146,20 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
       if constexpr (WIDE) {
 #pragma unroll
         for (int s = 0; s < KS; s += 2) {
-          const u32x4 x = load_once<STREAM && PA_FP8_STREAM_K>(reinterpret_cast<const u32x4*>(kp + kdim(s)));
+          const u32x4 x = load_once<false>(reinterpret_cast<const u32x4*>(kp + kdim(s)));
           st.k[tau][s].w = u32x2{x[0], x[1]};
           st.k[tau][s + 1].w = u32x2{x[2], x[3]};
         }
       } else {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) st.k[tau][s] = load_kv<KV, STREAM>(kp + kdim(s) * EBK);
+        for (int s = 0; s < KS; ++s) st.k[tau][s] = load_kv<KV, false>(kp + kdim(s) * EBK);
       }
     }
     const int64_t pb = (BS == 16 && vkey >= 16) ? p1 : p0;
     const int off = (BS == 16) ? (vkey & 15) : inblk + vkey;
     const uint8_t* vp = vc + pb * blk_stride + (static_cast<int64_t>(r) * BS + off) * EBK;
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-      st.v[n] = load_kv<KV, STREAM && (KV != DT_FP8 || PA_FP8_STREAM_V)>(vp + static_cast<int64_t>(16 * n) * BS * EBK);
+    for (int n = 0; n < NT; ++n) st.v[n] = load_kv<KV, STREAM>(vp + static_cast<int64_t>(16 * n) * BS * EBK);
   };
 
   auto compute = [&](const Step& st, int k0) {
@@ -321,7 +311,7 @@ __device__ __forceinline__ void attn_item256(const AttnArgs& a, int i, int tile,
     const int inblk = k0 - j0 * BS;
     const uint8_t* kp = kc + pb * blk_stride + (static_cast<int64_t>(inblk + r) * D + 8 * lg) * EBK;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) st.k[s] = load_kv<KV, STREAM>(kp + 32 * s * EBK);
+    for (int s = 0; s < KS; ++s) st.k[s] = load_kv<KV, false>(kp + 32 * s * EBK);
     const uint8_t* vp = vc + pb * blk_stride + (static_cast<int64_t>(r) * BS + inblk + vkey) * EBK;
 #pragma unroll
     for (int n = 0; n < NT; ++n) st.v[n] = load_raw4<KV, STREAM>(vp + static_cast<int64_t>(16 * n) * BS * EBK);
@@ -411,7 +401,7 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int fi
     const int h = w - e * a.num_kv_heads;
     const int i = uniform(a.items[2 * e]);
     const int tp = uniform(a.items[2 * e + 1]);
-    if constexpr (D == 256) attn_item256<CT, KV, BS, STREAM && PA_STREAM_D256>(a, i, tp >> 16, tp & 0xFFFF, h, lane);
+    if constexpr (D == 256) attn_item256<CT, KV, BS, STREAM>(a, i, tp >> 16, tp & 0xFFFF, h, lane);
     else attn_item<CT, KV, D, BS, PF16, STREAM>(a, i, tp >> 16, tp & 0xFFFF, h, lane);
     w = -1;
   }

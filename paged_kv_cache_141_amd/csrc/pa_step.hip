@@ -28,10 +28,10 @@ __global__ __launch_bounds__(kChunkThreads, 1) void step_kernel(AttnArgs a) {
   const int nchunk = static_cast<int>(gridDim.x) - ndec;
   if (g >= ndec) {
     chunk_items<CT, KV, D, BS>(a, g - ndec, nchunk, false);
-    decode_items<CT, KV, D, BS, kStepDecodePrefetch, false>(a, threadIdx.x & 63, -1, ndec * kChunkWaves);
+    decode_items<CT, KV, D, BS, kStepDecodePrefetch, true>(a, threadIdx.x & 63, -1, ndec * kChunkWaves);
   } else {
-    decode_items<CT, KV, D, BS, kStepDecodePrefetch, false>(a, threadIdx.x & 63, g * kChunkWaves + wave,
-                                                            ndec * kChunkWaves);
+    decode_items<CT, KV, D, BS, kStepDecodePrefetch, true>(a, threadIdx.x & 63, g * kChunkWaves + wave,
+                                                           ndec * kChunkWaves);
   }
 }
 
