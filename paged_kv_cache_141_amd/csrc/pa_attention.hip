@@ -20,7 +20,7 @@ __device__ __forceinline__ int item_size(int L, int ql, int G, int row0, int nro
 
 // One workgroup builds both work lists -- decode: (sequence, 16-row tile,
 // partition of a.partition keys); chunk: (sequence, 256-row block, partition
-// of 4096 keys) -- longest item first: items are bucketed by the number of
+// of 8192 keys) -- longest item first: items are bucketed by the number of
 // key steps they visit (32 keys for decode, 64 for chunks) and the buckets
 // are laid out in descending order, so the persistent kernels, which take
 // items in list order, start the long ones first and end on short ones.
@@ -32,13 +32,15 @@ __device__ __forceinline__ int item_size(int L, int ql, int G, int row0, int nro
 __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
   constexpr int NB0 = kPartitionMax / 32 + 1;            // decode buckets: 0 .. 64 steps
   constexpr int NB1 = kChunkPartition / kChunkKeys + 1;   // chunk buckets: 0 .. 64 tiles
-  __shared__ int hist[2][80];
+  constexpr int NBMAX = (NB0 > NB1 ? NB0 : NB1);
+  static_assert(NBMAX <= 192, "the bucket scan covers 3 x 64 buckets");
+  __shared__ int hist[2][NBMAX];
   __shared__ int scan[1024];                             // inclusive item-count scan of the batch
   __shared__ int sL[1024], sQ[1024], sNP[1024];          // per sequence: L, q_len, partitions (<0: chunk list)
   __shared__ int total[2];
   const int tid = threadIdx.x;
   const int G = a.group;
-  for (int x = tid; x < 2 * 80; x += 1024) hist[x / 80][x % 80] = 0;
+  for (int x = tid; x < 2 * NBMAX; x += 1024) hist[x / NBMAX][x % NBMAX] = 0;
 
   // batch of sequences [base, base + 1024): fill the per-sequence table and the scan
   auto load_batch = [&](int base) {
@@ -128,12 +130,12 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
     __syncthreads();                                     // hist is rewritten below
   }
   // bucket starts, longest bucket first: one wave per list scans the reversed
-  // histogram (at most 80 buckets: lanes take buckets b and b + 64)
+  // histogram (lanes take buckets b, b + 64 and b + 128)
   if (tid < 128) {
     const int list = tid >> 6, lane = tid & 63;
     const int nb = list ? NB1 : NB0;
     int carry = 0;
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < (nb + 63) / 64; ++half) {
       const int r = lane + 64 * half;                    // rank from the longest bucket
       const int b = nb - 1 - r;
       const int c = b >= 0 ? hist[list][b] : 0;
@@ -181,13 +183,19 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
   constexpr int LPH = D / 4;                             // lanes per head
   constexpr int HPB = 4 * (64 / LPH);                    // heads per workgroup
   const int token = blockIdx.x;
-  // sequence of this token: last i with qsl[i] <= token
+  // sequence of this token: last i with qsl[i] <= token.  A 64-way search:
+  // each round every lane probes one candidate and a ballot keeps the last
+  // one at or before the token (qsl is non-decreasing, qsl[lo] <= token).
+  const int lane = threadIdx.x & 63;
   int lo = 0, hi = a.num_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (uniform(a.qsl[mid]) <= token) lo = mid; else hi = mid - 1;
+  while (hi > lo) {
+    const int step = (hi - lo + 64) / 64;
+    const int cand = lo + lane * step;
+    const uint64_t ok = __ballot(cand <= hi && a.qsl[cand] <= token);
+    lo += (63 - __builtin_clzll(ok)) * step;
+    hi = min(hi, lo + step - 1);
   }
-  const int i = lo;
+  const int i = uniform(lo);
   const int q0 = a.qsl[i];
   const int ql = a.qsl[i + 1] - q0;
   const int row_pos = a.seq_lens[i] - ql + (token - q0);
@@ -199,14 +207,34 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
   if (head >= a.num_q_heads) return;
   const int d0 = (threadIdx.x % LPH) * 4;
   const int64_t row = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts;
+  // One pass over the partials, four at a time (all their loads issued
+  // together): the running max moves to the group's max and what was summed
+  // so far is rescaled to it.
   float M = -__builtin_inff();
-  for (int p = 0; p < np; ++p) M = fmaxf(M, a.part_m[row + p]);
   float den = 0.f;
   f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int p = 0; p < np; ++p) {
-    const float wgt = __builtin_amdgcn_exp2f(a.part_m[row + p] - M);
-    den += wgt * a.part_l[row + p];
-    num += wgt * *reinterpret_cast<const f32x4*>(a.part_acc + (row + p) * D + d0);
+  for (int p0 = 0; p0 < np; p0 += 4) {
+    float mv[4], lv[4];
+    f32x4 av[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool in = p0 + j < np;
+      mv[j] = in ? a.part_m[row + p0 + j] : -__builtin_inff();
+      lv[j] = in ? a.part_l[row + p0 + j] : 0.f;
+      av[j] = in ? *reinterpret_cast<const f32x4*>(a.part_acc + (row + p0 + j) * D + d0)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const float Mn = fmaxf(fmaxf(M, fmaxf(mv[0], mv[1])), fmaxf(mv[2], mv[3]));
+    const float r = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+    den *= r;
+    num *= r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float wgt = mv[j] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mv[j] - Mn);
+      den += wgt * lv[j];
+      num += wgt * av[j];
+    }
+    M = Mn;
   }
   const float inv = 1.f / den;
   uint8_t* op = static_cast<uint8_t*>(a.out) +

@@ -105,7 +105,7 @@ __device__ __forceinline__ void chunk_softmax(const float (&s)[16], float& m, f3
 
 // One workgroup (8 waves, two per SIMD) per work item: sequence i, kv head h,
 // rows [256*rb, 256*rb + 256) of the sequence's (token, head-in-group) rows,
-// keys of context partition `part` (4096 keys).  Wave w owns rows
+// keys of context partition `part` (8192 keys).  Wave w owns rows
 // 32w..32w+31 as two 16-row tiles.  Each 64-key tile is gathered through the
 // block table by all 512 threads with 16-byte loads -- straight into LDS for
 // 16-bit caches (global_load_lds), through registers for fp8, which is

@@ -63,7 +63,7 @@ constexpr int kChunkRows = 32 * kChunkWaves;   // two 16-row tiles per wave
 constexpr int chunk_rows_for(int64_t head_dim) { return head_dim == 256 ? kChunkRows / 2 : kChunkRows; }
 constexpr int kChunkKeys = 64;
 #ifndef PA_CHUNK_PARTITION
-#define PA_CHUNK_PARTITION 4096
+#define PA_CHUNK_PARTITION 8192
 #endif
 constexpr int kChunkPartition = PA_CHUNK_PARTITION;
 
@@ -123,7 +123,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // sized to fill one round of kPrefixItems workgroups (one per CU of the
 // GPU) without spilling a few into a second round: as many partitions as
 // fit that round, each at least 256 keys, rounded up to whole 64-key tiles
-// and at most 4096 keys.
+// and at most 8192 keys.
 #ifndef PA_PREFIX_ITEMS
 #define PA_PREFIX_ITEMS 256
 #endif

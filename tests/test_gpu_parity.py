@@ -167,8 +167,8 @@ def test_edge_lengths_long_context():
     # A step whose longest context passes 8192 keys, with 14 x 16 (sequence,
     # kv head) pairs, splits decode rows into 1024-key partitions: lengths at
     # those boundaries, a decode row one partition long, and a prompt chunk
-    # that crosses the chunk kernel's 4096-key partition boundary.
-    lens = [1, 1023, 1024, 1025, 2047, 2048, 2049, 4097, 8191, 8192, 8193, 12000, 4200, 9000]
+    # that crosses the chunk kernel's 8192-key partition boundary.
+    lens = [1, 1023, 1024, 1025, 2047, 2048, 2049, 4097, 8191, 8192, 8193, 12000, 8300, 9000]
     qlens = [1] * 12 + [200, 1]
     for kv, q, B in (("bf16", "bf16", 16), ("fp8_e4m3", "bf16", 32), ("f32", "f32", 64)):
         sc = 0.05 if kv == "fp8_e4m3" else 1.0
