@@ -31,6 +31,14 @@ __device__ __forceinline__ void load8_src(const uint8_t* p, float (&x)[8]) {
   }
 }
 
+// One source element -> fp32 (exact widening).
+template <int SRC>
+__device__ __forceinline__ float load1_src(const uint8_t* p) {
+  if constexpr (SRC == DT_F32) return *reinterpret_cast<const float*>(p);
+  else if constexpr (SRC == DT_BF16) return bf16_to_f32(*reinterpret_cast<const uint16_t*>(p));
+  else return f16_to_f32(*reinterpret_cast<const uint16_t*>(p));
+}
+
 template <int KV>
 __device__ __forceinline__ uint32_t encode1(float x, float scale) {
   if constexpr (KV == DT_F32) return f2u(x);
@@ -39,9 +47,14 @@ __device__ __forceinline__ uint32_t encode1(float x, float scale) {
   else return f32_to_e4m3(x, scale);
 }
 
-// One thread = 8 consecutive elements (one 16-byte source chunk for 16-bit
-// sources) of one (token, kv head) row.  K lands as one contiguous run of
-// 8 elements; V goes to 8 rows of the transposed tile at the token's offset.
+// One thread = 8 elements of one (token, kv head) row, C = d / 8 threads per
+// row.  K: thread c takes the 8 consecutive elements 8c .. 8c+7 (one 16-byte
+// chunk for 16-bit sources) and lands them as one contiguous run.  V: the
+// row goes down one column of the transposed [d][B] tile, one element per
+// dim row, B elements apart; thread c takes dims c, C + c, 2C + c, ..., so
+// that each store instruction writes C consecutive dims of a row -- stores
+// that fall in one cache line (4 dims of 16-bit bf16 at B = 16) merge into
+// one request instead of four.
 template <int SRC, int KV>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a) {
   const int chunks = a.head_dim / 8;
@@ -61,7 +74,12 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a
   const int64_t src_off = ((static_cast<int64_t>(t) * a.num_kv_heads + h) * a.head_dim + 8 * c) * EBS;
   float xk[8], xv[8];
   load8_src<SRC>(static_cast<const uint8_t*>(a.key) + src_off, xk);
-  load8_src<SRC>(static_cast<const uint8_t*>(a.value) + src_off, xv);
+  {
+    const uint8_t* vsrc = static_cast<const uint8_t*>(a.value) +
+                          ((static_cast<int64_t>(t) * a.num_kv_heads + h) * a.head_dim + c) * EBS;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xv[e] = load1_src<SRC>(vsrc + static_cast<int64_t>(e) * chunks * EBS);
+  }
 
   const int64_t tile = (blk * a.num_kv_heads + h) * static_cast<int64_t>(a.block_size) * a.head_dim;
   uint8_t* kdst = static_cast<uint8_t*>(a.k_cache) + (tile + static_cast<int64_t>(off) * a.head_dim + 8 * c) * EBK;
@@ -88,10 +106,11 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a
     *reinterpret_cast<u32x2*>(kdst) = w;
   }
 
-  // V tile is [d][B]: element (dim, off) at dim * B + off
+  // V tile is [d][B]: element (dim, off) at dim * B + off; this thread's dims
+  // are c + e * chunks
   uint8_t* vdst = static_cast<uint8_t*>(a.v_cache) +
-                  (tile + static_cast<int64_t>(8 * c) * a.block_size + off) * EBK;
-  const int64_t vstride = static_cast<int64_t>(a.block_size) * EBK;
+                  (tile + static_cast<int64_t>(c) * a.block_size + off) * EBK;
+  const int64_t vstride = static_cast<int64_t>(chunks) * a.block_size * EBK;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const uint32_t code = encode1<KV>(xv[e], a.v_scale);
