@@ -55,7 +55,10 @@ inline int decode_partition(int64_t max_seq_len, int64_t num_seqs, int64_t num_k
 // tiles, context partitions of kChunkPartition keys.  Fewer rows (decode,
 // short speculative runs) stay on the 16-row decode kernel.
 constexpr int kChunkMinRows = 65;
-constexpr int kChunkWaves = 8;                 // waves per chunk workgroup (2 per SIMD)
+#ifndef PA_CHUNK_WAVES
+#define PA_CHUNK_WAVES 8
+#endif
+constexpr int kChunkWaves = PA_CHUNK_WAVES;    // waves per chunk workgroup (2 per SIMD)
 constexpr int kChunkThreads = 64 * kChunkWaves;
 constexpr int kChunkRows = 32 * kChunkWaves;   // two 16-row tiles per wave
 // Rows of one chunk work item: 256 (two 16-row tiles per wave), or 128 for

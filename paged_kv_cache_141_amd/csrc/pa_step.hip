@@ -21,7 +21,7 @@ namespace pa {
 constexpr int kStepDecodePrefetch = 1;
 
 template <int CT, int KV, int D, int BS>
-__global__ __launch_bounds__(kChunkThreads, 1) void step_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kChunkThreads, 2) void step_kernel(AttnArgs a) {
   const int ndec = uniform(a.header[6]);
   const int g = blockIdx.x;
   const int wave = uniform(static_cast<int>(threadIdx.x) >> 6);
