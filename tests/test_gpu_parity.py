@@ -210,6 +210,20 @@ def test_many_sequences(chunks):
     assert_close(w, gpu_out(step), oracle_out(w), label=f"many_sequences chunks={chunks}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_very_long_context(kv):
+    # contexts of 128k tokens and more: 129 decode partitions of 1024 keys for one row, a
+    # prompt chunk 100,000 keys in (13 chunk partitions), partials merged
+    sc = 0.05 if kv == "fp8_e4m3" else 1.0
+    lens = [131077, 100100, 40000, 9]
+    qlens = [1, 100, 1, 1]
+    w = build("very_long", 61, lens, qlens, num_q_heads=4, num_kv_heads=1, head_dim=64, block_size=16,
+              kv_dtype=kv, q_dtype="bf16", k_scale=sc, v_scale=sc)
+    say("very_long", kv, w.max_seq_len)
+    step = wd.stage(w)
+    assert_close(w, gpu_out(step), oracle_out(w), label=f"very_long {kv}")
+
+
 # ------------------------------------------------------------------ invariants
 
 def test_placement_permutation_bit_exact():
