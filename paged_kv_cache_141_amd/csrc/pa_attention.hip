@@ -38,6 +38,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
   __shared__ int scan[1024];                             // inclusive item-count scan of the batch
   __shared__ int sL[1024], sQ[1024], sNP[1024];          // per sequence: L, q_len, partitions (<0: chunk list)
   __shared__ int total[2];
+  __shared__ int wtot[16];                               // per-wave totals of the batch scan
   const int tid = threadIdx.x;
   const int G = a.group;
   for (int x = tid; x < 2 * NBMAX; x += 1024) hist[x / NBMAX][x % NBMAX] = 0;
@@ -62,18 +63,24 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
         }
       }
     }
+    // inclusive scan of n: within each wave by shuffles, then the wave totals
+    const int lane = tid & 63, wv = tid >> 6;
+    int v = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(v, o);
+      if (lane >= o) v += u;
+    }
     __syncthreads();                                     // the previous batch is done with the table
     sL[tid] = L;
     sQ[tid] = ql;
     sNP[tid] = np;
-    scan[tid] = n;
+    if (lane == 63) wtot[wv] = v;
     __syncthreads();
-    for (int ofs = 1; ofs < 1024; ofs <<= 1) {           // inclusive Hillis-Steele scan
-      const int v = tid >= ofs ? scan[tid - ofs] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
+    int before = 0;
+    for (int x = 0; x < wv; ++x) before += wtot[x];
+    scan[tid] = v + before;
+    __syncthreads();
   };
   // item k of the batch: its sequence (batch-relative), list, tile, partition and bucket
   auto item = [&](int k, int& j, int& list, int& t, int& p, int& bucket) {
