@@ -214,29 +214,32 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
   if (head >= a.num_q_heads) return;
   const int d0 = (threadIdx.x % LPH) * 4;
   const int64_t row = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts;
-  // One pass over the partials, four at a time (all their loads issued
+  // One pass over the partials, eight at a time (all their loads issued
   // together): the running max moves to the group's max and what was summed
   // so far is rescaled to it.
+  constexpr int PG = 8;
   float M = -__builtin_inff();
   float den = 0.f;
   f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int p0 = 0; p0 < np; p0 += 4) {
-    float mv[4], lv[4];
-    f32x4 av[4];
+  for (int p0 = 0; p0 < np; p0 += PG) {
+    float mv[PG], lv[PG];
+    f32x4 av[PG];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < PG; ++j) {
       const bool in = p0 + j < np;
       mv[j] = in ? a.part_m[row + p0 + j] : -__builtin_inff();
       lv[j] = in ? a.part_l[row + p0 + j] : 0.f;
       av[j] = in ? *reinterpret_cast<const f32x4*>(a.part_acc + (row + p0 + j) * D + d0)
                  : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const float Mn = fmaxf(fmaxf(M, fmaxf(mv[0], mv[1])), fmaxf(mv[2], mv[3]));
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < PG; ++j) Mn = fmaxf(Mn, mv[j]);
     const float r = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
     den *= r;
     num *= r;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < PG; ++j) {
       const float wgt = mv[j] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mv[j] - Mn);
       den += wgt * lv[j];
       num += wgt * av[j];
