@@ -39,11 +39,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="llama7b_decode",
-                    help="tiny_decode | llama7b_decode | gqa_long_decode | "
-                         "mixed_chunked_prefill | fp8_shared_prefix")
-    ap.add_argument("--block-size", type=int, default=None, help="tokens per cache block (16, 32, 64)")
-    ap.add_argument("--kv-dtype", default=None, help="cache dtype override: bf16 | f16 | fp8_e4m3 (scale 2^-5)")
-    ap.add_argument("--head-dim", type=int, default=None,
+                    choices=["tiny_decode", "llama7b_decode", "gqa_long_decode", "mixed_chunked_prefill",
+                             "fp8_shared_prefix"])
+    ap.add_argument("--block-size", type=int, default=None, choices=[16, 32, 64], help="tokens per cache block")
+    ap.add_argument("--kv-dtype", default=None, choices=["bf16", "f16", "fp8_e4m3"],
+                    help="cache dtype override (fp8_e4m3: per-tensor scale 2^-5)")
+    ap.add_argument("--head-dim", type=int, default=None, choices=[64, 128, 256],
                     help="for gqa_long_decode / mixed_chunked_prefill: 256 keeps the KV bytes per token "
                          "with half the heads (16q/4kv)")
     ap.add_argument("--placement", default=None, help="shuffled | identity | private")

@@ -10,7 +10,7 @@
 namespace pa {
 
 template <int CT, int KV, int D, int BS>
-__global__ __launch_bounds__(kChunkThreads, 2) void chunk_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kChunkThreads, kChunkWavesPerSimd) void chunk_kernel(AttnArgs a) {
   chunk_items<CT, KV, D, BS>(a, blockIdx.x, gridDim.x, a.prefix_pass != 0);
 }
 

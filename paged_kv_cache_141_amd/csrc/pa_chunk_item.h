@@ -139,7 +139,7 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
   constexpr int EBK = Bytes<KV>::v;
   constexpr int KS = D / 32;
   constexpr int NT = D / 16;
-  constexpr int RT = D == 256 ? 1 : 2;                   // row tiles per wave
+  constexpr int RT = D == 256 ? kChunkRowTiles / 2 : kChunkRowTiles;   // row tiles per wave
   constexpr int ROWS = kChunkWaves * 16 * RT;            // rows of one item (chunk_rows_for(D))
 
   const int tid = threadIdx.x;
@@ -159,6 +159,7 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
   // 16-byte chunk a lane fetches, its block relative to the tile's first
   // block and its offset inside that block are the same for every tile.
   constexpr int NI = Lds::BUF / 1024 / kChunkWaves;       // loads per wave per tile
+  static_assert(Lds::BUF % (1024 * kChunkWaves) == 0, "a tile splits evenly over the waves");
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
   // Per load: the block relative to the tile's first block, and the byte
   // offset inside the block.

@@ -24,6 +24,12 @@ namespace pa {
 #ifndef PA_DECODE_FP8_WIDE
 #define PA_DECODE_FP8_WIDE 1
 #endif
+#ifndef PA_DECODE_PAIR_V
+#define PA_DECODE_PAIR_V 1
+#endif
+#ifndef PA_DECODE_NT_B64
+#define PA_DECODE_NT_B64 0
+#endif
 #ifndef PA_DECODE_WAVES_PER_SIMD
 #define PA_DECODE_WAVES_PER_SIMD 1
 #endif
@@ -130,8 +136,9 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
     Raw<KV> v[NT];
   };
   // Issue the loads of the 32-key step starting at key k0 (block-table
-  // gather: physical block(s) from the table register, then 16-byte reads).
-  auto issue = [&](Step& st, int k0) {
+  // gather: physical block(s) from the table register, then 16-byte reads):
+  // K, then V.
+  auto issue_k = [&](Step& st, int k0) {
     const int j0 = k0 / BS;
     const int64_t p0 = btv[j0 - jbase];
     int64_t p1 = p0;
@@ -155,7 +162,12 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
         for (int s = 0; s < KS; ++s) st.k[tau][s] = load_kv<KV, false>(kp + kdim(s) * EBK);
       }
     }
-    const int64_t pb = (BS == 16 && vkey >= 16) ? p1 : p0;
+  };
+  auto issue_v = [&](Step& st, int k0) {
+    const int j0 = k0 / BS;
+    const int64_t p0 = btv[j0 - jbase];
+    const int64_t pb = (BS == 16 && vkey >= 16) ? btv[min(j0 + 1, nblk - 1) - jbase] : p0;
+    const int inblk = k0 - j0 * BS;
     const int off = (BS == 16) ? (vkey & 15) : inblk + vkey;
     const uint8_t* vp = vc + pb * blk_stride + (static_cast<int64_t>(r) * BS + off) * EBK;
 #pragma unroll
@@ -198,18 +210,37 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   // Software pipeline: the loads of step s + PF are in flight while step s
   // computes (PF16 steps for 16-bit caches).
   constexpr int PF = (KV == DT_FP8) ? PA_DECODE_PREFETCH_FP8 : (KV == DT_F32 ? 0 : PF16);
-  constexpr int NB = PF + 1;
+  // 64-key blocks: a step reads half of each 128-byte V^T row, so the V loads
+  // of a block's two steps go out together (with the first step's K), and
+  // whole rows are read at once.  That takes one more step buffer: the second
+  // step's V lands a step earlier than its K.  (kstart is a multiple of 64,
+  // so even steps start blocks.)
+  constexpr bool PAIRV = BS == 64 && PF >= 2 && PA_DECODE_PAIR_V;
+  constexpr int NB = PF + 1 + (PAIRV ? 1 : 0);
+  static_assert(!PAIRV || NB % 2 == 0, "step parity must be static in the ring");
   Step buf[NB];
   const int nsteps = (kend - kstart + 31) / 32;
+  // issue step s into buf[b]
+  auto issue = [&](int b, int s) {
+    issue_k(buf[b], kstart + 32 * s);
+    if constexpr (PAIRV) {
+      if ((b & 1) == 0) {
+        issue_v(buf[b], kstart + 32 * s);
+        if (s + 1 < nsteps) issue_v(buf[(b + 1) % NB], kstart + 32 * (s + 1));
+      }
+    } else {
+      issue_v(buf[b], kstart + 32 * s);
+    }
+  };
 #pragma unroll
   for (int s = 0; s < PF; ++s)
-    if (s < nsteps) issue(buf[s], kstart + 32 * s);
+    if (s < nsteps) issue(s, s);
   for (int s0 = 0; s0 < nsteps; s0 += NB) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int s = s0 + b;
       if (s >= nsteps) break;
-      if (s + PF < nsteps) issue(buf[(b + PF) % NB], kstart + 32 * (s + PF));
+      if (s + PF < nsteps) issue((b + PF) % NB, s + PF);
       compute(buf[b], kstart + 32 * s);
     }
   }
@@ -406,7 +437,7 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int fi
     // half to the next step measured 1.5x slower with it (B 64: 1,080 against
     // 733 us for the LLaMA-7B decode kernel at B 16)
     if constexpr (D == 256) attn_item256<CT, KV, BS, STREAM && BS <= 16>(a, i, tp >> 16, tp & 0xFFFF, h, lane);
-    else attn_item<CT, KV, D, BS, PF16, STREAM && BS <= 32>(a, i, tp >> 16, tp & 0xFFFF, h, lane);
+    else attn_item<CT, KV, D, BS, PF16, STREAM && (BS <= 32 || PA_DECODE_NT_B64)>(a, i, tp >> 16, tp & 0xFFFF, h, lane);
     w = -1;
   }
 }

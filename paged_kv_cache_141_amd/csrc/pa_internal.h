@@ -58,11 +58,19 @@ constexpr int kChunkMinRows = 65;
 #ifndef PA_CHUNK_WAVES
 #define PA_CHUNK_WAVES 8
 #endif
-constexpr int kChunkWaves = PA_CHUNK_WAVES;    // waves per chunk workgroup (2 per SIMD)
+#ifndef PA_CHUNK_ROW_TILES
+#define PA_CHUNK_ROW_TILES 2
+#endif
+#ifndef PA_CHUNK_WAVES_PER_SIMD
+#define PA_CHUNK_WAVES_PER_SIMD 2
+#endif
+constexpr int kChunkWaves = PA_CHUNK_WAVES;    // waves per chunk workgroup
 constexpr int kChunkThreads = 64 * kChunkWaves;
-constexpr int kChunkRows = 32 * kChunkWaves;   // two 16-row tiles per wave
-// Rows of one chunk work item: 256 (two 16-row tiles per wave), or 128 for
-// head dim 256, whose accumulators leave room for one tile per wave.
+constexpr int kChunkRowTiles = PA_CHUNK_ROW_TILES;          // 16-row tiles per wave (head dim <= 128)
+constexpr int kChunkWavesPerSimd = PA_CHUNK_WAVES_PER_SIMD; // register budget: 512 / this per wave
+constexpr int kChunkRows = 16 * kChunkRowTiles * kChunkWaves;
+// Rows of one chunk work item: 256 (two 16-row tiles per wave), or half that
+// for head dim 256, whose accumulators leave room for half the row tiles.
 constexpr int chunk_rows_for(int64_t head_dim) { return head_dim == 256 ? kChunkRows / 2 : kChunkRows; }
 constexpr int kChunkKeys = 64;
 #ifndef PA_CHUNK_PARTITION

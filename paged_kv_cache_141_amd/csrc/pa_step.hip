@@ -18,10 +18,13 @@ namespace pa {
 // Decode waves here share their SIMD with a second wave (8 waves per CU), so
 // 16-bit K/V keep one step in flight instead of two: the register budget of
 // a wave is half the SIMD's.
-constexpr int kStepDecodePrefetch = 1;
+#ifndef PA_STEP_DECODE_PREFETCH
+#define PA_STEP_DECODE_PREFETCH 1
+#endif
+constexpr int kStepDecodePrefetch = PA_STEP_DECODE_PREFETCH;
 
 template <int CT, int KV, int D, int BS>
-__global__ __launch_bounds__(kChunkThreads, 2) void step_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kChunkThreads, kChunkWavesPerSimd) void step_kernel(AttnArgs a) {
   const int ndec = uniform(a.header[6]);
   const int g = blockIdx.x;
   const int wave = uniform(static_cast<int>(threadIdx.x) >> 6);
