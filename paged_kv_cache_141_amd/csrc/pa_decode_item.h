@@ -270,147 +270,6 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   }
 }
 
-// The same work item for head dim 256, in steps of 16 keys: the K rows of a
-// step are its keys in order (lane r reads key r), so lane (r, g) ends up with
-// row r's scores for keys 4g .. 4g+3 -- the K slots of the K=16 MFMA that
-// computes O^T += V^T P^T, whose V^T operand is 4 consecutive keys of one dim.
-// A step holds 16 KiB of 16-bit K/V; one step is in flight while the other
-// computes (two for fp8, half the bytes), so the accumulators (64 registers)
-// and the query (32) fit beside the prefetch.
-template <int CT, int KV, int BS, bool STREAM>
-__device__ __forceinline__ void attn_item256(const AttnArgs& a, int i, int tile, int part, int h, int lane) {
-  constexpr int D = 256;
-  constexpr int EBQ = Bytes<CT>::v;
-  constexpr int EBK = Bytes<KV>::v;
-  constexpr int KS = D / 32;
-  constexpr int NT = D / 16;
-  const int r = lane & 15;
-  const int lg = lane >> 4;
-
-  const int L = a.seq_lens[i];
-  const int q0 = a.qsl[i];
-  const int ql = a.qsl[i + 1] - q0;
-  const int G = a.group;
-  const int rows = ql * G;
-  const int row0 = tile * kTileRows;
-  const int R = row0 + r;
-  const bool valid = R < rows;
-  const int t = R / G;
-  const int token = q0 + t;
-  const int head = h * G + (R - t * G);
-  const int base_pos = L - ql;
-  const int row_pos = valid ? base_pos + t : -1;
-  const int max_pos = base_pos + (min(rows, row0 + kTileRows) - 1) / G;
-  const int min_pos = base_pos + row0 / G;
-  const int kstart = a.prefix_len + part * a.partition;
-  const int kend = min(min(L, kstart + a.partition), max_pos + 1);
-  if (kstart >= kend) return;
-
-  Frag<CT> qf[KS];
-  {
-    const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
-                        ((static_cast<int64_t>(token) * a.num_q_heads + head) * D + 8 * lg) * EBQ;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qf[s] = valid ? load_frag<CT, CT>(qp + 32 * s * EBQ) : frag_zero<CT>();
-  }
-  const int nblk = (L + BS - 1) / BS;
-  const int64_t tile_bytes = static_cast<int64_t>(BS) * D * EBK;
-  const int64_t blk_stride = tile_bytes * a.num_kv_heads;
-  const uint8_t* kc = static_cast<const uint8_t*>(a.k_cache) + h * tile_bytes;
-  const uint8_t* vc = static_cast<const uint8_t*>(a.v_cache) + h * tile_bytes;
-  const int jbase = kstart / BS;
-  const int nbt = min(nblk - jbase, a.partition / BS);
-  PartTable btv;
-  btv.load(a.block_tables + static_cast<int64_t>(i) * a.max_blocks_per_seq + jbase, nbt, lane);
-  const int vkey = 4 * lg;                          // first of the lane's 4 keys for V / P
-
-  float m = -__builtin_inff();
-  float lsum = 0.f;
-  const float slack = a.rescale_slack;
-  f32x4 acc[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  struct Step {
-    Raw<KV> k[KS];
-    Raw4<KV> v[NT];
-  };
-  // a 16-key step lies inside one block (B is 16, 32 or 64)
-  auto issue = [&](Step& st, int k0) {
-    const int j0 = k0 / BS;
-    const int64_t pb = btv[j0 - jbase];
-    const int inblk = k0 - j0 * BS;
-    const uint8_t* kp = kc + pb * blk_stride + (static_cast<int64_t>(inblk + r) * D + 8 * lg) * EBK;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) st.k[s] = load_kv<KV, false>(kp + 32 * s * EBK);
-    const uint8_t* vp = vc + pb * blk_stride + (static_cast<int64_t>(r) * BS + inblk + vkey) * EBK;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) st.v[n] = load_raw4<KV, STREAM>(vp + static_cast<int64_t>(16 * n) * BS * EBK);
-  };
-  auto compute = [&](const Step& st, int k0) {
-    f32x4 sf = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) sf = mma<CT>(sf, to_frag<CT, KV>(st.k[s]), qf[s]);
-    float sc[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sc[e] = sf[e];
-    if (k0 + 15 > min_pos) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sc[e] = (k0 + vkey + e <= row_pos) ? sc[e] : -__builtin_inff();
-    }
-    float p[4];
-    softmax_update<4, NT>(sc, m, lsum, acc, a.score_scale, slack, p);
-    const Frag4<CT> pf = pack_p4<CT>(p);
-    const bool tail = k0 + 16 > L;
-    const int keep = L - (k0 + vkey);
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      Frag4<CT> vf = to_frag4<CT, KV>(st.v[n]);
-      if (tail) frag4_keep_first<CT>(vf, keep);
-      acc[n] = mma16<CT>(acc[n], vf, pf);
-    }
-  };
-
-  constexpr int PF = (KV == DT_FP8) ? 2 : 1;
-  constexpr int NB = PF + 1;
-  Step buf[NB];
-  const int nsteps = (kend - kstart + 15) / 16;
-#pragma unroll
-  for (int s = 0; s < PF; ++s)
-    if (s < nsteps) issue(buf[s], kstart + 16 * s);
-  for (int s0 = 0; s0 < nsteps; s0 += NB) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int s = s0 + b;
-      if (s >= nsteps) break;
-      if (s + PF < nsteps) issue(buf[(b + PF) % NB], kstart + 16 * (s + PF));
-      compute(buf[b], kstart + 16 * s);
-    }
-  }
-
-  float ltot = lsum + __shfl_xor(lsum, 16);
-  ltot += __shfl_xor(ltot, 32);
-  if (!valid || row_pos < kstart) return;
-  const int nparts_row = (row_pos - a.prefix_len) / a.partition + 1;
-  if (nparts_row == 1 && a.prefix_len == 0) {
-    const float inv = a.v_scale / ltot;
-    uint8_t* op = static_cast<uint8_t*>(a.out) +
-                  ((static_cast<int64_t>(token) * a.num_q_heads + head) * D + 4 * lg) * EBQ;
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-      store4<CT>(op + 16 * n * EBQ, acc[n][0] * inv, acc[n][1] * inv, acc[n][2] * inv, acc[n][3] * inv);
-  } else {
-    const int64_t rowp = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts + a.prefix_parts + part;
-    if (lg == 0) {
-      a.part_m[rowp] = max_log2(m, a.score_scale);
-      a.part_l[rowp] = ltot;
-    }
-    float* pa = a.part_acc + rowp * D + 4 * lg;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(pa + 16 * n) = acc[n] * a.v_scale;
-  }
-}
-
 // A wave runs decode work items; item w covers list entry w / Hkv and kv
 // head w % Hkv.  Items 0 .. base-1 are dealt out one per wave in advance
 // (`first`, -1 for none): the first round costs no atomic, so a short step is
@@ -428,6 +287,9 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int fi
       w = base + uniform(__shfl(k, 0));
     }
     if (w >= total) break;
+    // head dim 256: a 32-key step is 32 KiB of 16-bit K/V, so one step is in
+    // flight while the other computes
+    constexpr int PFD = D == 256 ? 1 : PF16;
     const int e = w / a.num_kv_heads;
     const int h = w - e * a.num_kv_heads;
     const int i = uniform(a.items[2 * e]);
@@ -436,8 +298,7 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int fi
     // step's keys): a step that reads half of each row and leaves the other
     // half to the next step measured 1.5x slower with it (B 64: 1,080 against
     // 733 us for the LLaMA-7B decode kernel at B 16)
-    if constexpr (D == 256) attn_item256<CT, KV, BS, STREAM && BS <= 16>(a, i, tp >> 16, tp & 0xFFFF, h, lane);
-    else attn_item<CT, KV, D, BS, PF16, STREAM && (BS <= 32 || PA_DECODE_NT_B64)>(a, i, tp >> 16, tp & 0xFFFF, h, lane);
+    attn_item<CT, KV, D, BS, PFD, STREAM && (BS <= 32 || PA_DECODE_NT_B64)>(a, i, tp >> 16, tp & 0xFFFF, h, lane);
     w = -1;
   }
 }

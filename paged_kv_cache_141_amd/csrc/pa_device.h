@@ -182,64 +182,6 @@ __device__ __forceinline__ Frag<CT> pack_p(const float (&p)[8]) {
   return f;
 }
 
-// ---- four-element operands (the K=16 MFMA of the 16-key decode step)
-
-// Four operand elements of one lane (16-bit compute types only).
-template <int CT> struct Frag4 { u32x2 w; };
-// Four consecutive storage elements as loaded: 8 bytes (16-bit) or 4 (fp8).
-template <int SRC> struct Raw4 { u32x2 w; };
-template <> struct Raw4<DT_FP8> { uint32_t w; };
-
-template <int SRC, bool STREAM = false>
-__device__ __forceinline__ Raw4<SRC> load_raw4(const uint8_t* p) {
-  Raw4<SRC> r;
-  if constexpr (SRC == DT_FP8) r.w = load_once<STREAM>(reinterpret_cast<const uint32_t*>(p));
-  else r.w = load_once<STREAM>(reinterpret_cast<const u32x2*>(p));
-  return r;
-}
-
-template <int CT, int SRC>
-__device__ __forceinline__ Frag4<CT> to_frag4(const Raw4<SRC>& r) {
-  Frag4<CT> f;
-  if constexpr (SRC == DT_FP8) {
-    f.w[0] = widen2<CT>(r.w, false);
-    f.w[1] = widen2<CT>(r.w, true);
-  } else {
-    f.w = r.w;
-  }
-  return f;
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4v __attribute__((ext_vector_type(4)));
-
-// acc += A(16 x 16) * B(16 x 16), the K=16 MFMA: lane (r, g) holds K slots
-// 4g .. 4g+3 of row r of A and of column r of B.
-template <int CT>
-__device__ __forceinline__ f32x4 mma16(f32x4 acc, const Frag4<CT>& a, const Frag4<CT>& b) {
-  if constexpr (CT == DT_BF16)
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a.w), __builtin_bit_cast(s16x4, b.w),
-                                                     acc, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4v, a.w), __builtin_bit_cast(f16x4v, b.w),
-                                                 acc, 0, 0, 0);
-}
-
-template <int CT>
-__device__ __forceinline__ Frag4<CT> pack_p4(const float (&p)[4]) {
-  Frag4<CT> f;
-  f.w[0] = cvt2<CT>(p[0], p[1]);
-  f.w[1] = cvt2<CT>(p[2], p[3]);
-  return f;
-}
-
-template <int CT>
-__device__ __forceinline__ void frag4_keep_first(Frag4<CT>& f, int n) {
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-    f.w[q] &= (2 * q < n ? 0x0000FFFFu : 0u) | (2 * q + 1 < n ? 0xFFFF0000u : 0u);
-}
-
 template <int OT>
 __device__ __forceinline__ void store4(uint8_t* p, float a, float b, float c, float d) {
   if constexpr (OT == DT_F32)

@@ -124,9 +124,11 @@ SMALL = [
     ("fp8_e4m3", "bf16", 16, 128, 32, 8, [(0, 40)]),
     ("fp8_e4m3", "bf16", 32, 128, 16, 1, [(9, 9)]),           # G = 16
     ("fp8_e4m3", "f16", 64, 64, 8, 4, [(0, 3), (200, 20)]),
-    ("bf16", "bf16", 16, 256, 16, 4, [(0, 40), (90, 30)]),       # head dim 256: 16-key decode steps,
+    ("bf16", "bf16", 16, 256, 16, 4, [(0, 40), (90, 30)]),       # head dim 256: one step in flight,
     ("f16", "f16", 32, 256, 8, 8, [(3, 70)]),                   # 128-row chunk items
     ("fp8_e4m3", "bf16", 64, 256, 8, 2, [(0, 64), (130, 17)]),
+    ("fp8_e4m3", "f16", 16, 256, 8, 4, [(0, 20)]),
+    ("bf16", "bf16", 64, 256, 4, 4, [(5, 30)]),
 ]
 
 
