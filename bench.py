@@ -391,8 +391,8 @@ def bench_multistep(args):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(each sequence is independent; see the sharding notes).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(each sequence is independent, so the step shards by sequence across GPUs).", file=sys.stderr)
         sys.exit(2)
     if args.op == "prepare":
         return bench_prepare(args)

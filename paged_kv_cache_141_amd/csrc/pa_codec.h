@@ -57,7 +57,7 @@ __device__ __forceinline__ uint32_t f32_to_f16(float x) {
 // code = e4m3(fl32(x / scale)): correctly rounded fp32 quotient, RNE to three
 // mantissa bits, finite overflow and inf saturate to +-448, NaN -> sign|0x7F.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float x, float scale) {
-  const float y = x / scale;                 // IEEE division (no fast-math in this build)
+  const float y = x / scale;                 // IEEE division (compiled without fast-math)
   const uint32_t u = f2u(y);
   const uint32_t sign = (u >> 24) & 0x80u;
   const uint32_t a = u & 0x7FFFFFFFu;

@@ -216,7 +216,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   // step's V lands a step earlier than its K.  (kstart is a multiple of 64,
   // so even steps start blocks.)
   constexpr bool PAIRV = BS == 64 && PF >= 2 && PA_DECODE_PAIR_V;
-  constexpr int NB = PF + 1 + (PAIRV ? 1 : 0);
+  constexpr int NB = PAIRV ? (PF + 3) / 2 * 2 : PF + 1;   // PAIRV: PF + 2 rounded up to even
   static_assert(!PAIRV || NB % 2 == 0, "step parity must be static in the ring");
   Step buf[NB];
   const int nsteps = (kend - kstart + 31) / 32;

@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests run only where a GPU is visible; on CPU-only hosts they are skipped
-    # (the driver selects them with -m gpu on the GPU machine).
+    # (select them with -m gpu on a host with an MI355X).
     try:
         import torch
         has_gpu = torch.cuda.is_available()
