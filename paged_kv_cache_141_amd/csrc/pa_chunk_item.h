@@ -209,6 +209,7 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
       if (tid == 0) slot = atomicAdd(a.header + (prefix ? 4 : 2), 1);
       __syncthreads();
       w = base + uniform(slot);
+      __syncthreads();   // every wave has read slot before thread 0 writes it again
     }
     first = -1;
     if (w >= total) break;
