@@ -149,6 +149,7 @@ static pa_status_t attention_impl(const void* q, int32_t q_dtype, const void* k_
   a.prefix_part = w.prefix_part;
   a.prefix_parts = w.prefix_parts;
   a.chunk_rows = pa::chunk_rows_for(cache->head_dim);
+  a.chunk_partition = pa::kChunkPartition;
   a.prefix_rblocks = static_cast<int32_t>(ceil_div(static_cast<int64_t>(num_tokens) * a.group, a.chunk_rows));
   a.prefix_items = static_cast<int64_t>(a.prefix_rblocks) * w.prefix_parts * cache->num_kv_heads;
   a.score_scale = scale * cache->k_scale * 1.4426950408889634f;

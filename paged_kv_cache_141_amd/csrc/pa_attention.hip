@@ -20,8 +20,9 @@ __device__ __forceinline__ int item_size(int L, int ql, int G, int row0, int nro
 
 // One workgroup builds both work lists -- decode: (sequence, 16-row tile,
 // partition of a.partition keys); chunk: (sequence, 256-row block, partition
-// of 8192 keys) -- longest item first: items are bucketed by the number of
-// key steps they visit (32 keys for decode, 64 for chunks) and the buckets
+// of a.chunk_partition keys) -- longest item first: items are bucketed by the
+// number of key steps they visit (32 keys for decode, 64 for chunks, counted
+// in pairs for 16384-key partitions) and the buckets
 // are laid out in descending order, so the persistent kernels, which take
 // items in list order, start the long ones first and end on short ones.
 // Order within a bucket is arbitrary; no result depends on it.  It also
@@ -31,7 +32,10 @@ __device__ __forceinline__ int item_size(int L, int ql, int G, int row0, int nro
 // the batch's items so that all threads share them evenly.
 __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
   constexpr int NB0 = kPartitionMax / 32 + 1;            // decode buckets: 0 .. 64 steps
-  constexpr int NB1 = kChunkPartition / kChunkKeys + 1;   // chunk buckets: 0 .. 64 tiles
+  // chunk buckets: 0 .. 128, in units of cb tiles (2 for 16384-key partitions)
+  constexpr int CBMAX = kChunkPartitionMax > 8192 ? kChunkPartitionMax / 8192 : 1;
+  constexpr int NB1 = kChunkPartitionMax / (kChunkKeys * CBMAX) + 1;
+  const int cb = a.chunk_partition > 8192 ? a.chunk_partition / 8192 : 1;
   constexpr int NBMAX = (NB0 > NB1 ? NB0 : NB1);
   static_assert(NBMAX <= 192, "the bucket scan covers 3 x 64 buckets");
   __shared__ int hist[2][NBMAX];
@@ -54,7 +58,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
       const int own = L - a.prefix_len;                   // keys past the shared prefix
       if (ql > 0 && own > 0) {
         if (is_chunk_seq(a, rows)) {
-          np = (own + kChunkPartition - 1) / kChunkPartition;
+          np = (own + a.chunk_partition - 1) / a.chunk_partition;
           n = ((rows + a.chunk_rows - 1) / a.chunk_rows) * np;
           np = -np;
         } else {
@@ -96,7 +100,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
     const int npp = np < 0 ? -np : np;
     t = idx / npp;
     p = idx - t * npp;
-    bucket = list ? item_size(L, ql, G, t * a.chunk_rows, a.chunk_rows, p, kChunkPartition, kChunkKeys, a.prefix_len)
+    bucket = list ? (item_size(L, ql, G, t * a.chunk_rows, a.chunk_rows, p, a.chunk_partition, kChunkKeys,
+                               a.prefix_len) + cb - 1) / cb
                   : item_size(L, ql, G, t * kTileRows, kTileRows, p, a.partition, 32, a.prefix_len);
   };
 
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
     if (tid == 0) {
       float dsteps = 0.f, ctiles = 0.f;
       for (int b = 1; b < NB0; ++b) dsteps += static_cast<float>(b) * hist[0][b];
-      for (int b = 1; b < NB1; ++b) ctiles += static_cast<float>(b) * hist[1][b];
+      for (int b = 1; b < NB1; ++b) ctiles += static_cast<float>(b * cb) * hist[1][b];
       const float td = dsteps * a.num_kv_heads * a.step_dec_us;     // whole chip, full bandwidth
       const float tc = ctiles * a.num_kv_heads * a.step_chunk_us;   // whole chip
       const int n = a.step_groups;
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
   const int row_pos = a.seq_lens[i] - ql + (token - q0);
   const int own = row_pos - a.prefix_len;               // the row's keys past the shared prefix, minus one
   const int np = (a.prefix_len > 0 ? a.prefix_parts : 0) +
-                 (own >= 0 ? own / (is_chunk_seq(a, ql * a.group) ? kChunkPartition : a.partition) + 1 : 0);
+                 (own >= 0 ? own / (is_chunk_seq(a, ql * a.group) ? a.chunk_partition : a.partition) + 1 : 0);
   if (np <= 1 && a.prefix_len == 0) return;
   const int head = blockIdx.y * HPB + static_cast<int>(threadIdx.x) / LPH;
   if (head >= a.num_q_heads) return;
@@ -270,18 +275,19 @@ hipError_t launch_attention(int q, int kv, int d, int bs, const AttnArgs& a, hip
   if (e != hipSuccess) return e;
   // a step that can hold prompt chunks: one fused launch where the shape has one
   const bool chunks = q != DT_F32 && a.chunk_path && static_cast<int64_t>(a.max_query_len) * a.group >= kChunkMinRows;
-  AttnArgs f = a;
+  AttnArgs f = a;                             // what every kernel of this step reads
   const bool fused = PA_FUSED_STEP && chunks && (f.step_groups = static_cast<int32_t>(step_groups(q, kv, d, bs))) > 0;
+  f.chunk_partition = fused ? kChunkPartitionFused : kChunkPartition;
   if (fused) {
     const double eb = kv == DT_F32 ? 4 : (kv == DT_FP8 ? 1 : 2);
     f.fused = 1;
     f.step_dec_us = static_cast<float>(32.0 * d * 2 * eb / kFusedDecodeBytesPerUs);
     f.step_chunk_us = static_cast<float>(64.0 * a.chunk_rows * d * 4 / kFusedChunkFlopsPerUs);
   }
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, fused ? f : a);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, f);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.prefix_len > 0) {                     // the shared prefix, all rows at once
-    AttnArgs p = a;
+    AttnArgs p = f;
     p.prefix_pass = 1;
     if (ev[4] && (e = hipEventRecord(ev[4], stream)) != hipSuccess) return e;
     if ((e = launch_chunk(q, kv, d, bs, p, stream)) != hipSuccess) return e;
@@ -295,26 +301,26 @@ hipError_t launch_attention(int q, int kv, int d, int bs, const AttnArgs& a, hip
     if (ev[3] && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
   } else {
     if (ev[0] && (e = hipEventRecord(ev[0], stream)) != hipSuccess) return e;
-    if ((e = launch_decode(q, kv, d, bs, a, stream)) != hipSuccess) return e;
+    if ((e = launch_decode(q, kv, d, bs, f, stream)) != hipSuccess) return e;
     if (ev[1] && (e = hipEventRecord(ev[1], stream)) != hipSuccess) return e;
     if (chunks) {
       if (ev[2] && (e = hipEventRecord(ev[2], stream)) != hipSuccess) return e;
-      if ((e = launch_chunk(q, kv, d, bs, a, stream)) != hipSuccess) return e;
+      if ((e = launch_chunk(q, kv, d, bs, f, stream)) != hipSuccess) return e;
       if (ev[3] && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
     }
   }
   if ((a.max_parts > 1 || a.prefix_len > 0) && a.num_tokens > 0) {
     if (q == DT_F32) {
-      if (d == 64) launch_reduce<DT_F32, 64>(a, stream);
-      else launch_reduce<DT_F32, 128>(a, stream);
+      if (d == 64) launch_reduce<DT_F32, 64>(f, stream);
+      else launch_reduce<DT_F32, 128>(f, stream);
     } else if (q == DT_F16) {
-      if (d == 64) launch_reduce<DT_F16, 64>(a, stream);
-      else if (d == 128) launch_reduce<DT_F16, 128>(a, stream);
-      else launch_reduce<DT_F16, 256>(a, stream);
+      if (d == 64) launch_reduce<DT_F16, 64>(f, stream);
+      else if (d == 128) launch_reduce<DT_F16, 128>(f, stream);
+      else launch_reduce<DT_F16, 256>(f, stream);
     } else {
-      if (d == 64) launch_reduce<DT_BF16, 64>(a, stream);
-      else if (d == 128) launch_reduce<DT_BF16, 128>(a, stream);
-      else launch_reduce<DT_BF16, 256>(a, stream);
+      if (d == 64) launch_reduce<DT_BF16, 64>(f, stream);
+      else if (d == 128) launch_reduce<DT_BF16, 128>(f, stream);
+      else launch_reduce<DT_BF16, 256>(f, stream);
     }
     e = hipGetLastError();
   }

@@ -11,7 +11,7 @@ namespace pa {
 
 template <int CT, int KV, int D, int BS>
 __global__ __launch_bounds__(kChunkThreads, kChunkWavesPerSimd) void chunk_kernel(AttnArgs a) {
-  chunk_items<CT, KV, D, BS>(a, blockIdx.x, gridDim.x, a.prefix_pass != 0);
+  chunk_items<CT, KV, D, BS, kChunkPartition>(a, blockIdx.x, gridDim.x, a.prefix_pass != 0);
 }
 
 // One workgroup per resident slot, looping over chunk items.
@@ -22,6 +22,7 @@ hipError_t launch_chunk(int q, int kv, int d, int bs, const AttnArgs& a, hipStre
     if constexpr (CT == DT_F32) {
       return hipErrorInvalidValue;   // the chunk kernel stages 16-bit operands
     } else {
+      if (!a.prefix_pass && a.chunk_partition != kChunkPartition) return hipErrorInvalidValue;   // plan mismatch
       static const int64_t groups =
           resident_groups(reinterpret_cast<const void*>(&chunk_kernel<CT, KV, D, BS>), kChunkThreads);
       const int64_t want = a.prefix_pass ? a.prefix_items : a.max_citems * a.num_kv_heads;

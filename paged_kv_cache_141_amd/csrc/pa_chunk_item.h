@@ -105,10 +105,11 @@ __device__ __forceinline__ void chunk_softmax(const float (&s)[16], float& m, f3
 
 // One workgroup (8 waves, two per SIMD) per work item: sequence i, kv head h,
 // rows [256*rb, 256*rb + 256) of the sequence's (token, head-in-group) rows,
-// keys of context partition `part` (8192 keys).  Wave w owns rows
-// 32w..32w+31 as two 16-row tiles.  Each 64-key tile is gathered through the
-// block table by all 512 threads with 16-byte loads -- straight into LDS for
-// 16-bit caches (global_load_lds), through registers for fp8, which is
+// keys of context partition `part` (a.chunk_partition keys: 8192, 16384 in
+// the fused step).  Wave w owns rows 32w..32w+31 as two 16-row tiles.  Each
+// 64-key tile is gathered through the block table by all 512 threads with
+// 16-byte loads -- straight into LDS for 16-bit caches (global_load_lds),
+// through registers for fp8, which is
 // widened to the compute type on the way -- kChunkAhead tiles ahead of the
 // one being computed.  Each wave runs the transposed-score MFMA scheme of
 // the decode kernel, every LDS operand read feeding both of its row tiles.
@@ -124,7 +125,9 @@ constexpr int kChunkAhead = PA_CHUNK_AHEAD;              // tiles in flight (16-
 // The workgroup's first item is `first` (dealt out in advance, -1 for
 // none); after that it draws item base + k from the counter.  `prefix`: the
 // items are those of the shared-prefix pass instead of the chunk list.
-template <int CT, int KV, int D, int BS>
+// CPART: keys per partition of the chunk list, the value the plan used
+// (a.chunk_partition); the shared-prefix pass uses a.prefix_part <= CPART.
+template <int CT, int KV, int D, int BS, int CPART>
 __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int base, bool prefix) {
   using Lds = ChunkLds<D>;
   constexpr bool DIRECT = (KV != DT_FP8);                // 16-bit cache: global -> LDS directly
@@ -133,7 +136,7 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
   constexpr int AHEAD = D == 256 ? 1 : kChunkAhead;      // a 64 KB tile at d = 256: two buffers fit LDS
   constexpr int NBUF = DIRECT ? AHEAD + 1 : 2;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NBUF * Lds::BUF];
-  __shared__ int32_t btl[kChunkPartition / BS];          // the partition's physical block ids
+  __shared__ int32_t btl[CPART / BS];                    // the partition's physical block ids
   __shared__ int slot;
   constexpr int EBQ = Bytes<CT>::v;
   constexpr int EBK = Bytes<KV>::v;
@@ -246,7 +249,7 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
       rows = ql * G;
       base_pos = L - ql;
       tstep = 1;
-      cpart = kChunkPartition;
+      cpart = CPART;
       kstart = a.prefix_len + part * cpart;   // keys past a shared prefix only
       pslot = a.prefix_parts + part;
     }
@@ -509,7 +512,7 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
         const int token = q0 + t;
         const int head = h * G + (R - t * G);
         const float ltot = lacc[rt][0];
-        if (a.prefix_len == 0 && row_pos[rt] / kChunkPartition == 0) {
+        if (a.prefix_len == 0 && row_pos[rt] / CPART == 0) {
           const float inv = a.v_scale / ltot;
           uint8_t* op = static_cast<uint8_t*>(a.out) +
                         ((static_cast<int64_t>(token) * a.num_q_heads + head) * D + 4 * lg) * EBQ;

@@ -76,7 +76,16 @@ constexpr int kChunkKeys = 64;
 #ifndef PA_CHUNK_PARTITION
 #define PA_CHUNK_PARTITION 8192
 #endif
+#ifndef PA_CHUNK_PARTITION_FUSED
+#define PA_CHUNK_PARTITION_FUSED 16384
+#endif
+// Keys per chunk-item partition: kChunkPartition when the chunk kernel runs
+// alone, kChunkPartitionFused in the fused step, whose decode items fill in
+// behind the longer chunk items.  Workspace bounds use the shorter one.
 constexpr int kChunkPartition = PA_CHUNK_PARTITION;
+constexpr int kChunkPartitionFused = PA_CHUNK_PARTITION_FUSED;
+constexpr int kChunkPartitionMax = kChunkPartition > kChunkPartitionFused ? kChunkPartition : kChunkPartitionFused;
+static_assert(kChunkPartition <= kChunkPartitionFused, "workspace bounds assume the shorter partition apart");
 
 // Rescale threshold (log2 units): the running reference max of a row moves
 // only when a new score exceeds it by more than this, so the accumulator
@@ -219,6 +228,7 @@ struct AttnArgs {
   int32_t prefix_part, prefix_parts, prefix_rblocks;
   int32_t prefix_pass;       // 1: this chunk-kernel launch is the prefix pass
   int32_t chunk_rows;        // rows of one chunk item: chunk_rows_for(head dim)
+  int32_t chunk_partition;   // keys per chunk-item partition (kChunkPartition or kChunkPartitionFused)
   int64_t prefix_items;
   float score_scale;   // scale * k_scale * log2(e)
   float rescale_slack; // kRescaleSlack / score_scale (raw-score units)

@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kChunkThreads, kChunkWavesPerSimd) void step_kernel
   const int wave = uniform(static_cast<int>(threadIdx.x) >> 6);
   const int nchunk = static_cast<int>(gridDim.x) - ndec;
   if (g >= ndec) {
-    chunk_items<CT, KV, D, BS>(a, g - ndec, nchunk, false);
+    chunk_items<CT, KV, D, BS, kChunkPartitionFused>(a, g - ndec, nchunk, false);
     decode_items<CT, KV, D, BS, kStepDecodePrefetch, true>(a, threadIdx.x & 63, -1, ndec * kChunkWaves);
   } else {
     decode_items<CT, KV, D, BS, kStepDecodePrefetch, true>(a, threadIdx.x & 63, g * kChunkWaves + wave,
@@ -62,6 +62,7 @@ hipError_t launch_step(int q, int kv, int d, int bs, const AttnArgs& a, hipStrea
     if constexpr (CT == DT_F32 || D > 128) {
       return hipErrorInvalidValue;   // chunk items stage 16-bit operands; d 256 runs the kernels apart
     } else {
+      if (a.chunk_partition != kChunkPartitionFused) return hipErrorInvalidValue;   // plan mismatch
       hipLaunchKernelGGL((step_kernel<CT, KV, D, BS>), dim3(static_cast<unsigned>(a.step_groups)),
                          dim3(kChunkThreads), 0, stream, a);
       return hipGetLastError();

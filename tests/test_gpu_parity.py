@@ -181,6 +181,22 @@ def test_edge_lengths_long_context():
         assert_close(w, gpu_out(step), oracle_out(w), label=f"edge_long {kv} B={B}")
 
 
+def test_edge_lengths_fused_partition():
+    # 16-bit q with chunks runs the fused step, whose chunk items cover
+    # 16384-key partitions (8192 for f32, kernels apart): prompt chunks whose
+    # rows straddle key 16384 and 8192, one that ends on 16384, and decode
+    # rows at the boundary.
+    lens = [16500, 16384, 16385, 16383, 8300, 20000, 1, 16448]
+    qlens = [300, 1, 1, 64, 200, 1, 1, 64]
+    for kv, q, B in (("bf16", "bf16", 16), ("fp8_e4m3", "f16", 32), ("f32", "f32", 16)):
+        sc = 0.05 if kv == "fp8_e4m3" else 1.0
+        w = build("edge_fused", 37, lens, qlens, num_q_heads=8, num_kv_heads=4, head_dim=64,
+                  block_size=B, kv_dtype=kv, q_dtype=q, k_scale=sc, v_scale=sc)
+        say("edge_fused", kv, B)
+        step = wd.stage(w)
+        assert_close(w, gpu_out(step), oracle_out(w), label=f"edge_fused {kv} B={B}")
+
+
 def test_edge_lengths_many_pairs():
     # 256 sequences x 8 kv heads: enough (sequence, kv head) pairs for
     # 2048-key decode partitions (128 blocks of 16 keys: block ids in two
