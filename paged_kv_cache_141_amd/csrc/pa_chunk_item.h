@@ -143,7 +143,8 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
   constexpr int KS = D / 32;
   constexpr int NT = D / 16;
   constexpr int RT = D == 256 ? kChunkRowTiles / 2 : kChunkRowTiles;   // row tiles per wave
-  constexpr int ROWS = kChunkWaves * 16 * RT;            // rows of one item (chunk_rows_for(D))
+  constexpr int ROWS = kChunkWaves * 16 * RT;            // rows of one item
+  static_assert(ROWS == chunk_rows_for(D), "the plan and the kernel must agree on an item's rows");
 
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);                    // wave-uniform: keeps its branches scalar

@@ -71,7 +71,9 @@ constexpr int kChunkWavesPerSimd = PA_CHUNK_WAVES_PER_SIMD; // register budget: 
 constexpr int kChunkRows = 16 * kChunkRowTiles * kChunkWaves;
 // Rows of one chunk work item: 256 (two 16-row tiles per wave), or half that
 // for head dim 256, whose accumulators leave room for half the row tiles.
-constexpr int chunk_rows_for(int64_t head_dim) { return head_dim == 256 ? kChunkRows / 2 : kChunkRows; }
+constexpr int chunk_rows_for(int64_t head_dim) {
+  return head_dim == 256 ? 16 * (kChunkRowTiles / 2) * kChunkWaves : kChunkRows;
+}
 constexpr int kChunkKeys = 64;
 #ifndef PA_CHUNK_PARTITION
 #define PA_CHUNK_PARTITION 8192
