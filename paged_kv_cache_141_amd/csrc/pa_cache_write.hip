@@ -31,14 +31,6 @@ __device__ __forceinline__ void load8_src(const uint8_t* p, float (&x)[8]) {
   }
 }
 
-// One source element -> fp32 (exact widening).
-template <int SRC>
-__device__ __forceinline__ float load1_src(const uint8_t* p) {
-  if constexpr (SRC == DT_F32) return *reinterpret_cast<const float*>(p);
-  else if constexpr (SRC == DT_BF16) return bf16_to_f32(*reinterpret_cast<const uint16_t*>(p));
-  else return f16_to_f32(*reinterpret_cast<const uint16_t*>(p));
-}
-
 template <int KV>
 __device__ __forceinline__ uint32_t encode1(float x, float scale) {
   if constexpr (KV == DT_F32) return f2u(x);
@@ -47,74 +39,83 @@ __device__ __forceinline__ uint32_t encode1(float x, float scale) {
   else return f32_to_e4m3(x, scale);
 }
 
-// One thread = 8 elements of one (token, kv head) row, C = d / 8 threads per
-// row.  K: thread c takes the 8 consecutive elements 8c .. 8c+7 (one 16-byte
-// chunk for 16-bit sources) and lands them as one contiguous run.  V: the
-// row goes down one column of the transposed [d][B] tile, one element per
-// dim row, B elements apart; thread c takes dims c, C + c, 2C + c, ..., so
-// that each store instruction writes C consecutive dims of a row -- stores
-// that fall in one cache line (4 dims of 16-bit bf16 at B = 16) merge into
-// one request instead of four.
+// One workgroup = kWriteTokens consecutive tokens of one kv head.  Pass 1:
+// a thread takes 8 consecutive elements of one token's K and V rows (16-byte
+// loads for 16-bit sources); K lands as one contiguous run in its [B][d]
+// tile row, V's codes go to LDS as [dim][token].  Pass 2 writes V down the
+// transposed [d][B] tiles with the lanes running along the tokens: a store
+// instruction covers 16 tokens x 4 dims, so the tokens of a prompt chunk,
+// which sit in consecutive slots of one block, fill whole cache lines in one
+// request (four 32-byte dim rows at B = 16) instead of every token adding
+// two bytes to 32 lines from a different workgroup.
+constexpr int kWriteTokens = 16;
+
 template <int SRC, int KV>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a) {
-  const int chunks = a.head_dim / 8;
-  const int per_tok = a.num_kv_heads * chunks;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= static_cast<int64_t>(a.num_tokens) * per_tok) return;
-  const int t = static_cast<int>(idx / per_tok);
-  const int rem = static_cast<int>(idx - static_cast<int64_t>(t) * per_tok);
-  const int h = rem / chunks;
-  const int c = rem - h * chunks;
-  const int64_t s = a.slots[t];
-  if (s < 0) return;
-  const int64_t blk = s / a.block_size;
-  const int off = static_cast<int>(s - blk * a.block_size);
   constexpr int EBS = Bytes<SRC>::v;
   constexpr int EBK = Bytes<KV>::v;
-  const int64_t src_off = ((static_cast<int64_t>(t) * a.num_kv_heads + h) * a.head_dim + 8 * c) * EBS;
-  float xk[8], xv[8];
-  load8_src<SRC>(static_cast<const uint8_t*>(a.key) + src_off, xk);
-  {
-    const uint8_t* vsrc = static_cast<const uint8_t*>(a.value) +
-                          ((static_cast<int64_t>(t) * a.num_kv_heads + h) * a.head_dim + c) * EBS;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) xv[e] = load1_src<SRC>(vsrc + static_cast<int64_t>(e) * chunks * EBS);
-  }
+  __shared__ uint32_t vt[256 * kWriteTokens];            // V codes, [dim][token] (d <= 256)
+  __shared__ int64_t sslot[kWriteTokens];
+  const int h = blockIdx.y;
+  const int t0 = blockIdx.x * kWriteTokens;
+  const int nt = min(kWriteTokens, a.num_tokens - t0);
+  const int d = a.head_dim;
+  const int chunks = d / 8;
+  // pass 2 reads the slots from LDS; pass 1 reads its own, so that its source
+  // loads need not wait for a barrier
+  if (threadIdx.x < kWriteTokens) sslot[threadIdx.x] = static_cast<int>(threadIdx.x) < nt ? a.slots[t0 + threadIdx.x] : -1;
 
-  const int64_t tile = (blk * a.num_kv_heads + h) * static_cast<int64_t>(a.block_size) * a.head_dim;
-  uint8_t* kdst = static_cast<uint8_t*>(a.k_cache) + (tile + static_cast<int64_t>(off) * a.head_dim + 8 * c) * EBK;
-  if constexpr (KV == DT_F32) {
-    u32x4 lo, hi;
+  for (int x = threadIdx.x; x < nt * chunks; x += 256) {
+    const int tt = x / chunks;
+    const int c = x - tt * chunks;
+    const int64_t s = a.slots[t0 + tt];
+    if (s < 0) continue;
+    const int64_t blk = s / a.block_size;
+    const int off = static_cast<int>(s - blk * a.block_size);
+    const int64_t src_off = ((static_cast<int64_t>(t0 + tt) * a.num_kv_heads + h) * d + 8 * c) * EBS;
+    float xk[8], xv[8];
+    load8_src<SRC>(static_cast<const uint8_t*>(a.key) + src_off, xk);
+    load8_src<SRC>(static_cast<const uint8_t*>(a.value) + src_off, xv);
+    const int64_t tile = (blk * a.num_kv_heads + h) * static_cast<int64_t>(a.block_size) * d;
+    uint8_t* kdst = static_cast<uint8_t*>(a.k_cache) + (tile + static_cast<int64_t>(off) * d + 8 * c) * EBK;
+    if constexpr (KV == DT_F32) {
+      u32x4 lo, hi;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { lo[e] = f2u(xk[e]); hi[e] = f2u(xk[e + 4]); }
-    reinterpret_cast<u32x4*>(kdst)[0] = lo;
-    reinterpret_cast<u32x4*>(kdst)[1] = hi;
-  } else if constexpr (EBK == 2) {
-    u32x4 w;
+      for (int e = 0; e < 4; ++e) { lo[e] = f2u(xk[e]); hi[e] = f2u(xk[e + 4]); }
+      reinterpret_cast<u32x4*>(kdst)[0] = lo;
+      reinterpret_cast<u32x4*>(kdst)[1] = hi;
+    } else if constexpr (EBK == 2) {
+      u32x4 w;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = encode1<KV>(xk[2 * e], 1.f) | (encode1<KV>(xk[2 * e + 1], 1.f) << 16);
-    *reinterpret_cast<u32x4*>(kdst) = w;
-  } else {
-    u32x2 w;
+      for (int e = 0; e < 4; ++e)
+        w[e] = encode1<KV>(xk[2 * e], 1.f) | (encode1<KV>(xk[2 * e + 1], 1.f) << 16);
+      *reinterpret_cast<u32x4*>(kdst) = w;
+    } else {
+      u32x2 w;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      w[e] = encode1<KV>(xk[4 * e], a.k_scale) | (encode1<KV>(xk[4 * e + 1], a.k_scale) << 8) |
-             (encode1<KV>(xk[4 * e + 2], a.k_scale) << 16) |
-             (encode1<KV>(xk[4 * e + 3], a.k_scale) << 24);
+      for (int e = 0; e < 2; ++e) {
+        w[e] = encode1<KV>(xk[4 * e], a.k_scale) | (encode1<KV>(xk[4 * e + 1], a.k_scale) << 8) |
+               (encode1<KV>(xk[4 * e + 2], a.k_scale) << 16) |
+               (encode1<KV>(xk[4 * e + 3], a.k_scale) << 24);
+      }
+      *reinterpret_cast<u32x2*>(kdst) = w;
     }
-    *reinterpret_cast<u32x2*>(kdst) = w;
-  }
-
-  // V tile is [d][B]: element (dim, off) at dim * B + off; this thread's dims
-  // are c + e * chunks
-  uint8_t* vdst = static_cast<uint8_t*>(a.v_cache) +
-                  (tile + static_cast<int64_t>(c) * a.block_size + off) * EBK;
-  const int64_t vstride = static_cast<int64_t>(chunks) * a.block_size * EBK;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t code = encode1<KV>(xv[e], a.v_scale);
-    uint8_t* p = vdst + e * vstride;
+    for (int e = 0; e < 8; ++e) vt[(8 * c + e) * kWriteTokens + tt] = encode1<KV>(xv[e], a.v_scale);
+  }
+  __syncthreads();
+
+  // V tile is [d][B]: element (dim, off) at dim * B + off
+  for (int x = threadIdx.x; x < d * kWriteTokens; x += 256) {
+    const int tt = x % kWriteTokens;
+    const int dim = x / kWriteTokens;
+    const int64_t s = sslot[tt];
+    if (s < 0) continue;                                 // also the tokens past the last (slot -1)
+    const int64_t blk = s / a.block_size;
+    const int off = static_cast<int>(s - blk * a.block_size);
+    const int64_t tile = (blk * a.num_kv_heads + h) * static_cast<int64_t>(a.block_size) * d;
+    uint8_t* p = static_cast<uint8_t*>(a.v_cache) + (tile + static_cast<int64_t>(dim) * a.block_size + off) * EBK;
+    const uint32_t code = vt[x];
     if constexpr (EBK == 4) *reinterpret_cast<uint32_t*>(p) = code;
     else if constexpr (EBK == 2) *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(code);
     else *p = static_cast<uint8_t>(code);
@@ -123,11 +124,12 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a
 
 template <int SRC, int KV>
 static hipError_t launch_rc(const CacheWriteArgs& a, hipStream_t stream) {
-  const int64_t work = static_cast<int64_t>(a.num_tokens) * a.num_kv_heads * (a.head_dim / 8);
-  const int64_t blocks = (work + 255) / 256;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((reshape_and_cache_kernel<SRC, KV>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     stream, a);
+  if (a.head_dim > 256 || a.head_dim % 8 != 0) return hipErrorInvalidValue;
+  const int64_t groups = (static_cast<int64_t>(a.num_tokens) + kWriteTokens - 1) / kWriteTokens;
+  if (groups > 0x7FFFFFFF || a.num_kv_heads > 65535) return hipErrorInvalidValue;
+  if (groups == 0) return hipSuccess;
+  hipLaunchKernelGGL((reshape_and_cache_kernel<SRC, KV>), dim3(static_cast<unsigned>(groups), a.num_kv_heads),
+                     dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
