@@ -186,10 +186,14 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
 }
 
 // Merge of split-context partials.  One workgroup (4 waves) per token and
-// group of kReduceHeads q heads; tokens whose keys fit one partition were
-// written by the attention kernels and leave at once.  Each head takes D/4
+// group of q heads, or per token and all its heads (in turn) when the step
+// has many tokens; tokens whose keys fit one partition were written by the
+// attention kernels and leave at once.  Each head takes D/4
 // lanes, 4 dims per lane (16-byte loads):
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p
+#ifndef PA_REDUCE_MANY_TOKENS
+#define PA_REDUCE_MANY_TOKENS 1024
+#endif
 template <int OT, int D>
 __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
   constexpr int LPH = D / 4;                             // lanes per head
@@ -215,52 +219,60 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
   const int np = (a.prefix_len > 0 ? a.prefix_parts : 0) +
                  (own >= 0 ? own / (is_chunk_seq(a, ql * a.group) ? a.chunk_partition : a.partition) + 1 : 0);
   if (np <= 1 && a.prefix_len == 0) return;
-  const int head = blockIdx.y * HPB + static_cast<int>(threadIdx.x) / LPH;
-  if (head >= a.num_q_heads) return;
+  // head groups blockIdx.y, + gridDim.y, ... (one per workgroup, or all of
+  // them in one workgroup when the step has many tokens)
   const int d0 = (threadIdx.x % LPH) * 4;
-  const int64_t row = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts;
-  // One pass over the partials, eight at a time (all their loads issued
-  // together): the running max moves to the group's max and what was summed
-  // so far is rescaled to it.
-  constexpr int PG = 8;
-  float M = -__builtin_inff();
-  float den = 0.f;
-  f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int p0 = 0; p0 < np; p0 += PG) {
-    float mv[PG], lv[PG];
-    f32x4 av[PG];
+  const int ngroups = (a.num_q_heads + HPB - 1) / HPB;
+  for (int hg = blockIdx.y; hg < ngroups; hg += gridDim.y) {
+    const int head = hg * HPB + static_cast<int>(threadIdx.x) / LPH;
+    if (head >= a.num_q_heads) break;
+    const int64_t row = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts;
+    // One pass over the partials, eight at a time (all their loads issued
+    // together): the running max moves to the group's max and what was summed
+    // so far is rescaled to it.
+    constexpr int PG = 8;
+    float M = -__builtin_inff();
+    float den = 0.f;
+    f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < np; p0 += PG) {
+      float mv[PG], lv[PG];
+      f32x4 av[PG];
 #pragma unroll
-    for (int j = 0; j < PG; ++j) {
-      const bool in = p0 + j < np;
-      mv[j] = in ? a.part_m[row + p0 + j] : -__builtin_inff();
-      lv[j] = in ? a.part_l[row + p0 + j] : 0.f;
-      av[j] = in ? *reinterpret_cast<const f32x4*>(a.part_acc + (row + p0 + j) * D + d0)
-                 : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < PG; ++j) {
+        const bool in = p0 + j < np;
+        mv[j] = in ? a.part_m[row + p0 + j] : -__builtin_inff();
+        lv[j] = in ? a.part_l[row + p0 + j] : 0.f;
+        av[j] = in ? *reinterpret_cast<const f32x4*>(a.part_acc + (row + p0 + j) * D + d0)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      float Mn = M;
+#pragma unroll
+      for (int j = 0; j < PG; ++j) Mn = fmaxf(Mn, mv[j]);
+      const float r = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+      den *= r;
+      num *= r;
+#pragma unroll
+      for (int j = 0; j < PG; ++j) {
+        const float wgt = mv[j] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mv[j] - Mn);
+        den += wgt * lv[j];
+        num += wgt * av[j];
+      }
+      M = Mn;
     }
-    float Mn = M;
-#pragma unroll
-    for (int j = 0; j < PG; ++j) Mn = fmaxf(Mn, mv[j]);
-    const float r = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-    den *= r;
-    num *= r;
-#pragma unroll
-    for (int j = 0; j < PG; ++j) {
-      const float wgt = mv[j] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mv[j] - Mn);
-      den += wgt * lv[j];
-      num += wgt * av[j];
-    }
-    M = Mn;
+    const float inv = 1.f / den;
+    uint8_t* op = static_cast<uint8_t*>(a.out) +
+                  ((static_cast<int64_t>(token) * a.num_q_heads + head) * D + d0) * Bytes<OT>::v;
+    store4<OT>(op, num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
   }
-  const float inv = 1.f / den;
-  uint8_t* op = static_cast<uint8_t*>(a.out) +
-                ((static_cast<int64_t>(token) * a.num_q_heads + head) * D + d0) * Bytes<OT>::v;
-  store4<OT>(op, num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
 }
 
 template <int OT, int D>
 static void launch_reduce(const AttnArgs& a, hipStream_t stream) {
   constexpr int HPB = 4 * (64 / (D / 4));
-  const dim3 grid(a.num_tokens, (a.num_q_heads + HPB - 1) / HPB);
+  // a step with many tokens (prompt chunks) has few that need a merge: one
+  // workgroup per token then, so that the rest cost one early exit each
+  const int groups = (a.num_q_heads + HPB - 1) / HPB;
+  const dim3 grid(a.num_tokens, a.num_tokens >= PA_REDUCE_MANY_TOKENS ? 1 : groups);
   hipLaunchKernelGGL((reduce_kernel<OT, D>), grid, dim3(256), 0, stream, a);
 }
 
