@@ -84,9 +84,11 @@ def _src_values(shape, src, seed):
     ("f32", "f32", 16, 64, 1.0), ("bf16", "bf16", 16, 128, 1.0), ("f16", "f16", 32, 64, 1.0),
     ("f32", "bf16", 16, 128, 1.0), ("f32", "f16", 64, 128, 1.0), ("bf16", "f16", 16, 64, 1.0),
     ("bf16", "fp8_e4m3", 16, 128, 2.0 ** -5), ("bf16", "fp8_e4m3", 64, 128, 0.0123),
-    ("f32", "fp8_e4m3", 32, 64, 0.37), ("f16", "fp8_e4m3", 16, 64, 1.0)])
-def test_cache_write_bit_exact(src, kv, B, d, scale):
-    say(f"cache write {src}->{kv} B={B} d={d} scale={scale}")
+    ("f32", "fp8_e4m3", 32, 64, 0.37), ("f16", "fp8_e4m3", 16, 64, 1.0),
+    ("bf16", "bf16", 32, 256, 1.0), ("f32", "fp8_e4m3", 16, 256, 0.05)])
+@pytest.mark.parametrize("runs", [False, True])
+def test_cache_write_bit_exact(src, kv, B, d, scale, runs):
+    say(f"cache write {src}->{kv} B={B} d={d} scale={scale} runs={runs}")
     H, T, N = 3, 77, 24
     w = build("cw", 5, [T], [T], num_q_heads=H, num_kv_heads=H, head_dim=d, block_size=B,
               kv_dtype=kv, src_dtype=src, q_dtype="bf16" if kv != "f32" else "f32",
@@ -95,8 +97,16 @@ def test_cache_write_bit_exact(src, kv, B, d, scale):
     key = _src_values((T, H, d), src, 1)
     val = _src_values((T, H, d), src, 2)
     rng = np.random.default_rng(3)
-    slots = rng.permutation(N * B)[:T].astype(np.int64)
-    slots[::7] = -1                                     # padding tokens are skipped
+    if runs:
+        # a prompt chunk: consecutive slots through shuffled blocks, starting
+        # mid-block, with a stretch of padding
+        order = rng.permutation(N)
+        start = B // 2 + 3
+        slots = np.array([order[(start + t) // B] * B + (start + t) % B for t in range(T)], dtype=np.int64)
+        slots[40:45] = -1
+    else:
+        slots = rng.permutation(N * B)[:T].astype(np.int64)
+        slots[::7] = -1                                 # padding tokens are skipped
     kp, vp = w.initial_pool()
     oracle.cache.reshape_and_cache(kp, vp, key, val, src, kv, slots, B, w.k_scale, w.v_scale)
     kc, vc = wd.poisoned_pool(w, "cuda")
