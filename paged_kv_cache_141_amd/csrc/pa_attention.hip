@@ -105,10 +105,23 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
                   : item_size(L, ql, G, t * kTileRows, kTileRows, p, a.partition, 32, a.prefix_len);
   };
 
-  // pass 1: bucket sizes
+  // pass 1: bucket sizes.  With one batch, a thread's first KEEP items stay
+  // in registers for pass 2.
+  constexpr int KEEP = 4;
+  const bool one_batch = a.num_seqs <= 1024;
+  int cj[KEEP], cl[KEEP], ct[KEEP], cp[KEEP], cb2[KEEP];
   for (int base = 0; base < a.num_seqs; base += 1024) {
     load_batch(base);
-    for (int k = tid; k < scan[1023]; k += 1024) {
+    const int nk = scan[1023];
+#pragma unroll
+    for (int m = 0; m < KEEP; ++m) {
+      const int k = tid + 1024 * m;
+      if (k < nk) {
+        item(k, cj[m], cl[m], ct[m], cp[m], cb2[m]);
+        atomicAdd(&hist[cl[m]][cb2[m]], 1);
+      }
+    }
+    for (int k = tid + 1024 * KEEP; k < nk; k += 1024) {
       int j, list, t, p, bucket;
       item(k, j, list, t, p, bucket);
       atomicAdd(&hist[list][bucket], 1);
@@ -118,10 +131,15 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
   // fused step: split the step kernel's workgroups between the two lists by
   // their estimated times (the histograms hold the items' step / tile counts)
   if (a.fused) {
-    if (tid == 0) {
+    if (tid < 64) {                                      // one wave sums the histograms
       float dsteps = 0.f, ctiles = 0.f;
-      for (int b = 1; b < NB0; ++b) dsteps += static_cast<float>(b) * hist[0][b];
-      for (int b = 1; b < NB1; ++b) ctiles += static_cast<float>(b * cb) * hist[1][b];
+      for (int b = 1 + tid; b < NB0; b += 64) dsteps += static_cast<float>(b) * hist[0][b];
+      for (int b = 1 + tid; b < NB1; b += 64) ctiles += static_cast<float>(b * cb) * hist[1][b];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        dsteps += __shfl_xor(dsteps, o);
+        ctiles += __shfl_xor(ctiles, o);
+      }
       const float td = dsteps * a.num_kv_heads * a.step_dec_us;     // whole chip, full bandwidth
       const float tc = ctiles * a.num_kv_heads * a.step_chunk_us;   // whole chip
       const int n = a.step_groups;
@@ -137,7 +155,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
         const float k = fminf(sat, kFusedDecodeSaturation * td * n / (tc + kFusedDecodeSaturation * td));
         nd = min(max(static_cast<int>(k + 0.5f), 1), n - 1);
       }
-      a.header[6] = nd;
+      if (tid == 0) a.header[6] = nd;
     }
     __syncthreads();                                     // hist is rewritten below
   }
@@ -164,16 +182,28 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
   }
   __syncthreads();
   // pass 2: place every item in its bucket (a single batch is still loaded)
+  auto place = [&](int base, int j, int list, int t, int p, int bucket) {
+    const int pos = atomicAdd(&hist[list][bucket], 1);
+    if (pos >= (list ? a.max_citems : a.max_items)) return;   // only with metadata beyond the host bounds
+    int32_t* out = list ? a.citems : a.items;
+    out[2 * pos] = base + j;
+    out[2 * pos + 1] = (t << 16) | p;
+  };
   for (int base = 0; base < a.num_seqs; base += 1024) {
-    if (a.num_seqs > 1024) load_batch(base);
-    for (int k = tid; k < scan[1023]; k += 1024) {
+    if (!one_batch) load_batch(base);
+    const int nk = scan[1023];
+#pragma unroll
+    for (int m = 0; m < KEEP; ++m) {
+      const int k = tid + 1024 * m;
+      if (k < nk) {
+        if (!one_batch) item(k, cj[m], cl[m], ct[m], cp[m], cb2[m]);
+        place(base, cj[m], cl[m], ct[m], cp[m], cb2[m]);
+      }
+    }
+    for (int k = tid + 1024 * KEEP; k < nk; k += 1024) {
       int j, list, t, p, bucket;
       item(k, j, list, t, p, bucket);
-      const int pos = atomicAdd(&hist[list][bucket], 1);
-      if (pos >= (list ? a.max_citems : a.max_items)) continue;   // only with metadata beyond the host bounds
-      int32_t* out = list ? a.citems : a.items;
-      out[2 * pos] = base + j;
-      out[2 * pos + 1] = (t << 16) | p;
+      place(base, j, list, t, p, bucket);
     }
   }
   if (tid == 0) {
