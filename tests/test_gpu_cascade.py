@@ -91,3 +91,25 @@ def test_full_fp8_shared_prefix_sampled(B):
     w = workloads.make("fp8_shared_prefix", block_size=B)
     seqs = sorted(np.random.default_rng(B).choice(w.num_seqs, size=6, replace=False).tolist())
     run(w, seqs, label=f"full fp8 shared prefix B={B}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shared_prefix_step(seed):
+    # seeded random cascade steps: prefix of whole blocks, then per sequence a
+    # decode token, a short run or a prompt chunk past it
+    rng = np.random.default_rng([seed, 11])
+    d = int(rng.choice([64, 128, 256]))
+    B = int(rng.choice([16, 32, 64]))
+    kv = str(rng.choice(["f16", "bf16", "fp8_e4m3"]))
+    q = {"f16": "f16", "bf16": "bf16"}.get(kv) or str(rng.choice(["bf16", "f16"]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.choice([1, 2, 4]))
+    P = B * int(rng.integers(1, 9000 // B))
+    n = int(rng.integers(1, 17))
+    qlens = [int(rng.choice([1, 1, 1, int(rng.integers(2, 9)), int(rng.integers(16, 200))])) for _ in range(n)]
+    lens = [P + ql + int(rng.integers(0, 1500)) for ql in qlens]
+    sc = float(rng.choice([2.0 ** -5, 0.05])) if kv == "fp8_e4m3" else 1.0
+    w = build("pfx_rand", 200 + seed, lens, qlens, num_q_heads=G * hkv, num_kv_heads=hkv, head_dim=d,
+              block_size=B, kv_dtype=kv, q_dtype=q, k_scale=sc, v_scale=sc, shared_prefix_len=P)
+    run(w, label=f"random cascade seed={seed} {kv}/{q} d={d} B={B} Hq={G * hkv} Hkv={hkv} P={P} n={n} "
+                 f"tokens={sum(qlens)}")
