@@ -87,3 +87,30 @@ def test_fused_replays_bit_exact():
     first = wd.to_host_bits(st.attend()).copy()
     for _ in range(3):
         assert np.array_equal(first, wd.to_host_bits(st.attend()))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_mixed_step_graph_replays_bit_exact(kv):
+    # one mixed step (cache write of the new tokens, plan, fused kernel,
+    # merge) captured in a HIP graph; each replay, with eager library work
+    # and a poisoned output in between, must reproduce the eager output
+    sc = 2.0 ** -5 if kv == "fp8_e4m3" else 1.0
+    w = random_mixed(61, num_decode=48, chunk_specs=[(0, 200), (300, 150), (9000, 100)], max_decode_len=3000,
+                     num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, kv_dtype=kv, q_dtype="bf16",
+                     k_scale=sc, v_scale=sc)
+    say("mixed_graph", kv)
+    st = wd.stage(w, write_new=False)
+    out = st.step()
+    torch.cuda.synchronize()
+    eager = wd.to_host_bits(out).copy()
+    check(w, out, f"mixed_graph eager {kv}")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.step()
+    for rep in range(3):
+        st.out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(wd.to_host_bits(st.out), eager), f"replay {rep} differs from the eager step"
+        st.attend()                                  # eager work between replays
+        torch.cuda.synchronize()
