@@ -126,15 +126,24 @@ def paged_attention(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, seq_lens
     S = seq_lens.shape[0]
     for i in (range(S) if seqs is None else seqs):
         a, b = int(qsl[i]), int(qsl[i + 1])
-        n = b - a
-        if n == 0:
-            continue
-        L = int(seq_lens[i])
-        K, V = gather_sequence(k_pool, v_pool, kv_dtype, k_scale, v_scale, block_tables[i], L,
-                               block_size)
-        positions = L - n + np.arange(n)
-        out[a:b] = attend_rows(qf[a:b], K, V, positions, scale)
+        if b > a:
+            out[a:b] = attend_sequence(qf[a:b], k_pool, v_pool, kv_dtype, block_tables[i],
+                                       int(seq_lens[i]), block_size, scale, k_scale, v_scale)
     return out
+
+
+def attend_sequence(q_rows, k_pool, v_pool, kv_dtype, table_row, L, block_size, scale,
+                    k_scale=1.0, v_scale=1.0):
+    """Output ``[n][Hq][d]`` float64 of one request's n queries.
+
+    q_rows ``[n][Hq][d]`` (decoded values) are the request's last n positions
+    L - n .. L - 1; its L cached tokens are gathered through ``table_row``.
+    Requests are independent of one another.
+    """
+    n = q_rows.shape[0]
+    K, V = gather_sequence(k_pool, v_pool, kv_dtype, k_scale, v_scale, table_row, L, block_size)
+    positions = L - n + np.arange(n)
+    return attend_rows(q_rows, K, V, positions, scale)
 
 
 def block_sum_attention(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, seq_lens,

@@ -94,12 +94,17 @@ pa_status_t check_prefix(const pa_cache_t* c, int32_t q_dtype, int32_t max_seq_l
   return PA_OK;
 }
 
-static pa_status_t attention_impl(const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
-                                  const pa_cache_t* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                  const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
-                                  int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
-                                  int32_t max_query_len, int32_t prefix_len, float scale, void* out,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+}  // namespace
+
+namespace pa {
+
+int attention_entry(const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
+                    const pa_cache_t* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                    int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
+                    int32_t max_query_len, int32_t prefix_len, float scale, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream, size_t* required) {
+  if (required) *required = 0;
   pa_status_t st = check_attention_sizes(cache, num_q_heads, num_seqs, num_tokens, max_seq_len, max_query_len);
   if (st != PA_OK) return st;
   if ((st = check_prefix(cache, q_dtype, max_seq_len, prefix_len)) != PA_OK) return st;
@@ -115,6 +120,10 @@ static pa_status_t attention_impl(const void* q, int32_t q_dtype, const void* k_
     return PA_ERR_SHAPE;
   const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, cache->num_kv_heads,
                                                      cache->head_dim, max_seq_len, prefix_len);
+  if (required) {   // the caller sizes (or supplies) the workspace once it knows the need
+    *required = w.total;
+    return PA_OK;
+  }
   if (!workspace || workspace_bytes < w.total) return PA_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return PA_ERR_WORKSPACE;
 
@@ -141,6 +150,7 @@ static pa_status_t attention_impl(const void* q, int32_t q_dtype, const void* k_
   a.num_tokens = num_tokens;
   a.num_q_heads = num_q_heads;
   a.max_query_len = max_query_len;
+  a.max_seq_len = max_seq_len;
   a.num_kv_heads = cache->num_kv_heads;
   a.group = num_q_heads / cache->num_kv_heads;
   a.max_parts = w.max_parts;
@@ -160,7 +170,7 @@ static pa_status_t attention_impl(const void* q, int32_t q_dtype, const void* k_
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-}  // namespace
+}  // namespace pa
 
 extern "C" {
 
@@ -343,9 +353,10 @@ pa_status_t pa_attention(const void* q, int32_t q_dtype, const void* k_cache, co
                          int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
                          int32_t max_query_len, float scale, void* out, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  return attention_impl(q, q_dtype, k_cache, v_cache, cache, block_tables, max_blocks_per_seq, seq_lens,
-                        query_start_loc, num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, 0, scale,
-                        out, workspace, workspace_bytes, stream);
+  return static_cast<pa_status_t>(pa::attention_entry(q, q_dtype, k_cache, v_cache, cache, block_tables,
+                                                      max_blocks_per_seq, seq_lens, query_start_loc, num_seqs,
+                                                      num_tokens, num_q_heads, max_seq_len, max_query_len, 0, scale,
+                                                      out, workspace, workspace_bytes, stream, nullptr));
 }
 
 pa_status_t pa_attention_shared_prefix(const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
@@ -355,9 +366,28 @@ pa_status_t pa_attention_shared_prefix(const void* q, int32_t q_dtype, const voi
                                        int32_t num_q_heads, int32_t max_seq_len, int32_t max_query_len,
                                        int32_t prefix_len, float scale, void* out, void* workspace,
                                        size_t workspace_bytes, void* stream) {
-  return attention_impl(q, q_dtype, k_cache, v_cache, cache, block_tables, max_blocks_per_seq, seq_lens,
-                        query_start_loc, num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, prefix_len,
-                        scale, out, workspace, workspace_bytes, stream);
+  return static_cast<pa_status_t>(pa::attention_entry(q, q_dtype, k_cache, v_cache, cache, block_tables,
+                                                      max_blocks_per_seq, seq_lens, query_start_loc, num_seqs,
+                                                      num_tokens, num_q_heads, max_seq_len, max_query_len,
+                                                      prefix_len, scale, out, workspace, workspace_bytes, stream,
+                                                      nullptr));
+}
+
+pa_status_t pa_preferred_block_size(int32_t head_dim, int32_t kv_dtype, int32_t q_dtype, int32_t* block_size) {
+  if (!block_size) return PA_ERR_NULL;
+  if (!dtype_known(kv_dtype) || !dtype_known(q_dtype) || !pairing_ok(q_dtype, kv_dtype)) return PA_ERR_DTYPE;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PA_ERR_UNSUPPORTED;
+  if (head_dim == 256 && q_dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+  // Measured on MI355X, decode kernel over the GQA long-context decode step
+  // (32 q / 8 kv heads at d 128; the same KV bytes per token at d 64 and 256)
+  // and the LLaMA-7B decode step, at B = 16 / 32 / 64:
+  //  - 16-bit caches: 16 fastest at every head dim (a 32-key step reads each
+  //    V^T tile row whole: 32 bytes at B 16; at B 64 one load covers half a
+  //    128-byte row, and the reads stride across rows);
+  //  - fp8 caches: 32 fastest (a B-32 V^T row of codes is 32 bytes, the
+  //    same whole-row read as 16-bit at B 16).
+  *block_size = kv_dtype == PA_FP8_E4M3 ? 32 : 16;
+  return PA_OK;
 }
 
 pa_status_t pa_set_attention_events(void* before, void* after) {

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
     const int i = base + tid;
     int n = 0, L = 0, ql = 0, np = 0;
     if (i < a.num_seqs) {
-      L = a.seq_lens[i];
+      L = min(a.seq_lens[i], a.max_seq_len);
       ql = a.qsl[i + 1] - a.qsl[i];
       const int rows = ql * G;
       const int own = L - a.prefix_len;                   // keys past the shared prefix
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
     if (pos >= (list ? a.max_citems : a.max_items)) return;   // only with metadata beyond the host bounds
     int32_t* out = list ? a.citems : a.items;
     out[2 * pos] = base + j;
-    out[2 * pos + 1] = (t << 16) | p;
+    out[2 * pos + 1] = static_cast<int32_t>((static_cast<uint32_t>(t) << 16) | static_cast<uint32_t>(p));
   };
   for (int base = 0; base < a.num_seqs; base += 1024) {
     if (!one_batch) load_batch(base);
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
   const int i = uniform(lo);
   const int q0 = a.qsl[i];
   const int ql = a.qsl[i + 1] - q0;
-  const int row_pos = a.seq_lens[i] - ql + (token - q0);
+  const int row_pos = min(a.seq_lens[i], a.max_seq_len) - ql + (token - q0);
   const int own = row_pos - a.prefix_len;               // the row's keys past the shared prefix, minus one
   const int np = (a.prefix_len > 0 ? a.prefix_parts : 0) +
                  (own >= 0 ? own / (is_chunk_seq(a, ql * a.group) ? a.chunk_partition : a.partition) + 1 : 0);

@@ -242,9 +242,9 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
       h = w - e * a.num_kv_heads;
       i = uniform(a.citems[2 * e]);
       const int tp = uniform(a.citems[2 * e + 1]);
-      rblk = tp >> 16;
+      rblk = static_cast<int>(static_cast<uint32_t>(tp) >> 16);
       part = tp & 0xFFFF;
-      L = uniform(a.seq_lens[i]);
+      L = min(uniform(a.seq_lens[i]), a.max_seq_len);
       q0 = uniform(a.qsl[i]);
       const int ql = uniform(a.qsl[i + 1]) - q0;
       rows = ql * G;

@@ -71,7 +71,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   const int r = lane & 15;
   const int lg = lane >> 4;
 
-  const int L = a.seq_lens[i];
+  const int L = min(a.seq_lens[i], a.max_seq_len);
   const int q0 = a.qsl[i];
   const int ql = a.qsl[i + 1] - q0;
   const int G = a.group;
@@ -298,7 +298,9 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int fi
     // step's keys): a step that reads half of each row and leaves the other
     // half to the next step measured 1.5x slower with it (B 64: 1,080 against
     // 733 us for the LLaMA-7B decode kernel at B 16)
-    attn_item<CT, KV, D, BS, PFD, STREAM && (BS <= 32 || PA_DECODE_NT_B64)>(a, i, tp >> 16, tp & 0xFFFF, h, lane);
+    // (tile, partition) are the unsigned 16-bit halves of tp: tiles reach 0xFFFF
+    attn_item<CT, KV, D, BS, PFD, STREAM && (BS <= 32 || PA_DECODE_NT_B64)>(
+        a, i, static_cast<int>(static_cast<uint32_t>(tp) >> 16), tp & 0xFFFF, h, lane);
     w = -1;
   }
 }

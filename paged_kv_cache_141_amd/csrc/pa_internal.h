@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pa.h"
+
 namespace pa {
 
 // Rows of one attention work item: a 16-row MFMA tile of (query token,
@@ -124,7 +126,7 @@ inline int64_t max_work_items(int64_t num_seqs, int64_t num_tokens, int64_t grou
 // Workspace carve-up (byte offsets, each 256-byte aligned).
 struct WorkspaceLayout {
   size_t header;   // int32 [64]: [0]/[1] decode work counter/count, [2]/[3] chunk's, [4] prefix pass's
-  size_t items;    // int32x2 [max_items]: decode items (seq, tile << 16 | partition)
+  size_t items;    // int32x2 [max_items]: decode items (seq, tile << 16 | partition; unsigned halves)
   size_t citems;   // int32x2 [max_citems]: chunk items (seq, row block << 16 | partition)
   size_t part_m;   // float [T][Hq][MP]: running max (log2 units) per partition
   size_t part_l;   // float [T][Hq][MP]: softmax denominator per partition
@@ -219,6 +221,12 @@ struct AttnArgs {
   int32_t max_blocks_per_seq;
   int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, group;
   int32_t max_query_len;
+  // Host bound on the context lengths.  Every kernel reads a context
+  // length as min(seq_lens[i], max_seq_len): a sequence past the bound gets
+  // rows computed over its first max_seq_len keys -- wrong, but every
+  // block-table, pool, partial and item access stays inside the buffers the
+  // bound sized.
+  int32_t max_seq_len;
   int32_t max_parts;
   int32_t partition;   // decode partition length in keys (decode_partition)
   // Shared prefix (cascade): every sequence's first prefix_len keys are the
@@ -294,6 +302,17 @@ struct CommitArgs {
   const int32_t* num_scheduled;  // [num_reqs]
   int32_t max_reqs, num_reqs;
 };
+
+// The body of pa_attention / pa_attention_shared_prefix (a pa_status_t):
+// validates, lays out the workspace and launches.  With `required` non-null
+// it only writes the workspace bytes the step needs there (after the same
+// validation) and launches nothing.  (pa_api.hip)
+int attention_entry(const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
+                    const pa_cache_t* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
+                    int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
+                    int32_t max_query_len, int32_t prefix_len, float scale, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream, size_t* required);
 
 // Launchers.  Each returns hipSuccess or the launch error.
 

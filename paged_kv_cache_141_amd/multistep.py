@@ -71,7 +71,15 @@ class DecodeLoop:
 
     def capture(self):
         """Record the N steps once into a graph; ``graph.replay()`` reruns them
-        (from whatever num_computed and cache the device holds then)."""
+        from whatever num_computed and cache the device holds then.
+
+        The context bound and the workspace are fixed here: a replay is
+        correct only while every context it reaches stays within
+        ``max_seq_len``, e.g. when each replay starts from the captured state
+        (restore num_computed first), or when max_seq_len was sized for all
+        the replays.  A context past the bound is attended over its first
+        max_seq_len keys only -- a wrong row, never an access outside the
+        buffers."""
         import torch
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):      # captures on torch's capture stream, the current one inside

@@ -146,3 +146,36 @@ def test_shared_prefix_argument_errors():
                                                              ctypes.byref(b)) == 0
         sizes.append(b.value)
     assert sizes[0] > 0 and sizes[1] > 0
+
+
+def test_row_tile_limit():
+    # Work items carry a 16-row tile index in 16 unsigned bits: up to 0xFFFF
+    # tiles of (token, q head) rows per kv head are accepted, more are not.
+    lib = pa.library()
+    c = _cache(num_kv_heads=1, head_dim=64)
+    b = ctypes.c_size_t(0)
+    G = 64
+    ok_q = 0xFFFF * 16 // G                         # 16,383 tokens: 65,532 tiles
+    assert lib.pa_attention_workspace_size(ctypes.byref(c), G, 1, ok_q, ok_q, ok_q, ctypes.byref(b)) == 0
+    assert lib.pa_attention_workspace_size(ctypes.byref(c), G, 1, ok_q + 1, ok_q + 1, ok_q + 1,
+                                           ctypes.byref(b)) == 4
+    # the case past 2^15 tiles that a signed unpack got wrong is accepted
+    assert lib.pa_attention_workspace_size(ctypes.byref(c), G, 2, 8201, 8200, 8200, ctypes.byref(b)) == 0
+
+
+def test_preferred_block_size():
+    # 32 tokens for fp8 caches, 16 for 16-bit and fp32 ones, at every head dim
+    for d in (64, 128, 256):
+        for q, kv in ((pa.PA_BF16, pa.PA_BF16), (pa.PA_F16, pa.PA_F16)):
+            assert pa.preferred_block_size(d, kv, q) == 16
+        for q in (pa.PA_BF16, pa.PA_F16):
+            assert pa.preferred_block_size(d, pa.PA_FP8_E4M3, q) == 32
+    for d in (64, 128):
+        assert pa.preferred_block_size(d, pa.PA_F32, pa.PA_F32) == 16
+    lib = pa.library()
+    b = ctypes.c_int32(0)
+    assert lib.pa_preferred_block_size(256, pa.PA_F32, pa.PA_F32, ctypes.byref(b)) == 4   # d 256: 16-bit q only
+    assert lib.pa_preferred_block_size(96, pa.PA_BF16, pa.PA_BF16, ctypes.byref(b)) == 4
+    assert lib.pa_preferred_block_size(128, pa.PA_F16, pa.PA_BF16, ctypes.byref(b)) == 3  # no such pairing
+    assert lib.pa_preferred_block_size(128, 9, pa.PA_BF16, ctypes.byref(b)) == 3
+    assert lib.pa_preferred_block_size(128, pa.PA_BF16, pa.PA_BF16, None) == 1

@@ -13,7 +13,6 @@ import numpy as np
 import pytest
 
 import oracle
-import workloads
 from oracle import codecs
 from workloads import device as wd
 from workloads.generate import build
@@ -84,13 +83,6 @@ def test_head_dim_64_and_group_one():
     w = build("pfx_d64", 5, lens, [1, 1, 1, 1], num_q_heads=8, num_kv_heads=8, head_dim=64, block_size=32,
               kv_dtype="bf16", shared_prefix_len=P)
     run(w, label="d=64 G=1")
-
-
-@pytest.mark.parametrize("B", [16, 64])
-def test_full_fp8_shared_prefix_sampled(B):
-    w = workloads.make("fp8_shared_prefix", block_size=B)
-    seqs = sorted(np.random.default_rng(B).choice(w.num_seqs, size=6, replace=False).tolist())
-    run(w, seqs, label=f"full fp8 shared prefix B={B}")
 
 
 @pytest.mark.parametrize("seed", range(8))

@@ -6,8 +6,6 @@ with no NaN.  Invariants (placement permutation, shared vs private prefix
 blocks, run-to-run) must hold bit-exactly on the GPU.
 """
 
-import sys
-
 import numpy as np
 import pytest
 
@@ -17,44 +15,23 @@ from oracle import codecs
 from workloads import device as wd
 from workloads.generate import build, random_mixed
 
+from full_oracle import TOL, assert_close, attention, fill_pools, rows_of, say  # noqa: F401
+
 torch = pytest.importorskip("torch")
 import paged_kv_cache_141_amd as pa  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 2e-3, "f16": 2e-3, "bf16": 1e-2, "fp8_e4m3": 4e-2}
-
-
-def say(*a):
-    print(*a, file=sys.stderr, flush=True)
-
 
 def oracle_out(w, seqs=None):
-    kp, vp = oracle.cache.fill_pools(w, seqs)
-    return oracle.attention.paged_attention(
-        w.q_values(), w.q_dtype, kp, vp, w.kv_dtype, w.block_tables, w.seq_lens,
-        w.query_start_loc, w.block_size, w.scale, w.k_scale, w.v_scale, seqs=seqs)
+    kp, vp = fill_pools(w, seqs)
+    return attention(w, kp, vp, seqs)
 
 
 def gpu_out(step):
     out = step.attend()
     torch.cuda.synchronize()
     return codecs.decode(wd.to_host_bits(out), step.w.q_dtype)
-
-
-def rows_of(w, seqs):
-    qsl = w.query_start_loc
-    return np.concatenate([np.arange(qsl[i], qsl[i + 1]) for i in seqs]) if len(seqs) else \
-        np.zeros(0, dtype=np.int64)
-
-
-def assert_close(w, got, ref, seqs=None, label=""):
-    rows = rows_of(w, range(w.num_seqs) if seqs is None else seqs)
-    g, r = got[rows], ref[rows]
-    assert not np.isnan(g).any(), f"{label}: NaN in GPU output"
-    err = np.abs(g - r).max() if g.size else 0.0
-    say(f"{label}: max-abs err {err:.3e} (tol {TOL[w.kv_dtype]:.0e}) over {g.size} values")
-    assert err <= TOL[w.kv_dtype], f"{label}: max-abs error {err} > {TOL[w.kv_dtype]}"
 
 
 # ------------------------------------------------------------------ cache write
@@ -292,35 +269,29 @@ def test_metadata_checker():
     assert not ok and bad == 1
 
 
-# ------------------------------------------------------------------ full sizes, sampled
+# ------------------------------------------------------------------ full sizes, every row
+#
+# Each configuration at its full size, every query row against the oracle
+# (the block-wise sum equals ordinary attention: itwiki "vLLM",
+# "Block-wise attention").
 
-def _sample(w, k, seed=0, must=()):
-    rng = np.random.default_rng(seed)
-    pick = set(must) | set(rng.choice(w.num_seqs, size=min(k, w.num_seqs), replace=False).tolist())
-    return sorted(pick)
-
-
-def test_full_llama7b_decode_sampled():
+def test_full_llama7b_decode():
     w = workloads.make("llama7b_decode")
     say("full llama7b_decode: staging", w.summary())
-    step = wd.stage(w)
-    got = gpu_out(step)
-    seqs = _sample(w, 16, must=[int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens))])
-    assert_close(w, got, oracle_out(w, seqs), seqs, label="llama7b_decode sampled")
-    assert not np.isnan(got).any()
+    got = gpu_out(wd.stage(w))
+    kp, vp = fill_pools(w)
+    assert_close(w, got, attention(w, kp, vp), label="llama7b_decode, every row")
 
 
-def test_full_gqa_long_decode_sampled():
+def test_full_gqa_long_decode():
     w = workloads.make("gqa_long_decode")
     say("full gqa_long_decode: staging", w.summary())
-    step = wd.stage(w)
-    got = gpu_out(step)
-    seqs = _sample(w, 6, must=[int(np.argmax(w.seq_lens))])
-    assert_close(w, got, oracle_out(w, seqs), seqs, label="gqa_long_decode sampled")
-    assert not np.isnan(got).any()
+    got = gpu_out(wd.stage(w))
+    kp, vp = fill_pools(w)
+    assert_close(w, got, attention(w, kp, vp), label="gqa_long_decode, every row")
 
 
-def test_full_mixed_chunked_prefill_sampled():
+def test_full_mixed_chunked_prefill():
     w = workloads.make("mixed_chunked_prefill")
     say("full mixed_chunked_prefill: staging", w.summary())
     step = wd.stage(w, write_new=False)
@@ -334,17 +305,85 @@ def test_full_mixed_chunked_prefill_sampled():
     blk, off = ns // B, ns % B
     assert np.array_equal(kbits[blk, :, off, :], nk)
     assert np.array_equal(vbits[blk, :, :, off], nv)
-    seqs = _sample(w, 6, must=[256, 257, 259])
-    assert_close(w, got, oracle_out(w, seqs), seqs, label="mixed sampled (decode + chunks)")
-    assert not np.isnan(got).any()
+    del kbits, vbits
+    kp, vp = fill_pools(w)
+    ref = attention(w, kp, vp)
+    # the 1,024-token chunk at offset 8,192 (most of the chunk work) on its own line
+    assert_close(w, got, ref, [258], label="mixed step, chunk at offset 8192")
+    assert_close(w, got, ref, label="mixed step (decode + chunks), every row")
 
 
 @pytest.mark.parametrize("B", [16, 32, 64])
-def test_full_fp8_shared_prefix_sampled(B):
+def test_full_fp8_shared_prefix(B):
+    # through the block tables (pa_attention) and through the shared-prefix
+    # entry point (pa_attention_shared_prefix), both against the oracle
     w = workloads.make("fp8_shared_prefix", block_size=B)
     say(f"full fp8_shared_prefix B={B}: staging", w.summary())
     step = wd.stage(w)
     got = gpu_out(step)
-    seqs = _sample(w, 6, seed=B)
-    assert_close(w, got, oracle_out(w, seqs), seqs, label=f"fp8 shared prefix B={B} sampled")
-    assert not np.isnan(got).any()
+    cascade = gpu_out(step.use_shared_prefix(w.shared_prefix_len))
+    del step
+    kp, vp = fill_pools(w)
+    ref = attention(w, kp, vp)
+    assert_close(w, got, ref, label=f"fp8 shared prefix B={B} through the tables, every row")
+    assert_close(w, cascade, ref, label=f"fp8 shared prefix B={B} through the cascade, every row")
+
+
+def test_full_fp8_private_prefix_equals_shared():
+    # The private-copy twin (each sequence owns copies of the prefix blocks)
+    # gives bit for bit the output of the shared blocks, every row, so it meets
+    # the oracle exactly where the shared case does (test above).
+    s = wd.stage(workloads.make("fp8_shared_prefix", block_size=16))
+    shared = wd.to_host_bits(s.attend()).copy()
+    del s
+    w = workloads.make("fp8_shared_prefix", block_size=16, placement="private")
+    say("full fp8_private_prefix B=16: staging", w.summary())
+    p = wd.stage(w)
+    private = wd.to_host_bits(p.attend())
+    assert np.array_equal(shared, private)
+
+
+def test_decode_tiles_past_16_bits():
+    # fp32 q keeps every row on the decode kernel, whose work items carry the
+    # 16-row tile index in 16 unsigned bits.  An 8,200-token prompt with 64 q
+    # heads on one kv head has 524,800 (token, head) rows = 32,800 tiles: the
+    # tiles of tokens 8,192 on sit past 2^15.  Rows on both sides of that line
+    # and a decode row are compared with the oracle.
+    w = build("tiles16", 71, [8200, 300], [8200, 1], num_q_heads=64, num_kv_heads=1, head_dim=64,
+              block_size=16, kv_dtype="f32", q_dtype="f32")
+    say("tiles past 2^15:", w.summary())
+    got = gpu_out(wd.stage(w))
+    kp, vp = fill_pools(w)
+    toks = np.r_[0:3, 4000:4003, 8100:8200]
+    K, V = oracle.attention.gather_sequence(kp, vp, w.kv_dtype, 1.0, 1.0, w.block_tables[0], 8200, w.block_size)
+    qf = codecs.decode(w.q_values(), w.q_dtype)
+    ref = np.full(qf.shape, np.nan)
+    ref[toks] = oracle.attention.attend_rows(qf[toks], K, V, toks, w.scale)   # positions = token index
+    ref[8200:] = attention(w, kp, vp, [1])[8200:]
+    sel = np.r_[toks, 8200]
+    g, r = got[sel], ref[sel]
+    assert not np.isnan(g).any()
+    err = float(np.abs(g - r).max())
+    say(f"tiles past 2^15: max-abs err {err:.3e} over {g.size} values")
+    assert err <= TOL["f32"]
+
+
+PAIRS = [("bf16", "bf16"), ("f16", "f16"), ("fp8_e4m3", "bf16"), ("fp8_e4m3", "f16"), ("f32", "f32")]
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("kv,q", PAIRS)
+def test_attention_at_preferred_block_size(kv, q, d):
+    # the pool sized with the block size the library recommends for this head
+    # dim and precision: a mixed step at that block size against the oracle
+    if d == 256 and q == "f32":
+        pytest.skip("head dim 256 takes 16-bit queries only")
+    code = {"f32": pa.PA_F32, "f16": pa.PA_F16, "bf16": pa.PA_BF16, "fp8_e4m3": pa.PA_FP8_E4M3}
+    B = pa.preferred_block_size(d, code[kv], code[q])
+    label = f"preferred B={B} for kv={kv} q={q} d={d}"
+    say(label)
+    fp8 = kv == "fp8_e4m3"
+    w = random_mixed(400 + d, num_decode=11, chunk_specs=[(0, 70), (300, 45)], max_decode_len=2500,
+                     num_q_heads=16, num_kv_heads=4, head_dim=d, block_size=B, kv_dtype=kv, q_dtype=q,
+                     k_scale=2.0 ** -5 if fp8 else 1.0, v_scale=2.0 ** -5 if fp8 else 1.0)
+    assert_close(w, gpu_out(wd.stage(w)), oracle_out(w), label=label)

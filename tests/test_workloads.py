@@ -21,34 +21,20 @@ def test_kv_bytes_per_token_matches_printed_opt13b_example():
     assert round(b * g["tokens"] / 1e9, 1) == pytest.approx(g["stated_total_gb"], abs=0.1)
 
 
-def _budget_schedule(budget, cap, running_decodes, prompts):
-    """The page's fixed-budget rule: 1 token per running decode first, then
-    chunk = min(remaining prompt, remaining budget, cap) per waiting prompt."""
-    total = min(running_decodes, budget)
-    remaining = budget - total
-    chunks = []
-    for p in prompts:
-        if remaining <= 0:
-            break
-        left = p["prompt_len"] - p["computed"]
-        if left > 0:
-            c = min(left, remaining, cap)
-            chunks.append(c)
-            total += c
-            remaining -= c
-    return chunks, total
-
-
 def test_mixed_step_composition_follows_budget_rule():
+    # The golden file holds the page's worked composition of a 4,096-token
+    # step (decode tokens first, then chunks capped at 1,024 tokens); the
+    # generated mixed step must be exactly that step.
     g = json.load(open(os.path.join(GOLDEN, "chunked_prefill_budget.json")))
-    chunks, total = _budget_schedule(g["budget"], g["chunk_cap"], g["running_decodes"],
-                                     g["waiting_prompts"])
-    assert chunks == g["expected_chunks"] and total == g["expected_total_tokens"]
     w = workloads.make("mixed_chunked_prefill")
-    assert w.num_tokens == total <= g["budget"]
-    assert list(w.query_lens[256:]) == chunks
+    assert int((w.query_lens == 1).sum()) == g["running_decodes"]
+    assert w.num_tokens == g["expected_total_tokens"] <= g["budget"]
+    assert list(w.query_lens[256:]) == g["expected_chunks"]
+    assert max(g["expected_chunks"]) <= g["chunk_cap"]
     offsets = [p["computed"] for p in g["waiting_prompts"]]
     assert list(w.seq_lens[256:] - w.query_lens[256:]) == offsets
+    lens = [p["prompt_len"] for p in g["waiting_prompts"]]
+    assert all(int(L) <= P for L, P in zip(w.seq_lens[256:], lens))
 
 
 @pytest.mark.parametrize("name,kw", [("tiny_decode", {}), ("llama7b_decode", {"num_seqs": 40}),
