@@ -71,7 +71,7 @@ def library() -> ctypes.CDLL:
         "pa_reshape_and_cache": [P, P, I32, P, P, CP, P, I32, P],
         "pa_attention_workspace_size": [CP, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
         "pa_attention": [P, I32, P, P, CP, P, I32, P, P, I32, I32, I32, I32, I32, F, P, P, SZ, P],
-        "pa_preferred_block_size": [I32, I32, I32, ctypes.POINTER(I32)],
+        "pa_preferred_block_size": [I32, I32, I32, I32, ctypes.POINTER(I32)],
         "pa_attention_shared_prefix_workspace_size": [CP, I32, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
         "pa_attention_shared_prefix": [P, I32, P, P, CP, P, I32, P, P, I32, I32, I32, I32, I32, I32, F, P, P, SZ, P],
         "pa_check_metadata": [CP, P, I32, P, P, I32, I32, I32, I32, ctypes.POINTER(I32), P],
@@ -246,12 +246,13 @@ def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scal
     return out
 
 
-def preferred_block_size(head_dim: int, kv_dtype: int, q_dtype: int) -> int:
-    """Tokens per cache block the kernels run fastest with for this head dim
-    and (q dtype, cache dtype) pairing (``pa_preferred_block_size``; dtype
-    codes PA_F32 / PA_F16 / PA_BF16 / PA_FP8_E4M3)."""
+def preferred_block_size(head_dim: int, kv_dtype: int, q_dtype: int, group: int = 1) -> int:
+    """Tokens per cache block the kernels run fastest with for this head dim,
+    (q dtype, cache dtype) pairing and query group (q heads per kv head)
+    (``pa_preferred_block_size``; dtype codes PA_F32 / PA_F16 / PA_BF16 /
+    PA_FP8_E4M3)."""
     b = ctypes.c_int32(0)
-    _check(library().pa_preferred_block_size(head_dim, kv_dtype, q_dtype, ctypes.byref(b)),
+    _check(library().pa_preferred_block_size(head_dim, kv_dtype, q_dtype, group, ctypes.byref(b)),
            "pa_preferred_block_size")
     return int(b.value)
 

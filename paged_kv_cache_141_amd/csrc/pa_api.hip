@@ -373,20 +373,25 @@ pa_status_t pa_attention_shared_prefix(const void* q, int32_t q_dtype, const voi
                                                       nullptr));
 }
 
-pa_status_t pa_preferred_block_size(int32_t head_dim, int32_t kv_dtype, int32_t q_dtype, int32_t* block_size) {
+pa_status_t pa_preferred_block_size(int32_t head_dim, int32_t kv_dtype, int32_t q_dtype, int32_t group,
+                                    int32_t* block_size) {
   if (!block_size) return PA_ERR_NULL;
   if (!dtype_known(kv_dtype) || !dtype_known(q_dtype) || !pairing_ok(q_dtype, kv_dtype)) return PA_ERR_DTYPE;
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return PA_ERR_UNSUPPORTED;
   if (head_dim == 256 && q_dtype == PA_F32) return PA_ERR_UNSUPPORTED;
-  // Measured on MI355X, decode kernel over the GQA long-context decode step
-  // (32 q / 8 kv heads at d 128; the same KV bytes per token at d 64 and 256)
-  // and the LLaMA-7B decode step, at B = 16 / 32 / 64:
-  //  - 16-bit caches: 16 fastest at every head dim (a 32-key step reads each
-  //    V^T tile row whole: 32 bytes at B 16; at B 64 one load covers half a
-  //    128-byte row, and the reads stride across rows);
-  //  - fp8 caches: 32 fastest (a B-32 V^T row of codes is 32 bytes, the
-  //    same whole-row read as 16-bit at B 16).
-  *block_size = kv_dtype == PA_FP8_E4M3 ? 32 : 16;
+  if (group < 1) return PA_ERR_SHAPE;
+  // Decode kernel time on MI355X (one session), B = 16 / 32 / 64, us:
+  //   LLaMA-7B shape (group 1, d 128): bf16 737 / 746 / 835, fp8 395 / 402 / 452;
+  //   GQA long context (group 4):      bf16 d 64 425 / 420 / 462, d 128 408 / 410 / 459,
+  //                                    d 256 435 / 439 / 547;
+  //                                    fp8  d 64 247 / 247 / 256, d 128 225 / 222 / 249,
+  //                                    d 256 236 / 235 / 267.
+  // 64-token blocks are slowest everywhere: a 32-key step reads half of each
+  // 128-byte V^T row and strides across rows.  16 and 32 stay within 2 % of
+  // each other; 32 leads only where fp8 codes meet grouped queries (a B-32
+  // V^T row of codes is one 32-byte run, where B 16 splits a step's 32 keys
+  // over two 16-byte runs), and 16 leads for fp8 at group 1.
+  *block_size = (kv_dtype == PA_FP8_E4M3 && group >= 2) ? 32 : 16;
   return PA_OK;
 }
 

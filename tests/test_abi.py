@@ -164,18 +164,20 @@ def test_row_tile_limit():
 
 
 def test_preferred_block_size():
-    # 32 tokens for fp8 caches, 16 for 16-bit and fp32 ones, at every head dim
+    # 32 tokens for an fp8 cache under grouped queries, 16 otherwise, at every head dim
     for d in (64, 128, 256):
-        for q, kv in ((pa.PA_BF16, pa.PA_BF16), (pa.PA_F16, pa.PA_F16)):
-            assert pa.preferred_block_size(d, kv, q) == 16
-        for q in (pa.PA_BF16, pa.PA_F16):
-            assert pa.preferred_block_size(d, pa.PA_FP8_E4M3, q) == 32
+        for g in (1, 4, 8):
+            for q, kv in ((pa.PA_BF16, pa.PA_BF16), (pa.PA_F16, pa.PA_F16)):
+                assert pa.preferred_block_size(d, kv, q, g) == 16
+            for q in (pa.PA_BF16, pa.PA_F16):
+                assert pa.preferred_block_size(d, pa.PA_FP8_E4M3, q, g) == (32 if g >= 2 else 16)
     for d in (64, 128):
-        assert pa.preferred_block_size(d, pa.PA_F32, pa.PA_F32) == 16
+        assert pa.preferred_block_size(d, pa.PA_F32, pa.PA_F32, 4) == 16
     lib = pa.library()
     b = ctypes.c_int32(0)
-    assert lib.pa_preferred_block_size(256, pa.PA_F32, pa.PA_F32, ctypes.byref(b)) == 4   # d 256: 16-bit q only
-    assert lib.pa_preferred_block_size(96, pa.PA_BF16, pa.PA_BF16, ctypes.byref(b)) == 4
-    assert lib.pa_preferred_block_size(128, pa.PA_F16, pa.PA_BF16, ctypes.byref(b)) == 3  # no such pairing
-    assert lib.pa_preferred_block_size(128, 9, pa.PA_BF16, ctypes.byref(b)) == 3
-    assert lib.pa_preferred_block_size(128, pa.PA_BF16, pa.PA_BF16, None) == 1
+    assert lib.pa_preferred_block_size(256, pa.PA_F32, pa.PA_F32, 1, ctypes.byref(b)) == 4   # d 256: 16-bit q only
+    assert lib.pa_preferred_block_size(96, pa.PA_BF16, pa.PA_BF16, 1, ctypes.byref(b)) == 4
+    assert lib.pa_preferred_block_size(128, pa.PA_F16, pa.PA_BF16, 1, ctypes.byref(b)) == 3  # no such pairing
+    assert lib.pa_preferred_block_size(128, 9, pa.PA_BF16, 1, ctypes.byref(b)) == 3
+    assert lib.pa_preferred_block_size(128, pa.PA_BF16, pa.PA_BF16, 0, ctypes.byref(b)) == 2
+    assert lib.pa_preferred_block_size(128, pa.PA_BF16, pa.PA_BF16, 1, None) == 1

@@ -373,17 +373,19 @@ PAIRS = [("bf16", "bf16"), ("f16", "f16"), ("fp8_e4m3", "bf16"), ("fp8_e4m3", "f
 
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("kv,q", PAIRS)
-def test_attention_at_preferred_block_size(kv, q, d):
+@pytest.mark.parametrize("G", [1, 4])
+def test_attention_at_preferred_block_size(kv, q, d, G):
     # the pool sized with the block size the library recommends for this head
-    # dim and precision: a mixed step at that block size against the oracle
+    # dim, precision and query group: a mixed step at that block size against
+    # the oracle
     if d == 256 and q == "f32":
         pytest.skip("head dim 256 takes 16-bit queries only")
     code = {"f32": pa.PA_F32, "f16": pa.PA_F16, "bf16": pa.PA_BF16, "fp8_e4m3": pa.PA_FP8_E4M3}
-    B = pa.preferred_block_size(d, code[kv], code[q])
-    label = f"preferred B={B} for kv={kv} q={q} d={d}"
+    B = pa.preferred_block_size(d, code[kv], code[q], G)
+    label = f"preferred B={B} for kv={kv} q={q} d={d} G={G}"
     say(label)
     fp8 = kv == "fp8_e4m3"
-    w = random_mixed(400 + d, num_decode=11, chunk_specs=[(0, 70), (300, 45)], max_decode_len=2500,
-                     num_q_heads=16, num_kv_heads=4, head_dim=d, block_size=B, kv_dtype=kv, q_dtype=q,
+    w = random_mixed(400 + d + G, num_decode=11, chunk_specs=[(0, 70), (300, 45)], max_decode_len=2500,
+                     num_q_heads=4 * G, num_kv_heads=4, head_dim=d, block_size=B, kv_dtype=kv, q_dtype=q,
                      k_scale=2.0 ** -5 if fp8 else 1.0, v_scale=2.0 ** -5 if fp8 else 1.0)
     assert_close(w, gpu_out(wd.stage(w)), oracle_out(w), label=label)
