@@ -61,7 +61,9 @@ typedef enum {
   PA_ERR_UNSUPPORTED = 4, /* block size / head dim / scale outside the path    */
   PA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required           */
   PA_ERR_HIP = 6,         /* a HIP runtime call or launch failed               */
-  PA_ERR_METADATA = 7     /* pa_check_metadata found an invalid entry          */
+  PA_ERR_METADATA = 7,    /* pa_check_metadata found an invalid entry          */
+  PA_ERR_TOO_LARGE = 8    /* the step needs more device memory than the static
+                             scratch of pa_attention_noalloc holds            */
 } pa_status_t;
 
 /* Description of a KV cache pool (host struct, read during the call only). */
@@ -354,6 +356,35 @@ pa_status_t pa_set_prefix_events(void* before, void* after);
  */
 pa_status_t pa_preferred_block_size(int32_t head_dim, int32_t kv_dtype, int32_t q_dtype, int32_t group,
                                     int32_t* block_size);
+
+/*
+ * pa_attention for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc.
+ * Same arguments and result as pa_attention, without the workspace: the
+ * step's work lists and split-context partials live in a static device
+ * array of PA_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on each
+ * device it runs on until the process ends.  The call allocates nothing
+ * (no hipMalloc, no allocating library routine).
+ *
+ * A step whose pa_attention_workspace_size exceeds PA_NOALLOC_SCRATCH_BYTES
+ * returns PA_ERR_TOO_LARGE before anything is enqueued (the decode steps of
+ * the LLaMA-7B shape need about 4 MiB, 64 sequences at 32k contexts about
+ * 32 MiB; a 3,840-token mixed step with 9k contexts needs about 305 MiB and
+ * takes pa_attention with a caller workspace).  All calls on one device
+ * share that device's array, which keeps the last call's contents: calls
+ * that overlap on one device (two streams, or two host threads) race and
+ * give undefined rows.  Calls ordered on one stream are safe.  The first
+ * call on a device looks up the array's address there (PA_ERR_HIP if that
+ * fails).
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pa_status_t pa_attention_noalloc(const void* q, int32_t q_dtype, const void* k_cache,
+                                 const void* v_cache, const pa_cache_t* cache,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* seq_lens, const int32_t* query_start_loc,
+                                 int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                 int32_t max_seq_len, int32_t max_query_len, float scale,
+                                 void* out, void* stream);
 
 /* Static text for a status code. */
 const char* pa_status_string(pa_status_t status);

@@ -22,13 +22,15 @@ from typing import Optional
 __all__ = [
     "PagedAttentionError", "library", "library_path", "reshape_and_cache", "attention",
     "attention_workspace_size", "check_metadata", "copy_blocks", "apply_block_table_writes", "prepare_step", "commit_step",
-    "set_attention_events", "preferred_block_size", "PA_F32", "PA_F16",
+    "set_attention_events", "preferred_block_size", "attention_noalloc", "NOALLOC_SCRATCH_BYTES", "PA_F32", "PA_F16",
     "PA_BF16", "PA_FP8_E4M3",
 ]
 
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
 PA_OK = 0
 PA_ERR_METADATA = 7
+PA_ERR_TOO_LARGE = 8
+NOALLOC_SCRATCH_BYTES = 64 << 20      # PA_NOALLOC_SCRATCH_BYTES of include/pa.h
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "_lib", "libpa.so")
@@ -71,6 +73,7 @@ def library() -> ctypes.CDLL:
         "pa_reshape_and_cache": [P, P, I32, P, P, CP, P, I32, P],
         "pa_attention_workspace_size": [CP, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
         "pa_attention": [P, I32, P, P, CP, P, I32, P, P, I32, I32, I32, I32, I32, F, P, P, SZ, P],
+        "pa_attention_noalloc": [P, I32, P, P, CP, P, I32, P, P, I32, I32, I32, I32, I32, F, P, P],
         "pa_preferred_block_size": [I32, I32, I32, I32, ctypes.POINTER(I32)],
         "pa_attention_shared_prefix_workspace_size": [CP, I32, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
         "pa_attention_shared_prefix": [P, I32, P, P, CP, P, I32, P, P, I32, I32, I32, I32, I32, I32, F, P, P, SZ, P],
@@ -243,6 +246,38 @@ def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scal
     else:
         st = lib.pa_attention(*args, *tail)
         _check(st, "pa_attention")
+    return out
+
+
+def attention_noalloc(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale: float, *,
+                      max_seq_len: int, max_query_len: int, out, k_scale: float = 1.0, v_scale: float = 1.0,
+                      stream=None):
+    """``pa_attention_noalloc``: the step of :func:`attention`, with the work
+    lists and partials in the library's static device scratch instead of a
+    workspace.  Allocates nothing: the host bounds and ``out`` must be given
+    (raises PagedAttentionError with PA_ERR_TOO_LARGE for a step whose
+    workspace exceeds NOALLOC_SCRATCH_BYTES).  Calls that overlap on one
+    device race; calls ordered on one stream do not."""
+    torch = _torch()
+    spec = cache_spec(k_cache, v_cache, k_scale, v_scale)
+    if q.dim() != 3 or q.shape[2] != spec.head_dim:
+        raise ValueError(f"q must be [T, Hq, {spec.head_dim}]")
+    T, Hq, _ = q.shape
+    S = seq_lens.numel()
+    for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens),
+                    ("query_start_loc", query_start_loc)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if query_start_loc.numel() != S + 1 or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("metadata shapes disagree")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    st = library().pa_attention_noalloc(
+        _dev(q, "q"), _dtype_code(q), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), ctypes.byref(spec),
+        _dev(block_tables, "block_tables"), block_tables.shape[1], _dev(seq_lens, "seq_lens"),
+        _dev(query_start_loc, "query_start_loc"), S, T, Hq, int(max_seq_len), int(max_query_len), float(scale),
+        _dev(out, "out"), _stream(stream))
+    _check(st, "pa_attention_noalloc")
     return out
 
 

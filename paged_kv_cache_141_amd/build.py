@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libpa.so")
-SOURCES = ["pa_api.hip", "pa_cache_write.hip", "pa_blocks.hip", "pa_metadata.hip", "pa_attention.hip", "pa_decode.hip", "pa_chunk.hip", "pa_step.hip"]
+SOURCES = ["pa_api.hip", "pa_noalloc.hip", "pa_cache_write.hip", "pa_blocks.hip", "pa_metadata.hip", "pa_attention.hip", "pa_decode.hip", "pa_chunk.hip", "pa_step.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

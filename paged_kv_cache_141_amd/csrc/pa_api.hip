@@ -186,6 +186,7 @@ const char* pa_status_string(pa_status_t s) {
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP runtime error";
     case PA_ERR_METADATA: return "invalid metadata contents";
+    case PA_ERR_TOO_LARGE: return "the step needs more than the static scratch of pa_attention_noalloc";
   }
   return "unknown status";
 }

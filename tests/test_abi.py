@@ -27,7 +27,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(9):
         assert pa.status_string(s)
     assert pa.status_string(99) == "unknown status"
 
