@@ -63,6 +63,10 @@ def parse():
                          "eagerly and replayed from one captured HIP graph.")
     ap.add_argument("--graph-steps", type=int, default=8, help="decode steps per graph for --op multistep")
     ap.add_argument("--pairs", type=int, default=2048, help="block pairs per copy for --op")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="default run only: skip the records of the other configurations")
+    ap.add_argument("--config-cpu-seconds", type=float, default=3.0,
+                    help="oracle budget for each of the other configurations' records (0 disables it)")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="attend through pa_attention_shared_prefix over the workload's common prefix "
                          "(fp8_shared_prefix): the prefix is attended once for all rows")
@@ -388,69 +392,72 @@ def bench_multistep(args):
           flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(each sequence is independent, so the step shards by sequence across GPUs).", file=sys.stderr)
-        sys.exit(2)
-    if args.op == "prepare":
-        return bench_prepare(args)
-    if args.op == "multistep":
-        return bench_multistep(args)
-    if args.op != "step":
-        return bench_block_copies(args)
+def host_info():
+    """CPU model, BLAS library and host memory of the machine the oracle runs on."""
+    import numpy  # noqa: F401  (loads the BLAS that threadpool_info reports)
+    from threadpoolctl import threadpool_info
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    ram = None
+    try:
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal"):
+                ram = round(int(line.split()[1]) / 2 ** 20, 1)
+                break
+    except OSError:
+        pass
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    return {"cpu_model": model, "blas": ",".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in blas})),
+            "host_ram_GiB": ram, "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def copy_ceiling(steps=10, nbytes=4 << 30):
+    """A device-to-device copy of nbytes: the achievable HBM rate (read + write)."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_copied": nbytes, "GBps_read_plus_write": round(2 * nbytes / dt / 1e9, 1),
+            "frac_of_peak": round(2 * nbytes / dt / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def pct(xs, q):
+    import numpy as np
+    return round(float(np.percentile(np.asarray(xs), q)), 4)
+
+
+def measure_step(w, args, prefix=0, cpu_seconds=0.0):
+    """Stage workload w, run --warmup untimed steps, then time --steps steps
+    (cache write of the new tokens + attention).  Returns one record: wall and
+    per-step event times, throughput, the kernel rooflines and, with a budget,
+    the oracle's rate on a sample of the same workload."""
     import numpy as np
     import torch
 
-    if args.calibrate_copy:
-        n = args.calibrate_copy << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(args.warmup):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / args.steps
-        print(json.dumps({"calibrate_copy_bytes": n, "us_per_copy": round(dt * 1e6, 2),
-                          "copy_GBps_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
-        return
-
-    import workloads
     from workloads import accounting
     from workloads import device as wd
     import paged_kv_cache_141_amd as pa
 
-    kw = {}
-    if args.block_size:
-        kw["block_size"] = args.block_size
-    if args.placement:
-        kw["placement"] = args.placement
-    if args.head_dim:
-        kw["head_dim"] = args.head_dim
-    if args.kv_dtype:
-        kw["kv_dtype"] = args.kv_dtype
-        if args.kv_dtype == "fp8_e4m3":
-            kw.update(k_scale=workloads.generate.FP8_SCALE, v_scale=workloads.generate.FP8_SCALE)
-    w = workloads.make(args.config, **kw)
-    # overrides the configuration's name does not already carry go into it
-    # (the measured-traffic records are keyed by workload name)
-    if args.kv_dtype and args.config != "fp8_shared_prefix":
-        w.name += f"_{args.kv_dtype}"
-    if args.block_size and args.config != "fp8_shared_prefix":
-        w.name += f"_B{args.block_size}"
     print(f"[bench] staging {w.name}: {json.dumps(w.summary())}", file=sys.stderr, flush=True)
     t_stage = time.perf_counter()
     step = wd.stage(w, write_new=False)
-    prefix = 0
-    if args.shared_prefix:
+    if prefix:
         if not (w.shared_prefix_len and w.prefix_blocks_shared):
-            print("--shared-prefix needs a workload whose sequences share prefix blocks", file=sys.stderr)
-            sys.exit(2)
-        prefix = w.shared_prefix_len
+            raise SystemExit("--shared-prefix needs a workload whose sequences share prefix blocks")
         step.use_shared_prefix(prefix)
     torch.cuda.synchronize()
     print(f"[bench] staged in {time.perf_counter() - t_stage:.1f}s", file=sys.stderr, flush=True)
@@ -466,6 +473,7 @@ def main():
     prefix_pairs = [(ev.create(), ev.create()) for _ in range(args.steps)] if prefix else None
     cw = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    whole = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
 
     for _ in range(args.warmup):
         step.step()
@@ -477,10 +485,12 @@ def main():
             pa.set_chunk_events(chunk_pairs[k][0], chunk_pairs[k][1])
         if prefix_pairs:
             pa.set_prefix_events(prefix_pairs[k][0], prefix_pairs[k][1])
+        whole[k].record(stream)
         cw[k][0].record(stream)
         step.write_new()
         cw[k][1].record(stream)
         step.attend()
+    whole[args.steps].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     pa.set_attention_events(None, None)
@@ -488,6 +498,7 @@ def main():
     pa.set_prefix_events(None, None)
 
     step_s = (t1 - t0) / args.steps
+    step_ms = [whole[k].elapsed_time(whole[k + 1]) for k in range(args.steps)]
     attn_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
     cw_ms = [a.elapsed_time(b) for a, b in cw]
     chunk_ms = [ev.elapsed_ms(a, b) for a, b in chunk_pairs] if chunk_pairs else None
@@ -511,29 +522,23 @@ def main():
     # kernel, and each roofline is what its own work achieved over it.
     fused = bool(chunk_pairs) and w.head_dim <= 128
     main_kernel = "step_kernel" if fused else "attn_kernel"
-    traffic = measured_traffic(w.name, main_kernel)
+    name = w.name + ("_cascade" if prefix else "")
+    traffic = measured_traffic(name, main_kernel)
 
-    line = {
-        "metric": METRIC,
-        "value": round(kv_bytes / step_s / 1e9, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_s * 1e3, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16", "fp8_e4m3": "fp8_e4m3"}[w.kv_dtype],
-        "data": "synthetic",
-        "config": {"workload": w.name, "seqs": w.num_seqs, "query_tokens": w.num_tokens,
+    rec = {
+        "config": {"workload": name, "seqs": w.num_seqs, "query_tokens": w.num_tokens,
                    "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
                    "context_tokens": int(w.seq_lens.sum()), "max_seq_len": w.max_seq_len,
                    "kv_bytes": kv_bytes},
+        "ms_per_step": round(step_s * 1e3, 4),
+        "ms_step_events": {"median": pct(step_ms, 50), "p10": pct(step_ms, 10), "p90": pct(step_ms, 90)},
+        "kv_GBps": round(kv_bytes / step_s / 1e9, 2),
         "query_tokens_per_s": round(w.num_tokens / step_s, 1),
         "hbm_frac_step": round(kv_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "fragmentation": round(accounting.fragmentation(w), 5),
         "attention_kernel_us": round(attn_s * 1e6, 2),
+        "attention_kernel_us_p10_p90": [round(pct(attn_ms, 10) * 1e3, 2), round(pct(attn_ms, 90) * 1e3, 2)],
         "attention_kernel_kv_bytes": decode_bytes,
         "attention_kernel_unique_kv_bytes": unique_bytes,
         "attention_kernel_logical_GBps": round(decode_bytes / attn_s / 1e9, 2),
@@ -541,18 +546,17 @@ def main():
         "roofline": {"bound": "hbm", "kernel": main_kernel, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
-        "cpu_baseline": None,
     }
     if prefix_ms:
         # the prefix pass: every query row against every prefix key
         pflops = 4 * w.head_dim * w.num_q_heads * w.num_tokens * prefix
         tp = float(np.mean(prefix_ms)) / 1e3
-        line["config"]["shared_prefix_tokens"] = prefix
-        line["prefix_pass_us"] = round(tp * 1e6, 2)
-        line["roofline_prefix"] = {"bound": "mfma", "achieved": round(pflops / tp / 1e12, 2), "peak": 2500.0,
-                                   "unit": "TFLOP/s", "frac": round(pflops / tp / 1e12 / 2500.0, 4),
-                                   "flops": pflops, "prefix_kv_bytes": prefix * w.num_kv_heads * 2 * w.head_dim * eb,
-                                   "traffic": None}
+        rec["config"]["shared_prefix_tokens"] = prefix
+        rec["prefix_pass_us"] = round(tp * 1e6, 2)
+        rec["roofline_prefix"] = {"bound": "mfma", "achieved": round(pflops / tp / 1e12, 2), "peak": 2500.0,
+                                  "unit": "TFLOP/s", "frac": round(pflops / tp / 1e12 / 2500.0, 4),
+                                  "flops": pflops, "prefix_kv_bytes": prefix * w.num_kv_heads * 2 * w.head_dim * eb,
+                                  "traffic": measured_traffic(name, "chunk_kernel")}
     if chunk_ms:
         L = w.seq_lens.astype(np.int64)
         c = w.query_lens.astype(np.int64)
@@ -560,17 +564,121 @@ def main():
         flops = 4 * w.head_dim * w.num_q_heads * pairs_chunk
         t = float(np.mean(chunk_ms)) / 1e3
         peak = 2500.0   # dense bf16/fp16 MFMA, TFLOP/s
-        line["chunk_kernel_us"] = round(t * 1e6, 2)
-        line["roofline_chunk"] = {"bound": "mfma", "kernel": "step_kernel" if fused else "chunk_kernel",
-                                  "achieved": round(flops / t / 1e12, 2), "peak": peak,
-                                  "unit": "TFLOP/s", "frac": round(flops / t / 1e12 / peak, 4),
-                                  "flops": flops,
-                                  "traffic": None if fused else measured_traffic(w.name, "chunk_kernel")}
-        line["fused_step_kernel"] = fused
-        line["config"]["chunk_tokens"] = int((c * is_chunk).sum())
-    if args.cpu_seconds > 0:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        rec["chunk_kernel_us"] = round(t * 1e6, 2)
+        rec["roofline_chunk"] = {"bound": "mfma", "kernel": "step_kernel" if fused else "chunk_kernel",
+                                 "achieved": round(flops / t / 1e12, 2), "peak": peak,
+                                 "unit": "TFLOP/s", "frac": round(flops / t / 1e12 / peak, 4),
+                                 "flops": flops,
+                                 "traffic": None if fused else measured_traffic(name, "chunk_kernel")}
+        rec["fused_step_kernel"] = fused
+        rec["config"]["chunk_tokens"] = int((c * is_chunk).sum())
+    if cpu_seconds > 0:
+        print(f"[bench] timing the CPU oracle on a sample of {name}", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, cpu_seconds)
+    del step
+    torch.cuda.empty_cache()
+    return rec
+
+
+# The other configurations, each one record inside the default line: GQA
+# long-context decode, the mixed chunked-prefill step, the fp8 shared-prefix
+# step at B = 16/32/64 through the block tables and through the shared-prefix
+# (cascade) entry point, its private-copy twin, and the tiny decode step.
+OTHER_CONFIGS = [
+    ("gqa_long_decode", {}, False),
+    ("mixed_chunked_prefill", {}, False),
+    ("fp8_shared_prefix", {"block_size": 16}, False),
+    ("fp8_shared_prefix", {"block_size": 32}, False),
+    ("fp8_shared_prefix", {"block_size": 64}, False),
+    ("fp8_shared_prefix", {"block_size": 16}, True),
+    ("fp8_shared_prefix", {"block_size": 32}, True),
+    ("fp8_shared_prefix", {"block_size": 64}, True),
+    ("fp8_shared_prefix", {"block_size": 16, "placement": "private"}, False),
+    ("tiny_decode", {}, False),
+]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(each sequence is independent, so the step shards by sequence across GPUs).", file=sys.stderr)
+        sys.exit(2)
+    if args.op == "prepare":
+        return bench_prepare(args)
+    if args.op == "multistep":
+        return bench_multistep(args)
+    if args.op != "step":
+        return bench_block_copies(args)
+    import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"calibrate_copy_bytes": n, "us_per_copy": round(dt * 1e6, 2),
+                          "copy_GBps_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
+        return
+
+    import workloads
+
+    overrides = bool(args.block_size or args.placement or args.head_dim or args.kv_dtype or args.shared_prefix
+                     or args.config != "llama7b_decode")
+    kw = {}
+    if args.block_size:
+        kw["block_size"] = args.block_size
+    if args.placement:
+        kw["placement"] = args.placement
+    if args.head_dim:
+        kw["head_dim"] = args.head_dim
+    if args.kv_dtype:
+        kw["kv_dtype"] = args.kv_dtype
+        if args.kv_dtype == "fp8_e4m3":
+            kw.update(k_scale=workloads.generate.FP8_SCALE, v_scale=workloads.generate.FP8_SCALE)
+    w = workloads.make(args.config, **kw)
+    # overrides the configuration's name does not already carry go into it
+    # (the measured-traffic records are keyed by workload name)
+    if args.kv_dtype and args.config != "fp8_shared_prefix":
+        w.name += f"_{args.kv_dtype}"
+    if args.block_size and args.config != "fp8_shared_prefix":
+        w.name += f"_B{args.block_size}"
+    prefix = w.shared_prefix_len if args.shared_prefix else 0
+    rec = measure_step(w, args, prefix, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": rec["kv_GBps"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kv_dtype,
+        "data": "synthetic",
+    }
+    line.update(rec)
+    if line.get("cpu_baseline"):
+        line["cpu_baseline"]["host"] = host_info()
+    # the rest of the configurations (default run only), one record each
+    if not overrides and not args.no_configs:
+        line["copy_ceiling"] = copy_ceiling()
+        recs = {}
+        for name, ckw, casc in OTHER_CONFIGS:
+            cw = workloads.make(name, **ckw)
+            r = measure_step(cw, args, cw.shared_prefix_len if casc else 0, args.config_cpu_seconds)
+            recs[r["config"]["workload"]] = r
+        line["configs"] = recs
     print(json.dumps(line), flush=True)
 
 
