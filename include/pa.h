@@ -315,6 +315,28 @@ pa_status_t pa_check_metadata(const pa_cache_t* cache, const int32_t* block_tabl
                               int32_t* bad_seq, void* stream);
 
 /*
+ * Debug builds (the library compiled with -DPA_DEBUG=1, libpa_debug.so): the
+ * step plan checks each sequence's metadata before it makes work items
+ * (query_start_loc starts at 0, ends at num_tokens and does not decrease;
+ * 0 <= L <= max_seq_len; q_len <= L and <= max_query_len; ceil(L/B) <=
+ * max_blocks_per_seq and every used block id in [0, num_blocks)), the
+ * attention kernels check each block id they load, and the cache write each
+ * slot (< num_blocks * B).  The first violation is recorded as (code, index)
+ * in a per-device word pair, and the offending sequence, block or token is
+ * skipped (or read as block 0), so nothing is read or written outside the
+ * caller's buffers; the affected rows are undefined.  Codes: 1 bad
+ * query_start_loc, 2 q_len > L, 3 L outside [0, max_seq_len], 4 q_len >
+ * max_query_len, 5 a block id outside the pool (or too many blocks), 6 a slot
+ * outside the pool; index is the sequence (codes 1-5) or the token (6).
+ *
+ * pa_debug_check waits for `stream`, writes the recorded pair to *code and
+ * *index [host] (0, 0 when nothing was recorded), clears it, and returns
+ * PA_OK or PA_ERR_METADATA.  Release builds check nothing and return
+ * PA_ERR_UNSUPPORTED (with -1, -1).
+ */
+pa_status_t pa_debug_check(int32_t* code, int32_t* index, void* stream);
+
+/*
  * Measurement hook.  When both are non-NULL, every later pa_attention call
  * records hipEvent_t `before` on its stream immediately before launching the
  * decode attention kernel and `after` immediately after it, so

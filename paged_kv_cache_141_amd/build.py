@@ -17,6 +17,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "libpa.so")
+# the same sources with -DPA_DEBUG=1: metadata, block-id and slot checks that
+# record the first violation (pa_debug_check) instead of reading out of bounds
+DEBUG_LIB = os.path.join(OUT_DIR, "libpa_debug.so")
 SOURCES = ["pa_api.hip", "pa_noalloc.hip", "pa_cache_write.hip", "pa_blocks.hip", "pa_metadata.hip", "pa_attention.hip", "pa_decode.hip", "pa_chunk.hip", "pa_step.hip"]
 
 HIPCC_FLAGS = [
@@ -71,5 +74,37 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     return out
 
 
+# The host validation layer (the C ABI's argument checks, workspace sizing
+# and launch arguments) with AddressSanitizer and UndefinedBehaviorSanitizer,
+# linked against the stub launchers of tests/host_check instead of the
+# kernels: a CPU executable.  The sanitizers instrument host code only.
+HOST_CHECK = os.path.join(OUT_DIR, "host_check")
+HOST_CHECK_SRC = os.path.join(ROOT, "tests", "host_check", "host_check.cpp")
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_check(verbose: bool = False, out: str = HOST_CHECK) -> str:
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    objdir = out + ".obj"
+    os.makedirs(objdir, exist_ok=True)
+    flags = [f for f in HIPCC_FLAGS if f not in ("-O3", "-fPIC")] + ["-O1", "-g"]
+    common = [hipcc(), *flags, *SANITIZE, "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    srcs = [os.path.join(CSRC, "pa_api.hip"), os.path.join(CSRC, "pa_noalloc.hip"), HOST_CHECK_SRC]
+    objs = [os.path.join(objdir, os.path.basename(s).rsplit(".", 1)[0] + ".o") for s in srcs]
+    with ThreadPoolExecutor(len(srcs)) as pool:
+        list(pool.map(lambda so: _run([*common, "-c", so[0], "-o", so[1]], verbose), zip(srcs, objs)))
+    _run([hipcc(), "--offload-arch=gfx950", *SANITIZE, *objs, "-o", out], verbose)
+    shutil.rmtree(objdir, ignore_errors=True)
+    return out
+
+
+def build_all(verbose: bool = False):
+    """The release library and the debug-checked one, side by side."""
+    with ThreadPoolExecutor(2) as pool:
+        jobs = [pool.submit(build, verbose, LIB), pool.submit(build, verbose, DEBUG_LIB, ("PA_DEBUG=1",))]
+        return [j.result() for j in jobs]
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build_all(verbose=True))

@@ -60,6 +60,10 @@ pa_status_t check_attention_sizes(const pa_cache_t* c, int32_t num_q_heads, int3
                                                      c->head_dim, max_seq_len);
   if (ceil_div(max_seq_len, w.partition) > 0xFFFF) return PA_ERR_UNSUPPORTED;
   if (w.max_items > 0x7FFFFFFF / 64 || w.max_citems > 0x7FFFFFFF / 64) return PA_ERR_UNSUPPORTED;
+  // the partials' size, recomputed without wrap-around: at most 2^48 bytes
+  // (the layout's own size_t arithmetic is exact below that)
+  const double rows = static_cast<double>(num_tokens) * num_q_heads * w.max_parts;
+  if (rows * (c->head_dim + 2) * 4.0 > 281474976710656.0) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
@@ -151,6 +155,10 @@ int attention_entry(const void* q, int32_t q_dtype, const void* k_cache, const v
   a.num_q_heads = num_q_heads;
   a.max_query_len = max_query_len;
   a.max_seq_len = max_seq_len;
+  a.num_blocks = cache->num_blocks;
+  a.block_size = cache->block_size;
+  a.debug = PA_DEBUG ? pa::debug_words() : nullptr;
+  if (PA_DEBUG && !a.debug) return PA_ERR_HIP;
   a.num_kv_heads = cache->num_kv_heads;
   a.group = num_q_heads / cache->num_kv_heads;
   a.max_parts = w.max_parts;
@@ -210,6 +218,9 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value, int32_t src
   a.num_kv_heads = cache->num_kv_heads;
   a.head_dim = cache->head_dim;
   a.block_size = cache->block_size;
+  a.num_slots = static_cast<int64_t>(cache->num_blocks) * cache->block_size;
+  a.debug = PA_DEBUG ? pa::debug_words() : nullptr;
+  if (PA_DEBUG && !a.debug) return PA_ERR_HIP;
   a.k_scale = cache->k_scale;
   a.v_scale = cache->v_scale;
   const hipError_t e = pa::launch_reshape_and_cache(src_dtype, cache->kv_dtype, a,
@@ -394,6 +405,17 @@ pa_status_t pa_preferred_block_size(int32_t head_dim, int32_t kv_dtype, int32_t 
   // over two 16-byte runs), and 16 leads for fp8 at group 1.
   *block_size = (kv_dtype == PA_FP8_E4M3 && group >= 2) ? 32 : 16;
   return PA_OK;
+}
+
+pa_status_t pa_debug_check(int32_t* code, int32_t* index, void* stream) {
+  if (!code || !index) return PA_ERR_NULL;
+  if (!PA_DEBUG) {
+    *code = -1;
+    *index = -1;
+    return PA_ERR_UNSUPPORTED;
+  }
+  if (pa::read_debug_words(code, index, static_cast<hipStream_t>(stream)) != hipSuccess) return PA_ERR_HIP;
+  return *code == pa::kDebugNone ? PA_OK : PA_ERR_METADATA;
 }
 
 pa_status_t pa_set_attention_events(void* before, void* after) {

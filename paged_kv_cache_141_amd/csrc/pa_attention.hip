@@ -54,6 +54,30 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
     if (i < a.num_seqs) {
       L = min(a.seq_lens[i], a.max_seq_len);
       ql = a.qsl[i + 1] - a.qsl[i];
+#if PA_DEBUG
+      // debug build: a sequence whose metadata breaks the contract is
+      // recorded and skipped (no work items)
+      {
+        const int Lraw = a.seq_lens[i];
+        int code = kDebugNone;
+        if (ql < 0 || (i == 0 && a.qsl[0] != 0) || (i == a.num_seqs - 1 && a.qsl[a.num_seqs] != a.num_tokens))
+          code = kDebugQueryStart;
+        else if (Lraw < 0 || Lraw > a.max_seq_len) code = kDebugSeqLen;
+        else if (ql > Lraw) code = kDebugQueryLen;
+        else if (ql > a.max_query_len) code = kDebugMaxQuery;
+        else {
+          const int nb = (L + a.block_size - 1) / a.block_size;
+          if (nb > a.max_blocks_per_seq) code = kDebugBlockId;
+          const int32_t* row = a.block_tables + static_cast<int64_t>(i) * a.max_blocks_per_seq;
+          for (int j = 0; j < nb && code == kDebugNone; ++j)
+            if (row[j] < 0 || row[j] >= a.num_blocks) code = kDebugBlockId;
+        }
+        if (code != kDebugNone) {
+          debug_record(a.debug, code, i);
+          ql = 0;
+        }
+      }
+#endif
       const int rows = ql * G;
       const int own = L - a.prefix_len;                   // keys past the shared prefix
       if (ql > 0 && own > 0) {
@@ -249,6 +273,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
   const int np = (a.prefix_len > 0 ? a.prefix_parts : 0) +
                  (own >= 0 ? own / (is_chunk_seq(a, ql * a.group) ? a.chunk_partition : a.partition) + 1 : 0);
   if (np <= 1 && a.prefix_len == 0) return;
+  const int nparts = min(np, a.max_parts);   // equal for metadata within the contract
   // head groups blockIdx.y, + gridDim.y, ... (one per workgroup, or all of
   // them in one workgroup when the step has many tokens)
   const int d0 = (threadIdx.x % LPH) * 4;
@@ -264,12 +289,12 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
     float M = -__builtin_inff();
     float den = 0.f;
     f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int p0 = 0; p0 < np; p0 += PG) {
+    for (int p0 = 0; p0 < nparts; p0 += PG) {
       float mv[PG], lv[PG];
       f32x4 av[PG];
 #pragma unroll
       for (int j = 0; j < PG; ++j) {
-        const bool in = p0 + j < np;
+        const bool in = p0 + j < nparts;
         mv[j] = in ? a.part_m[row + p0 + j] : -__builtin_inff();
         lv[j] = in ? a.part_l[row + p0 + j] : 0.f;
         av[j] = in ? *reinterpret_cast<const f32x4*>(a.part_acc + (row + p0 + j) * D + d0)

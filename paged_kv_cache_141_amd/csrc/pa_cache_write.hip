@@ -3,9 +3,16 @@
 // Runner V2", section "Redesign 4": a flat per-token slot index; slot s is
 // offset s % B of physical block s / B, the itwiki "vLLM" article, section
 // "PagedAttention", "Block table").
+#include <mutex>
+
 #include "pa_device.h"
 
 namespace pa {
+
+#if PA_DEBUG
+// The debug words of one device: the first violation's code and index.
+static __device__ int32_t g_debug_words[2] = {0, 0};
+#endif
 
 // 8 consecutive source elements -> fp32 (exact widening).
 template <int SRC>
@@ -63,13 +70,25 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a
   const int chunks = d / 8;
   // pass 2 reads the slots from LDS; pass 1 reads its own, so that its source
   // loads need not wait for a barrier
-  if (threadIdx.x < kWriteTokens) sslot[threadIdx.x] = static_cast<int>(threadIdx.x) < nt ? a.slots[t0 + threadIdx.x] : -1;
+  if (threadIdx.x < kWriteTokens) {
+    int64_t s = static_cast<int>(threadIdx.x) < nt ? a.slots[t0 + threadIdx.x] : -1;
+#if PA_DEBUG
+    if (s >= a.num_slots) {                              // past the pool: recorded and skipped
+      if (h == 0) debug_record(a.debug, kDebugSlot, t0 + static_cast<int>(threadIdx.x));
+      s = -1;
+    }
+#endif
+    sslot[threadIdx.x] = s;
+  }
 
   for (int x = threadIdx.x; x < nt * chunks; x += 256) {
     const int tt = x / chunks;
     const int c = x - tt * chunks;
     const int64_t s = a.slots[t0 + tt];
     if (s < 0) continue;
+#if PA_DEBUG
+    if (s >= a.num_slots) continue;                      // recorded by pass 2's slot load
+#endif
     const int64_t blk = s / a.block_size;
     const int off = static_cast<int>(s - blk * a.block_size);
     const int64_t src_off = ((static_cast<int64_t>(t0 + tt) * a.num_kv_heads + h) * d + 8 * c) * EBS;
@@ -142,6 +161,47 @@ static hipError_t launch_rc_kv(int kv, const CacheWriteArgs& a, hipStream_t stre
     case DT_FP8: return launch_rc<SRC, DT_FP8>(a, stream);
   }
   return hipErrorInvalidValue;
+}
+
+int32_t* debug_words() {
+#if PA_DEBUG
+  static std::mutex lock;
+  static int32_t* addr[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> hold(lock);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_debug_words)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    addr[dev] = static_cast<int32_t*>(p);
+  }
+  return addr[dev];
+#else
+  return nullptr;
+#endif
+}
+
+hipError_t read_debug_words(int32_t* code, int32_t* index, hipStream_t stream) {
+#if PA_DEBUG
+  int32_t* words = debug_words();
+  if (!words) return hipErrorInvalidSymbol;
+  int32_t w[2] = {0, 0};
+  const int32_t zero[2] = {0, 0};
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e == hipSuccess) e = hipMemcpy(w, words, sizeof(w), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(words, zero, sizeof(zero), hipMemcpyHostToDevice);
+  *code = w[0];
+  *index = w[1];
+  return e;
+#else
+  (void)stream;
+  *code = -1;
+  *index = -1;
+  return hipErrorNotSupported;
+#endif
 }
 
 hipError_t launch_reshape_and_cache(int src, int kv, const CacheWriteArgs& a, hipStream_t stream) {

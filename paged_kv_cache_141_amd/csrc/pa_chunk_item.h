@@ -296,7 +296,17 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
         // used), so tile loads need no clamp
         const int32_t* bt = a.block_tables + static_cast<int64_t>(i) * a.max_blocks_per_seq + jbase;
         const int nb = min(nblk - jbase, cpart / BS);
-        for (int j = tid; j < cpart / BS; j += kChunkThreads) btl[j] = bt[min(j, nb - 1)];
+        for (int j = tid; j < cpart / BS; j += kChunkThreads) {
+          int id = bt[min(j, nb - 1)];
+#if PA_DEBUG
+          // debug build: an id outside the pool is recorded and replaced by block 0
+          if (id < 0 || id >= a.num_blocks) {
+            debug_record(a.debug, kDebugBlockId, i);
+            id = 0;
+          }
+#endif
+          btl[j] = id;
+        }
       }
       __syncthreads();
       const uint8_t* kc = static_cast<const uint8_t*>(a.k_cache) + h * tile_bytes;

@@ -43,6 +43,13 @@ struct PartTable {
     lo = lane < nbt ? bt[lane] : 0;
     hi = lane + 64 < nbt ? bt[lane + 64] : 0;
   }
+#if PA_DEBUG
+  // debug build: an id outside the pool is recorded and replaced by block 0
+  __device__ __forceinline__ void check(const AttnArgs& a, int seq) {
+    if (lo < 0 || lo >= a.num_blocks) { debug_record(a.debug, kDebugBlockId, seq); lo = 0; }
+    if (hi < 0 || hi >= a.num_blocks) { debug_record(a.debug, kDebugBlockId, seq); hi = 0; }
+  }
+#endif
   __device__ __forceinline__ int64_t operator[](int j) const {   // j wave-uniform
     const int a = __builtin_amdgcn_readlane(lo, j & 63);
     const int b = __builtin_amdgcn_readlane(hi, j & 63);
@@ -119,6 +126,9 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   const int nbt = min(nblk - jbase, a.partition / BS);
   PartTable btv;
   btv.load(a.block_tables + static_cast<int64_t>(i) * a.max_blocks_per_seq + jbase, nbt, lane);
+#if PA_DEBUG
+  btv.check(a, i);
+#endif
 
   // per-lane key offsets inside a 32-key step
   const int kkey0 = 8 * (r >> 2) + (r & 3);      // sub-tile 0; sub-tile 1 adds 4

@@ -245,6 +245,15 @@ __device__ __forceinline__ float max_log2(float m, float c) { return m == -__bui
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+#if PA_DEBUG
+// Debug build: record a violation in the debug words ([0] the first
+// violation's code, 0 for none; [1] its sequence or token) unless one is
+// recorded already (the code word is taken with a compare-and-swap from 0).
+__device__ __forceinline__ void debug_record(int32_t* words, int32_t code, int32_t index) {
+  if (atomicCAS(&words[0], 0, code) == 0) atomicExch(&words[1], index);
+}
+#endif
+
 // Host-side dispatch of a runtime (q dtype, kv dtype, head dim, block size)
 // to f(ct, kv, d, bs), each an std::integral_constant, for the combinations
 // the kernels are built for; others give hipErrorInvalidValue.

@@ -6,9 +6,30 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "pa.h"
 
 namespace pa {
+
+// Debug build (-DPA_DEBUG=1, libpa_debug.so): the plan kernel checks every
+// sequence's metadata and the cache write every slot before using them; the
+// first violation is recorded in a device word pair (code, index) that
+// pa_debug_check reads back, and the offending sequence or token is
+// skipped, so no kernel reads or writes outside its buffers.  Release
+// builds treat such metadata as undefined behaviour and check nothing.
+#ifndef PA_DEBUG
+#define PA_DEBUG 0
+#endif
+enum DebugCode : int32_t {
+  kDebugNone = 0,
+  kDebugQueryStart = 1,   // query_start_loc does not start at 0, end at num_tokens, or decreases
+  kDebugQueryLen = 2,     // q_len > L
+  kDebugSeqLen = 3,       // L > max_seq_len (or L < 0)
+  kDebugMaxQuery = 4,     // q_len > max_query_len
+  kDebugBlockId = 5,      // ceil(L/B) > max_blocks_per_seq, or a used block id outside [0, num_blocks)
+  kDebugSlot = 6,         // a cache-write slot >= num_blocks * B
+};
 
 // Rows of one attention work item: a 16-row MFMA tile of (query token,
 // q head) pairs of one sequence and kv head.
@@ -154,7 +175,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr int64_t kPrefixItems = PA_PREFIX_ITEMS;
 inline int32_t prefix_partition(int64_t prefix_len, int64_t num_tokens, int64_t group, int64_t num_kv_heads,
                                 int64_t chunk_rows) {
-  const int64_t units = ceil_div(num_tokens * group, chunk_rows) * num_kv_heads;
+  // (row blocks x kv heads; at least 1, so that an empty step sizes too)
+  const int64_t units = std::max<int64_t>(1, ceil_div(num_tokens * group, chunk_rows) * num_kv_heads);
   int64_t parts = kPrefixItems / units > 1 ? kPrefixItems / units : 1;
   const int64_t most = ceil_div(prefix_len, 256);
   parts = parts < most ? parts : most;
@@ -198,6 +220,8 @@ struct CacheWriteArgs {
   void* v_cache;
   const int64_t* slots;
   int32_t num_tokens, num_kv_heads, head_dim, block_size;
+  int64_t num_slots;   // num_blocks * block_size (the debug build checks slots against it)
+  int32_t* debug;      // debug build: the device's debug words (null in release builds)
   float k_scale, v_scale;
 };
 
@@ -227,6 +251,9 @@ struct AttnArgs {
   // block-table, pool, partial and item access stays inside the buffers the
   // bound sized.
   int32_t max_seq_len;
+  int32_t num_blocks;   // pool size N (the debug build checks block ids against it)
+  int32_t block_size;
+  int32_t* debug;       // debug build: the device's debug words (null in release builds)
   int32_t max_parts;
   int32_t partition;   // decode partition length in keys (decode_partition)
   // Shared prefix (cascade): every sequence's first prefix_len keys are the
@@ -318,6 +345,12 @@ int attention_entry(const void* q, int32_t q_dtype, const void* k_cache, const v
 
 hipError_t launch_reshape_and_cache(int src_dtype, int kv_dtype, const CacheWriteArgs& a,
                                     hipStream_t stream);   // (pa_cache_write.hip)
+// Debug build: the current device's debug words (a static device pair,
+// looked up once per device; null in release builds or if the lookup
+// fails), and a synchronous read-and-clear of them after the stream has
+// drained.  (pa_cache_write.hip)
+int32_t* debug_words();
+hipError_t read_debug_words(int32_t* code, int32_t* index, hipStream_t stream);
 hipError_t launch_copy_blocks(const BlockCopyArgs& a, hipStream_t stream);   // (pa_blocks.hip)
 hipError_t launch_table_writes(const TableWriteArgs& a, hipStream_t stream);  // (pa_metadata.hip)
 hipError_t launch_prepare_step(const StepArgs& a, hipStream_t stream);        // (pa_metadata.hip)

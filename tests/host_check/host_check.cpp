@@ -1,0 +1,265 @@
+// host_check.cpp -- the host validation layer of the C ABI (pa_api.hip and
+// pa_noalloc.hip: argument checks, workspace sizing, the launch arguments it
+// builds) compiled with AddressSanitizer and UndefinedBehaviorSanitizer and
+// linked against stub launchers instead of the kernels.  Every entry point
+// is driven with valid and invalid arguments, extremes included; each call
+// that reaches a stub must hand it buffers that fit what the caller passed.
+// Runs on the CPU; no device memory is touched (the pointers are never
+// dereferenced).  Exit status 0 when every check holds.
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <limits>
+#include <random>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+int g_fail = 0;
+#define CHECK(cond)                                                   \
+  do {                                                                \
+    if (!(cond)) {                                                    \
+      fprintf(stderr, "%s:%d: check failed: %s\n", __FILE__, __LINE__, #cond); \
+      ++g_fail;                                                       \
+    }                                                                 \
+  } while (0)
+
+pa::AttnArgs g_attn;
+pa::CacheWriteArgs g_write;
+int g_attn_launches = 0, g_write_launches = 0, g_other_launches = 0;
+}  // namespace
+
+// ---- stub launchers: record what the host layer would launch
+namespace pa {
+hipError_t launch_attention(int, int, int, int, const AttnArgs& a, hipStream_t, const hipEvent_t*) {
+  g_attn = a;
+  ++g_attn_launches;
+  return hipSuccess;
+}
+hipError_t launch_reshape_and_cache(int, int, const CacheWriteArgs& a, hipStream_t) {
+  g_write = a;
+  ++g_write_launches;
+  return hipSuccess;
+}
+hipError_t launch_copy_blocks(const BlockCopyArgs&, hipStream_t) { ++g_other_launches; return hipSuccess; }
+hipError_t launch_table_writes(const TableWriteArgs&, hipStream_t) { ++g_other_launches; return hipSuccess; }
+hipError_t launch_prepare_step(const StepArgs&, hipStream_t) { ++g_other_launches; return hipSuccess; }
+hipError_t launch_commit_step(const CommitArgs&, hipStream_t) { ++g_other_launches; return hipSuccess; }
+int32_t* debug_words() { return nullptr; }
+hipError_t read_debug_words(int32_t*, int32_t*, hipStream_t) { return hipErrorNotSupported; }
+}  // namespace pa
+
+namespace {
+
+void* const FAKE = reinterpret_cast<void*>(uintptr_t(1) << 40);     // 256-aligned, never dereferenced
+const int32_t* const FAKEI = static_cast<const int32_t*>(FAKE);
+
+pa_cache_t cache(int32_t N, int32_t B, int32_t H, int32_t d, int32_t dt, float ks = 1.f, float vs = 1.f) {
+  pa_cache_t c;
+  c.num_blocks = N;
+  c.block_size = B;
+  c.num_kv_heads = H;
+  c.head_dim = d;
+  c.kv_dtype = dt;
+  c.k_scale = ks;
+  c.v_scale = vs;
+  return c;
+}
+
+// The workspace regions handed to the kernels lie inside [ws, ws + bytes),
+// in order, 256-byte aligned, each as large as the launch arguments say.
+void check_layout(const pa::AttnArgs& a, uintptr_t ws, size_t bytes, int32_t d) {
+  const uintptr_t end = ws + bytes;
+  auto at = [](const void* p) { return reinterpret_cast<uintptr_t>(p); };
+  CHECK(at(a.header) == ws);
+  CHECK(at(a.items) >= ws + 64 * 4 && at(a.items) % 256 == 0);
+  CHECK(at(a.items) + static_cast<uintptr_t>(a.max_items) * 8 <= at(a.citems));
+  CHECK(at(a.citems) + static_cast<uintptr_t>(a.max_citems) * 8 <= at(a.part_m));
+  const uintptr_t rows = static_cast<uintptr_t>(a.num_tokens) * a.num_q_heads * a.max_parts;
+  CHECK(at(a.part_m) + rows * 4 <= at(a.part_l));
+  CHECK(at(a.part_l) + rows * 4 <= at(a.part_acc));
+  CHECK(at(a.part_acc) + rows * d * 4 <= end);
+  CHECK(a.max_parts >= 1 && a.partition >= 32 && a.max_seq_len >= 0);
+}
+
+pa_status_t attend(const pa_cache_t& c, int32_t q_dtype, int32_t Hq, int32_t S, int32_t T, int32_t max_seq,
+                   int32_t max_q, int32_t mbps, void* ws, size_t bytes, int32_t prefix = 0, float scale = 0.125f) {
+  if (prefix)
+    return pa_attention_shared_prefix(FAKE, q_dtype, FAKE, FAKE, &c, FAKEI, mbps, FAKEI, FAKEI, S, T, Hq, max_seq,
+                                      max_q, prefix, scale, FAKE, ws, bytes, nullptr);
+  return pa_attention(FAKE, q_dtype, FAKE, FAKE, &c, FAKEI, mbps, FAKEI, FAKEI, S, T, Hq, max_seq, max_q, scale,
+                      FAKE, ws, bytes, nullptr);
+}
+
+void argument_errors() {
+  const pa_cache_t ok = cache(16, 16, 2, 64, PA_BF16);
+  CHECK(attend(cache(16, 8, 2, 64, PA_BF16), PA_BF16, 4, 2, 2, 40, 1, 3, FAKE, 1 << 30) == PA_ERR_UNSUPPORTED);
+  CHECK(attend(cache(16, 16, 2, 96, PA_BF16), PA_BF16, 4, 2, 2, 40, 1, 3, FAKE, 1 << 30) == PA_ERR_UNSUPPORTED);
+  CHECK(attend(cache(16, 16, 2, 64, 9), PA_BF16, 4, 2, 2, 40, 1, 3, FAKE, 1 << 30) == PA_ERR_DTYPE);
+  CHECK(attend(ok, PA_F32, 4, 2, 2, 40, 1, 3, FAKE, 1 << 30) == PA_ERR_DTYPE);
+  CHECK(attend(ok, PA_BF16, 3, 2, 2, 40, 1, 3, FAKE, 1 << 30) == PA_ERR_SHAPE);
+  CHECK(attend(ok, PA_BF16, 4, 2, 2, 40, 1, 2, FAKE, 1 << 30) == PA_ERR_SHAPE);       // 2 blocks < 40 tokens
+  CHECK(attend(ok, PA_BF16, 4, 2, 2, 40, 41, 3, FAKE, 1 << 30) == PA_ERR_SHAPE);      // q bound above L bound
+  CHECK(attend(ok, PA_BF16, 4, 2, 2, 40, 1, 3, nullptr, 1 << 30) == PA_ERR_WORKSPACE);
+  CHECK(attend(ok, PA_BF16, 4, 2, 2, 40, 1, 3, static_cast<char*>(FAKE) + 16, 1 << 30) == PA_ERR_WORKSPACE);
+  CHECK(attend(ok, PA_BF16, 4, 2, 2, 40, 1, 3, FAKE, 1 << 30, 8) == PA_ERR_SHAPE);    // prefix not whole blocks
+  CHECK(attend(ok, PA_BF16, 4, -1, 2, 40, 1, 3, FAKE, 1 << 30) == PA_ERR_SHAPE);
+  CHECK(attend(ok, PA_BF16, 4, 2, 2, 40, 1, 3, FAKE, 1 << 30, 0, -1.f) == PA_ERR_UNSUPPORTED);
+  CHECK(attend(ok, PA_BF16, 4, 2, 2, 40, 1, 3, FAKE, 1 << 30, 0, std::numeric_limits<float>::quiet_NaN()) ==
+        PA_ERR_UNSUPPORTED);
+  CHECK(attend(cache(16, 16, 2, 64, PA_BF16, 2.f), PA_BF16, 4, 2, 2, 40, 1, 3, FAKE, 1 << 30) == PA_ERR_UNSUPPORTED);
+  CHECK(attend(cache(0, 16, 2, 64, PA_BF16), PA_BF16, 4, 2, 2, 40, 1, 3, FAKE, 1 << 30) == PA_ERR_SHAPE);
+  CHECK(attend(ok, PA_BF16, 4, 0, 0, 40, 1, 3, nullptr, 0) == PA_OK);                  // empty step: no-op
+  CHECK(pa_attention(nullptr, PA_BF16, FAKE, FAKE, &ok, FAKEI, 3, FAKEI, FAKEI, 2, 2, 4, 40, 1, 0.1f, FAKE, FAKE,
+                     1 << 30, nullptr) == PA_ERR_NULL);
+  size_t b = 0;
+  CHECK(pa_attention_workspace_size(nullptr, 4, 2, 2, 40, 1, &b) == PA_ERR_NULL);
+  CHECK(pa_attention_workspace_size(&ok, 4, 2, 2, 40, 1, nullptr) == PA_ERR_NULL);
+  // partials past 2^48 bytes are refused (2^20 tokens x 2^20 q heads)
+  const pa_cache_t wide = cache(16, 16, 1 << 16, 64, PA_BF16);
+  CHECK(pa_attention_workspace_size(&wide, 1 << 20, 1, 1 << 20, 4096, 1, &b) == PA_ERR_UNSUPPORTED);
+  // cache write
+  CHECK(pa_reshape_and_cache(FAKE, FAKE, 7, FAKE, FAKE, &ok, static_cast<const int64_t*>(FAKE), 4, nullptr) ==
+        PA_ERR_DTYPE);
+  CHECK(pa_reshape_and_cache(FAKE, FAKE, PA_BF16, FAKE, FAKE, &ok, static_cast<const int64_t*>(FAKE), -1, nullptr) ==
+        PA_ERR_SHAPE);
+  CHECK(pa_reshape_and_cache(nullptr, FAKE, PA_BF16, FAKE, FAKE, &ok, static_cast<const int64_t*>(FAKE), 4,
+                             nullptr) == PA_ERR_NULL);
+  // block copies: a pointer the runtime does not know is refused before any launch
+  CHECK(pa_copy_blocks(FAKE, FAKE, &ok, FAKE, FAKE, &ok, static_cast<const int64_t*>(FAKE), 1, nullptr) ==
+        PA_ERR_UNSUPPORTED);
+  const pa_cache_t other = cache(16, 32, 2, 64, PA_BF16);
+  CHECK(pa_copy_blocks(FAKE, FAKE, &ok, FAKE, FAKE, &other, static_cast<const int64_t*>(FAKE), 1, nullptr) ==
+        PA_ERR_SHAPE);
+  // metadata checker: argument errors only (a valid call copies from the device)
+  CHECK(pa_check_metadata(&ok, FAKEI, 0, FAKEI, FAKEI, 1, 1, 40, 1, nullptr, nullptr) == PA_ERR_SHAPE);
+  CHECK(pa_check_metadata(&ok, nullptr, 3, FAKEI, FAKEI, 1, 1, 40, 1, nullptr, nullptr) == PA_ERR_NULL);
+  // step inputs
+  CHECK(pa_prepare_step(FAKEI, 0, 4, FAKEI, FAKEI, FAKEI, 1, 1, 16, nullptr, nullptr, nullptr, nullptr, nullptr,
+                        nullptr) == PA_ERR_SHAPE);
+  CHECK(pa_commit_step(nullptr, 4, FAKEI, FAKEI, 1, nullptr) == PA_ERR_NULL);
+  CHECK(pa_apply_block_table_writes(nullptr, 4, 4, FAKEI, FAKEI, FAKEI, FAKEI, 1, 1, nullptr) == PA_ERR_NULL);
+  // debug record: a release build checks nothing
+  int32_t code = 0, index = 0;
+  CHECK(pa_debug_check(&code, &index, nullptr) == PA_ERR_UNSUPPORTED && code == -1 && index == -1);
+  // status strings and the version
+  for (int s = 0; s <= 9; ++s) CHECK(pa_status_string(static_cast<pa_status_t>(s)) != nullptr);
+  CHECK(strlen(pa_version()) > 0);
+  int32_t bs = 0;
+  CHECK(pa_preferred_block_size(128, PA_FP8_E4M3, PA_BF16, 4, &bs) == PA_OK && bs == 32);
+  CHECK(pa_preferred_block_size(128, PA_BF16, PA_BF16, 4, &bs) == PA_OK && bs == 16);
+  CHECK(pa_preferred_block_size(128, PA_BF16, PA_BF16, 0, &bs) == PA_ERR_SHAPE);
+  CHECK(pa_preferred_block_size(std::numeric_limits<int32_t>::min(), PA_BF16, PA_BF16, 1, &bs) == PA_ERR_UNSUPPORTED);
+}
+
+// Valid calls reach the stub with a workspace layout inside the caller's
+// buffer; one byte less is refused.
+void valid_calls() {
+  const int32_t dts[][2] = {{PA_BF16, PA_BF16}, {PA_F16, PA_FP8_E4M3}, {PA_F32, PA_F32}, {PA_BF16, PA_FP8_E4M3}};
+  for (auto& dt : dts) {
+    for (int32_t d : {64, 128, 256}) {
+      if (d == 256 && dt[0] == PA_F32) continue;
+      const float sc = dt[1] == PA_FP8_E4M3 ? 0.03125f : 1.f;
+      const pa_cache_t c = cache(1000, 16, 8, d, dt[1], sc, sc);
+      for (int32_t max_seq : {1, 17, 2048, 9216, 131072}) {
+        const int32_t S = 64, T = 64 + 1024, Hq = 32, max_q = max_seq < 1024 ? max_seq : 1024;
+        const int32_t mbps = (max_seq + 15) / 16;
+        size_t need = 0;
+        CHECK(pa_attention_workspace_size(&c, Hq, S, T, max_seq, max_q, &need) == PA_OK);
+        const int before = g_attn_launches;
+        CHECK(attend(c, dt[0], Hq, S, T, max_seq, max_q, mbps, FAKE, need) == PA_OK);
+        CHECK(g_attn_launches == before + 1);
+        check_layout(g_attn, reinterpret_cast<uintptr_t>(FAKE), need, d);
+        CHECK(g_attn.max_seq_len == max_seq && g_attn.num_blocks == 1000 && g_attn.block_size == 16);
+        CHECK(attend(c, dt[0], Hq, S, T, max_seq, max_q, mbps, FAKE, need - 1) == PA_ERR_WORKSPACE);
+        // shared prefix of whole blocks
+        if (dt[0] != PA_F32 && max_seq >= 2048) {
+          CHECK(pa_attention_shared_prefix_workspace_size(&c, Hq, S, T, max_seq, max_q, 1024, &need) == PA_OK);
+          CHECK(attend(c, dt[0], Hq, S, T, max_seq, max_q, mbps, FAKE, need, 1024) == PA_OK);
+          check_layout(g_attn, reinterpret_cast<uintptr_t>(FAKE), need, d);
+          CHECK(g_attn.prefix_parts >= 1 && g_attn.max_parts > g_attn.prefix_parts);
+        }
+      }
+    }
+  }
+  // the cache write hands the stub the pool geometry
+  const pa_cache_t c = cache(77, 32, 4, 128, PA_FP8_E4M3, 0.5f, 0.25f);
+  CHECK(pa_reshape_and_cache(FAKE, FAKE, PA_BF16, FAKE, FAKE, &c, static_cast<const int64_t*>(FAKE), 9, nullptr) ==
+        PA_OK);
+  CHECK(g_write_launches == 1 && g_write.num_slots == 77 * 32 && g_write.num_tokens == 9 &&
+        g_write.k_scale == 0.5f && g_write.v_scale == 0.25f);
+  // step inputs and commit reach their launchers
+  const int before = g_other_launches;
+  CHECK(pa_prepare_step(FAKEI, 8, 4, FAKEI, FAKEI, FAKEI, 2, 3, 16, static_cast<int32_t*>(FAKE),
+                        static_cast<int32_t*>(FAKE), static_cast<int64_t*>(FAKE), static_cast<int64_t*>(FAKE),
+                        static_cast<int32_t*>(FAKE), nullptr) == PA_OK);
+  CHECK(pa_commit_step(static_cast<int32_t*>(FAKE), 8, FAKEI, FAKEI, 2, nullptr) == PA_OK);
+  CHECK(g_other_launches == before + 2);
+}
+
+// Random sizes, extremes included: every call either fails validation or
+// reaches the stub with a layout that fits the size the library asked for
+// (and the size arithmetic never overflows: UBSan checks the signed part).
+void random_sizes() {
+  std::mt19937_64 rng(141);
+  const int32_t big = std::numeric_limits<int32_t>::max();
+  const int32_t picks[] = {-1, 0, 1, 2, 15, 16, 17, 63, 64, 65, 1000, 4096, 65535, 65536, 1 << 20, big - 1, big};
+  auto pick = [&]() { return picks[rng() % (sizeof(picks) / sizeof(picks[0]))]; };
+  int reached = 0;
+  for (int it = 0; it < 20000; ++it) {
+    const int32_t H = (rng() % 3 == 0) ? pick() : int32_t(1 + rng() % 16);
+    const int64_t hq = int64_t(H) * int64_t(1 + rng() % 8);
+    const int32_t Hq = (rng() % 3 == 0) ? pick() : int32_t(hq < big ? hq : big);
+    const int32_t d = (rng() % 4 == 0) ? pick() : (rng() % 2 ? 128 : 64);
+    const int32_t B = (rng() % 4 == 0) ? pick() : (16 << (rng() % 3));
+    const pa_cache_t c = cache((rng() % 4 == 0) ? pick() : 5000, B, H, d, PA_BF16);
+    const int32_t S = (rng() % 2) ? pick() : int32_t(rng() % 300);
+    const int32_t T = (rng() % 2) ? pick() : int32_t(rng() % 5000);
+    const int32_t max_seq = (rng() % 2) ? pick() : int32_t(rng() % 200000);
+    const int32_t max_q = (rng() % 2) ? pick() : int32_t(rng() % 5000);
+    const int32_t prefix = (rng() % 4 == 0) ? 16 * int32_t(rng() % 100) : 0;
+    size_t need = 0;
+    const pa_status_t st = prefix ? pa_attention_shared_prefix_workspace_size(&c, Hq, S, T, max_seq, max_q, prefix, &need)
+                                  : pa_attention_workspace_size(&c, Hq, S, T, max_seq, max_q, &need);
+    if (st != PA_OK) continue;
+    CHECK(need >= 256 && need < (size_t(1) << 52));
+    const int32_t mbps = B > 0 ? int32_t((int64_t(max_seq) + B - 1) / B) : 1;
+    const int before = g_attn_launches;
+    const pa_status_t at = attend(c, PA_BF16, Hq, S, T, max_seq, max_q, mbps > 0 ? mbps : 1, FAKE, need, prefix);
+    if (S == 0 || T == 0) {
+      CHECK(at == PA_OK && g_attn_launches == before);
+      continue;
+    }
+    CHECK(at == PA_OK);
+    if (at == PA_OK && g_attn_launches == before + 1) {
+      check_layout(g_attn, reinterpret_cast<uintptr_t>(FAKE), need, d);
+      ++reached;
+    }
+    // the no-allocation entry point: too large, or it goes on to the device
+    // (absent here) -- never a launch without its scratch
+    const pa_status_t na = pa_attention_noalloc(FAKE, PA_BF16, FAKE, FAKE, &c, FAKEI, mbps > 0 ? mbps : 1, FAKEI, FAKEI,
+                                                S, T, Hq, max_seq, max_q, 0.125f, FAKE, nullptr);
+    if (!prefix) {
+      if (need > PA_NOALLOC_SCRATCH_BYTES) CHECK(na == PA_ERR_TOO_LARGE);
+      else CHECK(na == PA_ERR_HIP || na == PA_OK);   // no device here: the scratch lookup fails
+    }
+  }
+  CHECK(reached > 100);
+  fprintf(stderr, "random sizes: %d calls reached the launcher\n", reached);
+}
+
+}  // namespace
+
+int main() {
+  argument_errors();
+  valid_calls();
+  random_sizes();
+  if (g_fail) {
+    fprintf(stderr, "host_check: %d checks failed\n", g_fail);
+    return 1;
+  }
+  printf("host_check: all checks passed\n");
+  return 0;
+}
