@@ -7,6 +7,7 @@ Always recompiles.  Cross-compiles for gfx950 on a host without a GPU.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -41,14 +42,39 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+
+
+def _scratch_kernels(stderr: str):
+    """Kernels whose resource remarks report scratch (spilled registers or a
+    stack): (name, bytes per lane)."""
+    out, name = [], None
+    for line in stderr.splitlines():
+        m = re.search(r"remark:\s+Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
+    noise = ("is not a recognized feature for this target", "remark:")
+    err = "\n".join(l for l in (r.stderr or "").splitlines() if not any(n in l for n in noise))
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}): {' '.join(cmd)}\n{err}")
+    # No kernel may spill: every kernel is sized to keep its state in
+    # registers, and a spilling build of a persistent decode kernel (head dim
+    # 256 at half a SIMD's registers) once took the GPU down.
+    spilled = _scratch_kernels(r.stderr or "") if RESOURCE_REMARKS in cmd else []
+    if spilled:
+        raise RuntimeError("kernels use scratch memory (register spills): " +
+                           ", ".join(f"{n} ({b} B/lane)" for n, b in spilled))
     if err.strip() and verbose:
         print(err, file=sys.stderr)
 
@@ -63,7 +89,7 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     common = [hipcc(), *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"),
               "-I", CSRC]
     objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
-    jobs = [[*common, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    jobs = [[*common, RESOURCE_REMARKS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with ThreadPoolExecutor(workers) as pool:
         list(pool.map(lambda c: _run(c, verbose), jobs))
