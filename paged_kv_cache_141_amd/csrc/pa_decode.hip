@@ -15,7 +15,9 @@ namespace pa {
 template <int CT, int KV, int D, int BS>
 __global__ __launch_bounds__(64, PA_DECODE_WAVES_PER_SIMD) void attn_kernel(AttnArgs a) {
   constexpr bool STREAM = true;
-  decode_items<CT, KV, D, BS, PA_DECODE_PREFETCH, STREAM>(a, threadIdx.x, blockIdx.x, gridDim.x);
+  // fp8 at head dim 256: two steps in flight (a deeper ring does not fit the registers)
+  constexpr int PF8 = D == 256 ? 2 : PA_DECODE_PREFETCH_FP8;
+  decode_items<CT, KV, D, BS, PA_DECODE_PREFETCH, PF8, STREAM>(a, threadIdx.x, blockIdx.x, gridDim.x);
 }
 
 // One wave per resident slot (the persistent grid); each loops over work

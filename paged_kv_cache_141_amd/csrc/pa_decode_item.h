@@ -68,7 +68,7 @@ struct PartTable {
 // eight consecutive keys 8*lg .. 8*lg+7, exactly the K slots the PV product
 // O^T = V^T * P^T needs from P^T, and V^T's rows (dims) are contiguous over
 // keys in the [d][B] tile, so both MFMA operands load straight from memory.
-template <int CT, int KV, int D, int BS, int PF16, bool STREAM>
+template <int CT, int KV, int D, int BS, int PF16, int PF8, bool STREAM>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, int part, int h,
                                           int lane) {
   constexpr int EBQ = Bytes<CT>::v;
@@ -219,7 +219,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
 
   // Software pipeline: the loads of step s + PF are in flight while step s
   // computes (PF16 steps for 16-bit caches).
-  constexpr int PF = (KV == DT_FP8) ? PA_DECODE_PREFETCH_FP8 : (KV == DT_F32 ? 0 : PF16);
+  constexpr int PF = (KV == DT_FP8) ? PF8 : (KV == DT_F32 ? 0 : PF16);
   // 64-key blocks: a step reads half of each 128-byte V^T row, so the V loads
   // of a block's two steps go out together (with the first step's K), and
   // whole rows are read at once.  That takes one more step buffer: the second
@@ -286,7 +286,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
 // not held up by a queue of atomics on one counter.  After that the wave
 // draws item base + k from the counter, and returns once it passes the
 // item count.
-template <int CT, int KV, int D, int BS, int PF16, bool STREAM>
+template <int CT, int KV, int D, int BS, int PF16, int PF8, bool STREAM>
 __device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int first, int base) {
   const int64_t total = static_cast<int64_t>(uniform(a.header[1])) * a.num_kv_heads;
   int w = first;
@@ -309,7 +309,7 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int fi
     // half to the next step measured 1.5x slower with it (B 64: 1,080 against
     // 733 us for the LLaMA-7B decode kernel at B 16)
     // (tile, partition) are the unsigned 16-bit halves of tp: tiles reach 0xFFFF
-    attn_item<CT, KV, D, BS, PFD, STREAM && (BS <= 32 || PA_DECODE_NT_B64)>(
+    attn_item<CT, KV, D, BS, PFD, PF8, STREAM && (BS <= 32 || PA_DECODE_NT_B64)>(
         a, i, static_cast<int>(static_cast<uint32_t>(tp) >> 16), tp & 0xFFFF, h, lane);
     w = -1;
   }

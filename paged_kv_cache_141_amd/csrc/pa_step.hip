@@ -22,6 +22,7 @@ namespace pa {
 #define PA_STEP_DECODE_PREFETCH 1
 #endif
 constexpr int kStepDecodePrefetch = PA_STEP_DECODE_PREFETCH;
+constexpr int kStepDecodePrefetchFp8 = 2;   // fp8 steps are half the bytes: two fit the same registers
 
 template <int CT, int KV, int D, int BS>
 __global__ __launch_bounds__(kChunkThreads, kChunkWavesPerSimd) void step_kernel(AttnArgs a) {
@@ -31,10 +32,12 @@ __global__ __launch_bounds__(kChunkThreads, kChunkWavesPerSimd) void step_kernel
   const int nchunk = static_cast<int>(gridDim.x) - ndec;
   if (g >= ndec) {
     chunk_items<CT, KV, D, BS, kChunkPartitionFused>(a, g - ndec, nchunk, false);
-    decode_items<CT, KV, D, BS, kStepDecodePrefetch, true>(a, threadIdx.x & 63, -1, ndec * kChunkWaves);
+    decode_items<CT, KV, D, BS, kStepDecodePrefetch, kStepDecodePrefetchFp8, true>(a, threadIdx.x & 63, -1,
+                                                                                  ndec * kChunkWaves);
   } else {
-    decode_items<CT, KV, D, BS, kStepDecodePrefetch, true>(a, threadIdx.x & 63, g * kChunkWaves + wave,
-                                                           ndec * kChunkWaves);
+    decode_items<CT, KV, D, BS, kStepDecodePrefetch, kStepDecodePrefetchFp8, true>(a, threadIdx.x & 63,
+                                                                                  g * kChunkWaves + wave,
+                                                                                  ndec * kChunkWaves);
   }
 }
 
