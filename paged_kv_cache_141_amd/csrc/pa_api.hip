@@ -53,17 +53,19 @@ pa_status_t check_attention_sizes(const pa_cache_t* c, int32_t num_q_heads, int3
     return PA_ERR_SHAPE;
   if (num_q_heads % c->num_kv_heads != 0) return PA_ERR_SHAPE;
   if (max_query_len > max_seq_len) return PA_ERR_SHAPE;
+  // every token belongs to a sequence with at most max_query_len of them
+  if (static_cast<int64_t>(num_tokens) > static_cast<int64_t>(num_seqs) * max_query_len) return PA_ERR_SHAPE;
   const int64_t group = num_q_heads / c->num_kv_heads;
   // work items pack (tile, partition) into 16 bits each
   if (ceil_div(static_cast<int64_t>(max_query_len) * group, pa::kTileRows) > 0xFFFF) return PA_ERR_UNSUPPORTED;
   const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, c->num_kv_heads,
-                                                     c->head_dim, max_seq_len);
+                                                     c->head_dim, max_seq_len, max_query_len,
+                                                     c->kv_dtype != PA_F32);
   if (ceil_div(max_seq_len, w.partition) > 0xFFFF) return PA_ERR_UNSUPPORTED;
   if (w.max_items > 0x7FFFFFFF / 64 || w.max_citems > 0x7FFFFFFF / 64) return PA_ERR_UNSUPPORTED;
-  // the partials' size, recomputed without wrap-around: at most 2^48 bytes
-  // (the layout's own size_t arithmetic is exact below that)
-  const double rows = static_cast<double>(num_tokens) * num_q_heads * w.max_parts;
-  if (rows * (c->head_dim + 2) * 4.0 > 281474976710656.0) return PA_ERR_UNSUPPORTED;
+  // the partials' size (the layout computes it without wrap-around): at most 2^48 bytes
+  if (w.part_rows < 0 || static_cast<double>(w.part_rows) * (c->head_dim + 2) * 4.0 > 281474976710656.0)
+    return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
@@ -123,7 +125,8 @@ int attention_entry(const void* q, int32_t q_dtype, const void* k_cache, const v
                                      static_cast<int64_t>(max_seq_len))
     return PA_ERR_SHAPE;
   const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, cache->num_kv_heads,
-                                                     cache->head_dim, max_seq_len, prefix_len);
+                                                     cache->head_dim, max_seq_len, max_query_len,
+                                                     q_dtype != PA_F32, prefix_len);
   if (required) {   // the caller sizes (or supplies) the workspace once it knows the need
     *required = w.total;
     return PA_OK;
@@ -161,7 +164,10 @@ int attention_entry(const void* q, int32_t q_dtype, const void* k_cache, const v
   if (PA_DEBUG && !a.debug) return PA_ERR_HIP;
   a.num_kv_heads = cache->num_kv_heads;
   a.group = num_q_heads / cache->num_kv_heads;
-  a.max_parts = w.max_parts;
+  a.dec_parts = w.dec_parts;
+  a.chunk_parts = w.chunk_parts;
+  a.dec_per_seq = w.dec_per_seq;
+  a.chunk_row_base = w.chunk_row_base;
   a.partition = w.partition;
   a.prefix_len = prefix_len;
   a.prefix_part = w.prefix_part;
@@ -341,7 +347,7 @@ pa_status_t pa_attention_workspace_size(const pa_cache_t* cache, int32_t num_q_h
   pa_status_t st = check_attention_sizes(cache, num_q_heads, num_seqs, num_tokens, max_seq_len, max_query_len);
   if (st != PA_OK) return st;
   *bytes = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, cache->num_kv_heads, cache->head_dim,
-                                max_seq_len)
+                                max_seq_len, max_query_len, cache->kv_dtype != PA_F32)
                .total;
   return PA_OK;
 }
@@ -354,7 +360,7 @@ pa_status_t pa_attention_shared_prefix_workspace_size(const pa_cache_t* cache, i
   if (st != PA_OK) return st;
   if (prefix_len < 0 || (cache && prefix_len % cache->block_size != 0) || prefix_len > max_seq_len) return PA_ERR_SHAPE;
   *bytes = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, cache->num_kv_heads, cache->head_dim,
-                                max_seq_len, prefix_len)
+                                max_seq_len, max_query_len, cache->kv_dtype != PA_F32, prefix_len)
                .total;
   return PA_OK;
 }

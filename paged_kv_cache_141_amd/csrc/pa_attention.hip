@@ -270,10 +270,15 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
   const int ql = a.qsl[i + 1] - q0;
   const int row_pos = min(a.seq_lens[i], a.max_seq_len) - ql + (token - q0);
   const int own = row_pos - a.prefix_len;               // the row's keys past the shared prefix, minus one
+  const bool chunk_kind = is_chunk_seq(a, ql * a.group);
   const int np = (a.prefix_len > 0 ? a.prefix_parts : 0) +
-                 (own >= 0 ? own / (is_chunk_seq(a, ql * a.group) ? a.chunk_partition : a.partition) + 1 : 0);
+                 (own >= 0 ? own / (chunk_kind ? a.chunk_partition : a.partition) + 1 : 0);
   if (np <= 1 && a.prefix_len == 0) return;
-  const int nparts = min(np, a.max_parts);   // equal for metadata within the contract
+  // the token's partial lists (head 0; heads follow at a stride of the list length)
+  const int64_t list0 = partial_row(a, chunk_kind, i, token, token - q0, 0);
+  if (list0 < 0) return;
+  const int list_len = chunk_kind ? a.chunk_parts : a.dec_parts;
+  const int nparts = min(np, list_len);   // equal for metadata within the contract
   // head groups blockIdx.y, + gridDim.y, ... (one per workgroup, or all of
   // them in one workgroup when the step has many tokens)
   const int d0 = (threadIdx.x % LPH) * 4;
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
   for (int hg = blockIdx.y; hg < ngroups; hg += gridDim.y) {
     const int head = hg * HPB + static_cast<int>(threadIdx.x) / LPH;
     if (head >= a.num_q_heads) break;
-    const int64_t row = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts;
+    const int64_t row = list0 + static_cast<int64_t>(head) * list_len;
     // One pass over the partials, eight at a time (all their loads issued
     // together): the running max moves to the group's max and what was summed
     // so far is rescaled to it.
@@ -376,7 +381,7 @@ hipError_t launch_attention(int q, int kv, int d, int bs, const AttnArgs& a, hip
       if (ev[3] && (e = hipEventRecord(ev[3], stream)) != hipSuccess) return e;
     }
   }
-  if ((a.max_parts > 1 || a.prefix_len > 0) && a.num_tokens > 0) {
+  if ((a.dec_parts > 1 || a.chunk_parts > 1 || a.prefix_len > 0) && a.num_tokens > 0) {
     if (q == DT_F32) {
       if (d == 64) launch_reduce<DT_F32, 64>(f, stream);
       else launch_reduce<DT_F32, 128>(f, stream);

@@ -532,7 +532,18 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
             store4<CT>(op + 16 * n * EBQ, acc[rt][n][0] * inv, acc[rt][n][1] * inv, acc[rt][n][2] * inv,
                        acc[rt][n][3] * inv);
         } else {
-          const int64_t rowp = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts + pslot;
+          // the row's list: a prompt chunk's (this item's sequence), or for
+          // the prefix pass the list of the row's own sequence and kind
+          int64_t row0;
+          if (prefix) {
+            const int s = seq_of_token(a, token);
+            const int s0 = a.qsl[s];
+            row0 = partial_row(a, is_chunk_seq(a, (a.qsl[s + 1] - s0) * G), s, token, token - s0, head);
+          } else {
+            row0 = partial_row(a, true, i, token, t, head);
+          }
+          if (row0 < 0) continue;
+          const int64_t rowp = row0 + pslot;
           if (lg == 0) {
             a.part_m[rowp] = max_log2(m[rt], a.score_scale);
             a.part_l[rowp] = ltot;

@@ -268,7 +268,9 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
     for (int n = 0; n < NT; ++n)
       store4<CT>(op + 16 * n * EBQ, acc[n][0] * inv, acc[n][1] * inv, acc[n][2] * inv, acc[n][3] * inv);
   } else {
-    const int64_t rowp = (static_cast<int64_t>(token) * a.num_q_heads + head) * a.max_parts + a.prefix_parts + part;
+    const int64_t row0 = partial_row(a, false, i, token, t, head);
+    if (row0 < 0) return;
+    const int64_t rowp = row0 + a.prefix_parts + part;
     if (lg == 0) {
       a.part_m[rowp] = max_log2(m, a.score_scale);
       a.part_l[rowp] = ltot;

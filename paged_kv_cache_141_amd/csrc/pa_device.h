@@ -33,6 +33,38 @@ __device__ __forceinline__ bool is_chunk_seq(const AttnArgs& a, int rows) {
   return a.chunk_path && rows >= kChunkMinRows;
 }
 
+// First partial row of (token, q head) -- the row of sequence seq whose
+// local query index is `local` -- in the workspace's partial lists (the
+// layout of WorkspaceLayout: decode-routed rows by sequence slot or token,
+// chunk-routed rows by token after chunk_row_base); -1 where the workspace
+// holds no list for it (a chunk row in a step the hints kept chunk-free, or
+// a decode row past its sequence's slots, both outside the contract).
+__device__ __forceinline__ int64_t partial_row(const AttnArgs& a, bool chunk_kind, int seq, int token, int local,
+                                               int head) {
+  if (chunk_kind) {
+    if (a.chunk_parts == 0) return -1;
+    return a.chunk_row_base + (static_cast<int64_t>(token) * a.num_q_heads + head) * a.chunk_parts;
+  }
+  int64_t slot = token;
+  if (a.dec_per_seq > 0) {
+    if (local < 0 || local >= a.dec_per_seq) return -1;
+    slot = static_cast<int64_t>(seq) * a.dec_per_seq + local;
+  }
+  return (slot * a.num_q_heads + head) * a.dec_parts;
+}
+
+// The sequence whose query rows hold `token`: the last i with
+// query_start_loc[i] <= token (binary search, one lane at a time).
+__device__ __forceinline__ int seq_of_token(const AttnArgs& a, int token) {
+  int lo = 0, hi = a.num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.qsl[mid] <= token) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 // Eight operand elements of one lane for a K=32 MFMA step (or eight K=4
 // steps for fp32): 16 bytes for 16-bit types, 32 bytes for fp32.
 template <int CT> struct Frag { u32x4 w; };

@@ -68,8 +68,12 @@ static_assert(kPartitionShort <= kPartitionMax && kPartitionLong <= kPartitionMa
 #endif
 constexpr int64_t kLongContext = PA_LONG_CONTEXT;
 constexpr int64_t kManyPairs = PA_MANY_PAIRS;
+// Contexts of 64k keys and more take the longest partitions whatever the
+// pair count: each (sequence, kv head) still has 32 or more of them, and
+// their partials -- a row's workspace share -- halve.
+constexpr int64_t kVeryLongContext = 65536;
 inline int decode_partition(int64_t max_seq_len, int64_t num_seqs, int64_t num_kv_heads) {
-  if (num_seqs * num_kv_heads >= kManyPairs) return kPartitionMax;
+  if (num_seqs * num_kv_heads >= kManyPairs || max_seq_len >= kVeryLongContext) return kPartitionMax;
   return max_seq_len >= kLongContext ? kPartitionLong : kPartitionShort;
 }
 
@@ -149,13 +153,26 @@ struct WorkspaceLayout {
   size_t header;   // int32 [64]: [0]/[1] decode work counter/count, [2]/[3] chunk's, [4] prefix pass's
   size_t items;    // int32x2 [max_items]: decode items (seq, tile << 16 | partition; unsigned halves)
   size_t citems;   // int32x2 [max_citems]: chunk items (seq, row block << 16 | partition)
-  size_t part_m;   // float [T][Hq][MP]: running max (log2 units) per partition
-  size_t part_l;   // float [T][Hq][MP]: softmax denominator per partition
-  size_t part_acc; // float [T][Hq][MP][d]: un-normalised output per partition
+  size_t part_m;   // float [rows]: running max (log2 units) per partition
+  size_t part_l;   // float [rows]: softmax denominator per partition
+  size_t part_acc; // float [rows][d]: un-normalised output per partition
   size_t total;
   int64_t max_items;
   int64_t max_citems;
-  int32_t max_parts;
+  // Partial rows.  A (token, q head) row owns dec_parts consecutive partial
+  // rows if its sequence is decode-routed, chunk_parts if chunk-routed.
+  // Decode rows sit at slot (i * dec_per_seq + local token) when dec_per_seq
+  // > 0, at the token index otherwise; chunk rows at chunk_row_base + their
+  // token index.  Two layouts, the smaller is used: one token-indexed list
+  // for both kinds (dec_parts = chunk_parts, chunk_row_base 0), or the split
+  // one, where decode rows need slots for at most S * floor(64 / G) tokens
+  // (a decode-routed sequence has q_len * G < kChunkMinRows) and only chunk
+  // rows pay for long contexts at the chunk partition length.
+  int64_t part_rows;
+  int64_t chunk_row_base;
+  int32_t dec_parts;
+  int32_t chunk_parts;   // 0: the step has no chunk rows (the hints rule them out)
+  int32_t dec_per_seq;
   int32_t partition;     // decode partition length in keys
   int32_t prefix_parts;  // partials of the shared-prefix pass (first in each row's list)
   int32_t prefix_part;   // keys per shared-prefix partition
@@ -184,9 +201,11 @@ inline int32_t prefix_partition(int64_t prefix_len, int64_t num_tokens, int64_t 
   return static_cast<int32_t>(p < 256 ? 256 : (p > kChunkPartition ? kChunkPartition : p));
 }
 
+// chunk_path: 16-bit queries (fp32 queries stay on the decode kernel);
+// max_query_len decides whether prompt chunks can occur at all.
 inline WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_tokens, int64_t num_q_heads,
                                         int64_t num_kv_heads, int64_t head_dim, int64_t max_seq_len,
-                                        int64_t prefix_len = 0) {
+                                        int64_t max_query_len, bool chunk_path, int64_t prefix_len = 0) {
   WorkspaceLayout w{};
   const int64_t group = num_kv_heads > 0 ? num_q_heads / num_kv_heads : 1;
   // keys past the shared prefix: what the decode and chunk kernels cover
@@ -200,8 +219,37 @@ inline WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_tokens, in
     w.prefix_part = prefix_partition(prefix_len, num_tokens, group, num_kv_heads, chunk_rows_for(head_dim));
     w.prefix_parts = static_cast<int32_t>(ceil_div(prefix_len, w.prefix_part));
   }
-  w.max_parts = w.prefix_parts + static_cast<int32_t>(ceil_div(own, w.partition));
-  const size_t rows = static_cast<size_t>(num_tokens) * num_q_heads * w.max_parts;
+  const int64_t dparts = w.prefix_parts + ceil_div(own, w.partition);
+  const bool chunks = chunk_path && max_query_len * group >= kChunkMinRows;
+  const int64_t cparts = chunks ? w.prefix_parts + ceil_div(own, kChunkPartition) : 0;
+  // one token-indexed list for both kinds ...
+  const int64_t mp = dparts > cparts ? dparts : cparts;
+  const double rows_shared = static_cast<double>(num_tokens) * num_q_heads * mp;
+  // ... or decode rows by (sequence, local token), chunk rows by token
+  const int64_t dq = chunk_path ? (kChunkMinRows - 1) / group : 0;
+  const double dtok = static_cast<double>(dq) * num_seqs;
+  const double rows_split = dtok * num_q_heads * dparts + (chunks ? static_cast<double>(num_tokens) * num_q_heads * cparts : 0.0);
+  // (dq >= 1: dec_per_seq = 0 means token slots, so a split layout needs one
+  // decode slot per sequence at least)
+  const bool split = chunk_path && dq >= 1 && dtok < num_tokens && rows_split < rows_shared;
+  const double rows_d = split ? rows_split : rows_shared;
+  if (rows_d > 4.0e15) {             // beyond any device (the caller's check refuses it): no layout
+    w.part_rows = -1;
+    w.total = ~size_t(0);
+    return w;
+  }
+  if (split) {
+    w.dec_per_seq = static_cast<int32_t>(dq);
+    w.dec_parts = static_cast<int32_t>(dparts);
+    w.chunk_parts = static_cast<int32_t>(cparts);
+    w.chunk_row_base = dq * num_seqs * num_q_heads * dparts;
+  } else {
+    w.dec_per_seq = 0;
+    w.dec_parts = w.chunk_parts = static_cast<int32_t>(mp);
+    w.chunk_row_base = 0;
+  }
+  w.part_rows = static_cast<int64_t>(rows_d);
+  const size_t rows = static_cast<size_t>(w.part_rows);
   size_t off = 0;
   w.header = off;   off = align256(off + 64 * sizeof(int32_t));
   w.items = off;    off = align256(off + static_cast<size_t>(w.max_items) * 2 * sizeof(int32_t));
@@ -254,7 +302,10 @@ struct AttnArgs {
   int32_t num_blocks;   // pool size N (the debug build checks block ids against it)
   int32_t block_size;
   int32_t* debug;       // debug build: the device's debug words (null in release builds)
-  int32_t max_parts;
+  // partial rows (WorkspaceLayout): decode rows' and chunk rows' counts,
+  // decode slots per sequence (0: by token), first chunk row
+  int32_t dec_parts, chunk_parts, dec_per_seq;
+  int64_t chunk_row_base;
   int32_t partition;   // decode partition length in keys (decode_partition)
   // Shared prefix (cascade): every sequence's first prefix_len keys are the
   // same blocks (sequence 0's table row is read for them) and every query row

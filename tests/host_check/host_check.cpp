@@ -77,11 +77,20 @@ void check_layout(const pa::AttnArgs& a, uintptr_t ws, size_t bytes, int32_t d) 
   CHECK(at(a.items) >= ws + 64 * 4 && at(a.items) % 256 == 0);
   CHECK(at(a.items) + static_cast<uintptr_t>(a.max_items) * 8 <= at(a.citems));
   CHECK(at(a.citems) + static_cast<uintptr_t>(a.max_citems) * 8 <= at(a.part_m));
-  const uintptr_t rows = static_cast<uintptr_t>(a.num_tokens) * a.num_q_heads * a.max_parts;
+  // every row's partial list: decode rows at most (slots) x Hq x dec_parts,
+  // then chunk rows T x Hq x chunk_parts from chunk_row_base (0 and equal
+  // lengths when one token-indexed list serves both)
+  const uintptr_t dslots = a.dec_per_seq > 0 ? uintptr_t(a.dec_per_seq) * a.num_seqs : uintptr_t(a.num_tokens);
+  const uintptr_t drows = dslots * a.num_q_heads * a.dec_parts;
+  const uintptr_t crows = uintptr_t(a.chunk_row_base) + uintptr_t(a.num_tokens) * a.num_q_heads * a.chunk_parts;
+  CHECK(a.dec_per_seq == 0 || uintptr_t(a.chunk_row_base) == drows);
+  const uintptr_t rows = drows > crows ? drows : crows;
   CHECK(at(a.part_m) + rows * 4 <= at(a.part_l));
   CHECK(at(a.part_l) + rows * 4 <= at(a.part_acc));
   CHECK(at(a.part_acc) + rows * d * 4 <= end);
-  CHECK(a.max_parts >= 1 && a.partition >= 32 && a.max_seq_len >= 0);
+  CHECK(a.dec_parts >= 1 && a.partition >= 32 && a.max_seq_len >= 0);
+  // a decode-routed sequence (q_len * G < 65) fits its slots
+  CHECK(a.dec_per_seq == 0 || int64_t(a.dec_per_seq) * a.group >= 64 / a.group * a.group);
 }
 
 pa_status_t attend(const pa_cache_t& c, int32_t q_dtype, int32_t Hq, int32_t S, int32_t T, int32_t max_seq,
@@ -119,7 +128,9 @@ void argument_errors() {
   CHECK(pa_attention_workspace_size(&ok, 4, 2, 2, 40, 1, nullptr) == PA_ERR_NULL);
   // partials past 2^48 bytes are refused (2^20 tokens x 2^20 q heads)
   const pa_cache_t wide = cache(16, 16, 1 << 16, 64, PA_BF16);
-  CHECK(pa_attention_workspace_size(&wide, 1 << 20, 1, 1 << 20, 4096, 1, &b) == PA_ERR_UNSUPPORTED);
+  CHECK(pa_attention_workspace_size(&wide, 1 << 20, 1 << 20, 1 << 20, 4096, 1, &b) == PA_ERR_UNSUPPORTED);
+  // more tokens than the sequences' query bound allows
+  CHECK(pa_attention_workspace_size(&ok, 4, 2, 5, 40, 2, &b) == PA_ERR_SHAPE);
   // cache write
   CHECK(pa_reshape_and_cache(FAKE, FAKE, 7, FAKE, FAKE, &ok, static_cast<const int64_t*>(FAKE), 4, nullptr) ==
         PA_ERR_DTYPE);
@@ -164,7 +175,8 @@ void valid_calls() {
       const float sc = dt[1] == PA_FP8_E4M3 ? 0.03125f : 1.f;
       const pa_cache_t c = cache(1000, 16, 8, d, dt[1], sc, sc);
       for (int32_t max_seq : {1, 17, 2048, 9216, 131072}) {
-        const int32_t S = 64, T = 64 + 1024, Hq = 32, max_q = max_seq < 1024 ? max_seq : 1024;
+        const int32_t S = 64, Hq = 32, max_q = max_seq < 1024 ? max_seq : 1024;
+        const int32_t T = 64 + 1024 < S * max_q ? 64 + 1024 : S * max_q;
         const int32_t mbps = (max_seq + 15) / 16;
         size_t need = 0;
         CHECK(pa_attention_workspace_size(&c, Hq, S, T, max_seq, max_q, &need) == PA_OK);
@@ -179,7 +191,7 @@ void valid_calls() {
           CHECK(pa_attention_shared_prefix_workspace_size(&c, Hq, S, T, max_seq, max_q, 1024, &need) == PA_OK);
           CHECK(attend(c, dt[0], Hq, S, T, max_seq, max_q, mbps, FAKE, need, 1024) == PA_OK);
           check_layout(g_attn, reinterpret_cast<uintptr_t>(FAKE), need, d);
-          CHECK(g_attn.prefix_parts >= 1 && g_attn.max_parts > g_attn.prefix_parts);
+          CHECK(g_attn.prefix_parts >= 1 && g_attn.dec_parts > g_attn.prefix_parts);
         }
       }
     }

@@ -181,3 +181,18 @@ def test_preferred_block_size():
     assert lib.pa_preferred_block_size(128, 9, pa.PA_BF16, 1, ctypes.byref(b)) == 3
     assert lib.pa_preferred_block_size(128, pa.PA_BF16, pa.PA_BF16, 0, ctypes.byref(b)) == 2
     assert lib.pa_preferred_block_size(128, pa.PA_BF16, pa.PA_BF16, 1, None) == 1
+
+
+def test_workspace_of_a_long_context_mixed_step():
+    # 64 sequences at 128k contexts, 4,096 query tokens (32 q / 8 kv heads):
+    # decode rows need slots for at most 64 x 16 tokens, so the partials of the
+    # long contexts are paid for per chunk token at the chunk partition only
+    lib = pa.library()
+    c = _cache(num_blocks=600000, num_kv_heads=8, head_dim=128)
+    b = ctypes.c_size_t(0)
+    assert lib.pa_attention_workspace_size(ctypes.byref(c), 32, 64, 4096, 131072, 4096, ctypes.byref(b)) == 0
+    assert b.value <= 3 * 10 ** 9
+    assert lib.pa_attention_workspace_size(ctypes.byref(c), 32, 64, 8192, 131072, 8192, ctypes.byref(b)) == 0
+    assert b.value <= 4 * 10 ** 9
+    # more tokens than num_seqs x max_query_len cannot be a valid step
+    assert lib.pa_attention_workspace_size(ctypes.byref(c), 32, 64, 4096, 131072, 8, ctypes.byref(b)) == 2

@@ -389,3 +389,27 @@ def test_attention_at_preferred_block_size(kv, q, d, G):
                      num_q_heads=4 * G, num_kv_heads=4, head_dim=d, block_size=B, kv_dtype=kv, q_dtype=q,
                      k_scale=2.0 ** -5 if fp8 else 1.0, v_scale=2.0 ** -5 if fp8 else 1.0)
     assert_close(w, gpu_out(wd.stage(w)), oracle_out(w), label=label)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_long_context_mixed_step(kv):
+    # decode rows at 20k-33k contexts beside two 512-token prompt chunks deep
+    # into 20k-token prompts: few sequences, many chunk tokens, so decode rows
+    # keep their partials in per-sequence slots and only chunk rows pay for
+    # the long contexts at the chunk partition length (the split layout)
+    sc = 2.0 ** -5 if kv == "fp8_e4m3" else 1.0
+    lens = [20000, 24000, 28000, 33000, 21000, 30500, 20480, 19999]
+    qlens = [1, 1, 1, 1, 1, 1, 512, 512]
+    w = build("long_mixed", 97, lens, qlens, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+              kv_dtype=kv, q_dtype="bf16", k_scale=sc, v_scale=sc)
+    lib = pa.library()
+    import ctypes
+    spec = pa._Cache(w.num_blocks, 16, 8, 128, pa.PA_BF16 if kv == "bf16" else pa.PA_FP8_E4M3, sc, sc)
+    split, shared = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.pa_attention_workspace_size(ctypes.byref(spec), 32, w.num_seqs, w.num_tokens, w.max_seq_len,
+                                           w.max_query_len, ctypes.byref(split)) == 0
+    say(f"long mixed {kv}: {w.num_tokens} tokens, workspace {split.value / 2 ** 20:.1f} MiB "
+        f"(token-indexed lists alone: {w.num_tokens * 32 * 17 * 520 / 2 ** 20:.1f} MiB)")
+    assert split.value < w.num_tokens * 32 * 17 * 520          # smaller than one list per token
+    got = gpu_out(wd.stage(w))
+    assert_close(w, got, oracle_out(w), label=f"long-context mixed step {kv}")
