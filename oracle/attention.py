@@ -63,16 +63,16 @@ def validate_metadata(seq_lens, query_start_loc, block_tables, num_blocks, block
 def gather_sequence(k_pool, v_pool, kv_dtype, k_scale, v_scale, table_row, L, block_size):
     """Contiguous K, V ``[L][Hkv][d]`` in float64 for one request.
 
-    Block j of the request is physical block ``table_row[j]``; K tiles are
-    ``[Hkv][B][d]`` and V tiles ``[Hkv][d][B]`` in the pools.
+    Block j of the request is physical block ``table_row[j]``; K and V tiles
+    are both ``[Hkv][B][d]`` in the pools.
     """
     nb = -(-int(L) // block_size)
     ids = np.asarray(table_row[:nb], dtype=np.int64)
     kt = k_pool[ids]                                   # [nb][Hkv][B][d]
-    vt = v_pool[ids]                                   # [nb][Hkv][d][B]
+    vt = v_pool[ids]                                   # [nb][Hkv][B][d]
     H, d = kt.shape[1], kt.shape[3]
     K = kt.transpose(0, 2, 1, 3).reshape(nb * block_size, H, d)[:L]
-    V = vt.transpose(0, 3, 1, 2).reshape(nb * block_size, H, d)[:L]
+    V = vt.transpose(0, 2, 1, 3).reshape(nb * block_size, H, d)[:L]
     K = codecs.decode(K, kv_dtype) * float(k_scale)
     V = codecs.decode(V, kv_dtype) * float(v_scale)
     return K, V
@@ -175,7 +175,7 @@ def block_sum_attention(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, seq_
                 phys = int(block_tables[i][j])
                 n_in = min(B, p + 1 - j * B)           # keys of block j at positions <= p
                 Kj = codecs.decode(k_pool[phys][:, :n_in, :], kv_dtype) * k_scale   # [Hkv][n][d]
-                Vj = codecs.decode(v_pool[phys][:, :, :n_in], kv_dtype) * v_scale   # [Hkv][d][n]
+                Vj = codecs.decode(v_pool[phys][:, :n_in, :], kv_dtype) * v_scale   # [Hkv][n][d]
                 qh = qf[a + t].reshape(Hkv, G, d)
                 numer[j] = np.exp(scale * np.einsum("hgd,hkd->hgk", qh, Kj))       # [Hkv][G][n]
                 vblk[j] = Vj
@@ -183,6 +183,7 @@ def block_sum_attention(q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, seq_
             o = np.zeros((Hkv, G, d))
             for j in range(nblocks):
                 A = numer[j] / denom[..., None]
-                o += np.einsum("hdk,hgk->hgd", vblk[j], A)                       # V_j A_ij^T
+                # V_j A_ij^T, V_j being the block's values as d x n columns
+                o += np.einsum("hkd,hgk->hgd", vblk[j], A)
             out[a + t] = o.reshape(Hq, d)
     return out

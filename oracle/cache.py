@@ -11,8 +11,8 @@ Reading of the slot encoding (the pages give none): slot = physical_block * B
 + offset_in_block, int64; a negative slot means "skip this token".
 
 Pool layouts (the pages are silent on layout; this is the layout the library
-defines): K is ``[N][Hkv][B][d]`` and V is ``[N][Hkv][d][B]``, i.e. each
-(block, head) tile is contiguous, keys are rows of K and columns of V.
+defines): K and V are both ``[N][Hkv][B][d]``, i.e. each (block, head) tile
+is contiguous and a token's d elements are one row of it.
 """
 
 from __future__ import annotations
@@ -54,9 +54,9 @@ def reshape_and_cache(k_pool: np.ndarray, v_pool: np.ndarray, key: np.ndarray, v
     kb = encode_tokens(np.asarray(key)[keep], src_dtype, kv_dtype, k_scale)
     vb = encode_tokens(np.asarray(value)[keep], src_dtype, kv_dtype, v_scale)
     st = k_pool.dtype
-    # K[blk][h][off][:] = enc(key[t][h][:]);  V[blk][h][:][off] = enc(value[t][h][:])
+    # K[blk][h][off][:] = enc(key[t][h][:]);  V[blk][h][off][:] = enc(value[t][h][:])
     k_pool[blk, :, off, :] = kb.astype(st, copy=False)
-    v_pool[blk, :, :, off] = vb.astype(st, copy=False)
+    v_pool[blk, :, off, :] = vb.astype(st, copy=False)
 
 
 def fill_pools(workload, seqs=None):

@@ -80,7 +80,7 @@ def test_bruteforce_python_loops_tiny_decode():
                 acc = 0.0
                 for pos in range(L):
                     blk = int(w.block_tables[i][pos // B])
-                    acc += ws[pos] * float(vflat[blk, g, e, pos % B])
+                    acc += ws[pos] * float(vflat[blk, g, pos % B, e])
                 assert abs(acc / tot - out[t, h, e]) < 1e-12
 
 
@@ -101,7 +101,7 @@ def test_matches_torch_sdpa_float64(kv):
         for pos in range(L):
             blk, off = int(w.block_tables[i][pos // w.block_size]), pos % w.block_size
             K[pos] = codecs.decode(kp[blk, :, off, :], w.kv_dtype) * w.k_scale
-            V[pos] = codecs.decode(vp[blk, :, :, off], w.kv_dtype) * w.v_scale
+            V[pos] = codecs.decode(vp[blk, :, off, :], w.kv_dtype) * w.v_scale
         qt = torch.from_numpy(qf[a:b]).permute(1, 0, 2)                     # [Hq][n][d]
         kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(w.group, 0)
         vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(w.group, 0)
@@ -263,7 +263,7 @@ def test_cache_write_layout_and_roundtrip(src, kv):
         for pos, slot in enumerate(w.slots(i)):
             blk, off = int(slot) // 16, int(slot) % 16
             got_k = codecs.decode(kp[blk, :, off, :], kv) * w.k_scale
-            got_v = codecs.decode(vp[blk, :, :, off], kv) * w.v_scale
+            got_v = codecs.decode(vp[blk, :, off, :], kv) * w.v_scale
             written_k[blk, :, off] = True
             if kv in ("f32",) or kv == src:
                 assert np.array_equal(got_k, kf[pos].astype(np.float64))
@@ -277,7 +277,7 @@ def test_cache_write_layout_and_roundtrip(src, kv):
             else:
                 rel = 2 ** -8 if kv == "bf16" else 2 ** -11
                 assert np.all(np.abs(got_k - kf[pos]) <= np.abs(kf[pos]) * rel + 6e-8)
-    assert np.all(kp.transpose(0, 1, 2, 3)[~written_k] == poison)
+    assert np.all(kp[~written_k] == poison) and np.all(vp[~written_k] == poison)
     assert written_k.sum() == w.num_kv_heads * int(w.seq_lens.sum())
 
 
@@ -292,7 +292,8 @@ def test_cache_write_skips_negative_slots():
     blk = int(w.block_tables[0, 0])
     assert np.all(kp[blk, 0, 0::2, :] == w.poison())
     assert np.array_equal(kp[blk, 0, 1:8:2, :], k[1::2, 0, :])
-    assert np.array_equal(vp[blk, 0, :, 1:8:2], v[1::2, 0, :].T)
+    assert np.all(vp[blk, 0, 0::2, :] == w.poison())
+    assert np.array_equal(vp[blk, 0, 1:8:2, :], v[1::2, 0, :])
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f16"])

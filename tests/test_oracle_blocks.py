@@ -33,7 +33,7 @@ def tokens(rng, n):
 
 def empty_pool(n):
     nan = np.uint32(0x7FC00000)   # fp32 poison: a block nobody wrote
-    return np.full((n, H, B, D), nan, np.uint32), np.full((n, H, D, B), nan, np.uint32)
+    return np.full((n, H, B, D), nan, np.uint32), np.full((n, H, B, D), nan, np.uint32)
 
 
 def write(kp, vp, k, v, slots):
@@ -102,7 +102,7 @@ def test_swap_out_and_back_leaves_attention_unchanged():
 def test_only_destinations_change_and_out_of_range_pairs_are_skipped():
     rng = np.random.default_rng(3)
     kp = rng.integers(0, 2 ** 32, size=(8, H, B, D), dtype=np.uint32)
-    vp = rng.integers(0, 2 ** 32, size=(8, H, D, B), dtype=np.uint32)
+    vp = rng.integers(0, 2 ** 32, size=(8, H, B, D), dtype=np.uint32)
     m = np.array([[0, 5], [2, 6], [-1, 7], [3, 8], [9, 1]])     # the last three are out of range
     ok, ov = BL.copy_blocks(kp, vp, kp, vp, m)
     for t in range(8):
@@ -125,7 +125,7 @@ def test_refuses_order_dependent_mappings():
 def test_fp8_blocks_copy_bytes():
     rng = np.random.default_rng(4)
     kp = rng.integers(0, 256, size=(4, H, B, D), dtype=np.uint8)
-    vp = rng.integers(0, 256, size=(4, H, D, B), dtype=np.uint8)
+    vp = rng.integers(0, 256, size=(4, H, B, D), dtype=np.uint8)
     ok, ov = BL.copy_blocks(kp, vp, kp, vp, np.array([[1, 3]]))
     assert ok.dtype == np.uint8 and ok[3].tobytes() == kp[1].tobytes() and ov[3].tobytes() == vp[1].tobytes()
     assert codecs.decode(ok[3], "fp8_e4m3").shape == (H, B, D)

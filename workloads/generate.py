@@ -242,13 +242,13 @@ class Workload:
     def initial_pool(self) -> Tuple[np.ndarray, np.ndarray]:
         """Pre-call pool images (raw bits) filled with the poison pattern.
 
-        K is ``[N][Hkv][B][d]``, V is ``[N][Hkv][d][B]``; both hold the
-        storage bits of ``kv_dtype``.
+        K and V are both ``[N][Hkv][B][d]`` and hold the storage bits of
+        ``kv_dtype``.
         """
         st = storage_type(self.kv_dtype)
         N, H, B, d = self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim
         k = np.full((N, H, B, d), self.poison(), dtype=st)
-        v = np.full((N, H, d, B), self.poison(), dtype=st)
+        v = np.full((N, H, B, d), self.poison(), dtype=st)
         return k, v
 
     def poison(self) -> int:
