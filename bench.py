@@ -202,7 +202,7 @@ def bench_block_copies(args):
     nblocks = 2 * n + 1
     gen = torch.Generator(device="cuda").manual_seed(141)
     kd = torch.randint(0, 127, (nblocks, H, B, d), dtype=torch.int8, device="cuda", generator=gen)
-    vd = torch.randint(0, 127, (nblocks, H, d, B), dtype=torch.int8, device="cuda", generator=gen)
+    vd = torch.randint(0, 127, (nblocks, H, B, d), dtype=torch.int8, device="cuda", generator=gen)
     kd = kd.view(torch.uint8).view(dt) if eb == 1 else kd.view(torch.uint8).repeat_interleave(eb, -1).view(dt)
     vd = vd.view(torch.uint8).view(dt) if eb == 1 else vd.view(torch.uint8).repeat_interleave(eb, -1).view(dt)
     rng = np.random.default_rng(141)
@@ -215,7 +215,7 @@ def bench_block_copies(args):
         names, bound, peak = ["copy_blocks"], "hbm", HBM_PEAK_GBS
     else:
         kh = torch.empty((n, H, B, d), dtype=dt, pin_memory=True)
-        vh = torch.empty((n, H, d, B), dtype=dt, pin_memory=True)
+        vh = torch.empty((n, H, B, d), dtype=dt, pin_memory=True)
         out = torch.from_numpy(np.stack([perm[:n], np.arange(n)], 1).astype(np.int64)).cuda()
         back = torch.from_numpy(np.stack([np.arange(n), perm[n:2 * n]], 1).astype(np.int64)).cuda()
         run = [lambda: pa.copy_blocks(kd, vd, kh, vh, out), lambda: pa.copy_blocks(kh, vh, kd, vd, back)]

@@ -30,10 +30,10 @@
  *
  * Cache layout (the pages give none; this is the library's definition):
  *    k_cache [num_blocks][num_kv_heads][block_size][head_dim]
- *    v_cache [num_blocks][num_kv_heads][head_dim][block_size]
- * i.e. every (block, kv head) tile is one contiguous run; keys are rows of
- * the K tile and columns of the V tile.  Slot s of the pool is token offset
- * s % B of physical block s / B.
+ *    v_cache [num_blocks][num_kv_heads][block_size][head_dim]
+ * i.e. every (block, kv head) tile is one contiguous run and a token's
+ * head_dim elements are one row of it, in both pools.  Slot s of the pool is
+ * token offset s % B of physical block s / B.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -71,7 +71,7 @@ typedef struct {
   int32_t num_blocks;   /* N: physical blocks in the pool                     */
   int32_t block_size;   /* B: tokens per block, one of 16, 32, 64             */
   int32_t num_kv_heads; /* Hkv                                                */
-  int32_t head_dim;     /* d: 64 or 128                                       */
+  int32_t head_dim;     /* d: 64, 128 or 256 (256 with 16-bit queries only)  */
   int32_t kv_dtype;     /* a pa_dtype_t                                       */
   float k_scale;        /* dequantisation multipliers: value = code * scale.  */
   float v_scale;        /* Must be 1.0f unless kv_dtype is PA_FP8_E4M3.       */
@@ -82,7 +82,7 @@ typedef struct {
  *
  * For each token t in [0, num_tokens) with s = slot_mapping[t] >= 0:
  *   k_cache[s / B][h][s % B][:] = enc(key[t][h][:])   for every kv head h
- *   v_cache[s / B][h][:][s % B] = enc(value[t][h][:])
+ *   v_cache[s / B][h][s % B][:] = enc(value[t][h][:])
  * where enc widens the source to fp32 exactly and then stores it as the
  * cache dtype: identity for fp32, round-to-nearest-even for fp16/bf16, and
  * for fp8 e4m3(fl32(x / scale)) with a correctly rounded fp32 division,

@@ -171,8 +171,8 @@ def cache_spec(k_cache, v_cache, k_scale: float = 1.0, v_scale: float = 1.0) -> 
     if k_cache.dim() != 4 or v_cache.dim() != 4:
         raise ValueError("caches must be 4-D")
     N, H, B, d = k_cache.shape
-    if tuple(v_cache.shape) != (N, H, d, B):
-        raise ValueError(f"v_cache must be [N, Hkv, d, B] = {(N, H, d, B)}, got {tuple(v_cache.shape)}")
+    if tuple(v_cache.shape) != (N, H, B, d):
+        raise ValueError(f"v_cache must be [N, Hkv, B, d] = {(N, H, B, d)}, got {tuple(v_cache.shape)}")
     if k_cache.dtype != v_cache.dtype:
         raise TypeError("k_cache and v_cache dtypes differ")
     return _Cache(N, B, H, d, _dtype_code(k_cache), float(k_scale), float(v_scale))

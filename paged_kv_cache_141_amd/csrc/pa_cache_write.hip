@@ -46,48 +46,57 @@ __device__ __forceinline__ uint32_t encode1(float x, float scale) {
   else return f32_to_e4m3(x, scale);
 }
 
-// One workgroup = kWriteTokens consecutive tokens of one kv head.  Pass 1:
-// a thread takes 8 consecutive elements of one token's K and V rows (16-byte
-// loads for 16-bit sources); K lands as one contiguous run in its [B][d]
-// tile row, V's codes go to LDS as [dim][token].  Pass 2 writes V down the
-// transposed [d][B] tiles with the lanes running along the tokens: a store
-// instruction covers 16 tokens x 4 dims, so the tokens of a prompt chunk,
-// which sit in consecutive slots of one block, fill whole cache lines in one
-// request (four 32-byte dim rows at B = 16) instead of every token adding
-// two bytes to 32 lines from a different workgroup.
+// One row of 8 consecutive elements (16-byte source loads for 16-bit
+// sources) encoded to the cache type and stored as one run.
+template <int KV>
+__device__ __forceinline__ void store8(uint8_t* dst, const float (&x)[8], float scale) {
+  if constexpr (KV == DT_F32) {
+    u32x4 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { lo[e] = f2u(x[e]); hi[e] = f2u(x[e + 4]); }
+    reinterpret_cast<u32x4*>(dst)[0] = lo;
+    reinterpret_cast<u32x4*>(dst)[1] = hi;
+  } else if constexpr (Bytes<KV>::v == 2) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = encode1<KV>(x[2 * e], 1.f) | (encode1<KV>(x[2 * e + 1], 1.f) << 16);
+    *reinterpret_cast<u32x4*>(dst) = w;
+  } else {
+    u32x2 w;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      w[e] = encode1<KV>(x[4 * e], scale) | (encode1<KV>(x[4 * e + 1], scale) << 8) |
+             (encode1<KV>(x[4 * e + 2], scale) << 16) | (encode1<KV>(x[4 * e + 3], scale) << 24);
+    *reinterpret_cast<u32x2*>(dst) = w;
+  }
+}
+
+// One workgroup = kWriteTokens consecutive tokens of one kv head; a thread
+// takes 8 consecutive elements of one token's K row and the same 8 of its V
+// row.  Both land as one contiguous run in the token's row of the [B][d]
+// tile, so the tokens of a prompt chunk, which sit in consecutive slots of
+// one block, fill whole cache lines.
 constexpr int kWriteTokens = 16;
 
 template <int SRC, int KV>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a) {
   constexpr int EBS = Bytes<SRC>::v;
   constexpr int EBK = Bytes<KV>::v;
-  __shared__ uint32_t vt[256 * kWriteTokens];            // V codes, [dim][token] (d <= 256)
-  __shared__ int64_t sslot[kWriteTokens];
   const int h = blockIdx.y;
   const int t0 = blockIdx.x * kWriteTokens;
   const int nt = min(kWriteTokens, a.num_tokens - t0);
   const int d = a.head_dim;
   const int chunks = d / 8;
-  // pass 2 reads the slots from LDS; pass 1 reads its own, so that its source
-  // loads need not wait for a barrier
-  if (threadIdx.x < kWriteTokens) {
-    int64_t s = static_cast<int>(threadIdx.x) < nt ? a.slots[t0 + threadIdx.x] : -1;
-#if PA_DEBUG
-    if (s >= a.num_slots) {                              // past the pool: recorded and skipped
-      if (h == 0) debug_record(a.debug, kDebugSlot, t0 + static_cast<int>(threadIdx.x));
-      s = -1;
-    }
-#endif
-    sslot[threadIdx.x] = s;
-  }
-
   for (int x = threadIdx.x; x < nt * chunks; x += 256) {
     const int tt = x / chunks;
     const int c = x - tt * chunks;
     const int64_t s = a.slots[t0 + tt];
-    if (s < 0) continue;
+    if (s < 0) continue;                                 // padding
 #if PA_DEBUG
-    if (s >= a.num_slots) continue;                      // recorded by pass 2's slot load
+    if (s >= a.num_slots) {                              // past the pool: recorded and skipped
+      if (h == 0 && c == 0) debug_record(a.debug, kDebugSlot, t0 + tt);
+      continue;
+    }
 #endif
     const int64_t blk = s / a.block_size;
     const int off = static_cast<int>(s - blk * a.block_size);
@@ -95,49 +104,10 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(CacheWriteArgs a
     float xk[8], xv[8];
     load8_src<SRC>(static_cast<const uint8_t*>(a.key) + src_off, xk);
     load8_src<SRC>(static_cast<const uint8_t*>(a.value) + src_off, xv);
-    const int64_t tile = (blk * a.num_kv_heads + h) * static_cast<int64_t>(a.block_size) * d;
-    uint8_t* kdst = static_cast<uint8_t*>(a.k_cache) + (tile + static_cast<int64_t>(off) * d + 8 * c) * EBK;
-    if constexpr (KV == DT_F32) {
-      u32x4 lo, hi;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { lo[e] = f2u(xk[e]); hi[e] = f2u(xk[e + 4]); }
-      reinterpret_cast<u32x4*>(kdst)[0] = lo;
-      reinterpret_cast<u32x4*>(kdst)[1] = hi;
-    } else if constexpr (EBK == 2) {
-      u32x4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = encode1<KV>(xk[2 * e], 1.f) | (encode1<KV>(xk[2 * e + 1], 1.f) << 16);
-      *reinterpret_cast<u32x4*>(kdst) = w;
-    } else {
-      u32x2 w;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        w[e] = encode1<KV>(xk[4 * e], a.k_scale) | (encode1<KV>(xk[4 * e + 1], a.k_scale) << 8) |
-               (encode1<KV>(xk[4 * e + 2], a.k_scale) << 16) |
-               (encode1<KV>(xk[4 * e + 3], a.k_scale) << 24);
-      }
-      *reinterpret_cast<u32x2*>(kdst) = w;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vt[(8 * c + e) * kWriteTokens + tt] = encode1<KV>(xv[e], a.v_scale);
-  }
-  __syncthreads();
-
-  // V tile is [d][B]: element (dim, off) at dim * B + off
-  for (int x = threadIdx.x; x < d * kWriteTokens; x += 256) {
-    const int tt = x % kWriteTokens;
-    const int dim = x / kWriteTokens;
-    const int64_t s = sslot[tt];
-    if (s < 0) continue;                                 // also the tokens past the last (slot -1)
-    const int64_t blk = s / a.block_size;
-    const int off = static_cast<int>(s - blk * a.block_size);
-    const int64_t tile = (blk * a.num_kv_heads + h) * static_cast<int64_t>(a.block_size) * d;
-    uint8_t* p = static_cast<uint8_t*>(a.v_cache) + (tile + static_cast<int64_t>(dim) * a.block_size + off) * EBK;
-    const uint32_t code = vt[x];
-    if constexpr (EBK == 4) *reinterpret_cast<uint32_t*>(p) = code;
-    else if constexpr (EBK == 2) *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(code);
-    else *p = static_cast<uint8_t>(code);
+    // element (off, dim) of the (blk, h) tile
+    const int64_t dst = ((blk * a.num_kv_heads + h) * static_cast<int64_t>(a.block_size) + off) * d + 8 * c;
+    store8<KV>(static_cast<uint8_t*>(a.k_cache) + dst * EBK, xk, a.k_scale);
+    store8<KV>(static_cast<uint8_t*>(a.v_cache) + dst * EBK, xv, a.v_scale);
   }
 }
 

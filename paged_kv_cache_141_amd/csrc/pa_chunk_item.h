@@ -16,24 +16,26 @@
 namespace pa {
 
 // LDS image of one 64-key tile in the 16-bit compute type: K rows [64][d]
-// and V^T rows [d][64], unpadded.  The 16-byte chunks of a row are XOR-
+// and V rows [64][d], unpadded.  The 16-byte chunks of a K row are XOR-
 // swizzled so that the 16 lanes of each MFMA operand read (16 different
-// rows, one chunk column) land in 16 different 16-byte bank groups.
+// rows, one chunk column) land in 16 different 16-byte bank groups.  A V
+// read covers whole rows, 16 lanes to a row; at d = 64 (128-byte rows) the
+// two rows one 32-lane pass reads, keys 8 apart, would share their banks,
+// so there row k is stored in place of row k ^ 1 when bit 3 of k is set.
 template <int D>
 struct ChunkLds {
   static constexpr int KROW = D * 2;                   // bytes per K row
-  static constexpr int VROW = kChunkKeys * 2;          // bytes per V^T row (128)
+  static constexpr int VROW = D * 2;                   // bytes per V row
   static constexpr int KBYTES = kChunkKeys * KROW;
-  static constexpr int BUF = KBYTES + D * VROW;
+  static constexpr int BUF = KBYTES + kChunkKeys * VROW;
   // The K rows one read touches are {8*(r/4) + 4*tau + r%4} (mod 32).
   static __device__ __forceinline__ int kswz(int key) {
     if constexpr (D >= 128) return (key & 3) | (((key >> 3) & 3) << 2);   // 16 distinct 16-byte groups
     else return ((key >> 1) & 1) | (((key >> 3) & 3) << 1);   // 128-byte rows pair up per 256 bytes
   }
-  // The V^T rows one read touches are 16 consecutive dims.
-  static __device__ __forceinline__ int vswz(int dim) { return (dim >> 1) & 7; }
+  static __host__ __device__ __forceinline__ int vrow(int key) { return D == 64 ? key ^ ((key >> 3) & 1) : key; }
   static __device__ __forceinline__ int koff(int key, int chunk) { return key * KROW + ((chunk ^ kswz(key)) << 4); }
-  static __device__ __forceinline__ int voff(int dim, int chunk) { return KBYTES + dim * VROW + ((chunk ^ vswz(dim)) << 4); }
+  static __device__ __forceinline__ int voff(int key, int byte) { return KBYTES + vrow(key) * VROW + byte; }
 };
 
 #ifndef PA_CHUNK_DMA_HINT
@@ -112,10 +114,11 @@ __device__ __forceinline__ void chunk_softmax(const float (&s)[16], float& m, f3
 // through registers for fp8, which is
 // widened to the compute type on the way -- kChunkAhead tiles ahead of the
 // one being computed.  Each wave runs the transposed-score MFMA scheme of
-// the decode kernel, every LDS operand read feeding both of its row tiles.
+// the decode kernel, every LDS operand read feeding both of its row tiles;
+// the V operands are read as runs of V rows and transposed in registers.
 //
 // Keys past a row's position get score -inf by selection, on the tiles that
-// hold such keys only; V columns of keys past the end of the sequence (they
+// hold such keys only; V rows of keys past the end of the sequence (they
 // hold whatever the pool has there) are overwritten with zero in LDS.
 #ifndef PA_CHUNK_AHEAD
 #define PA_CHUNK_AHEAD 2
@@ -182,23 +185,28 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
       dma_off[j] = ((kk % BS) * D + 8 * chunk) * EBK;
     } else {
       const int pv = pos - Lds::KBYTES;
-      const int dim = pv / Lds::VROW;
-      const int kk = 8 * (((pv % Lds::VROW) >> 4) ^ Lds::vswz(dim));   // first of the chunk's 8 keys
+      const int kk = Lds::vrow(pv / Lds::VROW);            // the row stored here (vrow is its own inverse)
       dma_rel[j] = kk / BS;
-      dma_off[j] = (dim * BS + kk % BS) * EBK;
+      dma_off[j] = (kk % BS) * D * EBK + pv % Lds::VROW;
     }
   }
 
   // LDS operand reads: lane (r, lg) reads K row kg*32 + 4*tau + rb, chunk
-  // 4s + lg, and V^T row 16n + r, chunk 4kg + lg.  The swizzle of those rows
-  // depends on r alone, so each lane needs one offset per s (K) and per kg
-  // (V); kg, tau and n then enter as immediate offsets.
+  // 4s + lg; the swizzle of those rows depends on r alone, so each lane
+  // needs one offset per s, and kg and tau enter as immediate offsets.  For
+  // V, slot e of the lane's P^T operand in key group kg is key
+  // 32*kg + 8*lg + e, and the lane reads run c (dims 16*SEG*c + SEG*r, VGeo)
+  // of that key's row: one offset for even e and one for odd e (they differ
+  // only where d = 64 rows swap), kg, e and c immediate.
+  using VG = VGeo<2, D>;
+  constexpr int SEG = VG::SEG, NSEG = VG::NSEG, VW = VG::WORDS;
   const int rb = 8 * (r >> 2) + (r & 3);
-  int kls[KS], vls[2];
+  int kls[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) kls[s] = Lds::koff(rb, 4 * s + lg);
+  int vls[2];
 #pragma unroll
-  for (int kg = 0; kg < 2; ++kg) vls[kg] = Lds::voff(r, 4 * kg + lg);
+  for (int e = 0; e < 2; ++e) vls[e] = Lds::voff(8 * lg + e, 2 * SEG * r) - e * Lds::VROW;
 
   // all-ones A operand: the PV product with it yields the row sums of P
   Frag<CT> ones;
@@ -341,12 +349,9 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
           if (FCH % kChunkThreads != 0 && c >= FCH) break;
           const int kk = c / (D / 16);
           const int cc = c % (D / 16);
-          kreg[j] = *reinterpret_cast<const u32x4*>(
-              kc + phys_of(kt, kk) * blk_stride + static_cast<int64_t>((kt + kk) % BS) * D + cc * 16);
-          const int dim = c / (kChunkKeys / 16);
-          const int kv0 = (c % (kChunkKeys / 16)) * 16;      // first of 16 keys
-          vreg[j] = *reinterpret_cast<const u32x4*>(
-              vc + phys_of(kt, kv0) * blk_stride + static_cast<int64_t>(dim) * BS + (kt + kv0) % BS);
+          const int64_t src = phys_of(kt, kk) * blk_stride + static_cast<int64_t>((kt + kk) % BS) * D + cc * 16;
+          kreg[j] = *reinterpret_cast<const u32x4*>(kc + src);
+          vreg[j] = *reinterpret_cast<const u32x4*>(vc + src);
         }
       };
       auto stage_fp8 = [&](const Regs& kreg, const Regs& vreg, uint8_t* buf) {
@@ -360,22 +365,17 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
           widen16<CT>(kreg[j], lo, hi);
           *reinterpret_cast<u32x4*>(buf + Lds::koff(kk, 2 * cc)) = lo;
           *reinterpret_cast<u32x4*>(buf + Lds::koff(kk, 2 * cc + 1)) = hi;
-          const int dim = c / (kChunkKeys / 16);
-          const int vc2 = (c % (kChunkKeys / 16)) * 2;
           widen16<CT>(vreg[j], lo, hi);
-          *reinterpret_cast<u32x4*>(buf + Lds::voff(dim, vc2)) = lo;
-          *reinterpret_cast<u32x4*>(buf + Lds::voff(dim, vc2 + 1)) = hi;
+          *reinterpret_cast<u32x4*>(buf + Lds::voff(kk, 32 * cc)) = lo;
+          *reinterpret_cast<u32x4*>(buf + Lds::voff(kk, 32 * cc + 16)) = hi;
         }
       };
-      // V^T columns of keys kt + [live, 64) are past the end: overwrite them
-      // with zero (all threads; the caller fences with a barrier).
+      // V rows of keys kt + [live, 64) are past the end: overwrite them with
+      // zero (all threads; the caller fences with a barrier).
       auto zero_tail = [&](uint8_t* buf, int live) {
-        for (int x = tid; x < D * kChunkKeys; x += kChunkThreads) {
-          const int dim = x / kChunkKeys;
-          const int key = x % kChunkKeys;
-          if (key >= live)
-            *reinterpret_cast<uint16_t*>(buf + Lds::voff(dim, key >> 3) + 2 * (key & 7)) = 0;
-        }
+        constexpr int CPR = Lds::VROW / 16;                 // 16-byte chunks per row
+        for (int x = live * CPR + tid; x < kChunkKeys * CPR; x += kChunkThreads)
+          *reinterpret_cast<u32x4*>(buf + Lds::voff(x / CPR, 16 * (x % CPR))) = u32x4{0u, 0u, 0u, 0u};
       };
 
       // ---- a tile's work on this wave's rows: scores (MFMA), softmax (VALU),
@@ -430,23 +430,31 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
 #pragma unroll
         for (int kg = 0; kg < 2; ++kg) {
 #pragma unroll
-          for (int n = 0; n < NT; ++n) {
-            Frag<CT> vf;
-            vf.w = *reinterpret_cast<const u32x4*>(buf + vls[kg] + 16 * n * Lds::VROW);
+          for (int c = 0; c < NSEG; ++c) {
+            Words<VW> run[8];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) acc[rt][n] = mma<CT>(acc[rt][n], vf, pf[rt][kg]);
+            for (int e = 0; e < 8; ++e) {
+              const uint8_t* p = buf + vls[e & 1] + (32 * kg + e) * Lds::VROW + 32 * SEG * c;
+              if constexpr (VW == 4) {
+                const u32x4 x = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) run[e].w[q] = x[q];
+              } else {
+                const u32x2 x = *reinterpret_cast<const u32x2*>(p);
+                run[e].w[0] = x[0];
+                run[e].w[1] = x[1];
+              }
+            }
+#pragma unroll
+            for (int jj = 0; jj < SEG; ++jj) {
+              const Frag<CT> vf = vt_frag16<CT>(run, jj);
+#pragma unroll
+              for (int rt = 0; rt < RT; ++rt) acc[rt][SEG * c + jj] = mma<CT>(acc[rt][SEG * c + jj], vf, pf[rt][kg]);
+            }
           }
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) lacc[rt] = mma<CT>(lacc[rt], ones, pf[rt][kg]);
         }
-        // pipeline: V fragment j + 4 loads while fragment j multiplies
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int j = 0; j < 2 * NT; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, RT, 0);
-          if (j + 4 < 2 * NT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * RT, 0);
       };
 
       const int ntiles = (kend - kstart + kChunkKeys - 1) / kChunkKeys;
@@ -523,14 +531,20 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
         const int token = q0 + t;
         const int head = h * G + (R - t * G);
         const float ltot = lacc[rt][0];
+        // accumulator element v of tile SEG*c + jj is dim 16*SEG*c + SEG*(4*lg + v) + jj
+        auto dim0 = [&](int c, int v) { return 16 * SEG * c + SEG * (4 * lg + v); };
         if (a.prefix_len == 0 && row_pos[rt] / CPART == 0) {
           const float inv = a.v_scale / ltot;
-          uint8_t* op = static_cast<uint8_t*>(a.out) +
-                        ((static_cast<int64_t>(token) * a.num_q_heads + head) * D + 4 * lg) * EBQ;
+          uint8_t* op = static_cast<uint8_t*>(a.out) + (static_cast<int64_t>(token) * a.num_q_heads + head) * D * EBQ;
 #pragma unroll
-          for (int n = 0; n < NT; ++n)
-            store4<CT>(op + 16 * n * EBQ, acc[rt][n][0] * inv, acc[rt][n][1] * inv, acc[rt][n][2] * inv,
-                       acc[rt][n][3] * inv);
+          for (int c = 0; c < NSEG; ++c)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+              for (int jj = 0; jj < SEG; jj += 4) {
+                const f32x4* x = &acc[rt][SEG * c + jj];
+                store4<CT>(op + (dim0(c, v) + jj) * EBQ, x[0][v] * inv, x[1][v] * inv, x[2][v] * inv, x[3][v] * inv);
+              }
         } else {
           // the row's list: a prompt chunk's (this item's sequence), or for
           // the prefix pass the list of the row's own sequence and kind
@@ -548,9 +562,16 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
             a.part_m[rowp] = max_log2(m[rt], a.score_scale);
             a.part_l[rowp] = ltot;
           }
-          float* pp = a.part_acc + rowp * D + 4 * lg;
+          float* pp = a.part_acc + rowp * D;
 #pragma unroll
-          for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(pp + 16 * n) = acc[rt][n] * a.v_scale;
+          for (int c = 0; c < NSEG; ++c)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+              for (int jj = 0; jj < SEG; jj += 4) {
+                const f32x4* x = &acc[rt][SEG * c + jj];
+                *reinterpret_cast<f32x4*>(pp + dim0(c, v) + jj) = f32x4{x[0][v], x[1][v], x[2][v], x[3][v]} * a.v_scale;
+              }
         }
       }
     }

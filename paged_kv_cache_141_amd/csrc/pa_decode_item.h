@@ -24,12 +24,6 @@ namespace pa {
 #ifndef PA_DECODE_FP8_WIDE
 #define PA_DECODE_FP8_WIDE 1
 #endif
-#ifndef PA_DECODE_PAIR_V
-#define PA_DECODE_PAIR_V 1
-#endif
-#ifndef PA_DECODE_NT_B64
-#define PA_DECODE_NT_B64 0
-#endif
 #ifndef PA_DECODE_WAVES_PER_SIMD
 #define PA_DECODE_WAVES_PER_SIMD 1
 #endif
@@ -63,18 +57,21 @@ struct PartTable {
 // Lane l = r + 16*lg (r = l % 16, lg = l / 16).  The 16x16 MFMA result tile
 // puts column r in lane r + 16*(row/4), element row%4.  The score tile is
 // computed transposed, S^T = K * Q^T (rows = keys, columns = query rows), with
-// K-tile row m of sub-tile tau holding key 8*(m/4) + 4*tau + m%4 of the
+// K-tile row m of sub-tile tau holding key 8*(m%4) + 4*tau + m/4 of the
 // 32-key step: then lane l ends up with the scores of query row r for the
-// eight consecutive keys 8*lg .. 8*lg+7, exactly the K slots the PV product
-// O^T = V^T * P^T needs from P^T, and V^T's rows (dims) are contiguous over
-// keys in the [d][B] tile, so both MFMA operands load straight from memory.
+// eight keys 4*e + lg (e = 0..7), and slot e of the lane's P^T operand is key
+// 4*e + lg.  The PV product O^T = V^T * P^T reads, for each of those keys, a
+// run of consecutive dims of its V row (VGeo): one instruction covers four
+// consecutive keys' whole rows, and the runs are transposed in registers.
 template <int CT, int KV, int D, int BS, int PF16, int PF8, bool STREAM>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, int part, int h,
                                           int lane) {
   constexpr int EBQ = Bytes<CT>::v;
   constexpr int EBK = Bytes<KV>::v;
   constexpr int KS = D / 32;     // K-steps of the QK^T product
-  constexpr int NT = D / 16;     // 16-dim output tiles
+  using VG = VGeo<EBK, D>;
+  constexpr int NT = VG::NT;     // 16-dim output tiles
+  constexpr int SEG = VG::SEG, NSEG = VG::NSEG, VW = VG::WORDS;
   const int r = lane & 15;
   const int lg = lane >> 4;
 
@@ -119,7 +116,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   const int64_t tile_bytes = static_cast<int64_t>(BS) * D * EBK;
   const int64_t blk_stride = tile_bytes * a.num_kv_heads;
   const uint8_t* kc = static_cast<const uint8_t*>(a.k_cache) + h * tile_bytes;
-  const uint8_t* vc = static_cast<const uint8_t*>(a.v_cache) + h * tile_bytes;
+  // the lane's first V run (dims SEG*r ..) of a tile
+  const uint8_t* vc = static_cast<const uint8_t*>(a.v_cache) + h * tile_bytes + SEG * r * EBK;
 
   // The partition's block-table entries, held in registers.
   const int jbase = kstart / BS;
@@ -130,9 +128,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   btv.check(a, i);
 #endif
 
-  // per-lane key offsets inside a 32-key step
-  const int kkey0 = 8 * (r >> 2) + (r & 3);      // sub-tile 0; sub-tile 1 adds 4
-  const int vkey = 8 * lg;                        // first of the lane's 8 keys for V / P
+  // the key of the lane's K-tile row in sub-tile 0 (sub-tile 1 adds 4)
+  const int kkey0 = 8 * (r & 3) + (r >> 2);
 
   float m = -__builtin_inff();
   float lsum = 0.f;
@@ -143,12 +140,12 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
 
   struct Step {
     Raw<KV> k[2][KS];
-    Raw<KV> v[NT];
+    Words<VW> v[8][NSEG];          // run c of key 4e + lg
   };
   // Issue the loads of the 32-key step starting at key k0 (block-table
-  // gather: physical block(s) from the table register, then 16-byte reads):
-  // K, then V.
-  auto issue_k = [&](Step& st, int k0) {
+  // gather: physical block(s) from the table register, then the reads): K,
+  // then V.
+  auto issue = [&](Step& st, int k0) {
     const int j0 = k0 / BS;
     const int64_t p0 = btv[j0 - jbase];
     int64_t p1 = p0;
@@ -172,19 +169,18 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
         for (int s = 0; s < KS; ++s) st.k[tau][s] = load_kv<KV, false>(kp + kdim(s) * EBK);
       }
     }
-  };
-  auto issue_v = [&](Step& st, int k0) {
-    const int j0 = k0 / BS;
-    const int64_t p0 = btv[j0 - jbase];
-    const int64_t pb = (BS == 16 && vkey >= 16) ? btv[min(j0 + 1, nblk - 1) - jbase] : p0;
-    const int inblk = k0 - j0 * BS;
-    const int off = (BS == 16) ? (vkey & 15) : inblk + vkey;
-    const uint8_t* vp = vc + pb * blk_stride + (static_cast<int64_t>(r) * BS + off) * EBK;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) st.v[n] = load_kv<KV, STREAM>(vp + static_cast<int64_t>(16 * n) * BS * EBK);
+    for (int e = 0; e < 8; ++e) {
+      const int kk = 4 * e + lg;
+      const int64_t pb = (BS == 16 && e >= 4) ? p1 : p0;   // wave-uniform per e
+      const int off = (BS == 16) ? (kk & 15) : inblk + kk;
+      const uint8_t* vp = vc + pb * blk_stride + static_cast<int64_t>(off) * D * EBK;
+#pragma unroll
+      for (int c = 0; c < NSEG; ++c) st.v[e][c] = load_words<VW, STREAM>(vp + 16 * SEG * c * EBK);
+    }
   };
 
-  auto compute = [&](const Step& st, int k0) {
+  auto compute = [&](Step& st, int k0) {
     // ---- S^T = K Q^T
     f32x4 sf[2];
 #pragma unroll
@@ -193,92 +189,127 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
 #pragma unroll
       for (int s = 0; s < KS; ++s) sf[tau] = mma<CT>(sf[tau], to_frag<CT, KV>(st.k[tau][s]), qf[s]);
     }
+    // element i2 of sub-tile tau is key 8*i2 + 4*tau + lg = 4*e + lg, e = 2*i2 + tau
     float sc[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { sc[e] = sf[0][e]; sc[4 + e] = sf[1][e]; }
+    for (int e = 0; e < 8; ++e) sc[e] = sf[e & 1][e >> 1];
     if (k0 + 31 > min_pos) {   // some key of this step is past some row's position
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sc[e] = (k0 + vkey + e <= row_pos) ? sc[e] : -__builtin_inff();
+      for (int e = 0; e < 8; ++e) sc[e] = (k0 + 4 * e + lg <= row_pos) ? sc[e] : -__builtin_inff();
     }
     // ---- online softmax (row r; the four lane groups share the row)
     float p[8];
     softmax_update<8, NT>(sc, m, lsum, acc, a.score_scale, slack, p);
 
-    // ---- O^T += V^T P^T (keys past the end hold poison: their V elements
-    // are replaced by zero, by selection)
+    // ---- O^T += V^T P^T (keys past the end hold poison: their V runs are
+    // replaced by zero, by selection)
     const Frag<CT> pf = pack_p<CT>(p);
-    const bool tail = k0 + 32 > L;
-    const int keep = L - (k0 + vkey);
+    if (k0 + 32 > L) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      Frag<CT> vf = to_frag<CT, KV>(st.v[n]);
-      if (tail) frag_keep_first<CT>(vf, keep);
-      acc[n] = mma<CT>(acc[n], vf, pf);
+      for (int e = 0; e < 8; ++e) {
+        const bool dead = k0 + 4 * e + lg >= L;
+#pragma unroll
+        for (int c = 0; c < NSEG; ++c)
+#pragma unroll
+          for (int x = 0; x < VW; ++x) st.v[e][c].w[x] = dead ? 0u : st.v[e][c].w[x];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NSEG; ++c) {
+      if constexpr (KV == DT_FP8) {
+        // byte jj of each run: 4x4 byte transposes of keys 0-3 and 4-7, then
+        // widened two codes at a time
+#pragma unroll
+        for (int x = 0; x < VW; ++x) {
+          uint32_t lo[4], hi[4];
+          byte_transpose4(st.v[0][c].w[x], st.v[1][c].w[x], st.v[2][c].w[x], st.v[3][c].w[x], lo);
+          byte_transpose4(st.v[4][c].w[x], st.v[5][c].w[x], st.v[6][c].w[x], st.v[7][c].w[x], hi);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            Frag<CT> vf;
+            vf.w[0] = widen2<CT>(lo[b], false);
+            vf.w[1] = widen2<CT>(lo[b], true);
+            vf.w[2] = widen2<CT>(hi[b], false);
+            vf.w[3] = widen2<CT>(hi[b], true);
+            const int j = SEG * c + 4 * x + b;
+            acc[j] = mma<CT>(acc[j], vf, pf);
+          }
+        }
+      } else {
+        Words<VW> run[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) run[e] = st.v[e][c];
+#pragma unroll
+        for (int jj = 0; jj < SEG; ++jj) {
+          const int j = SEG * c + jj;
+          if constexpr (KV == DT_F32) acc[j] = mma<CT>(acc[j], vt_frag32(run, jj), pf);
+          else acc[j] = mma<CT>(acc[j], vt_frag16<CT>(run, jj), pf);
+        }
+      }
     }
   };
 
   // Software pipeline: the loads of step s + PF are in flight while step s
   // computes (PF16 steps for 16-bit caches).
   constexpr int PF = (KV == DT_FP8) ? PF8 : (KV == DT_F32 ? 0 : PF16);
-  // 64-key blocks: a step reads half of each 128-byte V^T row, so the V loads
-  // of a block's two steps go out together (with the first step's K), and
-  // whole rows are read at once.  That takes one more step buffer: the second
-  // step's V lands a step earlier than its K.  (kstart is a multiple of 64,
-  // so even steps start blocks.)
-  constexpr bool PAIRV = BS == 64 && PF >= 2 && PA_DECODE_PAIR_V;
-  constexpr int NB = PAIRV ? (PF + 3) / 2 * 2 : PF + 1;   // PAIRV: PF + 2 rounded up to even
-  static_assert(!PAIRV || NB % 2 == 0, "step parity must be static in the ring");
+  constexpr int NB = PF + 1;
   Step buf[NB];
   const int nsteps = (kend - kstart + 31) / 32;
-  // issue step s into buf[b]
-  auto issue = [&](int b, int s) {
-    issue_k(buf[b], kstart + 32 * s);
-    if constexpr (PAIRV) {
-      if ((b & 1) == 0) {
-        issue_v(buf[b], kstart + 32 * s);
-        if (s + 1 < nsteps) issue_v(buf[(b + 1) % NB], kstart + 32 * (s + 1));
-      }
-    } else {
-      issue_v(buf[b], kstart + 32 * s);
-    }
-  };
 #pragma unroll
   for (int s = 0; s < PF; ++s)
-    if (s < nsteps) issue(s, s);
+    if (s < nsteps) issue(buf[s], kstart + 32 * s);
   for (int s0 = 0; s0 < nsteps; s0 += NB) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int s = s0 + b;
       if (s >= nsteps) break;
-      if (s + PF < nsteps) issue((b + PF) % NB, s + PF);
+      if (s + PF < nsteps) issue(buf[(b + PF) % NB], kstart + 32 * (s + PF));
       compute(buf[b], kstart + 32 * s);
     }
   }
 
-  // ---- finish: whole-row denominator, then the output or a partial
+  // ---- finish: whole-row denominator, then the output or a partial.  Lane
+  // (r, lg) holds, for each run c, dims 16*SEG*c + 4*SEG*lg + [0, 4*SEG) of
+  // row r: accumulator element v of tile SEG*c + jj is dim 16*SEG*c +
+  // SEG*(4*lg + v) + jj.
   float ltot = lsum + __shfl_xor(lsum, 16);
   ltot += __shfl_xor(ltot, 32);
   if (!valid || row_pos < kstart) return;
   const int nparts_row = (row_pos - a.prefix_len) / a.partition + 1;
+  auto dim0 = [&](int c, int v) { return 16 * SEG * c + SEG * (4 * lg + v); };
   if (nparts_row == 1 && a.prefix_len == 0) {
     const float inv = a.v_scale / ltot;
-    uint8_t* op = static_cast<uint8_t*>(a.out) +
-                  ((static_cast<int64_t>(token) * a.num_q_heads + head) * D + 4 * lg) * EBQ;
+    uint8_t* op = static_cast<uint8_t*>(a.out) + (static_cast<int64_t>(token) * a.num_q_heads + head) * D * EBQ;
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-      store4<CT>(op + 16 * n * EBQ, acc[n][0] * inv, acc[n][1] * inv, acc[n][2] * inv, acc[n][3] * inv);
+    for (int c = 0; c < NSEG; ++c)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int jj = 0; jj < SEG; jj += 4) {
+          const int j = SEG * c + jj;
+          store4<CT>(op + (dim0(c, v) + jj) * EBQ, acc[j][v] * inv, acc[j + 1][v] * inv, acc[j + 2][v] * inv,
+                     acc[j + 3][v] * inv);
+        }
   } else {
-    const int64_t row0 = partial_row(a, false, i, token, t, head);
-    if (row0 < 0) return;
-    const int64_t rowp = row0 + a.prefix_parts + part;
+    const int64_t prow = partial_row(a, false, i, token, t, head);
+    if (prow < 0) return;
+    const int64_t rowp = prow + a.prefix_parts + part;
     if (lg == 0) {
       a.part_m[rowp] = max_log2(m, a.score_scale);
       a.part_l[rowp] = ltot;
     }
-    float* pa = a.part_acc + rowp * D + 4 * lg;
+    float* pp = a.part_acc + rowp * D;
+    const float vs = a.v_scale;
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-      *reinterpret_cast<f32x4*>(pa + 16 * n) = acc[n] * a.v_scale;
+    for (int c = 0; c < NSEG; ++c)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int jj = 0; jj < SEG; jj += 4) {
+          const int j = SEG * c + jj;
+          *reinterpret_cast<f32x4*>(pp + dim0(c, v) + jj) =
+              f32x4{acc[j][v], acc[j + 1][v], acc[j + 2][v], acc[j + 3][v]} * vs;
+        }
   }
 }
 
@@ -306,12 +337,8 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int fi
     const int h = w - e * a.num_kv_heads;
     const int i = uniform(a.items[2 * e]);
     const int tp = uniform(a.items[2 * e + 1]);
-    // the hint only where a step reads whole V rows (B no more than the
-    // step's keys): a step that reads half of each row and leaves the other
-    // half to the next step measured 1.5x slower with it (B 64: 1,080 against
-    // 733 us for the LLaMA-7B decode kernel at B 16)
     // (tile, partition) are the unsigned 16-bit halves of tp: tiles reach 0xFFFF
-    attn_item<CT, KV, D, BS, PFD, PF8, STREAM && (BS <= 32 || PA_DECODE_NT_B64)>(
+    attn_item<CT, KV, D, BS, PFD, PF8, STREAM>(
         a, i, static_cast<int>(static_cast<uint32_t>(tp) >> 16), tp & 0xFFFF, h, lane);
     w = -1;
   }

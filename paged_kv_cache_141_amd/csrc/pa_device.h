@@ -222,22 +222,78 @@ __device__ __forceinline__ void store4(uint8_t* p, float a, float b, float c, fl
     *reinterpret_cast<u32x2*>(p) = u32x2{cvt2<OT>(a, b), cvt2<OT>(c, d)};
 }
 
-// Per-element keep-masks for an 8-element operand whose element e is kept
-// when e < n (n may be <= 0 or >= 8): zeroes elements by selection, no branches.
-template <int CT>
-__device__ __forceinline__ void frag_keep_first(Frag<CT>& f, int n) {
-  if constexpr (CT == DT_F32) {
+// ---- V operands from token-major V rows.
+//
+// The PV product O^T += V^T P^T takes V^T as its A operand: lane (r, lg)
+// must hold, for one output dim, the values of the eight keys of its K slots.
+// A V row in the cache (and in the chunk kernel's LDS tile) holds one key's
+// d values, so each lane reads, for each of its eight keys, a run of SEG
+// consecutive dims, and the operands are transposed in registers.  The runs
+// of lane r are segments c = 0 .. NSEG-1 at dims 16*SEG*c + SEG*r; output
+// tile j = SEG*c + jj then holds dims 16*SEG*c + SEG*n + jj in its rows n, so
+// the accumulator element v of lane (r, lg) in tile j is dim
+// 16*SEG*c + SEG*(4*lg + v) + jj of query row r.
+template <int EB, int D>
+struct VGeo {
+  static constexpr int NT = D / 16;                     // 16-dim output tiles
+  // dims per run: 16 bytes of 16-bit values (8 dims at most), all NT dims of
+  // fp8 codes (4 to 16 bytes), 4 fp32 values
+  static constexpr int SEG = EB == 1 ? NT : (EB == 4 ? 4 : (NT < 8 ? NT : 8));
+  static constexpr int NSEG = NT / SEG;
+  static constexpr int WORDS = SEG * EB / 4;             // 32-bit words per run
+  static_assert(NSEG * SEG == NT && WORDS >= 1 && WORDS <= 4, "V run geometry");
+};
+
+template <int N> struct Words { uint32_t w[N]; };
+
+template <int N, bool STREAM>
+__device__ __forceinline__ Words<N> load_words(const uint8_t* p) {
+  Words<N> r;
+  if constexpr (N == 4) {
+    const u32x4 x = load_once<STREAM>(reinterpret_cast<const u32x4*>(p));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f.w[e >> 2][e & 3] = e < n ? f.w[e >> 2][e & 3] : 0u;
+    for (int e = 0; e < 4; ++e) r.w[e] = x[e];
+  } else if constexpr (N == 2) {
+    const u32x2 x = load_once<STREAM>(reinterpret_cast<const u32x2*>(p));
+    r.w[0] = x[0];
+    r.w[1] = x[1];
   } else {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t keep = (2 * q < n ? 0x0000FFFFu : 0u) | (2 * q + 1 < n ? 0xFFFF0000u : 0u);
-      f.w[q] &= keep;
-    }
+    r.w[0] = load_once<STREAM>(reinterpret_cast<const uint32_t*>(p));
   }
+  return r;
 }
 
+// Operand of tile jj (within a run) from the eight runs v[0..7] of 16-bit
+// values, slot e of the lane taking run e: element jj of each run, two runs
+// per 32-bit word (one byte permute each).
+template <int CT, int N>
+__device__ __forceinline__ Frag<CT> vt_frag16(const Words<N> (&v)[8], int jj) {
+  const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
+  Frag<CT> f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) f.w[q] = __builtin_amdgcn_perm(v[2 * q + 1].w[jj >> 1], v[2 * q].w[jj >> 1], sel);
+  return f;
+}
+
+// fp32 values: element jj of run e goes to slot e unchanged.
+__device__ __forceinline__ Frag<DT_F32> vt_frag32(const Words<4> (&v)[8], int jj) {
+  Frag<DT_F32> f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.w[e >> 2][e & 3] = v[e].w[jj];
+  return f;
+}
+
+// 4x4 byte transpose: x[b] = byte b of a, b, c, d (in that order, low first).
+__device__ __forceinline__ void byte_transpose4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t (&x)[4]) {
+  const uint32_t ab0 = __builtin_amdgcn_perm(b, a, 0x06020400u);   // a0 b0 a2 b2
+  const uint32_t ab1 = __builtin_amdgcn_perm(b, a, 0x07030501u);   // a1 b1 a3 b3
+  const uint32_t cd0 = __builtin_amdgcn_perm(d, c, 0x06020400u);
+  const uint32_t cd1 = __builtin_amdgcn_perm(d, c, 0x07030501u);
+  x[0] = __builtin_amdgcn_perm(cd0, ab0, 0x05040100u);
+  x[1] = __builtin_amdgcn_perm(cd1, ab1, 0x05040100u);
+  x[2] = __builtin_amdgcn_perm(cd0, ab0, 0x07060302u);
+  x[3] = __builtin_amdgcn_perm(cd1, ab1, 0x07060302u);
+}
 
 // Online-softmax update for one query row whose keys are spread over the four
 // lanes r, r+16, r+32, r+48 (N raw scores per lane, already -inf where

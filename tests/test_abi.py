@@ -103,12 +103,12 @@ def test_workspace_size_grows_with_partitions():
 def test_binding_rejects_host_tensors():
     torch = pytest.importorskip("torch")
     k = torch.zeros(4, 2, 16, 64, dtype=torch.bfloat16)
-    v = torch.zeros(4, 2, 64, 16, dtype=torch.bfloat16)
+    v = torch.zeros(4, 2, 16, 64, dtype=torch.bfloat16)
     key = torch.zeros(1, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         pa.reshape_and_cache(key, key, k, v, torch.zeros(1, dtype=torch.int64))
     with pytest.raises(ValueError):
-        pa.cache_spec(k, k)      # V must be [N, H, d, B]
+        pa.cache_spec(k, v.transpose(2, 3).contiguous())      # V must be [N, H, B, d] like K
 
 
 def test_copy_blocks_argument_errors():

@@ -143,8 +143,8 @@ def test_slot_outside_the_pool_is_recorded_and_skipped():
     nk, nv = wd.to_host_bits(step.new_key), wd.to_host_bits(step.new_value)
     # every other token is in its slot (bf16 into a bf16 cache: the same bits)
     assert np.array_equal(after_k[blk[keep], :, off[keep], :], nk[keep])
-    assert np.array_equal(after_v[blk[keep], :, :, off[keep]], nv[keep])
+    assert np.array_equal(after_v[blk[keep], :, off[keep], :], nv[keep])
     # and nothing else of the pool changed: token t's own slot included
     after_k[blk[keep], :, off[keep], :] = before_k[blk[keep], :, off[keep], :]
-    after_v[blk[keep], :, :, off[keep]] = before_v[blk[keep], :, :, off[keep]]
+    after_v[blk[keep], :, off[keep], :] = before_v[blk[keep], :, off[keep], :]
     assert np.array_equal(after_k, before_k) and np.array_equal(after_v, before_v)

@@ -32,7 +32,7 @@ def rand_pool(rng, n, H, B, D, kv):
     dt = {"bf16": np.uint16, "f32": np.uint32, "fp8_e4m3": np.uint8}[kv]
     hi = {"bf16": 2 ** 16, "f32": 2 ** 32, "fp8_e4m3": 2 ** 8}[kv]
     return (rng.integers(0, hi, size=(n, H, B, D), dtype=np.uint64).astype(dt),
-            rng.integers(0, hi, size=(n, H, D, B), dtype=np.uint64).astype(dt))
+            rng.integers(0, hi, size=(n, H, B, D), dtype=np.uint64).astype(dt))
 
 
 TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8_e4m3": torch.uint8}
@@ -83,9 +83,9 @@ def test_swap_out_to_pinned_host_and_back_bit_exact():
 
 def test_pageable_host_pool_is_refused():
     gk = torch.zeros(4, 2, 16, 64, dtype=torch.bfloat16, device="cuda")
-    gv = torch.zeros(4, 2, 64, 16, dtype=torch.bfloat16, device="cuda")
+    gv = torch.zeros(4, 2, 16, 64, dtype=torch.bfloat16, device="cuda")
     hk = torch.zeros(4, 2, 16, 64, dtype=torch.bfloat16)
-    hv = torch.zeros(4, 2, 64, 16, dtype=torch.bfloat16)
+    hv = torch.zeros(4, 2, 16, 64, dtype=torch.bfloat16)
     m = torch.tensor([[0, 1]], dtype=torch.int64, device="cuda")
     with pytest.raises(ValueError):
         pa.copy_blocks(gk, gv, hk, hv, m)
@@ -116,7 +116,7 @@ def test_copy_on_write_step_end_to_end():
     scale = float(np.float32(1 / np.sqrt(D)))
 
     ok = np.full((N, H, B, D), 0x7FC0, np.uint16)
-    ov = np.full((N, H, D, B), 0x7FC0, np.uint16)
+    ov = np.full((N, H, B, D), 0x7FC0, np.uint16)
     C.reshape_and_cache(ok, ov, kb16[:P], vb16[:P], "bf16", "bf16", prompt_slots, B)
     ok, ov = BL.copy_blocks(ok, ov, ok, ov, np.array([[5, 9]]))
     C.reshape_and_cache(ok, ov, kb16[P:], vb16[P:], "bf16", "bf16", np.array([5 * B + 8, 9 * B + 8]), B)
@@ -125,7 +125,7 @@ def test_copy_on_write_step_end_to_end():
     def dev16(a):
         return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).cuda()
     gk = dev16(np.full((N, H, B, D), 0x7FC0, np.uint16))
-    gv = dev16(np.full((N, H, D, B), 0x7FC0, np.uint16))
+    gv = dev16(np.full((N, H, B, D), 0x7FC0, np.uint16))
     pa.reshape_and_cache(dev16(kb16[:P]), dev16(vb16[:P]), gk, gv, torch.from_numpy(prompt_slots).cuda())
     pa.copy_blocks(gk, gv, gk, gv, torch.tensor([[5, 9]], dtype=torch.int64, device="cuda"))
     pa.reshape_and_cache(dev16(kb16[P:]), dev16(vb16[P:]), gk, gv,

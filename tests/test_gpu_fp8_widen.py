@@ -31,14 +31,14 @@ def run(q_dtype, q_lens):
     nblk = -(-max(q_lens) // B)
     rng = np.random.default_rng(7)
     k = torch.from_numpy(rng.integers(0, 0x70, size=(N, 1, B, D), dtype=np.uint8)).to(dev)
-    v = torch.from_numpy(rng.integers(0, 0x70, size=(N, 1, D, B), dtype=np.uint8))
+    v = torch.from_numpy(rng.integers(0, 0x70, size=(N, 1, B, D), dtype=np.uint8))
     codes = np.arange(256, dtype=np.uint8).reshape(2, D)
     # sequence i: block i first, then blocks of the shared spare N - 1 (its
     # V codes are never a row's only key); position 0 of block i holds codes
     tables = np.full((S, nblk), N - 1, dtype=np.int32)
     for i in range(S):
         tables[i, 0] = i
-        v[i, 0, :, 0] = torch.from_numpy(codes[i % 2])
+        v[i, 0, 0, :] = torch.from_numpy(codes[i % 2])
     v = v.to(dev)
     qsl = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
     T = int(qsl[-1])

@@ -304,7 +304,7 @@ def test_full_mixed_chunked_prefill():
     B = w.block_size
     blk, off = ns // B, ns % B
     assert np.array_equal(kbits[blk, :, off, :], nk)
-    assert np.array_equal(vbits[blk, :, :, off], nv)
+    assert np.array_equal(vbits[blk, :, off, :], nv)
     del kbits, vbits
     kp, vp = fill_pools(w)
     ref = attention(w, kp, vp)

@@ -59,14 +59,14 @@ def poisoned_pool(w: Workload, device):
     bits = poison_pattern(w.kv_dtype)
     if w.kv_dtype == "f32":
         k = torch.full((N, H, B, d), bits, dtype=torch.int32, device=device).view(torch.float32)
-        v = torch.full((N, H, d, B), bits, dtype=torch.int32, device=device).view(torch.float32)
+        v = torch.full((N, H, B, d), bits, dtype=torch.int32, device=device).view(torch.float32)
     elif w.kv_dtype in ("f16", "bf16"):
         td = torch_dtype(w.kv_dtype)
         k = torch.full((N, H, B, d), bits, dtype=torch.int16, device=device).view(td)
-        v = torch.full((N, H, d, B), bits, dtype=torch.int16, device=device).view(td)
+        v = torch.full((N, H, B, d), bits, dtype=torch.int16, device=device).view(td)
     else:
         k = torch.full((N, H, B, d), bits, dtype=torch.uint8, device=device)
-        v = torch.full((N, H, d, B), bits, dtype=torch.uint8, device=device)
+        v = torch.full((N, H, B, d), bits, dtype=torch.uint8, device=device)
     return k, v
 
 
