@@ -365,12 +365,12 @@ pa_status_t pa_set_prefix_events(void* before, void* after);
  * The block size (tokens per cache block) the attention kernels run fastest
  * with for a head dim, a (q dtype, cache dtype) pairing and a query group
  * (group = q heads per kv head), as measured on MI355X over decode steps at
- * B = 16, 32 and 64: 32 for an fp8 cache read by grouped queries (group >= 2),
- * 16 otherwise.  The page chooses the block size among 16, 32 and 64 tokens
+ * B = 16, 32 and 64: 64 for an fp8 cache at head dim 256, 32 otherwise (the
+ * query group does not change the choice on this GPU; it is part of the
+ * question).  The page chooses the block size among 16, 32 and 64 tokens
  * by head dim and precision (techknowgenie "vLLM V1 core refactoring",
  * section "PagedAttention V3 kernel architecture and hardware-level memory
- * alignment", adaptive block tiling); on this GPU the query group also
- * decides it for fp8.  Writes 16, 32 or 64 to *block_size [host].  Every
+ * alignment", adaptive block tiling).  Writes 16, 32 or 64 to *block_size [host].  Every
  * block size works with every entry point; this is a performance choice for
  * the caller that sizes the pool.  PA_ERR_UNSUPPORTED for a head dim outside
  * {64, 128, 256} (or 256 with fp32), PA_ERR_DTYPE for a pairing pa_attention

@@ -399,17 +399,17 @@ pa_status_t pa_preferred_block_size(int32_t head_dim, int32_t kv_dtype, int32_t 
   if (head_dim == 256 && q_dtype == PA_F32) return PA_ERR_UNSUPPORTED;
   if (group < 1) return PA_ERR_SHAPE;
   // Decode kernel time on MI355X (one session), B = 16 / 32 / 64, us:
-  //   LLaMA-7B shape (group 1, d 128): bf16 737 / 746 / 835, fp8 395 / 402 / 452;
-  //   GQA long context (group 4):      bf16 d 64 425 / 420 / 462, d 128 408 / 410 / 459,
-  //                                    d 256 435 / 439 / 547;
-  //                                    fp8  d 64 247 / 247 / 256, d 128 225 / 222 / 249,
-  //                                    d 256 236 / 235 / 267.
-  // 64-token blocks are slowest everywhere: a 32-key step reads half of each
-  // 128-byte V^T row and strides across rows.  16 and 32 stay within 2 % of
-  // each other; 32 leads only where fp8 codes meet grouped queries (a B-32
-  // V^T row of codes is one 32-byte run, where B 16 splits a step's 32 keys
-  // over two 16-byte runs), and 16 leads for fp8 at group 1.
-  *block_size = (kv_dtype == PA_FP8_E4M3 && group >= 2) ? 32 : 16;
+  //   LLaMA-7B shape (group 1, d 128): bf16 708 / 709 / 716, fp8 383 / 377 / 380;
+  //   GQA long context (group 4):      bf16 d 64 425 / 418 / 420, d 128 406 / 405 / 404,
+  //                                    d 256 438 / 432 / 432;
+  //                                    fp8  d 64 243 / 239 / 239, d 128 224 / 221 / 221,
+  //                                    d 256 232 / 232 / 228.
+  // A 32-key step reads whole K and V rows at every B, so B matters only
+  // through the block-table lookups and the K rows a step gathers from one
+  // block or two: 32 is within 0.5 % of the fastest everywhere except fp8
+  // codes at d 256 (16-byte rows of 16 dims per lane), where 64 leads by 2 %.
+  // fp32 caches follow the 16-bit choice (not measured separately).
+  *block_size = (kv_dtype == PA_FP8_E4M3 && head_dim == 256) ? 64 : 32;
   return PA_OK;
 }
 

@@ -160,7 +160,8 @@ void argument_errors() {
   CHECK(strlen(pa_version()) > 0);
   int32_t bs = 0;
   CHECK(pa_preferred_block_size(128, PA_FP8_E4M3, PA_BF16, 4, &bs) == PA_OK && bs == 32);
-  CHECK(pa_preferred_block_size(128, PA_BF16, PA_BF16, 4, &bs) == PA_OK && bs == 16);
+  CHECK(pa_preferred_block_size(256, PA_FP8_E4M3, PA_BF16, 1, &bs) == PA_OK && bs == 64);
+  CHECK(pa_preferred_block_size(128, PA_BF16, PA_BF16, 4, &bs) == PA_OK && bs == 32);
   CHECK(pa_preferred_block_size(128, PA_BF16, PA_BF16, 0, &bs) == PA_ERR_SHAPE);
   CHECK(pa_preferred_block_size(std::numeric_limits<int32_t>::min(), PA_BF16, PA_BF16, 1, &bs) == PA_ERR_UNSUPPORTED);
 }

@@ -164,15 +164,15 @@ def test_row_tile_limit():
 
 
 def test_preferred_block_size():
-    # 32 tokens for an fp8 cache under grouped queries, 16 otherwise, at every head dim
+    # 64 tokens for an fp8 cache at head dim 256, 32 otherwise, at every query group
     for d in (64, 128, 256):
         for g in (1, 4, 8):
             for q, kv in ((pa.PA_BF16, pa.PA_BF16), (pa.PA_F16, pa.PA_F16)):
-                assert pa.preferred_block_size(d, kv, q, g) == 16
+                assert pa.preferred_block_size(d, kv, q, g) == 32
             for q in (pa.PA_BF16, pa.PA_F16):
-                assert pa.preferred_block_size(d, pa.PA_FP8_E4M3, q, g) == (32 if g >= 2 else 16)
+                assert pa.preferred_block_size(d, pa.PA_FP8_E4M3, q, g) == (64 if d == 256 else 32)
     for d in (64, 128):
-        assert pa.preferred_block_size(d, pa.PA_F32, pa.PA_F32, 4) == 16
+        assert pa.preferred_block_size(d, pa.PA_F32, pa.PA_F32, 4) == 32
     lib = pa.library()
     b = ctypes.c_int32(0)
     assert lib.pa_preferred_block_size(256, pa.PA_F32, pa.PA_F32, 1, ctypes.byref(b)) == 4   # d 256: 16-bit q only

@@ -31,6 +31,7 @@ decode tokens with prompt chunks under a 4,096-token budget, and a shared
 
 from __future__ import annotations
 
+import inspect
 import math
 import os
 from collections import deque
@@ -414,6 +415,8 @@ def make(name: str, **kw) -> Workload:
     """Build a named configuration; keyword arguments shrink or vary it."""
     if name not in CONFIGS:
         raise KeyError(f"unknown workload {name!r}; known: {sorted(CONFIGS)}")
+    if "head_dim" in kw and "head_dim" not in inspect.signature(CONFIGS[name]).parameters:
+        raise ValueError(f"{name} fixes its head dim; it takes no head_dim override")
     return CONFIGS[name](**kw)
 
 
