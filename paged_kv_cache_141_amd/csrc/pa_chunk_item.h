@@ -18,10 +18,11 @@ namespace pa {
 // LDS image of one 64-key tile in the 16-bit compute type: K rows [64][d]
 // and V rows [64][d], unpadded.  The 16-byte chunks of a K row are XOR-
 // swizzled so that the 16 lanes of each MFMA operand read (16 different
-// rows, one chunk column) land in 16 different 16-byte bank groups.  A V
-// read covers whole rows, 16 lanes to a row; at d = 64 (128-byte rows) the
-// two rows one 32-lane pass reads, keys 8 apart, would share their banks,
-// so there row k is stored in place of row k ^ 1 when bit 3 of k is set.
+// rows, one chunk column) land in 16 different 16-byte bank groups.  V rows
+// are read with transposing loads (lds_read_tr16), each 32-lane half of one
+// touching 8 rows at one 32-byte column; the 32-byte units of a V row are
+// XOR-swizzled by the row bits that differ inside such a half (bits 0, 1
+// and 3), so those 8 reads land in 8 different 32-byte bank groups.
 template <int D>
 struct ChunkLds {
   static constexpr int KROW = D * 2;                   // bytes per K row
@@ -33,10 +34,31 @@ struct ChunkLds {
     if constexpr (D >= 128) return (key & 3) | (((key >> 3) & 3) << 2);   // 16 distinct 16-byte groups
     else return ((key >> 1) & 1) | (((key >> 3) & 3) << 1);   // 128-byte rows pair up per 256 bytes
   }
-  static __host__ __device__ __forceinline__ int vrow(int key) { return D == 64 ? key ^ ((key >> 3) & 1) : key; }
+  // 32-byte unit swizzle of V row `key`; at d = 64 a row is half the banks,
+  // and bit 0 of the row already picks the half
+  static __device__ __forceinline__ int vswz(int key) {
+    if constexpr (D >= 128) return (key & 3) | (((key >> 3) & 1) << 2);
+    else return ((key >> 1) & 1) | (((key >> 3) & 1) << 1);
+  }
   static __device__ __forceinline__ int koff(int key, int chunk) { return key * KROW + ((chunk ^ kswz(key)) << 4); }
-  static __device__ __forceinline__ int voff(int key, int byte) { return KBYTES + vrow(key) * VROW + byte; }
+  // LDS byte of logical byte `byte` of V row `key`
+  static __device__ __forceinline__ int voff(int key, int byte) {
+    return KBYTES + key * VROW + ((((byte >> 5) ^ vswz(key))) << 5) + (byte & 31);
+  }
 };
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group,
+// lane 4e + a passes the address of 4 consecutive 16-bit elements, and lane
+// 4a + b receives element b of the four runs passed by lanes 4e + a, e = 0..3
+// (layout measured on gfx950).  With lane 4e + a pointing at row k0 + e,
+// columns 4a .. 4a+3 of a row-major matrix, lane n receives rows k0 .. k0+3
+// of column n.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(u32x2, x);
+}
 
 #ifndef PA_CHUNK_DMA_HINT
 #define PA_CHUNK_DMA_HINT ""
@@ -115,7 +137,7 @@ __device__ __forceinline__ void chunk_softmax(const float (&s)[16], float& m, f3
 // widened to the compute type on the way -- kChunkAhead tiles ahead of the
 // one being computed.  Each wave runs the transposed-score MFMA scheme of
 // the decode kernel, every LDS operand read feeding both of its row tiles;
-// the V operands are read as runs of V rows and transposed in registers.
+// the V^T operands come from the V rows through transposing LDS reads.
 //
 // Keys past a row's position get score -inf by selection, on the tiles that
 // hold such keys only; V rows of keys past the end of the sequence (they
@@ -185,28 +207,31 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
       dma_off[j] = ((kk % BS) * D + 8 * chunk) * EBK;
     } else {
       const int pv = pos - Lds::KBYTES;
-      const int kk = Lds::vrow(pv / Lds::VROW);            // the row stored here (vrow is its own inverse)
+      const int kk = pv / Lds::VROW;
+      const int pb = pv % Lds::VROW;                       // this LDS byte holds logical byte lb of row kk
+      const int lb = (((pb >> 5) ^ Lds::vswz(kk)) << 5) | (pb & 31);
       dma_rel[j] = kk / BS;
-      dma_off[j] = (kk % BS) * D * EBK + pv % Lds::VROW;
+      dma_off[j] = (kk % BS) * D * EBK + lb;
     }
   }
 
   // LDS operand reads: lane (r, lg) reads K row kg*32 + 4*tau + rb, chunk
   // 4s + lg; the swizzle of those rows depends on r alone, so each lane
-  // needs one offset per s, and kg and tau enter as immediate offsets.  For
-  // V, slot e of the lane's P^T operand in key group kg is key
-  // 32*kg + 8*lg + e, and the lane reads run c (dims 16*SEG*c + SEG*r, VGeo)
-  // of that key's row: one offset for even e and one for odd e (they differ
-  // only where d = 64 rows swap), kg, e and c immediate.
-  using VG = VGeo<2, D>;
-  constexpr int SEG = VG::SEG, NSEG = VG::NSEG, VW = VG::WORDS;
+  // needs one offset per s, and kg and tau enter as immediate offsets.  V:
+  // slot e of the lane's P^T operand in key group kg is key 32*kg + 8*lg + e;
+  // the V^T operand of output tile n (dims 16n .. 16n+15) takes two
+  // transposing reads, h = 0 and 1, in which lane (r, lg) points at row
+  // 32*kg + 8*lg + 4*h + r/4, dims 16n + 4*(r%4) .. +3.  The swizzle of those
+  // rows depends on r and lg alone: one offset per n (mod 8), the rest
+  // immediate.
+  constexpr int NV = NT < 8 ? NT : 8;
   const int rb = 8 * (r >> 2) + (r & 3);
   int kls[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) kls[s] = Lds::koff(rb, 4 * s + lg);
-  int vls[2];
+  int vto[NV];
 #pragma unroll
-  for (int e = 0; e < 2; ++e) vls[e] = Lds::voff(8 * lg + e, 2 * SEG * r) - e * Lds::VROW;
+  for (int n = 0; n < NV; ++n) vto[n] = Lds::voff(8 * lg + (r >> 2), 32 * n + 8 * (r & 3));
 
   // all-ones A operand: the PV product with it yields the row sums of P
   Frag<CT> ones;
@@ -430,27 +455,15 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
 #pragma unroll
         for (int kg = 0; kg < 2; ++kg) {
 #pragma unroll
-          for (int c = 0; c < NSEG; ++c) {
-            Words<VW> run[8];
+          for (int n = 0; n < NT; ++n) {
+            // rows 32kg + 8lg + {0..3} and {4..7}: slots 0-3 and 4-7
+            const uint8_t* p = buf + vto[n % NV] + 256 * (n / NV) + 32 * kg * Lds::VROW;
+            const u32x2 lo = lds_read_tr16(p);
+            const u32x2 hi = lds_read_tr16(p + 4 * Lds::VROW);
+            Frag<CT> vf;
+            vf.w = u32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint8_t* p = buf + vls[e & 1] + (32 * kg + e) * Lds::VROW + 32 * SEG * c;
-              if constexpr (VW == 4) {
-                const u32x4 x = *reinterpret_cast<const u32x4*>(p);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) run[e].w[q] = x[q];
-              } else {
-                const u32x2 x = *reinterpret_cast<const u32x2*>(p);
-                run[e].w[0] = x[0];
-                run[e].w[1] = x[1];
-              }
-            }
-#pragma unroll
-            for (int jj = 0; jj < SEG; ++jj) {
-              const Frag<CT> vf = vt_frag16<CT>(run, jj);
-#pragma unroll
-              for (int rt = 0; rt < RT; ++rt) acc[rt][SEG * c + jj] = mma<CT>(acc[rt][SEG * c + jj], vf, pf[rt][kg]);
-            }
+            for (int rt = 0; rt < RT; ++rt) acc[rt][n] = mma<CT>(acc[rt][n], vf, pf[rt][kg]);
           }
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) lacc[rt] = mma<CT>(lacc[rt], ones, pf[rt][kg]);
@@ -531,20 +544,15 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
         const int token = q0 + t;
         const int head = h * G + (R - t * G);
         const float ltot = lacc[rt][0];
-        // accumulator element v of tile SEG*c + jj is dim 16*SEG*c + SEG*(4*lg + v) + jj
-        auto dim0 = [&](int c, int v) { return 16 * SEG * c + SEG * (4 * lg + v); };
+        // accumulator element v of tile n is dim 16n + 4lg + v
         if (a.prefix_len == 0 && row_pos[rt] / CPART == 0) {
           const float inv = a.v_scale / ltot;
-          uint8_t* op = static_cast<uint8_t*>(a.out) + (static_cast<int64_t>(token) * a.num_q_heads + head) * D * EBQ;
+          uint8_t* op = static_cast<uint8_t*>(a.out) +
+                        ((static_cast<int64_t>(token) * a.num_q_heads + head) * D + 4 * lg) * EBQ;
 #pragma unroll
-          for (int c = 0; c < NSEG; ++c)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-#pragma unroll
-              for (int jj = 0; jj < SEG; jj += 4) {
-                const f32x4* x = &acc[rt][SEG * c + jj];
-                store4<CT>(op + (dim0(c, v) + jj) * EBQ, x[0][v] * inv, x[1][v] * inv, x[2][v] * inv, x[3][v] * inv);
-              }
+          for (int n = 0; n < NT; ++n)
+            store4<CT>(op + 16 * n * EBQ, acc[rt][n][0] * inv, acc[rt][n][1] * inv, acc[rt][n][2] * inv,
+                       acc[rt][n][3] * inv);
         } else {
           // the row's list: a prompt chunk's (this item's sequence), or for
           // the prefix pass the list of the row's own sequence and kind
@@ -562,16 +570,9 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
             a.part_m[rowp] = max_log2(m[rt], a.score_scale);
             a.part_l[rowp] = ltot;
           }
-          float* pp = a.part_acc + rowp * D;
+          float* pp = a.part_acc + rowp * D + 4 * lg;
 #pragma unroll
-          for (int c = 0; c < NSEG; ++c)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-#pragma unroll
-              for (int jj = 0; jj < SEG; jj += 4) {
-                const f32x4* x = &acc[rt][SEG * c + jj];
-                *reinterpret_cast<f32x4*>(pp + dim0(c, v) + jj) = f32x4{x[0][v], x[1][v], x[2][v], x[3][v]} * a.v_scale;
-              }
+          for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(pp + 16 * n) = acc[rt][n] * a.v_scale;
         }
       }
     }
