@@ -407,25 +407,27 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
       // then the PV product (MFMA)
       f32x4 sf[RT][2][2];                                    // raw scores of the last qk
       Frag<CT> pf[RT][2];                                    // P of the last softmax, MFMA operand
+      // Operand fragments are read from LDS a key group (32 keys) at a time
+      // into registers, then multiplied: the group's reads are all in flight
+      // together instead of each MFMA waiting for the read just before it.
       auto qk = [&](const uint8_t* buf) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int kg = 0; kg < 2; ++kg) {
+          Frag<CT> kf[2][KS];
 #pragma unroll
-          for (int kg = 0; kg < 2; ++kg)
+          for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-            for (int tau = 0; tau < 2; ++tau) sf[rt][kg][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < KS; ++s)
+              kf[tau][s].w = *reinterpret_cast<const u32x4*>(buf + kls[s] + (kg * 32 + 4 * tau) * Lds::KROW);
 #pragma unroll
-        for (int kg = 0; kg < 2; ++kg)
+          for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-          for (int tau = 0; tau < 2; ++tau) {
+            for (int rt = 0; rt < RT; ++rt) {
+              sf[rt][kg][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-              Frag<CT> kf;
-              kf.w = *reinterpret_cast<const u32x4*>(buf + kls[s] + (kg * 32 + 4 * tau) * Lds::KROW);
-#pragma unroll
-              for (int rt = 0; rt < RT; ++rt) sf[rt][kg][tau] = mma<CT>(sf[rt][kg][tau], kf, qf[rt][s]);
+              for (int s = 0; s < KS; ++s) sf[rt][kg][tau] = mma<CT>(sf[rt][kg][tau], kf[tau][s], qf[rt][s]);
             }
-          }
+        }
       };
       auto softmax = [&](int kt) {
         float sc[RT][16];
@@ -454,14 +456,18 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
       auto pv = [&](const uint8_t* buf) {
 #pragma unroll
         for (int kg = 0; kg < 2; ++kg) {
+          // rows 32kg + 8lg + {0..3} and {4..7}: slots 0-3 and 4-7 of tile n
+          u32x2 lo[NT], hi[NT];
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
-            // rows 32kg + 8lg + {0..3} and {4..7}: slots 0-3 and 4-7
             const uint8_t* p = buf + vto[n % NV] + 256 * (n / NV) + 32 * kg * Lds::VROW;
-            const u32x2 lo = lds_read_tr16(p);
-            const u32x2 hi = lds_read_tr16(p + 4 * Lds::VROW);
+            lo[n] = lds_read_tr16(p);
+            hi[n] = lds_read_tr16(p + 4 * Lds::VROW);
+          }
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
             Frag<CT> vf;
-            vf.w = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            vf.w = u32x4{lo[n][0], lo[n][1], hi[n][0], hi[n][1]};
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) acc[rt][n] = mma<CT>(acc[rt][n], vf, pf[rt][kg]);
           }
