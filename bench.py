@@ -21,6 +21,7 @@ import argparse
 import ctypes
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -105,12 +106,20 @@ KERNEL_SOURCES = {"attn_kernel": ("pa_decode.hip", "pa_decode_item.h"),
                   "step_kernel": ("pa_step.hip", "pa_decode_item.h", "pa_chunk_item.h")}
 
 
+def _code_only(text):
+    """C++ source without its comments and blank space: what the compiler sees."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(kernel):
-    """Hash of the sources one kernel is compiled from (its own file plus the
-    shared device headers): counter runs stay valid until these change."""
+    """Hash of the code one kernel is compiled from (its own file plus the
+    shared device headers, comments left out): counter runs stay valid until
+    that code changes."""
     h = hashlib.sha256()
     for f in (*KERNEL_SOURCES[kernel], "pa_device.h", "pa_codec.h", "pa_internal.h"):
-        h.update(open(os.path.join(ROOT, "paged_kv_cache_141_amd", "csrc", f), "rb").read())
+        h.update(_code_only(open(os.path.join(ROOT, "paged_kv_cache_141_amd", "csrc", f)).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -86,10 +86,9 @@ template <> struct Raw<DT_FP8> { u32x2 w; };
 
 // Cache data a decode item reads once: STREAM gives the loads the
 // non-temporal hint (global_load ... nt).  The decode items give it to their
-// V loads, not their K loads.  Measured against no hint, each pair in one
-// session: GQA decode 431 -> 408 us with V alone (430 with K too), LLaMA-7B
-// 790 -> 733 us; fp8 private-prefix decode 373 -> 365 us (385 with K too);
-// the fused mixed step 620 -> 616 us (645 with K too).
+// V loads, not their K loads.  Decode kernel us in one session, no hint / V
+// only / K and V: LLaMA-7B 777 / 712 / 733, GQA 439 / 406 / 428, GQA fp8
+// 235 / 221 / 231; the fused mixed step with K too 624 against 595.
 template <bool STREAM, typename T>
 __device__ __forceinline__ T load_once(const T* p) {
   if constexpr (STREAM) return __builtin_nontemporal_load(p);
