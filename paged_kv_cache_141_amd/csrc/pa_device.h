@@ -221,13 +221,14 @@ __device__ __forceinline__ void store4(uint8_t* p, float a, float b, float c, fl
     *reinterpret_cast<u32x2*>(p) = u32x2{cvt2<OT>(a, b), cvt2<OT>(c, d)};
 }
 
-// ---- V operands from token-major V rows.
+// ---- V operands from token-major V rows (the decode items; the chunk
+// items read theirs from LDS with transposing loads instead).
 //
 // The PV product O^T += V^T P^T takes V^T as its A operand: lane (r, lg)
 // must hold, for one output dim, the values of the eight keys of its K slots.
-// A V row in the cache (and in the chunk kernel's LDS tile) holds one key's
-// d values, so each lane reads, for each of its eight keys, a run of SEG
-// consecutive dims, and the operands are transposed in registers.  The runs
+// A V row in the cache holds one key's d values, so each lane reads, for
+// each of its eight keys, a run of SEG consecutive dims, and the operands
+// are transposed in registers.  The runs
 // of lane r are segments c = 0 .. NSEG-1 at dims 16*SEG*c + SEG*r; output
 // tile j = SEG*c + jj then holds dims 16*SEG*c + SEG*n + jj in its rows n, so
 // the accumulator element v of lane (r, lg) in tile j is dim
