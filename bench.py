@@ -75,21 +75,34 @@ def parse():
 
 
 class HipEvents:
-    """hipEvent_t pairs from the HIP runtime torch loaded (the one the library uses)."""
+    """hipEvent_t pairs from the HIP runtime torch loaded (the one the library uses).
 
-    def __init__(self):
+    The events only time work: they are read after a full device
+    synchronize, so they are created without the system-scope fence that a
+    default event performs when it is recorded (a cache writeback and
+    invalidate, which costs the step it brackets several microseconds)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
+
+    def __init__(self, fence=False):
         import torch
         lib = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
         self.hip = ctypes.CDLL(lib if os.path.exists(lib) else "libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.flags = 0 if fence else self.DISABLE_SYSTEM_FENCE
 
     def create(self):
         ev = ctypes.c_void_p()
-        assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+        assert self.hip.hipEventCreateWithFlags(ctypes.byref(ev), self.flags) == 0
         return ev.value
+
+    def record(self, e, stream):
+        """Record event e on a torch stream."""
+        assert self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream.cuda_stream)) == 0
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -480,9 +493,8 @@ def measure_step(w, args, prefix=0, cpu_seconds=0.0):
     is_chunk = (chunk_rows >= 65) & (w.q_dtype != "f32")
     chunk_pairs = [(ev.create(), ev.create()) for _ in range(args.steps)] if is_chunk.any() else None
     prefix_pairs = [(ev.create(), ev.create()) for _ in range(args.steps)] if prefix else None
-    cw = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    whole = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    cw = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    whole = [ev.create() for _ in range(args.steps + 1)]
 
     for _ in range(args.warmup):
         step.step()
@@ -494,12 +506,12 @@ def measure_step(w, args, prefix=0, cpu_seconds=0.0):
             pa.set_chunk_events(chunk_pairs[k][0], chunk_pairs[k][1])
         if prefix_pairs:
             pa.set_prefix_events(prefix_pairs[k][0], prefix_pairs[k][1])
-        whole[k].record(stream)
-        cw[k][0].record(stream)
+        ev.record(whole[k], stream)
+        ev.record(cw[k][0], stream)
         step.write_new()
-        cw[k][1].record(stream)
+        ev.record(cw[k][1], stream)
         step.attend()
-    whole[args.steps].record(stream)
+    ev.record(whole[args.steps], stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     pa.set_attention_events(None, None)
@@ -507,13 +519,15 @@ def measure_step(w, args, prefix=0, cpu_seconds=0.0):
     pa.set_prefix_events(None, None)
 
     step_s = (t1 - t0) / args.steps
-    step_ms = [whole[k].elapsed_time(whole[k + 1]) for k in range(args.steps)]
+    step_ms = [ev.elapsed_ms(whole[k], whole[k + 1]) for k in range(args.steps)]
     attn_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
-    cw_ms = [a.elapsed_time(b) for a, b in cw]
+    cw_ms = [ev.elapsed_ms(a, b) for a, b in cw]
     chunk_ms = [ev.elapsed_ms(a, b) for a, b in chunk_pairs] if chunk_pairs else None
     prefix_ms = [ev.elapsed_ms(a, b) for a, b in prefix_pairs] if prefix_pairs else None
-    for a, b in pairs + (chunk_pairs or []) + (prefix_pairs or []):
+    for a, b in pairs + cw + (chunk_pairs or []) + (prefix_pairs or []):
         ev.destroy(a), ev.destroy(b)
+    for e in whole:
+        ev.destroy(e)
     attn_s = float(np.mean(attn_ms)) / 1e3
     # the decode kernel reads the KV of the sequences routed to it (all but chunk sequences)
     eb = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}[w.kv_dtype]
