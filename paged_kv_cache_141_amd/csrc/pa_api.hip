@@ -60,8 +60,9 @@ pa_status_t check_attention_sizes(const pa_cache_t* c, int32_t num_q_heads, int3
   if (ceil_div(static_cast<int64_t>(max_query_len) * group, pa::kTileRows) > 0xFFFF) return PA_ERR_UNSUPPORTED;
   const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, c->num_kv_heads,
                                                      c->head_dim, max_seq_len, max_query_len,
-                                                     c->kv_dtype != PA_F32);
-  if (ceil_div(max_seq_len, w.partition) > 0xFFFF) return PA_ERR_UNSUPPORTED;
+                                                     c->kv_dtype != PA_F32, pa::kv_elem_bytes(c->kv_dtype));
+  if (ceil_div(max_seq_len, w.partition) + static_cast<int64_t>(w.split_max) * (w.split_f - 1) > 0xFFFF)
+    return PA_ERR_UNSUPPORTED;
   if (w.max_items > 0x7FFFFFFF / 64 || w.max_citems > 0x7FFFFFFF / 64) return PA_ERR_UNSUPPORTED;
   // the partials' size (the layout computes it without wrap-around): at most 2^48 bytes
   if (w.part_rows < 0 || static_cast<double>(w.part_rows) * (c->head_dim + 2) * 4.0 > 281474976710656.0)
@@ -126,7 +127,8 @@ int attention_entry(const void* q, int32_t q_dtype, const void* k_cache, const v
     return PA_ERR_SHAPE;
   const pa::WorkspaceLayout w = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, cache->num_kv_heads,
                                                      cache->head_dim, max_seq_len, max_query_len,
-                                                     q_dtype != PA_F32, prefix_len);
+                                                     q_dtype != PA_F32, pa::kv_elem_bytes(cache->kv_dtype),
+                                                     prefix_len);
   if (required) {   // the caller sizes (or supplies) the workspace once it knows the need
     *required = w.total;
     return PA_OK;
@@ -169,6 +171,8 @@ int attention_entry(const void* q, int32_t q_dtype, const void* k_cache, const v
   a.dec_per_seq = w.dec_per_seq;
   a.chunk_row_base = w.chunk_row_base;
   a.partition = w.partition;
+  a.split_f = w.split_f;
+  a.split_max = w.split_max;
   a.prefix_len = prefix_len;
   a.prefix_part = w.prefix_part;
   a.prefix_parts = w.prefix_parts;
@@ -347,7 +351,8 @@ pa_status_t pa_attention_workspace_size(const pa_cache_t* cache, int32_t num_q_h
   pa_status_t st = check_attention_sizes(cache, num_q_heads, num_seqs, num_tokens, max_seq_len, max_query_len);
   if (st != PA_OK) return st;
   *bytes = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, cache->num_kv_heads, cache->head_dim,
-                                max_seq_len, max_query_len, cache->kv_dtype != PA_F32)
+                                max_seq_len, max_query_len, cache->kv_dtype != PA_F32,
+                                pa::kv_elem_bytes(cache->kv_dtype))
                .total;
   return PA_OK;
 }
@@ -360,7 +365,8 @@ pa_status_t pa_attention_shared_prefix_workspace_size(const pa_cache_t* cache, i
   if (st != PA_OK) return st;
   if (prefix_len < 0 || (cache && prefix_len % cache->block_size != 0) || prefix_len > max_seq_len) return PA_ERR_SHAPE;
   *bytes = pa::workspace_layout(num_seqs, num_tokens, num_q_heads, cache->num_kv_heads, cache->head_dim,
-                                max_seq_len, max_query_len, cache->kv_dtype != PA_F32, prefix_len)
+                                max_seq_len, max_query_len, cache->kv_dtype != PA_F32,
+                                pa::kv_elem_bytes(cache->kv_dtype), prefix_len)
                .total;
   return PA_OK;
 }

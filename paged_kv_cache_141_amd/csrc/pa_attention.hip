@@ -5,21 +5,21 @@
 
 namespace pa {
 
-// Keys a work item visits (its partition clipped to the sequence and to the
-// causal reach of its last row), in units of the kernel's key step; 0 for an
-// item with nothing to do.  Must agree with the kernels' own bounds.
-__device__ __forceinline__ int item_size(int L, int ql, int G, int row0, int nrows, int part, int P,
-                                         int step, int kbase) {
+// Keys a work item visits (its keys [kstart, kstart + len) clipped to the
+// sequence and to the causal reach of its last row), in units of the
+// kernel's key step; 0 for an item with nothing to do.  Must agree with the
+// kernels' own bounds.
+__device__ __forceinline__ int item_size(int L, int ql, int G, int row0, int nrows, int kstart, int len,
+                                         int step) {
   const int rows = ql * G;
   const int last = min(rows, row0 + nrows) - 1;
   const int max_pos = L - ql + last / G;
-  const int kstart = kbase + part * P;
-  const int kend = min(min(L, kstart + P), max_pos + 1);
+  const int kend = min(min(L, kstart + len), max_pos + 1);
   return kend > kstart ? (kend - kstart + step - 1) / step : 0;
 }
 
 // One workgroup builds both work lists -- decode: (sequence, 16-row tile,
-// partition of a.partition keys); chunk: (sequence, 256-row block, partition
+// item of the tile's DecodeCut); chunk: (sequence, 256-row block, partition
 // of a.chunk_partition keys) -- longest item first: items are bucketed by the
 // number of key steps they visit (32 keys for decode, 64 for chunks, counted
 // in pairs for 16384-key partitions) and the buckets
@@ -30,6 +30,14 @@ __device__ __forceinline__ int item_size(int L, int ql, int G, int row0, int nro
 //
 // Sequences are taken 1024 at a time; a scan of their item counts flattens
 // the batch's items so that all threads share them evenly.
+//
+// Tail split (a.split_f > 1): a first pass counts the decode list's
+// (sequence, row tile) pairs and whole partitions.  With fewer than
+// kSplitItemsPerWave partitions per decode wave it sets S, the partitions
+// each tile cuts into fine items, so that the fine items come to
+// kSplitRounds partitions per wave: S = ceil(kSplitRounds * waves / (pairs *
+// Hkv)), at most a.split_max.  S goes to header[7] for the decode kernel
+// and the merge.
 __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
   constexpr int NB0 = kPartitionMax / 32 + 1;            // decode buckets: 0 .. 64 steps
   // chunk buckets: 0 .. 128, in units of cb tiles (2 for 16384-key partitions)
@@ -46,6 +54,44 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int G = a.group;
   for (int x = tid; x < 2 * NBMAX; x += 1024) hist[x / NBMAX][x % NBMAX] = 0;
+
+  int S = 0;
+  if (a.split_f > 1) {
+    // this thread's decode (sequence, row tile) pairs and their whole partitions
+    int pairs = 0, parts = 0;
+    for (int i = tid; i < a.num_seqs; i += 1024) {
+      const int L = min(a.seq_lens[i], a.max_seq_len);
+      const int rows = (a.qsl[i + 1] - a.qsl[i]) * G;
+      const int own = L - a.prefix_len;
+      if (rows > 0 && own > 0 && !is_chunk_seq(a, rows)) {
+        const int tiles = (rows + kTileRows - 1) / kTileRows;
+        pairs += tiles;
+        parts += tiles * ((own + a.partition - 1) / a.partition);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      pairs += __shfl_xor(pairs, o);
+      parts += __shfl_xor(parts, o);
+    }
+    if ((tid & 63) == 0) {
+      wtot[tid >> 6] = pairs;
+      scan[tid >> 6] = parts;
+    }
+    __syncthreads();
+    pairs = parts = 0;
+    for (int x = 0; x < 16; ++x) {
+      pairs += wtot[x];
+      parts += scan[x];
+    }
+    __syncthreads();                                     // wtot and scan are the batch scan's next
+    if (pairs > 0 && static_cast<int64_t>(parts) * a.num_kv_heads <
+                         static_cast<int64_t>(kSplitItemsPerWave) * a.decode_waves) {
+      const int64_t pk = static_cast<int64_t>(pairs) * a.num_kv_heads;
+      const int64_t want = static_cast<int64_t>(ceilf(kSplitRounds * a.decode_waves / static_cast<float>(pk)));
+      S = static_cast<int>(want < a.split_max ? want : a.split_max);
+    }
+  }
 
   // batch of sequences [base, base + 1024): fill the per-sequence table and the scan
   auto load_batch = [&](int base) {
@@ -86,7 +132,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
           n = ((rows + a.chunk_rows - 1) / a.chunk_rows) * np;
           np = -np;
         } else {
-          np = (own + a.partition - 1) / a.partition;
+          np = DecodeCut(own, a.partition, a.split_f, S).n;
           n = ((rows + kTileRows - 1) / kTileRows) * np;
         }
       }
@@ -124,9 +170,13 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
     const int npp = np < 0 ? -np : np;
     t = idx / npp;
     p = idx - t * npp;
-    bucket = list ? (item_size(L, ql, G, t * a.chunk_rows, a.chunk_rows, p, a.chunk_partition, kChunkKeys,
-                               a.prefix_len) + cb - 1) / cb
-                  : item_size(L, ql, G, t * kTileRows, kTileRows, p, a.partition, 32, a.prefix_len);
+    if (list) {
+      bucket = (item_size(L, ql, G, t * a.chunk_rows, a.chunk_rows, a.prefix_len + p * a.chunk_partition,
+                          a.chunk_partition, kChunkKeys) + cb - 1) / cb;
+    } else {
+      const DecodeCut cut(L - a.prefix_len, a.partition, a.split_f, S);
+      bucket = item_size(L, ql, G, t * kTileRows, kTileRows, a.prefix_len + cut.start(p), cut.len(p), 32);
+    }
   };
 
   // pass 1: bucket sizes.  With one batch, a thread's first KEEP items stay
@@ -236,6 +286,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
     a.header[2] = 0;
     a.header[4] = 0;
     a.header[3] = static_cast<int32_t>(total[1] < a.max_citems ? total[1] : a.max_citems);
+    a.header[7] = S;
   }
 }
 
@@ -268,11 +319,16 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
   const int i = uniform(lo);
   const int q0 = a.qsl[i];
   const int ql = a.qsl[i + 1] - q0;
-  const int row_pos = min(a.seq_lens[i], a.max_seq_len) - ql + (token - q0);
+  const int L = min(a.seq_lens[i], a.max_seq_len);
+  const int row_pos = L - ql + (token - q0);
   const int own = row_pos - a.prefix_len;               // the row's keys past the shared prefix, minus one
   const bool chunk_kind = is_chunk_seq(a, ql * a.group);
-  const int np = (a.prefix_len > 0 ? a.prefix_parts : 0) +
-                 (own >= 0 ? own / (chunk_kind ? a.chunk_partition : a.partition) + 1 : 0);
+  // the row's partials: the prefix pass's, then one per item up to the one
+  // holding the row's last key
+  int np = a.prefix_len > 0 ? a.prefix_parts : 0;
+  if (own >= 0)
+    np += chunk_kind ? own / a.chunk_partition + 1
+                     : DecodeCut(L - a.prefix_len, a.partition, a.split_f, uniform(a.header[7])).item_of(own) + 1;
   if (np <= 1 && a.prefix_len == 0) return;
   // the token's partial lists (head 0; heads follow at a stride of the list length)
   const int64_t list0 = partial_row(a, chunk_kind, i, token, token - q0, 0);
@@ -350,6 +406,10 @@ hipError_t launch_attention(int q, int kv, int d, int bs, const AttnArgs& a, hip
   AttnArgs f = a;                             // what every kernel of this step reads
   const bool fused = PA_FUSED_STEP && chunks && (f.step_groups = static_cast<int32_t>(step_groups(q, kv, d, bs))) > 0;
   f.chunk_partition = fused ? kChunkPartitionFused : kChunkPartition;
+  // the tail split serves the decode kernel's own list (in the fused step,
+  // chunk items make the tail)
+  if (fused) f.split_f = 1;
+  if (f.split_f > 1) f.decode_waves = static_cast<int32_t>(decode_waves(q, kv, d, bs));
   if (fused) {
     const double eb = kv == DT_F32 ? 4 : (kv == DT_FP8 ? 1 : 2);
     f.fused = 1;

@@ -20,13 +20,28 @@ __global__ __launch_bounds__(64, PA_DECODE_WAVES_PER_SIMD) void attn_kernel(Attn
   decode_items<CT, KV, D, BS, PA_DECODE_PREFETCH, PF8, STREAM>(a, threadIdx.x, blockIdx.x, gridDim.x);
 }
 
+template <int CT, int KV, int D, int BS>
+static int64_t decode_slots() {
+  static const int64_t slots = resident_groups(reinterpret_cast<const void*>(&attn_kernel<CT, KV, D, BS>), 64);
+  return slots;
+}
+
+int64_t decode_waves(int q, int kv, int d, int bs) {
+  int64_t n = 0;
+  dispatch_attention(q, kv, d, bs, [&](auto ct, auto kvt, auto dt, auto bst) -> hipError_t {
+    n = decode_slots<decltype(ct)::value, decltype(kvt)::value, decltype(dt)::value, decltype(bst)::value>();
+    return hipSuccess;
+  });
+  return n;
+}
+
 // One wave per resident slot (the persistent grid); each loops over work
 // items until the list is done.
 hipError_t launch_decode(int q, int kv, int d, int bs, const AttnArgs& a, hipStream_t stream) {
   return dispatch_attention(q, kv, d, bs, [&](auto ct, auto kvt, auto dt, auto bst) -> hipError_t {
     constexpr int CT = decltype(ct)::value, KV = decltype(kvt)::value;
     constexpr int D = decltype(dt)::value, BS = decltype(bst)::value;
-    static const int64_t slots = resident_groups(reinterpret_cast<const void*>(&attn_kernel<CT, KV, D, BS>), 64);
+    const int64_t slots = decode_slots<CT, KV, D, BS>();
     const int64_t want = a.max_items * a.num_kv_heads;
     const int64_t waves = want < slots ? (want > 0 ? want : 1) : slots;
     hipLaunchKernelGGL((attn_kernel<CT, KV, D, BS>), dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream, a);

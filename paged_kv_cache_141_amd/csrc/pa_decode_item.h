@@ -52,7 +52,8 @@ struct PartTable {
 };
 
 // One work item: sequence i, kv head h, rows [16*tile, 16*tile+16) of the
-// sequence's q_len*G (token, head-in-group) rows, keys of partition `part`.
+// sequence's q_len*G (token, head-in-group) rows, the keys of item `part` of
+// the tile's DecodeCut (S = split_s split partitions).
 //
 // Lane l = r + 16*lg (r = l % 16, lg = l / 16).  The 16x16 MFMA result tile
 // puts column r in lane r + 16*(row/4), element row%4.  The score tile is
@@ -64,7 +65,7 @@ struct PartTable {
 // run of consecutive dims of its V row (VGeo): one instruction covers four
 // consecutive keys' whole rows, and the runs are transposed in registers.
 template <int CT, int KV, int D, int BS, int PF16, int PF8, bool STREAM>
-__device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, int part, int h,
+__device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, int part, int split_s, int h,
                                           int lane) {
   constexpr int EBQ = Bytes<CT>::v;
   constexpr int EBK = Bytes<KV>::v;
@@ -92,8 +93,10 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   const int last_R = min(rows, row0 + kTileRows) - 1;
   const int max_pos = base_pos + last_R / G;
   const int min_pos = base_pos + row0 / G;
-  const int kstart = a.prefix_len + part * a.partition;   // keys past a shared prefix only
-  const int kend = min(min(L, kstart + a.partition), max_pos + 1);
+  const DecodeCut cut(L - a.prefix_len, a.partition, a.split_f, split_s);
+  const int klen = cut.len(part);
+  const int kstart = a.prefix_len + cut.start(part);       // keys past a shared prefix only
+  const int kend = min(min(L, kstart + klen), max_pos + 1);
   if (kstart >= kend) return;
 
   // Which dims K-step s gives lane group lg: [32s + 8lg, +8) -- or, for fp8
@@ -121,7 +124,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
 
   // The partition's block-table entries, held in registers.
   const int jbase = kstart / BS;
-  const int nbt = min(nblk - jbase, a.partition / BS);
+  const int nbt = min(nblk - jbase, klen / BS);
   PartTable btv;
   btv.load(a.block_tables + static_cast<int64_t>(i) * a.max_blocks_per_seq + jbase, nbt, lane);
 #if PA_DEBUG
@@ -275,7 +278,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   float ltot = lsum + __shfl_xor(lsum, 16);
   ltot += __shfl_xor(ltot, 32);
   if (!valid || row_pos < kstart) return;
-  const int nparts_row = (row_pos - a.prefix_len) / a.partition + 1;
+  const int nparts_row = cut.item_of(row_pos - a.prefix_len) + 1;
   auto dim0 = [&](int c, int v) { return 16 * SEG * c + SEG * (4 * lg + v); };
   if (nparts_row == 1 && a.prefix_len == 0) {
     const float inv = a.v_scale / ltot;
@@ -322,6 +325,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
 template <int CT, int KV, int D, int BS, int PF16, int PF8, bool STREAM>
 __device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int first, int base) {
   const int64_t total = static_cast<int64_t>(uniform(a.header[1])) * a.num_kv_heads;
+  const int split_s = uniform(a.header[7]);
   int w = first;
   while (true) {
     if (w < 0) {
@@ -339,7 +343,7 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int fi
     const int tp = uniform(a.items[2 * e + 1]);
     // (tile, partition) are the unsigned 16-bit halves of tp: tiles reach 0xFFFF
     attn_item<CT, KV, D, BS, PFD, PF8, STREAM>(
-        a, i, static_cast<int>(static_cast<uint32_t>(tp) >> 16), tp & 0xFFFF, h, lane);
+        a, i, static_cast<int>(static_cast<uint32_t>(tp) >> 16), tp & 0xFFFF, split_s, h, lane);
     w = -1;
   }
 }

@@ -80,6 +80,60 @@ inline int decode_partition(int64_t max_seq_len, int64_t num_seqs, int64_t num_k
   return max_seq_len >= kLongContext ? kPartitionLong : kPartitionShort;
 }
 
+// Tail split of the decode list.  Waves take items longest first, so the
+// step ends within about one item of the last wave's share; with few, large
+// items per wave that imbalance is a large part of the step (at head dim
+// 256, 2.5 items of 1 MB per wave, the last waves ran alone for the final
+// 25 % of a 437 us kernel).  So when there are fewer (sequence, kv head)
+// pairs than decode waves, partitions hold at least kSplitPartBytes of K and
+// V, and there are fewer than kSplitItemsPerWave of them per wave, each row
+// tile's last S partitions are cut into fine items; sorted longest first,
+// those end the list and even the waves out.  Each item costs its wave a
+// start-up (a chain of dependent loads that queue behind the step's KV
+// stream), so fine items hold at least kSplitBytes (256 keys at head dim
+// 256), and the plan kernel sizes the fine work to kSplitRounds partitions
+// per decode wave (at most kSplitItems fine items per row tile).  Measured
+// on 1k-32k contexts with 1024-key partitions: head dim 256 kernel 435 ->
+// 408 us (bf16), 226 -> 215 us (fp8); slower where items are smaller or more
+// numerous (fp8 at head dim 128, 256 KB partitions: 216 -> 228 us; bf16 at
+// 128, five partitions per wave: 1-2 %), so the split stays off there.  The
+// partial slots of a row tile are its items in key order.  Steps that can
+// hold prompt chunks keep whole partitions: there the chunk items end the
+// step.
+#ifndef PA_SPLIT_ROUNDS
+#define PA_SPLIT_ROUNDS 0.5
+#endif
+#ifndef PA_SPLIT_BYTES
+#define PA_SPLIT_BYTES (128 << 10)
+#endif
+#ifndef PA_SPLIT_PART_BYTES
+#define PA_SPLIT_PART_BYTES (512 << 10)
+#endif
+#ifndef PA_SPLIT_ITEMS_PER_WAVE
+#define PA_SPLIT_ITEMS_PER_WAVE 4
+#endif
+constexpr int kSplitMinKeys = 256;
+constexpr int64_t kSplitBytes = PA_SPLIT_BYTES;
+constexpr int64_t kSplitPartBytes = PA_SPLIT_PART_BYTES;
+constexpr int kSplitItems = 32;
+constexpr float kSplitRounds = PA_SPLIT_ROUNDS;
+constexpr int kSplitItemsPerWave = PA_SPLIT_ITEMS_PER_WAVE;
+// Fine items per split partition (1: no split), for head_dim and KV
+// elements of kv_bytes bytes.
+inline int split_factor(int64_t partition, int64_t num_seqs, int64_t num_kv_heads, bool chunks,
+                        int64_t head_dim, int64_t kv_bytes) {
+  const int64_t key_bytes = head_dim * 2 * kv_bytes;   // K and V of one key
+  if (!(kSplitRounds > 0.f) || chunks || num_seqs * num_kv_heads >= kManyPairs ||
+      partition * key_bytes < kSplitPartBytes)
+    return 1;
+  int64_t fine = kSplitMinKeys;                          // keys per fine item: a power of two
+  while (fine < partition && fine * key_bytes < kSplitBytes) fine *= 2;
+  return fine < partition ? static_cast<int>(partition / fine) : 1;
+}
+inline int64_t kv_elem_bytes(int32_t kv_dtype) {
+  return kv_dtype == PA_F32 ? 4 : (kv_dtype == PA_FP8_E4M3 ? 1 : 2);
+}
+
 // A sequence with more than kChunkMinRows - 1 (token, head) rows per kv head
 // (a prompt chunk) goes to the chunk kernel: 256-row blocks, 64-key LDS
 // tiles, context partitions of kChunkPartition keys.  Fewer rows (decode,
@@ -153,7 +207,7 @@ inline int64_t max_work_items(int64_t num_seqs, int64_t num_tokens, int64_t grou
 
 // Workspace carve-up (byte offsets, each 256-byte aligned).
 struct WorkspaceLayout {
-  size_t header;   // int32 [64]: [0]/[1] decode work counter/count, [2]/[3] chunk's, [4] prefix pass's
+  size_t header;   // int32 [64]: [0]/[1] decode work counter/count, [2]/[3] chunk's, [4] prefix pass's; [6] fused decode workgroups, [7] split partitions per row tile
   size_t items;    // int32x2 [max_items]: decode items (seq, tile << 16 | partition; unsigned halves)
   size_t citems;   // int32x2 [max_citems]: chunk items (seq, row block << 16 | partition)
   size_t part_m;   // float [rows]: running max (log2 units) per partition
@@ -177,6 +231,8 @@ struct WorkspaceLayout {
   int32_t chunk_parts;   // 0: the step has no chunk rows (the hints rule them out)
   int32_t dec_per_seq;
   int32_t partition;     // decode partition length in keys
+  int32_t split_f;       // fine items per split partition (1: no tail split)
+  int32_t split_max;     // most partitions a row tile has split (0 without the split)
   int32_t prefix_parts;  // partials of the shared-prefix pass (first in each row's list)
   int32_t prefix_part;   // keys per shared-prefix partition
 };
@@ -208,13 +264,20 @@ inline int32_t prefix_partition(int64_t prefix_len, int64_t num_tokens, int64_t 
 // max_query_len decides whether prompt chunks can occur at all.
 inline WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_tokens, int64_t num_q_heads,
                                         int64_t num_kv_heads, int64_t head_dim, int64_t max_seq_len,
-                                        int64_t max_query_len, bool chunk_path, int64_t prefix_len = 0) {
+                                        int64_t max_query_len, bool chunk_path, int64_t kv_bytes,
+                                        int64_t prefix_len = 0) {
   WorkspaceLayout w{};
   const int64_t group = num_kv_heads > 0 ? num_q_heads / num_kv_heads : 1;
   // keys past the shared prefix: what the decode and chunk kernels cover
   const int64_t own = max_seq_len - prefix_len > 0 ? max_seq_len - prefix_len : 1;
   w.partition = decode_partition(own, num_seqs, num_kv_heads);
-  w.max_items = max_work_items(num_seqs, num_tokens, group, own, kTileRows, w.partition);
+  const bool chunks = chunk_path && max_query_len * group >= kChunkMinRows;
+  w.split_f = split_factor(w.partition, num_seqs, num_kv_heads, chunks, head_dim, kv_bytes);
+  w.split_max = w.split_f > 1 ? kSplitItems / w.split_f : 0;
+  // items (and partial slots) per decode row tile: its partitions, plus
+  // split_f - 1 more for each split one
+  const int64_t dec_items_per_tile = ceil_div(own, w.partition) + static_cast<int64_t>(w.split_max) * (w.split_f - 1);
+  w.max_items = (ceil_div(num_tokens * group, kTileRows) + num_seqs) * dec_items_per_tile;
   w.max_citems = max_work_items(num_seqs, num_tokens, group, own, chunk_rows_for(head_dim), kChunkPartition);
   w.prefix_parts = 0;
   w.prefix_part = 0;
@@ -222,8 +285,7 @@ inline WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_tokens, in
     w.prefix_part = prefix_partition(prefix_len, num_tokens, group, num_kv_heads, chunk_rows_for(head_dim));
     w.prefix_parts = static_cast<int32_t>(ceil_div(prefix_len, w.prefix_part));
   }
-  const int64_t dparts = w.prefix_parts + ceil_div(own, w.partition);
-  const bool chunks = chunk_path && max_query_len * group >= kChunkMinRows;
+  const int64_t dparts = w.prefix_parts + dec_items_per_tile;
   const int64_t cparts = chunks ? w.prefix_parts + ceil_div(own, kChunkPartition) : 0;
   // one token-indexed list for both kinds ...
   const int64_t mp = dparts > cparts ? dparts : cparts;
@@ -310,6 +372,10 @@ struct AttnArgs {
   int32_t dec_parts, chunk_parts, dec_per_seq;
   int64_t chunk_row_base;
   int32_t partition;   // decode partition length in keys (decode_partition)
+  // Tail split (split_factor): fine items per split partition (1: none), the
+  // most partitions per row tile the plan may split, and the decode waves
+  // the plan sizes the fine work for.  The plan's choice of S is header[7].
+  int32_t split_f, split_max, decode_waves;
   // Shared prefix (cascade): every sequence's first prefix_len keys are the
   // same blocks (sequence 0's table row is read for them) and every query row
   // sits at or past prefix_len.  The prefix pass attends all rows to those
@@ -419,6 +485,8 @@ hipError_t launch_attention(int q_dtype, int kv_dtype, int head_dim, int block_s
 // (pa_chunk.hip; 16-bit q only); both draw items from the plan's lists.
 hipError_t launch_decode(int q_dtype, int kv_dtype, int head_dim, int block_size, const AttnArgs& a,
                          hipStream_t stream);
+// The decode kernel's grid: one wave per resident slot (pa_decode.hip).
+int64_t decode_waves(int q_dtype, int kv_dtype, int head_dim, int block_size);
 hipError_t launch_chunk(int q_dtype, int kv_dtype, int head_dim, int block_size, const AttnArgs& a,
                         hipStream_t stream);
 // The fused step kernel (pa_step.hip): its grid (one workgroup per CU, 0 if
