@@ -604,11 +604,12 @@ def measure_step(w, args, prefix=0, cpu_seconds=0.0):
 
 
 # The other configurations, each one record inside the default line: GQA
-# long-context decode, the mixed chunked-prefill step, the fp8 shared-prefix
+# long-context decode (head dims 128 and 256), the mixed chunked-prefill step, the fp8 shared-prefix
 # step at B = 16/32/64 through the block tables and through the shared-prefix
 # (cascade) entry point, its private-copy twin, and the tiny decode step.
 OTHER_CONFIGS = [
     ("gqa_long_decode", {}, False),
+    ("gqa_long_decode", {"head_dim": 256}, False),
     ("mixed_chunked_prefill", {}, False),
     ("fp8_shared_prefix", {"block_size": 16}, False),
     ("fp8_shared_prefix", {"block_size": 32}, False),

@@ -31,13 +31,12 @@ __device__ __forceinline__ int item_size(int L, int ql, int G, int row0, int nro
 // Sequences are taken 1024 at a time; a scan of their item counts flattens
 // the batch's items so that all threads share them evenly.
 //
-// Tail split (a.split_f > 1): a first pass counts the decode list's
-// (sequence, row tile) pairs and whole partitions.  With fewer than
-// kSplitItemsPerWave partitions per decode wave it sets S, the partitions
-// each tile cuts into fine items, so that the fine items come to
-// kSplitRounds partitions per wave: S = ceil(kSplitRounds * waves / (pairs *
-// Hkv)), at most a.split_max.  S goes to header[7] for the decode kernel
-// and the merge.
+// Tail split (a.split_f > 1): with fewer than kSplitItemsPerWave whole
+// partitions per decode wave the plan sets S, the partitions each row tile
+// cuts into fine items, so that the fine items come to kSplitRounds
+// partitions per wave: S = ceil(kSplitRounds * waves / (row tiles * Hkv)),
+// at most a.split_max.  S goes to header[7] for the decode kernel and the
+// merge.
 __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
   constexpr int NB0 = kPartitionMax / 32 + 1;            // decode buckets: 0 .. 64 steps
   // chunk buckets: 0 .. 128, in units of cb tiles (2 for 16384-key partitions)
@@ -55,43 +54,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
   const int G = a.group;
   for (int x = tid; x < 2 * NBMAX; x += 1024) hist[x / NBMAX][x % NBMAX] = 0;
 
-  int S = 0;
-  if (a.split_f > 1) {
-    // this thread's decode (sequence, row tile) pairs and their whole partitions
-    int pairs = 0, parts = 0;
-    for (int i = tid; i < a.num_seqs; i += 1024) {
-      const int L = min(a.seq_lens[i], a.max_seq_len);
-      const int rows = (a.qsl[i + 1] - a.qsl[i]) * G;
-      const int own = L - a.prefix_len;
-      if (rows > 0 && own > 0 && !is_chunk_seq(a, rows)) {
-        const int tiles = (rows + kTileRows - 1) / kTileRows;
-        pairs += tiles;
-        parts += tiles * ((own + a.partition - 1) / a.partition);
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      pairs += __shfl_xor(pairs, o);
-      parts += __shfl_xor(parts, o);
-    }
-    if ((tid & 63) == 0) {
-      wtot[tid >> 6] = pairs;
-      scan[tid >> 6] = parts;
-    }
-    __syncthreads();
-    pairs = parts = 0;
-    for (int x = 0; x < 16; ++x) {
-      pairs += wtot[x];
-      parts += scan[x];
-    }
-    __syncthreads();                                     // wtot and scan are the batch scan's next
-    if (pairs > 0 && static_cast<int64_t>(parts) * a.num_kv_heads <
-                         static_cast<int64_t>(kSplitItemsPerWave) * a.decode_waves) {
-      const int64_t pk = static_cast<int64_t>(pairs) * a.num_kv_heads;
-      const int64_t want = static_cast<int64_t>(ceilf(kSplitRounds * a.decode_waves / static_cast<float>(pk)));
-      S = static_cast<int>(want < a.split_max ? want : a.split_max);
-    }
-  }
+  int S = 0;                                             // tail split: partitions each row tile cuts
+  const bool one_batch = a.num_seqs <= 1024;
 
   // batch of sequences [base, base + 1024): fill the per-sequence table and the scan
   auto load_batch = [&](int base) {
@@ -124,6 +88,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
         }
       }
 #endif
+    }
+    if (i < a.num_seqs) {
       const int rows = ql * G;
       const int own = L - a.prefix_len;                   // keys past the shared prefix
       if (ql > 0 && own > 0) {
@@ -179,13 +145,38 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
     }
   };
 
+  // Tail split (the host allows it only below 1,024 (sequence, kv head)
+  // pairs, so with one batch, and only in steps without chunk rows): the
+  // batch's item count with whole partitions is then its partition count.
+  // With fewer than kSplitItemsPerWave per decode wave, S follows from the
+  // row tiles, and the batch is counted again with the split.
+  if (one_batch) {
+    load_batch(0);
+    if (a.split_f > 1 && static_cast<int64_t>(scan[1023]) * a.num_kv_heads <
+                             static_cast<int64_t>(kSplitItemsPerWave) * a.decode_waves) {
+      const int own = sL[tid] - a.prefix_len;
+      int tiles = sQ[tid] > 0 && own > 0 ? (sQ[tid] * G + kTileRows - 1) / kTileRows : 0;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) tiles += __shfl_xor(tiles, o);
+      if ((tid & 63) == 0) wtot[tid >> 6] = tiles;
+      __syncthreads();
+      int pairs = 0;
+      for (int x = 0; x < 16; ++x) pairs += wtot[x];
+      if (pairs > 0) {
+        const int64_t pk = static_cast<int64_t>(pairs) * a.num_kv_heads;
+        const int64_t want = static_cast<int64_t>(ceilf(kSplitRounds * a.decode_waves / static_cast<float>(pk)));
+        S = static_cast<int>(want < a.split_max ? want : a.split_max);
+        load_batch(0);                                   // (its first barrier orders the wtot reads)
+      }
+    }
+  }
+
   // pass 1: bucket sizes.  With one batch, a thread's first KEEP items stay
   // in registers for pass 2.
   constexpr int KEEP = 4;
-  const bool one_batch = a.num_seqs <= 1024;
   int cj[KEEP], cl[KEEP], ct[KEEP], cp[KEEP], cb2[KEEP];
   for (int base = 0; base < a.num_seqs; base += 1024) {
-    load_batch(base);
+    if (!one_batch) load_batch(base);
     const int nk = scan[1023];
 #pragma unroll
     for (int m = 0; m < KEEP; ++m) {
