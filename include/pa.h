@@ -390,8 +390,9 @@ pa_status_t pa_preferred_block_size(int32_t head_dim, int32_t kv_dtype, int32_t 
  *
  * A step whose pa_attention_workspace_size exceeds PA_NOALLOC_SCRATCH_BYTES
  * returns PA_ERR_TOO_LARGE before anything is enqueued (the decode steps of
- * the LLaMA-7B shape need about 4 MiB, 64 sequences at 32k contexts about
- * 32 MiB; a 3,840-token mixed step with 9k contexts needs about 305 MiB and
+ * the LLaMA-7B shape need about 4 MiB, 64 sequences at 32k contexts with 8
+ * kv heads of dim 128 about 57 MiB with a bf16 cache and 33 MiB with fp8; a
+ * 3,840-token mixed step with 9k contexts needs about 305 MiB and
  * takes pa_attention with a caller workspace).  All calls on one device
  * share that device's array, which keeps the last call's contents: calls
  * that overlap on one device (two streams, or two host threads) race and

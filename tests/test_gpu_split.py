@@ -110,3 +110,20 @@ def test_no_split_where_it_does_not_pay():
     step.attend()
     torch.cuda.synchronize()
     assert split_partitions(step) == 0
+
+
+def test_split_after_shared_prefix():
+    # pa_attention_shared_prefix: the prefix pass's partials come first in
+    # each row's list, the split suffix items after them
+    P = 4096
+    own = log_lens(141300, 8, 1500, 12000)
+    w = build("split_pfx", 141301, P + own, [1] * 6 + [3, 2], num_q_heads=16, num_kv_heads=4, head_dim=256,
+              block_size=16, kv_dtype="bf16", shared_prefix_len=P)
+    step = wd.stage(w)
+    step.use_shared_prefix(P)
+    out = step.attend()
+    torch.cuda.synchronize()
+    got = codecs.decode(wd.to_host_bits(out), w.q_dtype)
+    assert split_partitions(step) > 0
+    kp, vp = fill_pools(w)
+    assert_close(w, got, attention(w, kp, vp), label="split after a 4,096-token shared prefix")

@@ -9,7 +9,7 @@ import pytest
 
 import paged_kv_cache_141_amd as pa
 from workloads import device as wd
-from workloads.generate import random_mixed
+from workloads.generate import build, random_mixed
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: the calls below fail or finish before any launch
 
@@ -66,6 +66,10 @@ def test_noalloc_equals_pa_attention_on_two_calls():
         random_mixed(84, num_decode=12, chunk_specs=[], max_decode_len=3000, num_q_heads=16, num_kv_heads=4,
                      head_dim=64, block_size=32, kv_dtype="fp8_e4m3", q_dtype="bf16", k_scale=2.0 ** -5,
                      v_scale=2.0 ** -5),
+        # ... then a decode step whose last partitions the plan cuts finer
+        # (head dim 256, 9k-14k contexts): more partial slots per row
+        build("noalloc_split", 85, [9000, 14000, 11000, 9500], [1, 1, 2, 1], num_q_heads=16, num_kv_heads=4,
+              head_dim=256, block_size=16, kv_dtype="bf16"),
     ]
     for k, w in enumerate(steps):
         need = ctypes.c_size_t(0)
@@ -75,6 +79,8 @@ def test_noalloc_equals_pa_attention_on_two_calls():
         assert 0 < need.value <= pa.NOALLOC_SCRATCH_BYTES
         step = wd.stage(w)
         ref = wd.to_host_bits(step.attend()).copy()             # pa_attention, caller workspace
+        if w.name == "noalloc_split":                           # the plan did cut partitions finer
+            assert int(step.workspace[:64].view(torch.int32)[7].item()) > 0
         out = torch.full_like(step.q, float("nan"))
         _noalloc(step, out)
         torch.cuda.synchronize()
