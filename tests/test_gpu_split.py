@@ -127,3 +127,28 @@ def test_split_after_shared_prefix():
     assert split_partitions(step) > 0
     kp, vp = fill_pools(w)
     assert_close(w, got, attention(w, kp, vp), label="split after a 4,096-token shared prefix")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_decode_steps(seed):
+    # seeded random decode-only steps around the split's conditions: head dim
+    # 128 or 256, every cache type, block size 16/32/64, group 1-8, 2-24
+    # sequences with contexts up to 30k and up to 4 query tokens each; every
+    # row against the oracle whether or not the plan splits
+    rng = np.random.default_rng([141400, seed])
+    d = int(rng.choice([128, 256]))
+    kv, q = [("bf16", "bf16"), ("f16", "f16"), ("fp8_e4m3", "bf16"), ("fp8_e4m3", "f16")][int(rng.integers(4))]
+    B = int(rng.choice([16, 32, 64]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    n = int(rng.integers(2, 25))
+    L = log_lens(141401 + seed, n, 300, 30000)
+    ql = rng.integers(1, 5, size=n)
+    ql = np.minimum(ql, max(1, 64 // G))           # q_len * G < 65: decode rows
+    fp8 = kv == "fp8_e4m3"
+    w = build("split_rand", 141402 + seed, L, ql, num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=d, block_size=B,
+              kv_dtype=kv, q_dtype=q, k_scale=2.0 ** -5 if fp8 else 1.0, v_scale=2.0 ** -5 if fp8 else 1.0)
+    step, got, ref = run(w)
+    label = f"random decode seed {seed}: kv={kv} d={d} B={B} G={G} Hkv={Hkv} seqs={n}, split {split_partitions(step)}"
+    say(label)
+    assert_close(w, got, ref, label=label)
