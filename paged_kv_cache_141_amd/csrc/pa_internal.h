@@ -217,7 +217,8 @@ struct WorkspaceLayout {
   int64_t max_items;
   int64_t max_citems;
   // Partial rows.  A (token, q head) row owns dec_parts consecutive partial
-  // rows if its sequence is decode-routed, chunk_parts if chunk-routed.
+  // rows if its sequence is decode-routed (one per decode item of its row
+  // tile, the tail split's fine items included), chunk_parts if chunk-routed.
   // Decode rows sit at slot (i * dec_per_seq + local token) when dec_per_seq
   // > 0, at the token index otherwise; chunk rows at chunk_row_base + their
   // token index.  Two layouts, the smaller is used: one token-indexed list
