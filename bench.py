@@ -68,6 +68,8 @@ def parse():
                     help="default run only: skip the records of the other configurations")
     ap.add_argument("--config-cpu-seconds", type=float, default=3.0,
                     help="oracle budget for each of the other configurations' records (0 disables it)")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="time the step as pa_reshape_and_cache + pa_attention instead of pa_write_and_attend")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="attend through pa_attention_shared_prefix over the workload's common prefix "
                          "(fp8_shared_prefix): the prefix is attended once for all rows")
@@ -494,16 +496,23 @@ def measure_step(w, args, prefix=0, cpu_seconds=0.0):
     chunk_pairs = [(ev.create(), ev.create()) for _ in range(args.steps)] if is_chunk.any() else None
     prefix_pairs = [(ev.create(), ev.create()) for _ in range(args.steps)] if prefix else None
     whole = (ev.create(), ev.create())
+    # A step is the cache write of its new tokens and its attention: one
+    # pa_write_and_attend call (the write in the plan's launch), or, through
+    # the shared-prefix entry point or with --separate-write, the two calls.
+    joint = not prefix and not args.separate_write
 
     for _ in range(args.warmup):
-        step.step()
+        if joint:
+            step.write_and_attend()
+        else:
+            step.step()
     torch.cuda.synchronize()
     # The timed steps carry the events the kernel rooflines need (the library
-    # records them around its kernels) and, on every fourth step, a pair
-    # around the cache write; each event costs the step a little.  Per-step
-    # times are the periods between consecutive attention kernels' starts
-    # (each spans one whole step: merge, cache write, plan).
-    cw = {k: (ev.create(), ev.create()) for k in range(0, args.steps, 4)}
+    # records them around its kernels) and, with separate calls, a pair around
+    # the cache write on every fourth step; each event costs the step a
+    # little.  Per-step times are the periods between consecutive attention
+    # kernels' starts (each spans one whole step: merge, cache write, plan).
+    cw = {} if joint else {k: (ev.create(), ev.create()) for k in range(0, args.steps, 4)}
     t0 = time.perf_counter()
     ev.record(whole[0], stream)
     for k in range(args.steps):
@@ -512,6 +521,9 @@ def measure_step(w, args, prefix=0, cpu_seconds=0.0):
             pa.set_chunk_events(chunk_pairs[k][0], chunk_pairs[k][1])
         if prefix_pairs:
             pa.set_prefix_events(prefix_pairs[k][0], prefix_pairs[k][1])
+        if joint:
+            step.write_and_attend()
+            continue
         if k in cw:
             ev.record(cw[k][0], stream)
             step.write_new()
@@ -574,7 +586,10 @@ def measure_step(w, args, prefix=0, cpu_seconds=0.0):
         "attention_kernel_kv_bytes": decode_bytes,
         "attention_kernel_unique_kv_bytes": unique_bytes,
         "attention_kernel_logical_GBps": round(decode_bytes / attn_s / 1e9, 2),
-        "cache_write_us": round(float(np.mean(cw_ms)) * 1e3, 2),
+        "step_calls": "pa_write_and_attend" if joint else "pa_reshape_and_cache + pa_attention" +
+                      ("_shared_prefix" if prefix else ""),
+        # with the joint call the write shares the plan's launch and has no time of its own
+        "cache_write_us": round(float(np.mean(cw_ms)) * 1e3, 2) if cw_ms else None,
         "roofline": {"bound": "hbm", "kernel": main_kernel, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},

@@ -101,6 +101,35 @@ pa_status_t check_prefix(const pa_cache_t* c, int32_t q_dtype, int32_t max_seq_l
   return PA_OK;
 }
 
+// The cache write's checks and launch arguments (pa_reshape_and_cache and
+// pa_write_and_attend).  a.num_tokens == 0 means nothing to write.
+pa_status_t cache_write_args(const void* key, const void* value, int32_t src_dtype, void* k_cache, void* v_cache,
+                             const pa_cache_t* cache, const int64_t* slot_mapping, int32_t num_tokens,
+                             pa::CacheWriteArgs& a) {
+  a = pa::CacheWriteArgs{};
+  pa_status_t st = check_cache(cache);
+  if (st != PA_OK) return st;
+  if (src_dtype != PA_F32 && src_dtype != PA_F16 && src_dtype != PA_BF16) return PA_ERR_DTYPE;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+  a.key = key;
+  a.value = value;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.slots = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.head_dim = cache->head_dim;
+  a.block_size = cache->block_size;
+  a.num_slots = static_cast<int64_t>(cache->num_blocks) * cache->block_size;
+  a.debug = PA_DEBUG ? pa::debug_words() : nullptr;
+  if (PA_DEBUG && !a.debug) return PA_ERR_HIP;
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
+  return PA_OK;
+}
+
 }  // namespace
 
 namespace pa {
@@ -110,7 +139,8 @@ int attention_entry(const void* q, int32_t q_dtype, const void* k_cache, const v
                     const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
                     int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
                     int32_t max_query_len, int32_t prefix_len, float scale, void* out,
-                    void* workspace, size_t workspace_bytes, void* stream, size_t* required) {
+                    void* workspace, size_t workspace_bytes, void* stream, size_t* required,
+                    const CacheWriteArgs* write, int32_t write_src) {
   if (required) *required = 0;
   pa_status_t st = check_attention_sizes(cache, num_q_heads, num_seqs, num_tokens, max_seq_len, max_query_len);
   if (st != PA_OK) return st;
@@ -119,7 +149,13 @@ int attention_entry(const void* q, int32_t q_dtype, const void* k_cache, const v
   if (!pairing_ok(q_dtype, cache->kv_dtype)) return PA_ERR_DTYPE;
   if (!isfinite(scale) || !(scale > 0.f)) return PA_ERR_UNSUPPORTED;
   if (cache->head_dim == 256 && q_dtype == PA_F32) return PA_ERR_UNSUPPORTED;   // 16-bit queries only
-  if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+  if (num_seqs == 0 || num_tokens == 0) {       // no attention: the cache write alone, if any
+    if (!write || write->num_tokens == 0) return PA_OK;
+    return pa::launch_reshape_and_cache(write_src, cache->kv_dtype, *write, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess
+               ? PA_OK
+               : PA_ERR_HIP;
+  }
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !out)
     return PA_ERR_NULL;
   if (max_blocks_per_seq <= 0 || static_cast<int64_t>(max_blocks_per_seq) * cache->block_size <
@@ -184,7 +220,7 @@ int attention_entry(const void* q, int32_t q_dtype, const void* k_cache, const v
   a.rescale_slack = pa::kRescaleSlack / a.score_scale;
   a.v_scale = cache->v_scale;
   const hipError_t e = pa::launch_attention(q_dtype, cache->kv_dtype, cache->head_dim, cache->block_size, a,
-                                            static_cast<hipStream_t>(stream), g_events);
+                                            static_cast<hipStream_t>(stream), g_events, write, write_src);
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -212,30 +248,29 @@ const char* pa_status_string(pa_status_t s) {
 pa_status_t pa_reshape_and_cache(const void* key, const void* value, int32_t src_dtype, void* k_cache,
                                  void* v_cache, const pa_cache_t* cache, const int64_t* slot_mapping,
                                  int32_t num_tokens, void* stream) {
-  pa_status_t st = check_cache(cache);
-  if (st != PA_OK) return st;
-  if (src_dtype != PA_F32 && src_dtype != PA_F16 && src_dtype != PA_BF16) return PA_ERR_DTYPE;
-  if (num_tokens < 0) return PA_ERR_SHAPE;
-  if (num_tokens == 0) return PA_OK;
-  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
-  pa::CacheWriteArgs a{};
-  a.key = key;
-  a.value = value;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.slots = slot_mapping;
-  a.num_tokens = num_tokens;
-  a.num_kv_heads = cache->num_kv_heads;
-  a.head_dim = cache->head_dim;
-  a.block_size = cache->block_size;
-  a.num_slots = static_cast<int64_t>(cache->num_blocks) * cache->block_size;
-  a.debug = PA_DEBUG ? pa::debug_words() : nullptr;
-  if (PA_DEBUG && !a.debug) return PA_ERR_HIP;
-  a.k_scale = cache->k_scale;
-  a.v_scale = cache->v_scale;
+  pa::CacheWriteArgs a;
+  const pa_status_t st = cache_write_args(key, value, src_dtype, k_cache, v_cache, cache, slot_mapping, num_tokens, a);
+  if (st != PA_OK || a.num_tokens == 0) return st;
   const hipError_t e = pa::launch_reshape_and_cache(src_dtype, cache->kv_dtype, a,
                                                     static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status_t pa_write_and_attend(const void* key, const void* value, int32_t src_dtype, const int64_t* slot_mapping,
+                                int32_t num_new_tokens, const void* q, int32_t q_dtype, void* k_cache,
+                                void* v_cache, const pa_cache_t* cache, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
+                                int32_t num_q_heads, int32_t max_seq_len, int32_t max_query_len, float scale,
+                                void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  pa::CacheWriteArgs w;
+  const pa_status_t st =
+      cache_write_args(key, value, src_dtype, k_cache, v_cache, cache, slot_mapping, num_new_tokens, w);
+  if (st != PA_OK) return st;
+  return static_cast<pa_status_t>(pa::attention_entry(
+      q, q_dtype, k_cache, v_cache, cache, block_tables, max_blocks_per_seq, seq_lens, query_start_loc, num_seqs,
+      num_tokens, num_q_heads, max_seq_len, max_query_len, 0, scale, out, workspace, workspace_bytes, stream,
+      nullptr, w.num_tokens > 0 ? &w : nullptr, src_dtype));
 }
 
 pa_status_t pa_copy_blocks(const void* src_k, const void* src_v, const pa_cache_t* src_cache, void* dst_k,

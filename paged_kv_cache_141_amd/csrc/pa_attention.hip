@@ -1,6 +1,7 @@
 // pa_attention.hip -- one attention step: the work-list kernel, the decode
 // and chunk kernels (pa_decode.hip, pa_chunk.hip), and the log-sum-exp merge
 // of split-context partials.
+#include "pa_cache_write.h"
 #include "pa_device.h"
 
 namespace pa {
@@ -37,7 +38,7 @@ __device__ __forceinline__ int item_size(int L, int ql, int G, int row0, int nro
 // partitions per wave: S = ceil(kSplitRounds * waves / (row tiles * Hkv)),
 // at most a.split_max.  S goes to header[7] for the decode kernel and the
 // merge.
-__global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
+__device__ __forceinline__ void plan_block(AttnArgs a) {
   constexpr int NB0 = kPartitionMax / 32 + 1;            // decode buckets: 0 .. 64 steps
   // chunk buckets: 0 .. 128, in units of cb tiles (2 for 16384-key partitions)
   constexpr int CBMAX = kChunkPartitionMax > 8192 ? kChunkPartitionMax / 8192 : 1;
@@ -281,6 +282,53 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) {
   }
 }
 
+__global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) { plan_block(a); }
+
+// The plan beside a cache write of the step's new tokens, in one launch:
+// workgroup 0 builds the work lists while the others scatter the new K/V
+// rows, kPlanWriteTokens tokens of one kv head each.  The two are
+// independent (the plan reads only the step's metadata), and the attention
+// kernels that follow see both.
+constexpr int kPlanWriteTokens = 64;
+
+template <int SRC, int KV>
+__global__ __launch_bounds__(1024) void plan_write_kernel(AttnArgs a, CacheWriteArgs w) {
+  if (blockIdx.x == 0) {
+    plan_block(a);
+    return;
+  }
+  const int b = static_cast<int>(blockIdx.x) - 1;
+  const int h = b % w.num_kv_heads;
+  const int t0 = (b / w.num_kv_heads) * kPlanWriteTokens;
+  write_rows<SRC, KV>(w, t0, min(kPlanWriteTokens, w.num_tokens - t0), h, threadIdx.x, 1024);
+}
+
+template <int SRC>
+static hipError_t launch_plan_write_kv(int kv, const AttnArgs& a, const CacheWriteArgs& w, unsigned groups,
+                                       hipStream_t stream) {
+  switch (kv) {
+    case DT_F32: hipLaunchKernelGGL((plan_write_kernel<SRC, DT_F32>), dim3(groups), dim3(1024), 0, stream, a, w); break;
+    case DT_F16: hipLaunchKernelGGL((plan_write_kernel<SRC, DT_F16>), dim3(groups), dim3(1024), 0, stream, a, w); break;
+    case DT_BF16: hipLaunchKernelGGL((plan_write_kernel<SRC, DT_BF16>), dim3(groups), dim3(1024), 0, stream, a, w); break;
+    case DT_FP8: hipLaunchKernelGGL((plan_write_kernel<SRC, DT_FP8>), dim3(groups), dim3(1024), 0, stream, a, w); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+static hipError_t launch_plan_write(int src, int kv, const AttnArgs& a, const CacheWriteArgs& w, hipStream_t stream) {
+  if (w.head_dim > 256 || w.head_dim % 8 != 0 || w.num_kv_heads <= 0) return hipErrorInvalidValue;
+  const int64_t groups = 1 + (static_cast<int64_t>(w.num_tokens) + kPlanWriteTokens - 1) / kPlanWriteTokens *
+                                 w.num_kv_heads;
+  if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
+  switch (src) {
+    case DT_F32: return launch_plan_write_kv<DT_F32>(kv, a, w, static_cast<unsigned>(groups), stream);
+    case DT_F16: return launch_plan_write_kv<DT_F16>(kv, a, w, static_cast<unsigned>(groups), stream);
+    case DT_BF16: return launch_plan_write_kv<DT_BF16>(kv, a, w, static_cast<unsigned>(groups), stream);
+  }
+  return hipErrorInvalidValue;
+}
+
 // Merge of split-context partials.  One workgroup (4 waves) per token and
 // group of q heads, or per token and all its heads (in turn) when the step
 // has many tokens; tokens whose keys fit one partition were written by the
@@ -383,12 +431,13 @@ static void launch_reduce(const AttnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((reduce_kernel<OT, D>), grid, dim3(256), 0, stream, a);
 }
 
-// plan -> [shared-prefix pass] -> decode kernel -> chunk kernel (when a
-// prompt chunk can be present) -> partition merge.  ev[0..1] bracket the decode kernel, ev[4..5] the
+// plan (with the step's cache write when `write` is given) -> [shared-prefix
+// pass] -> decode kernel -> chunk kernel (when a prompt chunk can be present)
+// -> partition merge.  ev[0..1] bracket the decode kernel, ev[4..5] the
 // shared-prefix pass, ev[2..3] the chunk
 // kernel (each may be null).
 hipError_t launch_attention(int q, int kv, int d, int bs, const AttnArgs& a, hipStream_t stream,
-                            const hipEvent_t* ev) {
+                            const hipEvent_t* ev, const CacheWriteArgs* write, int write_src) {
   // the pairing and shape must exist before anything is enqueued
   hipError_t e = dispatch_attention(q, kv, d, bs, [](auto, auto, auto, auto) { return hipSuccess; });
   if (e != hipSuccess) return e;
@@ -407,8 +456,12 @@ hipError_t launch_attention(int q, int kv, int d, int bs, const AttnArgs& a, hip
     f.step_dec_us = static_cast<float>(32.0 * d * 2 * eb / kFusedDecodeBytesPerUs);
     f.step_chunk_us = static_cast<float>(64.0 * a.chunk_rows * d * 4 / kFusedChunkFlopsPerUs);
   }
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, f);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (write && write->num_tokens > 0) {       // the step's cache write in the plan's launch
+    if ((e = launch_plan_write(write_src, kv, f, *write, stream)) != hipSuccess) return e;
+  } else {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, f);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (a.prefix_len > 0) {                     // the shared prefix, all rows at once
     AttnArgs p = f;
     p.prefix_pass = 1;

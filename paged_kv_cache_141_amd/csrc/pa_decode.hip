@@ -28,7 +28,7 @@ static int64_t decode_slots() {
 
 int64_t decode_waves(int q, int kv, int d, int bs) {
   int64_t n = 0;
-  dispatch_attention(q, kv, d, bs, [&](auto ct, auto kvt, auto dt, auto bst) -> hipError_t {
+  (void)dispatch_attention(q, kv, d, bs, [&](auto ct, auto kvt, auto dt, auto bst) -> hipError_t {
     n = decode_slots<decltype(ct)::value, decltype(kvt)::value, decltype(dt)::value, decltype(bst)::value>();
     return hipSuccess;
   });

@@ -454,13 +454,17 @@ struct CommitArgs {
 // The body of pa_attention / pa_attention_shared_prefix (a pa_status_t):
 // validates, lays out the workspace and launches.  With `required` non-null
 // it only writes the workspace bytes the step needs there (after the same
-// validation) and launches nothing.  (pa_api.hip)
+// validation) and launches nothing.  `write` (may be null; checked by the
+// caller): the step's cache write of new tokens (source dtype write_src),
+// launched beside the work-list build -- or alone when the step has no
+// attention rows.  (pa_api.hip)
 int attention_entry(const void* q, int32_t q_dtype, const void* k_cache, const void* v_cache,
                     const pa_cache_t* cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* seq_lens, const int32_t* query_start_loc, int32_t num_seqs,
                     int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
                     int32_t max_query_len, int32_t prefix_len, float scale, void* out,
-                    void* workspace, size_t workspace_bytes, void* stream, size_t* required);
+                    void* workspace, size_t workspace_bytes, void* stream, size_t* required,
+                    const CacheWriteArgs* write = nullptr, int32_t write_src = 0);
 
 // Launchers.  Each returns hipSuccess or the launch error.
 
@@ -480,8 +484,11 @@ hipError_t launch_commit_step(const CommitArgs& a, hipStream_t stream);       //
 // events[0..1] (may be null) are recorded around the decode kernel,
 // events[2..3] around the chunk kernel and events[4..5] around the
 // shared-prefix pass.  (pa_attention.hip)
+// write (may be null): the step's cache write (source dtype write_src),
+// launched beside the work-list build instead of on its own.
 hipError_t launch_attention(int q_dtype, int kv_dtype, int head_dim, int block_size,
-                            const AttnArgs& a, hipStream_t stream, const hipEvent_t* events);
+                            const AttnArgs& a, hipStream_t stream, const hipEvent_t* events,
+                            const CacheWriteArgs* write = nullptr, int write_src = 0);
 // The decode kernel alone (pa_decode.hip) and the chunk kernel alone
 // (pa_chunk.hip; 16-bit q only); both draw items from the plan's lists.
 hipError_t launch_decode(int q_dtype, int kv_dtype, int head_dim, int block_size, const AttnArgs& a,

@@ -29,13 +29,20 @@ int g_fail = 0;
 pa::AttnArgs g_attn;
 pa::CacheWriteArgs g_write;
 int g_attn_launches = 0, g_write_launches = 0, g_other_launches = 0;
+int g_joint_writes = 0, g_joint_src = -1;   // cache writes handed to the attention launcher
 }  // namespace
 
 // ---- stub launchers: record what the host layer would launch
 namespace pa {
-hipError_t launch_attention(int, int, int, int, const AttnArgs& a, hipStream_t, const hipEvent_t*) {
+hipError_t launch_attention(int, int, int, int, const AttnArgs& a, hipStream_t, const hipEvent_t*,
+                            const CacheWriteArgs* w, int src) {
   g_attn = a;
   ++g_attn_launches;
+  if (w) {
+    g_write = *w;
+    g_joint_src = src;
+    ++g_joint_writes;
+  }
   return hipSuccess;
 }
 hipError_t launch_reshape_and_cache(int, int, const CacheWriteArgs& a, hipStream_t) {
@@ -203,6 +210,34 @@ void valid_calls() {
         PA_OK);
   CHECK(g_write_launches == 1 && g_write.num_slots == 77 * 32 && g_write.num_tokens == 9 &&
         g_write.k_scale == 0.5f && g_write.v_scale == 0.25f);
+  // the joint write-and-attend call: both argument sets checked before any
+  // launch; the write goes to the attention launcher, or alone without rows
+  {
+    const pa_cache_t cb = cache(77, 32, 4, 128, PA_BF16);
+    const int64_t* slots = static_cast<const int64_t*>(FAKE);
+    const int a0 = g_attn_launches, w0 = g_write_launches, j0 = g_joint_writes;
+    CHECK(pa_write_and_attend(FAKE, FAKE, PA_F32, slots, 5, FAKE, PA_BF16, FAKE, FAKE, &cb, FAKEI, 4, FAKEI, FAKEI,
+                              2, 2, 8, 100, 1, 0.1f, FAKE, FAKE, size_t(1) << 40, nullptr) == PA_OK);
+    CHECK(g_attn_launches == a0 + 1 && g_joint_writes == j0 + 1 && g_write_launches == w0);
+    CHECK(g_write.num_tokens == 5 && g_write.num_slots == 77 * 32 && g_joint_src == PA_F32);
+    // a bad write argument or a bad attention argument: nothing launched
+    CHECK(pa_write_and_attend(nullptr, FAKE, PA_F32, slots, 5, FAKE, PA_BF16, FAKE, FAKE, &cb, FAKEI, 4, FAKEI,
+                              FAKEI, 2, 2, 8, 100, 1, 0.1f, FAKE, FAKE, size_t(1) << 40, nullptr) == PA_ERR_NULL);
+    CHECK(pa_write_and_attend(FAKE, FAKE, PA_FP8_E4M3, slots, 5, FAKE, PA_BF16, FAKE, FAKE, &cb, FAKEI, 4, FAKEI,
+                              FAKEI, 2, 2, 8, 100, 1, 0.1f, FAKE, FAKE, size_t(1) << 40, nullptr) == PA_ERR_DTYPE);
+    CHECK(pa_write_and_attend(FAKE, FAKE, PA_F32, slots, 5, FAKE, PA_F16, FAKE, FAKE, &cb, FAKEI, 4, FAKEI, FAKEI,
+                              2, 2, 8, 100, 1, 0.1f, FAKE, FAKE, size_t(1) << 40, nullptr) == PA_ERR_DTYPE);
+    CHECK(pa_write_and_attend(FAKE, FAKE, PA_F32, slots, 5, FAKE, PA_BF16, FAKE, FAKE, &cb, FAKEI, 4, FAKEI, FAKEI,
+                              2, 2, 8, 100, 1, 0.1f, FAKE, FAKE, 16, nullptr) == PA_ERR_WORKSPACE);
+    CHECK(g_attn_launches == a0 + 1 && g_joint_writes == j0 + 1 && g_write_launches == w0);
+    // no new tokens: pa_attention; no attention rows: the write alone
+    CHECK(pa_write_and_attend(nullptr, nullptr, PA_F32, nullptr, 0, FAKE, PA_BF16, FAKE, FAKE, &cb, FAKEI, 4, FAKEI,
+                              FAKEI, 2, 2, 8, 100, 1, 0.1f, FAKE, FAKE, size_t(1) << 40, nullptr) == PA_OK);
+    CHECK(g_attn_launches == a0 + 2 && g_joint_writes == j0 + 1);
+    CHECK(pa_write_and_attend(FAKE, FAKE, PA_BF16, slots, 3, nullptr, PA_BF16, FAKE, FAKE, &cb, nullptr, 4, nullptr,
+                              nullptr, 0, 0, 8, 100, 1, 0.1f, nullptr, nullptr, 0, nullptr) == PA_OK);
+    CHECK(g_attn_launches == a0 + 2 && g_write_launches == w0 + 1 && g_write.num_tokens == 3);
+  }
   // step inputs and commit reach their launchers
   const int before = g_other_launches;
   CHECK(pa_prepare_step(FAKEI, 8, 4, FAKEI, FAKEI, FAKEI, 2, 3, 16, static_cast<int32_t*>(FAKE),

@@ -1,0 +1,61 @@
+"""pa_write_and_attend: the cache write of a step's new tokens and the
+step's attention in one call, against the two separate calls on the same
+inputs -- pools and output bit-exact -- and against the fp64 oracle."""
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import codecs
+from workloads import device as wd
+from workloads.generate import build, random_mixed
+
+from full_oracle import assert_close, attention, fill_pools, say
+
+torch = pytest.importorskip("torch")
+import paged_kv_cache_141_amd as pa  # noqa: E402,F401
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    return wd.to_host_bits(t).copy()
+
+
+CASES = [
+    ("tiny_decode", lambda: workloads.make("tiny_decode")),
+    ("decode bf16, split tail, d 256", lambda: build("wa_split", 3, [9000, 14000, 11000, 9500], [1, 1, 2, 1],
+                                                    num_q_heads=16, num_kv_heads=4, head_dim=256, block_size=16,
+                                                    kv_dtype="bf16")),
+    ("mixed bf16 (fused launch)", lambda: random_mixed(5, num_decode=20, chunk_specs=[(0, 100), (700, 300)],
+                                                       max_decode_len=3000, num_q_heads=32, num_kv_heads=8,
+                                                       head_dim=128, block_size=16, kv_dtype="bf16")),
+    ("mixed fp8 from f32 rows", lambda: random_mixed(6, num_decode=12, chunk_specs=[(0, 80)], max_decode_len=2000,
+                                                     num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=32,
+                                                     kv_dtype="fp8_e4m3", src_dtype="f32", q_dtype="f16",
+                                                     k_scale=2.0 ** -5, v_scale=2.0 ** -5)),
+    ("mixed d 256 (kernels apart)", lambda: random_mixed(7, num_decode=8, chunk_specs=[(0, 70)], max_decode_len=1500,
+                                                         num_q_heads=8, num_kv_heads=4, head_dim=256, block_size=64,
+                                                         kv_dtype="f16")),
+]
+
+
+@pytest.mark.parametrize("name,make", CASES, ids=[c[0] for c in CASES])
+def test_joint_call_equals_two_calls(name, make):
+    w = make()
+    say(f"write_and_attend: {name}: {w.summary()}")
+    # two calls
+    a = wd.stage(w, write_new=False)
+    a.write_new()
+    ref = _bits(a.attend())
+    ref_k, ref_v = _bits(a.k_cache), _bits(a.v_cache)
+    # one call, on an identically staged pool
+    b = wd.stage(w, write_new=False)
+    out = torch.full_like(b.q, float("nan"))
+    got = _bits(b.write_and_attend(out=out))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(b.k_cache), ref_k) and np.array_equal(_bits(b.v_cache), ref_v)
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} of {got.size} elements differ"
+    # and the oracle
+    kp, vp = fill_pools(w)
+    assert_close(w, codecs.decode(got, w.q_dtype), attention(w, kp, vp), label=f"write_and_attend {name}")
