@@ -50,6 +50,24 @@ def _attn(cache, q_dtype=pa.PA_BF16, q=FAKE, ws=FAKE, ws_bytes=1 << 40, Hq=4, S=
                             S, T, Hq, max_seq, max_q, scale, out, ws, ws_bytes, None)
 
 
+def _write_attend(cache, key=FAKE, src=pa.PA_BF16, slots=FAKE, n_new=4, q_dtype=pa.PA_BF16, ws_bytes=1 << 40):
+    lib = pa.library()
+    return lib.pa_write_and_attend(key, FAKE, src, slots, n_new, FAKE, q_dtype, FAKE, FAKE, ctypes.byref(cache),
+                                   FAKE, 3, FAKE, FAKE, 2, 2, 4, 40, 1, 0.125, FAKE, FAKE, ws_bytes, None)
+
+
+def test_write_and_attend_argument_errors():
+    # both argument sets are checked before anything is enqueued; the cache
+    # write's come first
+    assert _write_attend(_cache(), key=None) == 1                 # PA_ERR_NULL
+    assert _write_attend(_cache(), slots=None) == 1
+    assert _write_attend(_cache(), src=pa.PA_FP8_E4M3) == 3       # rows come as f32, f16 or bf16
+    assert _write_attend(_cache(), n_new=-1) == 2                 # PA_ERR_SHAPE
+    assert _write_attend(_cache(block_size=8)) == 4               # the cache spec, for both
+    assert _write_attend(_cache(), q_dtype=pa.PA_F32) == 3        # the attention's pairing
+    assert _write_attend(_cache(), ws_bytes=64) == 5              # the attention's workspace
+
+
 def test_attention_argument_errors():
     assert _attn(_cache(block_size=8)) == 4                       # PA_ERR_UNSUPPORTED
     assert _attn(_cache(head_dim=96)) == 4
