@@ -1,8 +1,9 @@
 """Several decode steps as one device-resident loop, capturable in a HIP graph.
 
 Each step: ``prepare_step`` (step inputs from the persistent per-slot state)
--> ``reshape_and_cache`` (the step's new K/V) -> ``attention`` ->
-``commit_step`` (the tokens are cached: num_computed advances).  Nothing in
+-> ``write_and_attend`` (the step's new K/V written in the launch that
+builds its work lists, then attention) -> ``commit_step`` (the tokens are
+cached: num_computed advances).  Nothing in
 the loop allocates, synchronises or needs the host, so the whole sequence of
 launches can be captured once and replayed (techknowgenie "vLLM V1 core
 refactoring", section on the PagedAttention V3 kernel architecture: a GPU
@@ -23,7 +24,7 @@ class DecodeLoop:
     num_computed int32 [max_reqs] (device), advanced by each step;
     idx_mapping  int32 [R] (device): the batch's persistent slots;
     q            [N, R, Hq, d]; key, value [N, R, Hkv, d] (device): per-step
-                 inputs, in the dtypes pa.attention / pa.reshape_and_cache take;
+                 inputs, in the dtypes pa.write_and_attend takes;
     max_seq_len  host bound on the context length at the last step.
     ``out[s]`` holds step s's attention output after ``run()`` (or a replay).
     """
@@ -56,11 +57,9 @@ class DecodeLoop:
     def step(self, s: int, stream=None):
         qsl, lens, _, slots, tables = pa.prepare_step(self.table, self.idx, self.num_computed, self.sched, self.R,
                                                       self.B, out=self.meta, stream=stream)
-        pa.reshape_and_cache(self.key[s], self.value[s], self.k_cache, self.v_cache, slots, self.k_scale,
-                             self.v_scale, stream=stream)
-        pa.attention(self.q[s], self.k_cache, self.v_cache, tables, lens, qsl, self.scale,
-                     max_seq_len=self.max_seq_len, max_query_len=1, out=self.out[s], workspace=self.workspace,
-                     k_scale=self.k_scale, v_scale=self.v_scale, stream=stream)
+        pa.write_and_attend(self.key[s], self.value[s], slots, self.q[s], self.k_cache, self.v_cache, tables, lens,
+                            qsl, self.scale, max_seq_len=self.max_seq_len, max_query_len=1, out=self.out[s],
+                            workspace=self.workspace, k_scale=self.k_scale, v_scale=self.v_scale, stream=stream)
         pa.commit_step(self.num_computed, self.idx, self.sched, stream=stream)
 
     def run(self, stream=None):
