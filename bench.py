@@ -69,7 +69,8 @@ def parse():
     ap.add_argument("--config-cpu-seconds", type=float, default=3.0,
                     help="oracle budget for each of the other configurations' records (0 disables it)")
     ap.add_argument("--separate-write", action="store_true",
-                    help="time the step as pa_reshape_and_cache + pa_attention instead of pa_write_and_attend")
+                    help="time the step as pa_reshape_and_cache + pa_attention[_shared_prefix] instead of "
+                         "pa_write_and_attend")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="attend through pa_attention_shared_prefix over the workload's common prefix "
                          "(fp8_shared_prefix): the prefix is attended once for all rows")
@@ -497,9 +498,9 @@ def measure_step(w, args, prefix=0, cpu_seconds=0.0):
     prefix_pairs = [(ev.create(), ev.create()) for _ in range(args.steps)] if prefix else None
     whole = (ev.create(), ev.create())
     # A step is the cache write of its new tokens and its attention: one
-    # pa_write_and_attend call (the write in the plan's launch), or, through
-    # the shared-prefix entry point or with --separate-write, the two calls.
-    joint = not prefix and not args.separate_write
+    # pa_write_and_attend call (the write in the plan's launch), or, with
+    # --separate-write, the two calls.
+    joint = not args.separate_write
 
     for _ in range(args.warmup):
         if joint:

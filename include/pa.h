@@ -152,7 +152,9 @@ pa_status_t pa_attention(const void* q, int32_t q_dtype, const void* k_cache,
  * One step's cache write and attention in one call: the same result as
  * pa_reshape_and_cache(key, value, src_dtype, k_cache, v_cache, cache,
  * slot_mapping, num_new_tokens, stream) followed by pa_attention(q, ...,
- * stream) with the remaining arguments, enqueued on `stream` (the itwiki
+ * stream) with the remaining arguments -- or, with prefix_len > 0,
+ * pa_attention_shared_prefix(q, ..., prefix_len, ...) -- enqueued on
+ * `stream` (the itwiki
  * "vLLM" article, section "PagedAttention": a step writes its new K/V into
  * the paged cache and then attends over it; the llm-wiki "vLLM 0.25 Model
  * Runner V2", section "Redesign 4", for the flat slot index).  The write
@@ -161,7 +163,7 @@ pa_status_t pa_attention(const void* q, int32_t q_dtype, const void* k_cache,
  *
  * Arguments, layouts and ownership are those of the two calls; the
  * workspace comes from pa_attention_workspace_size with the attention's
- * arguments.  Every argument of both is checked before anything is
+ * arguments (pa_attention_shared_prefix_workspace_size with prefix_len > 0).  Every argument of both is checked before anything is
  * enqueued, and on any error nothing is: the status is the first failing
  * check's (the cache write's checks first).  num_new_tokens == 0 is
  * pa_attention; num_seqs == 0 or num_tokens == 0 is the cache write alone.
@@ -173,8 +175,8 @@ pa_status_t pa_write_and_attend(const void* key, const void* value, int32_t src_
                                 int32_t max_blocks_per_seq, const int32_t* seq_lens,
                                 const int32_t* query_start_loc, int32_t num_seqs,
                                 int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
-                                int32_t max_query_len, float scale, void* out, void* workspace,
-                                size_t workspace_bytes, void* stream);
+                                int32_t max_query_len, int32_t prefix_len, float scale, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Paged attention of a step whose sequences all share a prefix (cascade).

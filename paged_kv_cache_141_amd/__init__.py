@@ -70,8 +70,8 @@ def _load(path: str) -> ctypes.CDLL:
         "pa_reshape_and_cache": [P, P, I32, P, P, CP, P, I32, P],
         "pa_attention_workspace_size": [CP, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
         "pa_attention": [P, I32, P, P, CP, P, I32, P, P, I32, I32, I32, I32, I32, F, P, P, SZ, P],
-        "pa_write_and_attend": [P, P, I32, P, I32, P, I32, P, P, CP, P, I32, P, P, I32, I32, I32, I32, I32, F, P,
-                                P, SZ, P],
+        "pa_write_and_attend": [P, P, I32, P, I32, P, I32, P, P, CP, P, I32, P, P, I32, I32, I32, I32, I32, I32, F,
+                                P, P, SZ, P],
         "pa_attention_noalloc": [P, I32, P, P, CP, P, I32, P, P, I32, I32, I32, I32, I32, F, P, P],
         "pa_preferred_block_size": [I32, I32, I32, I32, ctypes.POINTER(I32)],
         "pa_attention_shared_prefix_workspace_size": [CP, I32, I32, I32, I32, I32, I32, ctypes.POINTER(SZ)],
@@ -282,10 +282,11 @@ def attention(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scal
 
 def write_and_attend(key, value, slot_mapping, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
                      scale: float, *, max_seq_len: int, max_query_len: int, out=None, workspace=None,
-                     k_scale: float = 1.0, v_scale: float = 1.0, stream=None):
+                     k_scale: float = 1.0, v_scale: float = 1.0, prefix_len: int = 0, stream=None):
     """The step's cache write of key/value ``[T_new, Hkv, d]`` into their
     slots, then paged attention of q (``pa_write_and_attend``: the two calls'
-    result with one launch fewer); returns ``out``."""
+    result with one launch fewer; with ``prefix_len`` > 0 the attention is the
+    shared-prefix one); returns ``out``."""
     torch = _torch()
     spec = cache_spec(k_cache, v_cache, k_scale, v_scale)
     if key.shape != value.shape or key.dtype != value.dtype:
@@ -312,8 +313,15 @@ def write_and_attend(key, value, slot_mapping, q, k_cache, v_cache, block_tables
     lib = library()
     if workspace is None:
         need = ctypes.c_size_t(0)
-        _check(lib.pa_attention_workspace_size(ctypes.byref(spec), Hq, S, T, int(max_seq_len), int(max_query_len),
-                                               ctypes.byref(need)), "pa_attention_workspace_size")
+        if prefix_len:
+            _check(lib.pa_attention_shared_prefix_workspace_size(ctypes.byref(spec), Hq, S, T, int(max_seq_len),
+                                                                 int(max_query_len), int(prefix_len),
+                                                                 ctypes.byref(need)),
+                   "pa_attention_shared_prefix_workspace_size")
+        else:
+            _check(lib.pa_attention_workspace_size(ctypes.byref(spec), Hq, S, T, int(max_seq_len),
+                                                   int(max_query_len), ctypes.byref(need)),
+                   "pa_attention_workspace_size")
         workspace = torch.empty(max(int(need.value), 256), dtype=torch.uint8, device=q.device)
     kp = _dev(key, "key") if Tn else None
     vp = _dev(value, "value") if Tn else None
@@ -322,7 +330,7 @@ def write_and_attend(key, value, slot_mapping, q, k_cache, v_cache, block_tables
         kp, vp, _dtype_code(key), sp, Tn, _dev(q, "q"), _dtype_code(q), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), ctypes.byref(spec), _dev(block_tables, "block_tables"), block_tables.shape[1],
         _dev(seq_lens, "seq_lens"), _dev(query_start_loc, "query_start_loc"), S, T, Hq, int(max_seq_len),
-        int(max_query_len), float(scale), _dev(out, "out"), _dev(workspace, "workspace"),
+        int(max_query_len), int(prefix_len), float(scale), _dev(out, "out"), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "pa_write_and_attend")
     return out

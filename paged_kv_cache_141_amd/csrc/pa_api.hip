@@ -261,16 +261,17 @@ pa_status_t pa_write_and_attend(const void* key, const void* value, int32_t src_
                                 void* v_cache, const pa_cache_t* cache, const int32_t* block_tables,
                                 int32_t max_blocks_per_seq, const int32_t* seq_lens,
                                 const int32_t* query_start_loc, int32_t num_seqs, int32_t num_tokens,
-                                int32_t num_q_heads, int32_t max_seq_len, int32_t max_query_len, float scale,
-                                void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                                int32_t num_q_heads, int32_t max_seq_len, int32_t max_query_len,
+                                int32_t prefix_len, float scale, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   pa::CacheWriteArgs w;
   const pa_status_t st =
       cache_write_args(key, value, src_dtype, k_cache, v_cache, cache, slot_mapping, num_new_tokens, w);
   if (st != PA_OK) return st;
   return static_cast<pa_status_t>(pa::attention_entry(
       q, q_dtype, k_cache, v_cache, cache, block_tables, max_blocks_per_seq, seq_lens, query_start_loc, num_seqs,
-      num_tokens, num_q_heads, max_seq_len, max_query_len, 0, scale, out, workspace, workspace_bytes, stream,
-      nullptr, w.num_tokens > 0 ? &w : nullptr, src_dtype));
+      num_tokens, num_q_heads, max_seq_len, max_query_len, prefix_len, scale, out, workspace, workspace_bytes,
+      stream, nullptr, w.num_tokens > 0 ? &w : nullptr, src_dtype));
 }
 
 pa_status_t pa_copy_blocks(const void* src_k, const void* src_v, const pa_cache_t* src_cache, void* dst_k,

@@ -217,26 +217,34 @@ void valid_calls() {
     const int64_t* slots = static_cast<const int64_t*>(FAKE);
     const int a0 = g_attn_launches, w0 = g_write_launches, j0 = g_joint_writes;
     CHECK(pa_write_and_attend(FAKE, FAKE, PA_F32, slots, 5, FAKE, PA_BF16, FAKE, FAKE, &cb, FAKEI, 4, FAKEI, FAKEI,
-                              2, 2, 8, 100, 1, 0.1f, FAKE, FAKE, size_t(1) << 40, nullptr) == PA_OK);
+                              2, 2, 8, 100, 1, 0, 0.1f, FAKE, FAKE, size_t(1) << 40, nullptr) == PA_OK);
     CHECK(g_attn_launches == a0 + 1 && g_joint_writes == j0 + 1 && g_write_launches == w0);
     CHECK(g_write.num_tokens == 5 && g_write.num_slots == 77 * 32 && g_joint_src == PA_F32);
     // a bad write argument or a bad attention argument: nothing launched
     CHECK(pa_write_and_attend(nullptr, FAKE, PA_F32, slots, 5, FAKE, PA_BF16, FAKE, FAKE, &cb, FAKEI, 4, FAKEI,
-                              FAKEI, 2, 2, 8, 100, 1, 0.1f, FAKE, FAKE, size_t(1) << 40, nullptr) == PA_ERR_NULL);
+                              FAKEI, 2, 2, 8, 100, 1, 0, 0.1f, FAKE, FAKE, size_t(1) << 40, nullptr) == PA_ERR_NULL);
     CHECK(pa_write_and_attend(FAKE, FAKE, PA_FP8_E4M3, slots, 5, FAKE, PA_BF16, FAKE, FAKE, &cb, FAKEI, 4, FAKEI,
-                              FAKEI, 2, 2, 8, 100, 1, 0.1f, FAKE, FAKE, size_t(1) << 40, nullptr) == PA_ERR_DTYPE);
+                              FAKEI, 2, 2, 8, 100, 1, 0, 0.1f, FAKE, FAKE, size_t(1) << 40, nullptr) == PA_ERR_DTYPE);
     CHECK(pa_write_and_attend(FAKE, FAKE, PA_F32, slots, 5, FAKE, PA_F16, FAKE, FAKE, &cb, FAKEI, 4, FAKEI, FAKEI,
-                              2, 2, 8, 100, 1, 0.1f, FAKE, FAKE, size_t(1) << 40, nullptr) == PA_ERR_DTYPE);
+                              2, 2, 8, 100, 1, 0, 0.1f, FAKE, FAKE, size_t(1) << 40, nullptr) == PA_ERR_DTYPE);
     CHECK(pa_write_and_attend(FAKE, FAKE, PA_F32, slots, 5, FAKE, PA_BF16, FAKE, FAKE, &cb, FAKEI, 4, FAKEI, FAKEI,
-                              2, 2, 8, 100, 1, 0.1f, FAKE, FAKE, 16, nullptr) == PA_ERR_WORKSPACE);
+                              2, 2, 8, 100, 1, 0, 0.1f, FAKE, FAKE, 16, nullptr) == PA_ERR_WORKSPACE);
     CHECK(g_attn_launches == a0 + 1 && g_joint_writes == j0 + 1 && g_write_launches == w0);
     // no new tokens: pa_attention; no attention rows: the write alone
     CHECK(pa_write_and_attend(nullptr, nullptr, PA_F32, nullptr, 0, FAKE, PA_BF16, FAKE, FAKE, &cb, FAKEI, 4, FAKEI,
-                              FAKEI, 2, 2, 8, 100, 1, 0.1f, FAKE, FAKE, size_t(1) << 40, nullptr) == PA_OK);
+                              FAKEI, 2, 2, 8, 100, 1, 0, 0.1f, FAKE, FAKE, size_t(1) << 40, nullptr) == PA_OK);
     CHECK(g_attn_launches == a0 + 2 && g_joint_writes == j0 + 1);
     CHECK(pa_write_and_attend(FAKE, FAKE, PA_BF16, slots, 3, nullptr, PA_BF16, FAKE, FAKE, &cb, nullptr, 4, nullptr,
-                              nullptr, 0, 0, 8, 100, 1, 0.1f, nullptr, nullptr, 0, nullptr) == PA_OK);
+                              nullptr, 0, 0, 8, 100, 1, 0, 0.1f, nullptr, nullptr, 0, nullptr) == PA_OK);
     CHECK(g_attn_launches == a0 + 2 && g_write_launches == w0 + 1 && g_write.num_tokens == 3);
+    // with a shared prefix (whole blocks, every query past it)
+    CHECK(pa_write_and_attend(FAKE, FAKE, PA_F32, slots, 5, FAKE, PA_BF16, FAKE, FAKE, &cb, FAKEI, 4, FAKEI, FAKEI,
+                              2, 2, 8, 100, 1, 64, 0.1f, FAKE, FAKE, size_t(1) << 40, nullptr) == PA_OK);
+    CHECK(g_attn_launches == a0 + 3 && g_joint_writes == j0 + 2 && g_attn.prefix_len == 64 &&
+          g_attn.prefix_parts >= 1);
+    CHECK(pa_write_and_attend(FAKE, FAKE, PA_F32, slots, 5, FAKE, PA_BF16, FAKE, FAKE, &cb, FAKEI, 4, FAKEI, FAKEI,
+                              2, 2, 8, 100, 1, 40, 0.1f, FAKE, FAKE, size_t(1) << 40, nullptr) == PA_ERR_SHAPE);
+    CHECK(g_attn_launches == a0 + 3);
   }
   // step inputs and commit reach their launchers
   const int before = g_other_launches;

@@ -53,7 +53,7 @@ def _attn(cache, q_dtype=pa.PA_BF16, q=FAKE, ws=FAKE, ws_bytes=1 << 40, Hq=4, S=
 def _write_attend(cache, key=FAKE, src=pa.PA_BF16, slots=FAKE, n_new=4, q_dtype=pa.PA_BF16, ws_bytes=1 << 40):
     lib = pa.library()
     return lib.pa_write_and_attend(key, FAKE, src, slots, n_new, FAKE, q_dtype, FAKE, FAKE, ctypes.byref(cache),
-                                   FAKE, 3, FAKE, FAKE, 2, 2, 4, 40, 1, 0.125, FAKE, FAKE, ws_bytes, None)
+                                   FAKE, 3, FAKE, FAKE, 2, 2, 4, 40, 1, 0, 0.125, FAKE, FAKE, ws_bytes, None)
 
 
 def test_write_and_attend_argument_errors():

@@ -59,3 +59,24 @@ def test_joint_call_equals_two_calls(name, make):
     # and the oracle
     kp, vp = fill_pools(w)
     assert_close(w, codecs.decode(got, w.q_dtype), attention(w, kp, vp), label=f"write_and_attend {name}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_joint_call_with_a_shared_prefix(kv):
+    # pa_write_and_attend with prefix_len > 0 against pa_reshape_and_cache +
+    # pa_attention_shared_prefix
+    P = 2048
+    fp8 = kv == "fp8_e4m3"
+    w = build("wa_prefix", 11, [P + 10, P + 700, P + 1, P + 333, P + 1500], [1, 1, 1, 2, 1], num_q_heads=16,
+              num_kv_heads=4, head_dim=128, block_size=32, kv_dtype=kv, shared_prefix_len=P,
+              k_scale=2.0 ** -5 if fp8 else 1.0, v_scale=2.0 ** -5 if fp8 else 1.0)
+    a = wd.stage(w, write_new=False).use_shared_prefix(P)
+    a.write_new()
+    ref = _bits(a.attend())
+    b = wd.stage(w, write_new=False).use_shared_prefix(P)
+    got = _bits(b.write_and_attend(out=torch.full_like(b.q, float("nan"))))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(b.k_cache), _bits(a.k_cache)) and np.array_equal(_bits(b.v_cache), _bits(a.v_cache))
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} of {got.size} elements differ"
+    kp, vp = fill_pools(w)
+    assert_close(w, codecs.decode(got, w.q_dtype), attention(w, kp, vp), label=f"write_and_attend prefix {kv}")

@@ -127,13 +127,11 @@ class DeviceStep:
         """The same pass through one call (``pa_write_and_attend``)."""
         import paged_kv_cache_141_amd as pa
         w = self.w
-        if self.prefix_len:
-            raise ValueError("pa_write_and_attend has no shared-prefix form")
         return pa.write_and_attend(self.new_key, self.new_value, self.new_slots, self.q, self.k_cache, self.v_cache,
                                    self.block_tables, self.seq_lens, self.query_start_loc, w.scale,
                                    max_seq_len=w.max_seq_len, max_query_len=w.max_query_len,
                                    out=self.out if out is None else out, workspace=self.workspace,
-                                   k_scale=w.k_scale, v_scale=w.v_scale, stream=stream)
+                                   k_scale=w.k_scale, v_scale=w.v_scale, prefix_len=self.prefix_len, stream=stream)
 
 
 def stage(w: Workload, device="cuda", batch_tokens: Optional[int] = None,
