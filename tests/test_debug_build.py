@@ -148,3 +148,38 @@ def test_slot_outside_the_pool_is_recorded_and_skipped():
     after_k[blk[keep], :, off[keep], :] = before_k[blk[keep], :, off[keep], :]
     after_v[blk[keep], :, off[keep], :] = before_v[blk[keep], :, off[keep], :]
     assert np.array_equal(after_k, before_k) and np.array_equal(after_v, before_v)
+
+
+def _write_and_attend(lib, step, slots):
+    import torch
+    w = step.w
+    spec = pa.cache_spec(step.k_cache, step.v_cache, w.k_scale, w.v_scale)
+    out = torch.full_like(step.q, float("nan"))
+    st = lib.pa_write_and_attend(
+        _p(step.new_key), _p(step.new_value), pa._dtype_code(step.new_key), _p(slots), slots.numel(), _p(step.q),
+        pa._dtype_code(step.q), _p(step.k_cache), _p(step.v_cache), ctypes.byref(spec), _p(step.block_tables),
+        step.block_tables.shape[1], _p(step.seq_lens), _p(step.query_start_loc), w.num_seqs, w.num_tokens,
+        w.num_q_heads, w.max_seq_len, w.max_query_len, 0, w.scale, _p(out), _p(step.workspace),
+        step.workspace.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, pa.status_string(st)
+    return out
+
+
+@pytest.mark.gpu
+def test_joint_call_checks_its_write_and_its_metadata():
+    # pa_write_and_attend in the debug library: valid inputs leave the record
+    # clear and give the release build's output; a slot past the pool is
+    # recorded (its token skipped) by the write that shares the plan's launch
+    from workloads import device as wd
+    dbg = pa.debug_library()
+    pa.debug_check(dbg)
+    w = _mixed()
+    step = wd.stage(w, write_new=False)
+    got = wd.to_host_bits(_write_and_attend(dbg, step, step.new_slots)).copy()
+    assert pa.debug_check(dbg) == (0, 0)
+    ref = wd.to_host_bits(_write_and_attend(pa.library(), step, step.new_slots))
+    assert np.array_equal(got, ref)
+    slots = step.new_slots.clone()
+    slots[7] = w.num_blocks * w.block_size + 1
+    _write_and_attend(dbg, step, slots)
+    assert pa.debug_check(dbg) == (CODE["slot"], 7)
