@@ -501,10 +501,11 @@ def measure_step(w, args, prefix=0, cpu_seconds=0.0):
     # pa_write_and_attend call (the write in the plan's launch), or, with
     # --separate-write, the two calls.
     joint = not args.separate_write
+    run = step.bound_step() if joint else None     # the call's arguments marshalled once
 
     for _ in range(args.warmup):
         if joint:
-            step.write_and_attend()
+            run()
         else:
             step.step()
     torch.cuda.synchronize()
@@ -523,7 +524,7 @@ def measure_step(w, args, prefix=0, cpu_seconds=0.0):
         if prefix_pairs:
             pa.set_prefix_events(prefix_pairs[k][0], prefix_pairs[k][1])
         if joint:
-            step.write_and_attend()
+            run()
             continue
         if k in cw:
             ev.record(cw[k][0], stream)

@@ -336,6 +336,50 @@ def write_and_attend(key, value, slot_mapping, q, k_cache, v_cache, block_tables
     return out
 
 
+def bind_write_and_attend(key, value, slot_mapping, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
+                          scale: float, *, max_seq_len: int, max_query_len: int, out, workspace,
+                          k_scale: float = 1.0, v_scale: float = 1.0, prefix_len: int = 0, stream=None):
+    """``write_and_attend`` with its arguments marshalled once: returns a
+    callable that issues the same ``pa_write_and_attend`` call (same
+    buffers, stream and sizes) each time it is called, for loops that run
+    one step shape over fixed buffers whose contents change between calls.
+    The tensors must stay alive and in place while the callable is used."""
+    torch = _torch()
+    spec = cache_spec(k_cache, v_cache, k_scale, v_scale)
+    Tn = key.shape[0]
+    if key.shape != value.shape or key.dtype != value.dtype or slot_mapping.dtype != torch.int64 \
+            or slot_mapping.numel() != Tn:
+        raise ValueError("key, value and slot_mapping disagree")
+    if key.dim() != 3 or key.shape[1] != spec.num_kv_heads or key.shape[2] != spec.head_dim:
+        raise ValueError(f"key must be [T, {spec.num_kv_heads}, {spec.head_dim}]")
+    if q.dim() != 3 or q.shape[2] != spec.head_dim or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must be [T, Hq, d] of one dtype")
+    T, Hq, _ = q.shape
+    S = seq_lens.numel()
+    for name, t in (("block_tables", block_tables), ("seq_lens", seq_lens),
+                    ("query_start_loc", query_start_loc)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+    if query_start_loc.numel() != S + 1 or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("metadata shapes disagree")
+    fn = library().pa_write_and_attend
+    args = (_dev(key, "key") if Tn else None, _dev(value, "value") if Tn else None, _dtype_code(key),
+            _dev(slot_mapping, "slot_mapping") if Tn else None, Tn, _dev(q, "q"), _dtype_code(q),
+            _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), ctypes.byref(spec),
+            _dev(block_tables, "block_tables"), block_tables.shape[1], _dev(seq_lens, "seq_lens"),
+            _dev(query_start_loc, "query_start_loc"), S, T, Hq, int(max_seq_len), int(max_query_len),
+            int(prefix_len), float(scale), _dev(out, "out"), _dev(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    keep = (spec, key, value, slot_mapping, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, out,
+            workspace)
+
+    def call():
+        _check(fn(*args), "pa_write_and_attend")
+        return keep[10]
+
+    return call
+
+
 def attention_noalloc(q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale: float, *,
                       max_seq_len: int, max_query_len: int, out, k_scale: float = 1.0, v_scale: float = 1.0,
                       stream=None):

@@ -80,3 +80,19 @@ def test_joint_call_with_a_shared_prefix(kv):
     assert np.array_equal(got, ref), f"{int((got != ref).sum())} of {got.size} elements differ"
     kp, vp = fill_pools(w)
     assert_close(w, codecs.decode(got, w.q_dtype), attention(w, kp, vp), label=f"write_and_attend prefix {kv}")
+
+
+def test_bound_call_equals_the_plain_call():
+    # bind_write_and_attend marshals once and issues the same call: two
+    # calls of the bound form give the plain call's pools and output
+    w = build("wa_bound", 13, [700, 2300, 40], [1, 1, 1], num_q_heads=8, num_kv_heads=2, head_dim=128,
+              block_size=16, kv_dtype="bf16")
+    a = wd.stage(w, write_new=False)
+    ref = _bits(a.write_and_attend())
+    b = wd.stage(w, write_new=False)
+    run = b.bound_step()
+    run()
+    got = _bits(run())
+    torch.cuda.synchronize()
+    assert np.array_equal(got, ref)
+    assert np.array_equal(_bits(b.k_cache), _bits(a.k_cache)) and np.array_equal(_bits(b.v_cache), _bits(a.v_cache))

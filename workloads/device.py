@@ -123,6 +123,17 @@ class DeviceStep:
         self.write_new(stream)
         return self.attend(stream=stream)
 
+    def bound_step(self, stream=None):
+        """A callable issuing this pass through one ``pa_write_and_attend`` call
+        whose arguments are marshalled once (``pa.bind_write_and_attend``)."""
+        import paged_kv_cache_141_amd as pa
+        w = self.w
+        return pa.bind_write_and_attend(self.new_key, self.new_value, self.new_slots, self.q, self.k_cache,
+                                        self.v_cache, self.block_tables, self.seq_lens, self.query_start_loc,
+                                        w.scale, max_seq_len=w.max_seq_len, max_query_len=w.max_query_len,
+                                        out=self.out, workspace=self.workspace, k_scale=w.k_scale,
+                                        v_scale=w.v_scale, prefix_len=self.prefix_len, stream=stream)
+
     def write_and_attend(self, out=None, stream=None):
         """The same pass through one call (``pa_write_and_attend``)."""
         import paged_kv_cache_141_amd as pa
