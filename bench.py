@@ -488,6 +488,9 @@ def measure_step(w, args, prefix=0, cpu_seconds=0.0):
     print(f"[bench] staged in {time.perf_counter() - t_stage:.1f}s", file=sys.stderr, flush=True)
 
     kv_bytes = accounting.workload_kv_bytes(w)
+    # the step's HBM share is priced on each physical block once (a prefix
+    # whose blocks the tables share is read from HBM once, then from cache)
+    step_unique_bytes = accounting.workload_kv_bytes(w, unique=True)
     stream = torch.cuda.current_stream()
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
@@ -581,7 +584,8 @@ def measure_step(w, args, prefix=0, cpu_seconds=0.0):
         "ms_step_events": {"median": pct(step_ms, 50), "p10": pct(step_ms, 10), "p90": pct(step_ms, 90)},
         "kv_GBps": round(kv_bytes / step_s / 1e9, 2),
         "query_tokens_per_s": round(w.num_tokens / step_s, 1),
-        "hbm_frac_step": round(kv_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "hbm_frac_step": round(step_unique_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "step_unique_kv_bytes": step_unique_bytes,
         "fragmentation": round(accounting.fragmentation(w), 5),
         "attention_kernel_us": round(attn_s * 1e6, 2),
         "attention_kernel_us_p10_p90": [round(pct(attn_ms, 10) * 1e3, 2), round(pct(attn_ms, 90) * 1e3, 2)],

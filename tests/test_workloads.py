@@ -115,4 +115,8 @@ def test_accounting_formulas():
     s = workloads.make("fp8_shared_prefix", num_seqs=4)
     assert accounting.workload_kv_bytes(s, unique=True) == \
         (8000 + int((s.seq_lens - 8000).sum())) * 8 * 128 * 2
+    t = workloads.make("fp8_shared_prefix", num_seqs=4, placement="private")
+    assert not t.prefix_blocks_shared
+    assert accounting.workload_kv_bytes(t, unique=True) == accounting.workload_kv_bytes(t) == \
+        int(t.seq_lens.sum()) * 8 * 128 * 2
     assert accounting.fragmentation(workloads.make("llama7b_decode")) < 0.04

@@ -27,12 +27,13 @@ def kv_bytes_per_token_model(hidden: int, layers: int, elem_bytes: int) -> int:
 def workload_kv_bytes(w: Workload, unique: bool = False) -> int:
     """KV bytes one attention pass must read.
 
-    unique=True counts each physical block once (a shared prefix is then
-    counted once instead of once per sequence).
+    unique=True counts each physical block once (a prefix whose blocks the
+    tables share is then counted once instead of once per sequence; private
+    copies of it count per sequence).
     """
     eb = DTYPE_BYTES[w.kv_dtype]
     per_token = w.num_kv_heads * 2 * w.head_dim * eb
-    if not unique:
+    if not unique or not w.prefix_blocks_shared:
         return int(w.seq_lens.astype(np.int64).sum()) * per_token
     P = w.shared_prefix_len
     return (P + int((w.seq_lens.astype(np.int64) - P).sum())) * per_token
