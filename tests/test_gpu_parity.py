@@ -34,6 +34,32 @@ def gpu_out(step):
     return codecs.decode(wd.to_host_bits(out), step.w.q_dtype)
 
 
+def timed_call_out(w, prefix=0, calls=2):
+    """The step as the throughput measurement issues it: the new tokens'
+    cache write and the attention in one pa_write_and_attend call, arguments
+    marshalled once, called ``calls`` times (a repeat writes the same bytes).
+    Checks the new tokens' slots byte for byte; returns the decoded output."""
+    step = wd.stage(w, write_new=False)
+    if prefix:
+        step.use_shared_prefix(prefix)
+    run = step.bound_step()
+    for _ in range(calls):
+        out = run()
+    torch.cuda.synchronize()
+    kbits, vbits = wd.to_host_bits(step.k_cache), wd.to_host_bits(step.v_cache)
+    nk, nv, ns = w.new_token_batch()
+    blk, off = ns // w.block_size, ns % w.block_size
+    # the oracle's encoding of the new rows (bf16 into fp8 caches)
+    ek = oracle.cache.encode_tokens(nk, w.src_dtype, w.kv_dtype, w.k_scale)
+    ev = oracle.cache.encode_tokens(nv, w.src_dtype, w.kv_dtype, w.v_scale)
+    assert np.array_equal(kbits[blk, :, off, :], ek), "new K rows"
+    assert np.array_equal(vbits[blk, :, off, :], ev), "new V rows"
+    got = codecs.decode(wd.to_host_bits(out), w.q_dtype)
+    del step, kbits, vbits
+    torch.cuda.empty_cache()
+    return got
+
+
 # ------------------------------------------------------------------ cache write
 
 SPECIAL_F32 = np.array([0.0, -0.0, 1.0, -1.5, 3.0e38, -3.4e38, np.inf, -np.inf, np.nan, 1e-40,
@@ -273,12 +299,14 @@ def test_metadata_checker():
 #
 # Each configuration at its full size, every query row against the oracle
 # (the block-wise sum equals ordinary attention: itwiki "vLLM",
-# "Block-wise attention").
+# "Block-wise attention"), through the call and launches the throughput
+# measurement times (timed_call_out), with the step's cache write checked
+# byte for byte at every new slot.
 
 def test_full_llama7b_decode():
     w = workloads.make("llama7b_decode")
     say("full llama7b_decode: staging", w.summary())
-    got = gpu_out(wd.stage(w))
+    got = timed_call_out(w)
     kp, vp = fill_pools(w)
     assert_close(w, got, attention(w, kp, vp), label="llama7b_decode, every row")
 
@@ -286,7 +314,7 @@ def test_full_llama7b_decode():
 def test_full_gqa_long_decode():
     w = workloads.make("gqa_long_decode")
     say("full gqa_long_decode: staging", w.summary())
-    got = gpu_out(wd.stage(w))
+    got = timed_call_out(w)
     kp, vp = fill_pools(w)
     assert_close(w, got, attention(w, kp, vp), label="gqa_long_decode, every row")
 
@@ -294,18 +322,7 @@ def test_full_gqa_long_decode():
 def test_full_mixed_chunked_prefill():
     w = workloads.make("mixed_chunked_prefill")
     say("full mixed_chunked_prefill: staging", w.summary())
-    step = wd.stage(w, write_new=False)
-    out = step.step()                         # cache write of all new tokens + attention
-    torch.cuda.synchronize()
-    got = codecs.decode(wd.to_host_bits(out), w.q_dtype)
-    # the step's cache write, byte for byte, at every new slot
-    kbits, vbits = wd.to_host_bits(step.k_cache), wd.to_host_bits(step.v_cache)
-    nk, nv, ns = w.new_token_batch()
-    B = w.block_size
-    blk, off = ns // B, ns % B
-    assert np.array_equal(kbits[blk, :, off, :], nk)
-    assert np.array_equal(vbits[blk, :, off, :], nv)
-    del kbits, vbits
+    got = timed_call_out(w)                   # cache write of all new tokens + attention
     kp, vp = fill_pools(w)
     ref = attention(w, kp, vp)
     # the 1,024-token chunk at offset 8,192 (most of the chunk work) on its own line
@@ -319,10 +336,8 @@ def test_full_fp8_shared_prefix(B):
     # entry point (pa_attention_shared_prefix), both against the oracle
     w = workloads.make("fp8_shared_prefix", block_size=B)
     say(f"full fp8_shared_prefix B={B}: staging", w.summary())
-    step = wd.stage(w)
-    got = gpu_out(step)
-    cascade = gpu_out(step.use_shared_prefix(w.shared_prefix_len))
-    del step
+    got = timed_call_out(w)
+    cascade = timed_call_out(w, prefix=w.shared_prefix_len)
     kp, vp = fill_pools(w)
     ref = attention(w, kp, vp)
     assert_close(w, got, ref, label=f"fp8 shared prefix B={B} through the tables, every row")
@@ -333,14 +348,11 @@ def test_full_fp8_private_prefix_equals_shared():
     # The private-copy twin (each sequence owns copies of the prefix blocks)
     # gives bit for bit the output of the shared blocks, every row, so it meets
     # the oracle exactly where the shared case does (test above).
-    s = wd.stage(workloads.make("fp8_shared_prefix", block_size=16))
-    shared = wd.to_host_bits(s.attend()).copy()
-    del s
+    shared = timed_call_out(workloads.make("fp8_shared_prefix", block_size=16))
     w = workloads.make("fp8_shared_prefix", block_size=16, placement="private")
     say("full fp8_private_prefix B=16: staging", w.summary())
-    p = wd.stage(w)
-    private = wd.to_host_bits(p.attend())
-    assert np.array_equal(shared, private)
+    private = timed_call_out(w)
+    assert np.array_equal(shared.view(np.uint64), private.view(np.uint64))
 
 
 def test_decode_tiles_past_16_bits():

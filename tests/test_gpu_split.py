@@ -15,6 +15,7 @@ import math
 import numpy as np
 import pytest
 
+import oracle.cache
 import workloads
 from oracle import codecs
 from workloads import device as wd
@@ -88,12 +89,27 @@ def test_split_decode_every_row(kv, q, d, B, Hq, Hkv, lens, qlens):
 
 def test_full_gqa_long_decode_d256():
     # the head-dim-256 GQA step (16 q / 4 kv heads, 1k-32k contexts), where
-    # the split cuts the kernel's tail
+    # the split cuts the kernel's tail, issued as the throughput measurement
+    # issues it: one pa_write_and_attend call (arguments marshalled once)
+    # for the new tokens' cache write and the attention, called twice
     w = workloads.make("gqa_long_decode", head_dim=256)
     say("full gqa_long_decode d256: staging", w.summary())
-    step, got, ref = run(w)
+    step = wd.stage(w, write_new=False)
+    call = step.bound_step()
+    call()
+    out = call()
+    torch.cuda.synchronize()
     assert split_partitions(step) > 0
-    assert_close(w, got, ref, label="gqa_long_decode d256, every row")
+    nk, nv, ns = w.new_token_batch()
+    blk, off = ns // w.block_size, ns % w.block_size
+    assert np.array_equal(wd.to_host_bits(step.k_cache)[blk, :, off, :],
+                          oracle.cache.encode_tokens(nk, w.src_dtype, w.kv_dtype, w.k_scale))
+    assert np.array_equal(wd.to_host_bits(step.v_cache)[blk, :, off, :],
+                          oracle.cache.encode_tokens(nv, w.src_dtype, w.kv_dtype, w.v_scale))
+    got = codecs.decode(wd.to_host_bits(out), w.q_dtype)
+    del step
+    kp, vp = fill_pools(w)
+    assert_close(w, got, attention(w, kp, vp), label="gqa_long_decode d256, every row")
 
 
 def test_no_split_where_it_does_not_pay():
