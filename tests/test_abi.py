@@ -129,6 +129,31 @@ def test_binding_rejects_host_tensors():
         pa.cache_spec(k, v.transpose(2, 3).contiguous())      # V must be [N, H, B, d] like K
 
 
+def test_write_and_attend_binding_checks_before_the_call():
+    # both Python faces of pa_write_and_attend reject mismatched shapes,
+    # metadata dtypes and host tensors before the library is called
+    torch = pytest.importorskip("torch")
+    k = torch.zeros(4, 2, 16, 64, dtype=torch.bfloat16)
+    key = torch.zeros(3, 2, 64, dtype=torch.bfloat16)
+    slots = torch.zeros(3, dtype=torch.int64)
+    q = torch.zeros(3, 4, 64, dtype=torch.bfloat16)
+    bt = torch.zeros(3, 4, dtype=torch.int32)
+    lens = torch.ones(3, dtype=torch.int32)
+    qsl = torch.arange(4, dtype=torch.int32)
+    kw = dict(max_seq_len=64, max_query_len=1, out=torch.empty_like(q), workspace=torch.empty(256, dtype=torch.uint8))
+    for fn in (pa.write_and_attend, pa.bind_write_and_attend):
+        with pytest.raises(ValueError):                           # value rows disagree with key rows
+            fn(key, key[:2], slots, q, k, k.clone(), bt, lens, qsl, 0.125, **kw)
+        with pytest.raises(ValueError):                           # key head dim is not the cache's
+            fn(key[..., :32], key[..., :32], slots, q, k, k.clone(), bt, lens, qsl, 0.125, **kw)
+        with pytest.raises(TypeError):                            # seq_lens must be int32
+            fn(key, key, slots, q, k, k.clone(), bt, lens.long(), qsl, 0.125, **kw)
+        with pytest.raises(ValueError):                           # query_start_loc needs S + 1 entries
+            fn(key, key, slots, q, k, k.clone(), bt, lens, qsl[:3], 0.125, **kw)
+        with pytest.raises(ValueError):                           # host tensors
+            fn(key, key, slots, q, k, k.clone(), bt, lens, qsl, 0.125, **kw)
+
+
 def test_copy_blocks_argument_errors():
     lib = pa.library()
     c = _cache()
