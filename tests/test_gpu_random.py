@@ -78,3 +78,33 @@ def test_random_step(seed):
     err = float(np.abs(got - ref).max())
     say(f"  max-abs err {err:.3e} (tol {TOL[w.kv_dtype]:.0e}) over {got.size} values")
     assert err <= TOL[w.kv_dtype], f"{label}: max-abs error {err} > {TOL[w.kv_dtype]}"
+
+
+@pytest.mark.parametrize("seed", range(100, 112))
+def test_random_step_through_the_joint_call(seed):
+    # the same draws through pa_write_and_attend (the new tokens' cache
+    # write in the plan's launch): the whole pools byte for byte against the
+    # oracle's cache write, every row against the oracle's attention
+    spec = draw_step(seed)
+    lens, qlens = spec.pop("lens"), spec.pop("qlens")
+    label = (f"joint random seed={seed} n={len(lens)} max_len={max(lens)} tokens={sum(qlens)} "
+             f"{spec['kv_dtype']}/{spec['q_dtype']} d={spec['head_dim']} B={spec['block_size']} "
+             f"Hq={spec['num_q_heads']} Hkv={spec['num_kv_heads']}")
+    say(label)
+    w = build("random_joint", 100 + seed, lens, qlens, **spec)
+    kp, vp = oracle.cache.fill_pools(w)
+    ref = oracle.attention.paged_attention(
+        w.q_values(), w.q_dtype, kp, vp, w.kv_dtype, w.block_tables, w.seq_lens,
+        w.query_start_loc, w.block_size, w.scale, w.k_scale, w.v_scale)
+    step = wd.stage(w, write_new=False)
+    out = step.write_and_attend(out=torch.full_like(step.q, float("nan")))
+    torch.cuda.synchronize()
+    assert np.array_equal(wd.to_host_bits(step.k_cache), kp), f"{label}: K pool"
+    assert np.array_equal(wd.to_host_bits(step.v_cache), vp), f"{label}: V pool"
+    got = codecs.decode(wd.to_host_bits(out), w.q_dtype)
+    if got.size == 0:
+        return
+    assert not np.isnan(got).any(), f"{label}: NaN in GPU output"
+    err = float(np.abs(got - ref).max())
+    say(f"  max-abs err {err:.3e} (tol {TOL[w.kv_dtype]:.0e}) over {got.size} values")
+    assert err <= TOL[w.kv_dtype], f"{label}: max-abs error {err} > {TOL[w.kv_dtype]}"
