@@ -338,22 +338,29 @@ static hipError_t launch_plan_write(int src, int kv, const AttnArgs& a, const Ca
 #ifndef PA_REDUCE_MANY_TOKENS
 #define PA_REDUCE_MANY_TOKENS 1024
 #endif
-template <int OT, int D>
+template <int OT, int D, int PG>
 __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
   constexpr int LPH = D / 4;                             // lanes per head
   constexpr int HPB = 4 * (64 / LPH);                    // heads per workgroup
   const int token = blockIdx.x;
-  // sequence of this token: last i with qsl[i] <= token.  A 64-way search:
-  // each round every lane probes one candidate and a ballot keeps the last
-  // one at or before the token (qsl is non-decreasing, qsl[lo] <= token).
-  const int lane = threadIdx.x & 63;
-  int lo = 0, hi = a.num_seqs - 1;
-  while (hi > lo) {
-    const int step = (hi - lo + 64) / 64;
-    const int cand = lo + lane * step;
-    const uint64_t ok = __ballot(cand <= hi && a.qsl[cand] <= token);
-    lo += (63 - __builtin_clzll(ok)) * step;
-    hi = min(hi, lo + step - 1);
+  int lo = 0;
+  if (a.num_tokens == a.num_seqs && a.max_query_len == 1) {
+    // one query token per sequence (the counts leave no other way): token i
+    // is sequence i's, with no search
+    lo = token;
+  } else {
+    // sequence of this token: last i with qsl[i] <= token.  A 64-way search:
+    // each round every lane probes one candidate and a ballot keeps the last
+    // one at or before the token (qsl is non-decreasing, qsl[lo] <= token).
+    const int lane = threadIdx.x & 63;
+    int hi = a.num_seqs - 1;
+    while (hi > lo) {
+      const int step = (hi - lo + 64) / 64;
+      const int cand = lo + lane * step;
+      const uint64_t ok = __ballot(cand <= hi && a.qsl[cand] <= token);
+      lo += (63 - __builtin_clzll(ok)) * step;
+      hi = min(hi, lo + step - 1);
+    }
   }
   const int i = uniform(lo);
   const int q0 = a.qsl[i];
@@ -382,10 +389,9 @@ __global__ __launch_bounds__(256) void reduce_kernel(AttnArgs a) {
     const int head = hg * HPB + static_cast<int>(threadIdx.x) / LPH;
     if (head >= a.num_q_heads) break;
     const int64_t row = list0 + static_cast<int64_t>(head) * list_len;
-    // One pass over the partials, eight at a time (all their loads issued
+    // One pass over the partials, PG at a time (all their loads issued
     // together): the running max moves to the group's max and what was summed
     // so far is rescaled to it.
-    constexpr int PG = 8;
     float M = -__builtin_inff();
     float den = 0.f;
     f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -426,9 +432,16 @@ static void launch_reduce(const AttnArgs& a, hipStream_t stream) {
   constexpr int HPB = 4 * (64 / (D / 4));
   // a step with many tokens (prompt chunks) has few that need a merge: one
   // workgroup per token then, so that the rest cost one early exit each
+  const bool many = a.num_tokens >= PA_REDUCE_MANY_TOKENS;
   const int groups = (a.num_q_heads + HPB - 1) / HPB;
-  const dim3 grid(a.num_tokens, a.num_tokens >= PA_REDUCE_MANY_TOKENS ? 1 : groups);
-  hipLaunchKernelGGL((reduce_kernel<OT, D>), grid, dim3(256), 0, stream, a);
+  const dim3 grid(a.num_tokens, many ? 1 : groups);
+  // Rows with more than 8 partials (long contexts, a shared prefix's pass)
+  // read 32 per round: fewer dependent load rounds.  Steps with many tokens
+  // keep 8: the wider group's registers slow their early exits.
+  if (!many && (a.dec_parts > 8 || a.chunk_parts > 8))
+    hipLaunchKernelGGL((reduce_kernel<OT, D, 32>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((reduce_kernel<OT, D, 8>), grid, dim3(256), 0, stream, a);
 }
 
 // plan (with the step's cache write when `write` is given) -> [shared-prefix
