@@ -251,9 +251,15 @@ __device__ __forceinline__ void plan_block(AttnArgs a) {
   auto place = [&](int base, int j, int list, int t, int p, int bucket) {
     const int pos = atomicAdd(&hist[list][bucket], 1);
     if (pos >= (list ? a.max_citems : a.max_items)) return;   // only with metadata beyond the host bounds
-    int32_t* out = list ? a.citems : a.items;
-    out[2 * pos] = base + j;
-    out[2 * pos + 1] = static_cast<int32_t>((static_cast<uint32_t>(t) << 16) | static_cast<uint32_t>(p));
+    const int32_t tp = static_cast<int32_t>((static_cast<uint32_t>(t) << 16) | static_cast<uint32_t>(p));
+    if (list) {
+      a.citems[2 * pos] = base + j;
+      a.citems[2 * pos + 1] = tp;
+    } else {
+      // decode items also carry L (clipped to max_seq_len) and q_len
+      *reinterpret_cast<int4*>(a.items + kDecodeItemWords * static_cast<int64_t>(pos)) =
+          int4{base + j, tp, sL[j], sQ[j]};
+    }
   };
   for (int base = 0; base < a.num_seqs; base += 1024) {
     if (!one_batch) load_batch(base);

@@ -65,8 +65,8 @@ struct PartTable {
 // run of consecutive dims of its V row (VGeo): one instruction covers four
 // consecutive keys' whole rows, and the runs are transposed in registers.
 template <int CT, int KV, int D, int BS, int PF16, int PF8, bool STREAM>
-__device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, int part, int split_s, int h,
-                                          int lane) {
+__device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, int part, int L, int ql,
+                                          int split_s, int h, int lane) {
   constexpr int EBQ = Bytes<CT>::v;
   constexpr int EBK = Bytes<KV>::v;
   constexpr int KS = D / 32;     // K-steps of the QK^T product
@@ -76,9 +76,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   const int r = lane & 15;
   const int lg = lane >> 4;
 
-  const int L = min(a.seq_lens[i], a.max_seq_len);
   const int q0 = a.qsl[i];
-  const int ql = a.qsl[i + 1] - q0;
   const int G = a.group;
   const int rows = ql * G;
   const int row0 = tile * kTileRows;
@@ -339,11 +337,12 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int fi
     constexpr int PFD = D == 256 ? 1 : PF16;
     const int e = w / a.num_kv_heads;
     const int h = w - e * a.num_kv_heads;
-    const int i = uniform(a.items[2 * e]);
-    const int tp = uniform(a.items[2 * e + 1]);
+    const int4 rec = *reinterpret_cast<const int4*>(a.items + kDecodeItemWords * static_cast<int64_t>(e));
+    const int i = uniform(rec.x);
+    const int tp = uniform(rec.y);
     // (tile, partition) are the unsigned 16-bit halves of tp: tiles reach 0xFFFF
-    attn_item<CT, KV, D, BS, PFD, PF8, STREAM>(
-        a, i, static_cast<int>(static_cast<uint32_t>(tp) >> 16), tp & 0xFFFF, split_s, h, lane);
+    attn_item<CT, KV, D, BS, PFD, PF8, STREAM>(a, i, static_cast<int>(static_cast<uint32_t>(tp) >> 16), tp & 0xFFFF,
+                                               uniform(rec.z), uniform(rec.w), split_s, h, lane);
     w = -1;
   }
 }

@@ -35,6 +35,11 @@ enum DebugCode : int32_t {
 // q head) pairs of one sequence and kv head.
 constexpr int kTileRows = 16;
 
+// A decode item's record: sequence, (row tile << 16 | item of the tile's cut),
+// and the sequence's context length and query count as the plan read them, so
+// that an item's first loads need not wait for the sequence's metadata.
+constexpr int kDecodeItemWords = 4;
+
 // Keys of one context partition handled by one decode work item.  A row
 // whose keys span more than one partition gets partial (max, sum, acc)
 // results that a log-sum-exp reduce merges.  Longer partitions mean fewer
@@ -208,7 +213,7 @@ inline int64_t max_work_items(int64_t num_seqs, int64_t num_tokens, int64_t grou
 // Workspace carve-up (byte offsets, each 256-byte aligned).
 struct WorkspaceLayout {
   size_t header;   // int32 [64]: [0]/[1] decode work counter/count, [2]/[3] chunk's, [4] prefix pass's; [6] fused decode workgroups, [7] split partitions per row tile
-  size_t items;    // int32x2 [max_items]: decode items (seq, tile << 16 | partition; unsigned halves)
+  size_t items;    // int32x4 [max_items]: decode items (seq, tile << 16 | partition with unsigned halves, L, q_len)
   size_t citems;   // int32x2 [max_citems]: chunk items (seq, row block << 16 | partition)
   size_t part_m;   // float [rows]: running max (log2 units) per partition
   size_t part_l;   // float [rows]: softmax denominator per partition
@@ -318,7 +323,7 @@ inline WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_tokens, in
   const size_t rows = static_cast<size_t>(w.part_rows);
   size_t off = 0;
   w.header = off;   off = align256(off + 64 * sizeof(int32_t));
-  w.items = off;    off = align256(off + static_cast<size_t>(w.max_items) * 2 * sizeof(int32_t));
+  w.items = off;    off = align256(off + static_cast<size_t>(w.max_items) * kDecodeItemWords * sizeof(int32_t));
   w.citems = off;   off = align256(off + static_cast<size_t>(w.max_citems) * 2 * sizeof(int32_t));
   w.part_m = off;   off = align256(off + rows * sizeof(float));
   w.part_l = off;   off = align256(off + rows * sizeof(float));

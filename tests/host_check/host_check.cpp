@@ -82,7 +82,7 @@ void check_layout(const pa::AttnArgs& a, uintptr_t ws, size_t bytes, int32_t d) 
   auto at = [](const void* p) { return reinterpret_cast<uintptr_t>(p); };
   CHECK(at(a.header) == ws);
   CHECK(at(a.items) >= ws + 64 * 4 && at(a.items) % 256 == 0);
-  CHECK(at(a.items) + static_cast<uintptr_t>(a.max_items) * 8 <= at(a.citems));
+  CHECK(at(a.items) + static_cast<uintptr_t>(a.max_items) * 16 <= at(a.citems));
   CHECK(at(a.citems) + static_cast<uintptr_t>(a.max_citems) * 8 <= at(a.part_m));
   // every row's partial list: decode rows at most (slots) x Hq x dec_parts,
   // then chunk rows T x Hq x chunk_parts from chunk_row_base (0 and equal
