@@ -96,3 +96,68 @@ def test_bound_call_equals_the_plain_call():
     torch.cuda.synchronize()
     assert np.array_equal(got, ref)
     assert np.array_equal(_bits(b.k_cache), _bits(a.k_cache)) and np.array_equal(_bits(b.v_cache), _bits(a.v_cache))
+
+
+def _tiny_bf16():
+    return build("wa_edge", 21, [40, 300, 17, 1000], [1, 2, 1, 1], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                 block_size=16, kv_dtype="bf16")
+
+
+def test_joint_call_with_nothing_to_write():
+    # no new rows (null key/value/slot pointers, 0 tokens): the attention alone
+    w = _tiny_bf16()
+    a = wd.stage(w)
+    ref = _bits(a.attend())
+    b = wd.stage(w)
+    e = b.new_key[:0]
+    out = pa.write_and_attend(e, b.new_value[:0], b.new_slots[:0], b.q, b.k_cache, b.v_cache, b.block_tables,
+                              b.seq_lens, b.query_start_loc, w.scale, max_seq_len=w.max_seq_len,
+                              max_query_len=w.max_query_len, out=torch.full_like(b.q, float("nan")),
+                              workspace=b.workspace)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(out), ref)
+    assert np.array_equal(_bits(b.k_cache), _bits(a.k_cache)) and np.array_equal(_bits(b.v_cache), _bits(a.v_cache))
+
+
+def test_joint_call_with_no_query_rows():
+    # writes but an empty step (no sequences): the cache write alone
+    w = _tiny_bf16()
+    a = wd.stage(w, write_new=False)
+    a.write_new()
+    torch.cuda.synchronize()
+    b = wd.stage(w, write_new=False)
+    dev = b.q.device
+    q0 = b.q[:0]
+    out = pa.write_and_attend(b.new_key, b.new_value, b.new_slots, q0, b.k_cache, b.v_cache,
+                              torch.zeros(0, b.block_tables.shape[1], dtype=torch.int32, device=dev),
+                              torch.zeros(0, dtype=torch.int32, device=dev), torch.zeros(1, dtype=torch.int32, device=dev),
+                              w.scale, max_seq_len=w.max_seq_len, max_query_len=1, out=torch.empty_like(q0),
+                              workspace=b.workspace)
+    torch.cuda.synchronize()
+    assert out.numel() == 0
+    assert np.array_equal(_bits(b.k_cache), _bits(a.k_cache)) and np.array_equal(_bits(b.v_cache), _bits(a.v_cache))
+
+
+def test_joint_call_skips_negative_slots():
+    # rows whose slot is negative are not written, in the joint call as in
+    # pa_reshape_and_cache: every other new row lands, the skipped slots keep
+    # what the pool held (here the poison), and both calls give one output
+    w = _tiny_bf16()
+    a = wd.stage(w, write_new=False)
+    b = wd.stage(w, write_new=False)
+    slots = a.new_slots.clone()
+    slots[1] = -1
+    slots[3] = -7
+    pa.reshape_and_cache(a.new_key, a.new_value, a.k_cache, a.v_cache, slots, w.k_scale, w.v_scale)
+    ref = _bits(a.attend())
+    out = pa.write_and_attend(b.new_key, b.new_value, slots, b.q, b.k_cache, b.v_cache, b.block_tables,
+                              b.seq_lens, b.query_start_loc, w.scale, max_seq_len=w.max_seq_len,
+                              max_query_len=w.max_query_len, out=torch.full_like(b.q, float("nan")),
+                              workspace=b.workspace)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(b.k_cache), _bits(a.k_cache)) and np.array_equal(_bits(b.v_cache), _bits(a.v_cache))
+    # NaN-poisoned skipped slots make NaN rows on both sides: compare bits
+    assert np.array_equal(_bits(out), ref)
+    kb = _bits(b.k_cache)
+    s = int(a.new_slots[1].item())
+    assert np.all(kb[s // w.block_size, :, s % w.block_size, :] == w.poison())
