@@ -243,6 +243,7 @@ __device__ __forceinline__ void chunk_items(const AttnArgs& a, int first, int ba
   while (true) {
     int w = first;
     if (w < 0) {
+      if (base >= total) break;   // every item was dealt out: a draw could only come back empty
       if (tid == 0) slot = atomicAdd(a.header + (prefix ? 4 : 2), 1);
       __syncthreads();
       w = base + uniform(slot);

@@ -319,7 +319,9 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
 // (`first`, -1 for none): the first round costs no atomic, so a short step is
 // not held up by a queue of atomics on one counter.  After that the wave
 // draws item base + k from the counter, and returns once it passes the
-// item count.
+// item count -- or at once when base already does: with every item dealt
+// out, a draw could only come back empty, and the waves' last draws would
+// all queue on the counter together.
 template <int CT, int KV, int D, int BS, int PF16, int PF8, bool STREAM>
 __device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int first, int base) {
   const int64_t total = static_cast<int64_t>(uniform(a.header[1])) * a.num_kv_heads;
@@ -327,6 +329,7 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int fi
   int w = first;
   while (true) {
     if (w < 0) {
+      if (base >= total) break;
       int k = 0;
       if (lane == 0) k = atomicAdd(a.header, 1);
       w = base + uniform(__shfl(k, 0));
