@@ -58,11 +58,15 @@ __device__ __forceinline__ void plan_block(AttnArgs a) {
   int S = 0;                                             // tail split: partitions each row tile cuts
   const bool one_batch = a.num_seqs <= 1024;
 
-  // batch of sequences [base, base + 1024): fill the per-sequence table and the scan
-  auto load_batch = [&](int base) {
+  // batch of sequences [base, base + 1024): fill the per-sequence table and
+  // the scan (`again`: the same batch counted again, L and q_len from the table)
+  auto load_batch = [&](int base, bool again) {
     const int i = base + tid;
     int n = 0, L = 0, ql = 0, np = 0;
-    if (i < a.num_seqs) {
+    if (again) {
+      L = sL[tid];
+      ql = sQ[tid];
+    } else if (i < a.num_seqs) {
       L = min(a.seq_lens[i], a.max_seq_len);
       ql = a.qsl[i + 1] - a.qsl[i];
 #if PA_DEBUG
@@ -152,7 +156,7 @@ __device__ __forceinline__ void plan_block(AttnArgs a) {
   // With fewer than kSplitItemsPerWave per decode wave, S follows from the
   // row tiles, and the batch is counted again with the split.
   if (one_batch) {
-    load_batch(0);
+    load_batch(0, false);
     if (a.split_f > 1 && static_cast<int64_t>(scan[1023]) * a.num_kv_heads <
                              static_cast<int64_t>(kSplitItemsPerWave) * a.decode_waves) {
       const int own = sL[tid] - a.prefix_len;
@@ -167,7 +171,7 @@ __device__ __forceinline__ void plan_block(AttnArgs a) {
         const int64_t pk = static_cast<int64_t>(pairs) * a.num_kv_heads;
         const int64_t want = static_cast<int64_t>(ceilf(kSplitRounds * a.decode_waves / static_cast<float>(pk)));
         S = static_cast<int>(want < a.split_max ? want : a.split_max);
-        load_batch(0);                                   // (its first barrier orders the wtot reads)
+        load_batch(0, true);                             // (its first barrier orders the wtot reads)
       }
     }
   }
@@ -177,7 +181,7 @@ __device__ __forceinline__ void plan_block(AttnArgs a) {
   constexpr int KEEP = 4;
   int cj[KEEP], cl[KEEP], ct[KEEP], cp[KEEP], cb2[KEEP];
   for (int base = 0; base < a.num_seqs; base += 1024) {
-    if (!one_batch) load_batch(base);
+    if (!one_batch) load_batch(base, false);
     const int nk = scan[1023];
 #pragma unroll
     for (int m = 0; m < KEEP; ++m) {
@@ -262,7 +266,7 @@ __device__ __forceinline__ void plan_block(AttnArgs a) {
     }
   };
   for (int base = 0; base < a.num_seqs; base += 1024) {
-    if (!one_batch) load_batch(base);
+    if (!one_batch) load_batch(base, false);
     const int nk = scan[1023];
 #pragma unroll
     for (int m = 0; m < KEEP; ++m) {
