@@ -33,28 +33,6 @@ __device__ __forceinline__ bool is_chunk_seq(const AttnArgs& a, int rows) {
   return a.chunk_path && rows >= kChunkMinRows;
 }
 
-// The decode items of one row tile of a sequence with `own` keys past the
-// shared prefix: partitions of P keys, except that the last S of them (from
-// partition ps on) are cut into items of P / F keys.  Item j < ps covers keys
-// [j P, j P + P), item j >= ps covers [ps P + (j - ps) P/F, + P/F); item j
-// writes partial slot j, so a row's slots are its items in key order.  The
-// plan, the decode kernel and the merge all derive the cut from (own, P, F, S).
-struct DecodeCut {
-  int P, Pf, ps, n;   // n: the tile's items
-  __device__ __forceinline__ DecodeCut(int own, int partition, int F, int S) {
-    P = partition;
-    Pf = partition / F;
-    const int npc = own > 0 ? (own + P - 1) / P : 0;
-    ps = F > 1 ? max(npc - S, 0) : npc;
-    const int rest = own - ps * P;   // keys of the split partitions
-    n = ps + (rest > 0 ? (rest + Pf - 1) / Pf : 0);
-  }
-  __device__ __forceinline__ int start(int j) const { return j < ps ? j * P : ps * P + (j - ps) * Pf; }
-  __device__ __forceinline__ int len(int j) const { return j < ps ? P : Pf; }
-  // the item holding key k (k >= 0)
-  __device__ __forceinline__ int item_of(int k) const { return k < ps * P ? k / P : ps + (k - ps * P) / Pf; }
-};
-
 // First partial row of (token, q head) -- the row of sequence seq whose
 // local query index is `local` -- in the workspace's partial lists (the
 // layout of WorkspaceLayout: decode-routed rows by sequence slot or token,

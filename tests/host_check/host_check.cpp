@@ -308,10 +308,47 @@ void random_sizes() {
 
 }  // namespace
 
+// The tail split's cut of a row tile's keys (pa::DecodeCut), which the plan,
+// the decode items and the merge each derive on their own: its items tile
+// [0, own) in key order with no gap or overlap, item_of maps every key to
+// the item that holds it, the last item is not empty, only the last S
+// partitions are cut, and the item count stays within the workspace's
+// per-tile bound ceil(own / P) + split_max * (F - 1).
+void decode_cut() {
+  const int parts[] = {512, 1024, 2048};
+  for (int P : parts)
+    for (int F = 1; F <= 8; F *= 2) {
+      const int smax = F > 1 ? pa::kSplitItems / F : 0;
+      for (int S = 0; S <= smax + 2; ++S)
+        for (int own = 0; own <= 5 * P + 3; own += (own < 3 * P ? 37 : 1)) {
+          const int s = S < smax ? S : smax;   // the plan caps S at split_max
+          const pa::DecodeCut cut(own, P, F, s);
+          const int npc = (own + P - 1) / P;
+          CHECK(cut.n <= npc + smax * (F - 1));
+          CHECK(F > 1 || cut.n == npc);
+          CHECK(cut.ps == (F > 1 ? (npc > s ? npc - s : 0) : npc));
+          if (own == 0) {
+            CHECK(cut.n == 0);
+            continue;
+          }
+          CHECK(cut.start(0) == 0);
+          for (int j = 0; j + 1 < cut.n; ++j) CHECK(cut.start(j + 1) == cut.start(j) + cut.len(j));
+          CHECK(cut.start(cut.n - 1) < own && cut.start(cut.n - 1) + cut.len(cut.n - 1) >= own);
+          for (int j = 0; j < cut.n; ++j) {
+            CHECK(cut.len(j) == (j < cut.ps ? P : P / F));
+            const int end = cut.start(j) + cut.len(j) < own ? cut.start(j) + cut.len(j) : own;
+            CHECK(cut.item_of(cut.start(j)) == j && cut.item_of(end - 1) == j);
+          }
+          CHECK(cut.item_of(own - 1) == cut.n - 1);
+        }
+    }
+}
+
 int main() {
   argument_errors();
   valid_calls();
   random_sizes();
+  decode_cut();
   if (g_fail) {
     fprintf(stderr, "host_check: %d checks failed\n", g_fail);
     return 1;
