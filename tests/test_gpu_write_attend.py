@@ -161,3 +161,62 @@ def test_joint_call_skips_negative_slots():
     kb = _bits(b.k_cache)
     s = int(a.new_slots[1].item())
     assert np.all(kb[s // w.block_size, :, s % w.block_size, :] == w.poison())
+
+
+def _joint_against_oracle(w, prefix, label):
+    import oracle
+    kp, vp = oracle.cache.fill_pools(w)
+    ref = oracle.attention.paged_attention(w.q_values(), w.q_dtype, kp, vp, w.kv_dtype, w.block_tables, w.seq_lens,
+                                           w.query_start_loc, w.block_size, w.scale, w.k_scale, w.v_scale)
+    step = wd.stage(w, write_new=False)
+    if prefix:
+        step.use_shared_prefix(prefix)
+    out = step.write_and_attend(out=torch.full_like(step.q, float("nan")))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(step.k_cache), kp) and np.array_equal(_bits(step.v_cache), vp), f"{label}: pools"
+    got = codecs.decode(_bits(out), w.q_dtype)
+    tol = {"f32": 2e-3, "f16": 2e-3, "bf16": 1e-2, "fp8_e4m3": 4e-2}[w.kv_dtype]
+    assert not np.isnan(got).any(), f"{label}: NaN"
+    err = float(np.abs(got - ref).max())
+    say(f"{label}: max-abs err {err:.2e} (tol {tol:.0e})")
+    assert err <= tol, f"{label}: {err}"
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shared_prefix_steps_through_the_joint_call(seed):
+    # seeded cascade steps (prefix of whole blocks; per sequence a decode
+    # token, a short run or a prompt chunk past it) with their cache write
+    rng = np.random.default_rng([seed, 17])
+    d = int(rng.choice([64, 128, 256]))
+    B = int(rng.choice([16, 32, 64]))
+    kv = str(rng.choice(["f16", "bf16", "fp8_e4m3"]))
+    q = {"f16": "f16", "bf16": "bf16"}.get(kv) or str(rng.choice(["bf16", "f16"]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.choice([1, 2, 4]))
+    P = B * int(rng.integers(1, 6000 // B))
+    n = int(rng.integers(1, 13))
+    qlens = [int(rng.choice([1, 1, 1, int(rng.integers(2, 9)), int(rng.integers(16, 160))])) for _ in range(n)]
+    lens = [P + ql + int(rng.integers(0, 1200)) for ql in qlens]
+    sc = float(rng.choice([2.0 ** -5, 0.05])) if kv == "fp8_e4m3" else 1.0
+    w = build("wa_pfx_rand", 500 + seed, lens, qlens, num_q_heads=G * hkv, num_kv_heads=hkv, head_dim=d,
+              block_size=B, kv_dtype=kv, q_dtype=q, k_scale=sc, v_scale=sc, shared_prefix_len=P)
+    _joint_against_oracle(w, P, f"joint cascade seed={seed} {kv}/{q} d={d} B={B} G={G} Hkv={hkv} P={P} n={n}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_fused_mixed_steps_through_the_joint_call(seed):
+    # seeded mixed steps that take the fused launch (16-bit q, head dim <= 128,
+    # prompt chunks of at least 65 rows per kv head) with their cache write
+    rng = np.random.default_rng([seed, 19])
+    d = int(rng.choice([64, 128]))
+    B = int(rng.choice([16, 32, 64]))
+    kv = str(rng.choice(["f16", "bf16", "fp8_e4m3"]))
+    q = {"f16": "f16", "bf16": "bf16"}.get(kv) or str(rng.choice(["bf16", "f16"]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    chunks = [(int(rng.integers(0, 8000)), int(rng.integers(-(-65 // G), 400))) for _ in range(int(rng.integers(1, 4)))]
+    sc = float(rng.choice([2.0 ** -5, 0.05])) if kv == "fp8_e4m3" else 1.0
+    w = random_mixed(600 + seed, num_decode=int(rng.integers(1, 120)), chunk_specs=chunks,
+                     max_decode_len=int(rng.integers(10, 5000)), num_q_heads=G * hkv, num_kv_heads=hkv, head_dim=d,
+                     block_size=B, kv_dtype=kv, q_dtype=q, k_scale=sc, v_scale=sc, name="wa_mixed_rand")
+    _joint_against_oracle(w, 0, f"joint fused seed={seed} {kv}/{q} d={d} B={B} G={G} Hkv={hkv} chunks={chunks}")
