@@ -51,9 +51,19 @@ __device__ __forceinline__ void plan_block(AttnArgs a) {
   __shared__ int sL[1024], sQ[1024], sNP[1024];          // per sequence: L, q_len, partitions (<0: chunk list)
   __shared__ int total[2];
   __shared__ int wtot[16];                               // per-wave totals of the batch scan
+  __shared__ int hset[kShareSlots];                      // first blocks seen (one batch), -1 free
+  __shared__ int shared_blocks;
   const int tid = threadIdx.x;
   const int G = a.group;
   for (int x = tid; x < 2 * NBMAX; x += 1024) hist[x / NBMAX][x % NBMAX] = 0;
+  // sharing is looked for in steps of one batch with at least kShareMinSeqs
+  // sequences and no declared prefix (a caller that declares one has said
+  // what is shared; the decode items then read only the blocks past it)
+  const bool find_sharing = a.num_seqs <= 1024 && a.num_seqs >= kShareMinSeqs && a.prefix_len == 0;
+  if (find_sharing)
+    for (int x = tid; x < kShareSlots; x += 1024) hset[x] = -1;
+  if (tid == 0) shared_blocks = 0;
+  int first_block = -1;                                  // this thread's sequence's first block
 
   int S = 0;                                             // tail split: partitions each row tile cuts
   const bool one_batch = a.num_seqs <= 1024;
@@ -69,6 +79,8 @@ __device__ __forceinline__ void plan_block(AttnArgs a) {
     } else if (i < a.num_seqs) {
       L = min(a.seq_lens[i], a.max_seq_len);
       ql = a.qsl[i + 1] - a.qsl[i];
+      if (find_sharing && a.max_blocks_per_seq > 0)
+        first_block = a.block_tables[static_cast<int64_t>(i) * a.max_blocks_per_seq];
 #if PA_DEBUG
       // debug build: a sequence whose metadata breaks the contract is
       // recorded and skipped (no work items)
@@ -157,6 +169,25 @@ __device__ __forceinline__ void plan_block(AttnArgs a) {
   // row tiles, and the batch is counted again with the split.
   if (one_batch) {
     load_batch(0, false);
+    // Block sharing (find_sharing): do two of the batch's decode-routed
+    // sequences start in the same block?  Then their tables share
+    // blocks, and the decode kernel deals its items by XCD so that each L2
+    // holds one class of kv heads (decode_items_dealt).  A hash set in LDS of
+    // the first blocks finds a repeat; the loads were issued beside the
+    // sequence's metadata.  (Load-balancing only: no result depends on it.)
+    if (find_sharing && tid < a.num_seqs && sQ[tid] > 0 && sL[tid] > 0 && sNP[tid] > 0 && first_block >= 0) {
+      int slot = static_cast<int>((static_cast<uint32_t>(first_block) * 2654435761u) >> (32 - kShareBits));
+      for (int probe = 0; probe < kShareSlots; ++probe) {
+        const int prev = atomicCAS(&hset[slot], -1, first_block);
+        if (prev == -1) break;
+        if (prev == first_block) {
+          shared_blocks = 1;
+          break;
+        }
+        slot = (slot + 1) & (kShareSlots - 1);
+      }
+    }
+    if (find_sharing) __syncthreads();                   // (uniform)
     if (a.split_f > 1 && static_cast<int64_t>(scan[1023]) * a.num_kv_heads <
                              static_cast<int64_t>(kSplitItemsPerWave) * a.decode_waves) {
       const int own = sL[tid] - a.prefix_len;
@@ -289,7 +320,9 @@ __device__ __forceinline__ void plan_block(AttnArgs a) {
     a.header[4] = 0;
     a.header[3] = static_cast<int32_t>(total[1] < a.max_citems ? total[1] : a.max_citems);
     a.header[7] = S;
+    a.header[kShareWord] = shared_blocks;
   }
+  if (tid < 8) a.header[kXcdCounters + tid] = 0;
 }
 
 __global__ __launch_bounds__(1024) void plan_kernel(AttnArgs a) { plan_block(a); }

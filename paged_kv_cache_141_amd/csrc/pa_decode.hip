@@ -11,13 +11,21 @@
 namespace pa {
 
 // Wave g starts on item g, then draws items from a counter until the list
-// is done.  V is read with the non-temporal hint (STREAM; K without it).
+// is done -- or, when the plan found decode-routed sequences starting in the
+// same block (their tables share blocks) and the grid has at least eight
+// waves, from its XCD's class of items (decode_items_dealt).  V is read with
+// the non-temporal hint (STREAM; K without it).
 template <int CT, int KV, int D, int BS>
 __global__ __launch_bounds__(64, PA_DECODE_WAVES_PER_SIMD) void attn_kernel(AttnArgs a) {
   constexpr bool STREAM = true;
   // fp8 at head dim 256: two steps in flight (a deeper ring does not fit the registers)
   constexpr int PF8 = D == 256 ? 2 : PA_DECODE_PREFETCH_FP8;
-  decode_items<CT, KV, D, BS, PA_DECODE_PREFETCH, PF8, STREAM>(a, threadIdx.x, blockIdx.x, gridDim.x);
+  // the plan's header words, read together
+  const int64_t total = decode_total(a);
+  const int split_s = uniform(a.header[7]);
+  const int shared = uniform(a.header[kShareWord]);
+  decode_items_dealt<CT, KV, D, BS, PA_DECODE_PREFETCH, PF8, STREAM>(a, threadIdx.x, blockIdx.x, gridDim.x, total,
+                                                                     split_s, shared != 0 && gridDim.x >= 8);
 }
 
 template <int CT, int KV, int D, int BS>

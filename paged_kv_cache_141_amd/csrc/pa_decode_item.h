@@ -314,8 +314,31 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
   }
 }
 
-// A wave runs decode work items; item w covers list entry w / Hkv and kv
-// head w % Hkv.  Items 0 .. base-1 are dealt out one per wave in advance
+// Decode item w: list entry w / Hkv, kv head w % Hkv.
+template <int CT, int KV, int D, int BS, int PF16, int PF8, bool STREAM>
+__device__ __forceinline__ void decode_item(const AttnArgs& a, int64_t w, int split_s, int lane) {
+  // head dim 256: a 32-key step is 32 KiB of 16-bit K/V, so one step is in
+  // flight while the other computes
+  constexpr int PFD = D == 256 ? 1 : PF16;
+  const int64_t e = w / a.num_kv_heads;
+  const int h = static_cast<int>(w - e * a.num_kv_heads);
+  const int4 rec = *reinterpret_cast<const int4*>(a.items + kDecodeItemWords * e);
+  const int i = uniform(rec.x);
+  const int tp = uniform(rec.y);
+  // (tile, partition) are the unsigned 16-bit halves of tp: tiles reach 0xFFFF
+  attn_item<CT, KV, D, BS, PFD, PF8, STREAM>(a, i, static_cast<int>(static_cast<uint32_t>(tp) >> 16), tp & 0xFFFF,
+                                             uniform(rec.z), uniform(rec.w), split_s, h, lane);
+}
+
+// The decode items of a launch: the list's entries (plan header word 1)
+// times the kv heads.
+__device__ __forceinline__ int64_t decode_total(const AttnArgs& a) {
+  return static_cast<int64_t>(uniform(a.header[1])) * a.num_kv_heads;
+}
+
+// A wave runs decode work items (`total` of them, from decode_total;
+// `split_s` the tail split's partitions per row tile, plan header word 7);
+// item w covers list entry w / Hkv and kv head w % Hkv.  Items 0 .. base-1 are dealt out one per wave in advance
 // (`first`, -1 for none): the first round costs no atomic, so a short step is
 // not held up by a queue of atomics on one counter.  After that the wave
 // draws item base + k from the counter, and returns once it passes the
@@ -323,9 +346,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, int i, int tile, in
 // out, a draw could only come back empty, and the waves' last draws would
 // all queue on the counter together.
 template <int CT, int KV, int D, int BS, int PF16, int PF8, bool STREAM>
-__device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int first, int base) {
-  const int64_t total = static_cast<int64_t>(uniform(a.header[1])) * a.num_kv_heads;
-  const int split_s = uniform(a.header[7]);
+__device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int first, int base, int64_t total,
+                                             int split_s) {
   int w = first;
   while (true) {
     if (w < 0) {
@@ -335,18 +357,40 @@ __device__ __forceinline__ void decode_items(const AttnArgs& a, int lane, int fi
       w = base + uniform(__shfl(k, 0));
     }
     if (w >= total) break;
-    // head dim 256: a 32-key step is 32 KiB of 16-bit K/V, so one step is in
-    // flight while the other computes
-    constexpr int PFD = D == 256 ? 1 : PF16;
-    const int e = w / a.num_kv_heads;
-    const int h = w - e * a.num_kv_heads;
-    const int4 rec = *reinterpret_cast<const int4*>(a.items + kDecodeItemWords * static_cast<int64_t>(e));
-    const int i = uniform(rec.x);
-    const int tp = uniform(rec.y);
-    // (tile, partition) are the unsigned 16-bit halves of tp: tiles reach 0xFFFF
-    attn_item<CT, KV, D, BS, PFD, PF8, STREAM>(a, i, static_cast<int>(static_cast<uint32_t>(tp) >> 16), tp & 0xFFFF,
-                                               uniform(rec.z), uniform(rec.w), split_s, h, lane);
+    decode_item<CT, KV, D, BS, PF16, PF8, STREAM>(a, w, split_s, lane);
     w = -1;
+  }
+}
+
+// The decode kernel's item loop: wave b of nw starts on item b, dealt out in
+// advance like decode_items' first round, and then draws -- from the one
+// counter, or, with `by_xcd`, from its XCD's class of items.  The class form
+// is for steps whose block tables share blocks.  Workgroups (here one wave
+// each) go to the chip's eight XCDs in turn, each XCD with its own L2, so
+// wave b runs on XCD b % 8; it takes only items of class b % 8 (item w is
+// in class w % 8, so a class holds whole kv heads when 8 divides Hkv, and
+// one XCD's L2 holds the shared blocks of its heads instead of every XCD's
+// L2 holding all of them), drawing them from its class's counter (header
+// words kXcdCounters .. +7, zeroed by the plan).  Every item runs once when
+// the grid has at least eight waves (each class then has a wave); the
+// caller asks for classes only then.  Without shared blocks the classes are
+// slower: an XCD held to some heads reads fixed offsets of every block.  One
+// call site of the item body for both forms keeps the kernel's code small.
+template <int CT, int KV, int D, int BS, int PF16, int PF8, bool STREAM>
+__device__ __forceinline__ void decode_items_dealt(const AttnArgs& a, int lane, int b, int nw, int64_t total,
+                                                   int split_s, bool by_xcd) {
+  const int c = b & 7;
+  const int64_t dealt = by_xcd ? (nw - c + 7) >> 3 : nw;    // waves drawing from the same counter
+  const int64_t stride = by_xcd ? 8 : 1;
+  const int64_t first = by_xcd ? c : 0;                      // the counter's items: first + stride * m
+  int32_t* const counter = by_xcd ? a.header + kXcdCounters + c : a.header;
+  int64_t w = b;
+  while (w < total) {
+    decode_item<CT, KV, D, BS, PF16, PF8, STREAM>(a, w, split_s, lane);
+    if (first + stride * dealt >= total) break;             // every item was dealt out
+    int k = 0;
+    if (lane == 0) k = atomicAdd(counter, 1);
+    w = first + stride * (dealt + uniform(__shfl(k, 0)));
   }
 }
 

@@ -40,6 +40,21 @@ constexpr int kTileRows = 16;
 // that an item's first loads need not wait for the sequence's metadata.
 constexpr int kDecodeItemWords = 4;
 
+// Workspace header words: [0]/[1] decode work counter and item count,
+// [2]/[3] the chunk list's, [4] the shared-prefix pass's counter, [6] the
+// fused launch's decode workgroups, [7] the tail split's partitions per row
+// tile, [kShareWord] 1 when two decode-routed sequences start in the same
+// block (looked for in steps without a declared prefix), [kXcdCounters ..
+// +7] the decode kernel's per-XCD class counters.
+constexpr int kShareWord = 8;
+constexpr int kXcdCounters = 16;
+// The plan's hash set of first blocks (LDS): 2^kShareBits slots; steps of
+// fewer than kShareMinSeqs sequences are not looked at (too small for the
+// L2 to matter, and the look costs the plan about half a microsecond).
+constexpr int kShareBits = 11;
+constexpr int kShareSlots = 1 << kShareBits;
+constexpr int kShareMinSeqs = 8;
+
 // Keys of one context partition handled by one decode work item.  A row
 // whose keys span more than one partition gets partial (max, sum, acc)
 // results that a log-sum-exp reduce merges.  Longer partitions mean fewer

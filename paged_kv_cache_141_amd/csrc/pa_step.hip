@@ -32,12 +32,11 @@ __global__ __launch_bounds__(kChunkThreads, kChunkWavesPerSimd) void step_kernel
   const int nchunk = static_cast<int>(gridDim.x) - ndec;
   if (g >= ndec) {
     chunk_items<CT, KV, D, BS, kChunkPartitionFused>(a, g - ndec, nchunk, false);
-    decode_items<CT, KV, D, BS, kStepDecodePrefetch, kStepDecodePrefetchFp8, true>(a, threadIdx.x & 63, -1,
-                                                                                  ndec * kChunkWaves);
+    decode_items<CT, KV, D, BS, kStepDecodePrefetch, kStepDecodePrefetchFp8, true>(
+        a, threadIdx.x & 63, -1, ndec * kChunkWaves, decode_total(a), uniform(a.header[7]));
   } else {
-    decode_items<CT, KV, D, BS, kStepDecodePrefetch, kStepDecodePrefetchFp8, true>(a, threadIdx.x & 63,
-                                                                                  g * kChunkWaves + wave,
-                                                                                  ndec * kChunkWaves);
+    decode_items<CT, KV, D, BS, kStepDecodePrefetch, kStepDecodePrefetchFp8, true>(
+        a, threadIdx.x & 63, g * kChunkWaves + wave, ndec * kChunkWaves, decode_total(a), uniform(a.header[7]));
   }
 }
 
